@@ -1,0 +1,191 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) Stable LatentMoE layer forward.
+ *
+ * The layer (pages cited by title and section):
+ *   "Kimi K3の896エキスパートを「896人の専門家」と呼ぶと何がズレるか" (lilting.ch)
+ *     section "ルーターは計算の割当器":       s = Sigmoid(W_r x); a per-expert
+ *       balancing bias is added to s only to choose the top-k; the mixing
+ *       weights are the chosen experts' unbiased scores, normalised.
+ *     section "K3のエキスパートは896個の小型LLMではない" (its three equations
+ *       and flowchart): z = W_down x;  u = sum_{i in TopK} p_i E_i(z);
+ *       y = E_1^shared(x) + E_2^shared(x) + W_up RMSNorm(u).
+ *   "Kimi K3 テクニカルレポート" (jiwasawa.github.io), section "幅のスケーリング:
+ *     Stable LatentMoE": expert activation SiTU-GLU, taken here as
+ *     act(g, v) = c*tanh(SiLU(g)/c) * c*tanh(v/c) (c = situ_c).
+ *   "Kimi K3 ... Open Frontier Intelligence" (ai-tech-express.jp), section
+ *     "MXFP4 Quantization-Aware Training": MXFP4 weights (OCP MX v1.0 e2m1
+ *     elements, one e8m0 scale per 32 elements along K).
+ *
+ * Calling convention (all entry points):
+ *   - Every pointer argument is a DEVICE pointer (hipMalloc'd or equivalent)
+ *     unless stated; descriptors and weight structs are HOST memory read
+ *     during the call only. Device pointers must be 16-byte aligned.
+ *   - The caller owns every buffer. The library allocates no device memory:
+ *     scratch comes from the caller's workspace `ws` of at least
+ *     moe_workspace_bytes(desc, op) bytes (16-byte aligned; NULL allowed when
+ *     that size is 0). Calls that share a workspace must be stream-ordered.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream). Calls only
+ *     enqueue work and return; nothing synchronises the host.
+ *   - Arguments are validated on the host before any HIP call; a failing call
+ *     returns a negative status and enqueues nothing. moe_last_error() gives a
+ *     thread-local description. Non-finite input values are not checked; the
+ *     results for them are unspecified.
+ *
+ * Layouts (row-major, K contiguous for every weight, as an [out, in] linear):
+ *   x [T, d]            y [T, d]           z, n [T, d_lat]
+ *   W_r [E, d]          router_bias [E] fp32
+ *   W_ld [d_lat, d]     W_lu [d, d_lat]    rms_gain [d_lat] fp32 (NULL = 1)
+ *   W_g, W_v [E, F, d_lat]   W_o [E, d_lat, F]
+ *   W_gs, W_vs [S, Fs, d]    W_os [S, d, Fs]
+ *   MXFP4 weight [R, K]: data = packed bytes [R, K/2] (element 2i in the low
+ *   nibble of byte i), scale = e8m0 bytes [R, K/32].
+ *   topk_idx [T, k] int32, topk_gate [T, k] fp32 (slot order = key descending,
+ *   ties to the lower expert index).
+ *   Permutation: rows of expert e are offsets[e] .. offsets[e+1]-1 (offsets has
+ *   E+1 entries), ordered by ascending (token, slot); perm_src[row] = t*k + j;
+ *   inv_pos[t*k + j] = row.
+ *
+ * Supported dtype combinations: act = F32 with every weight F32; or act = BF16
+ * with router/shared weights BF16 and latent / expert weights BF16 or MXFP4.
+ * Other combinations return MOE_ERR_UNSUPPORTED. d, d_lat, F and Fs must be
+ * multiples of 32; 1 <= k <= E <= 4096; T >= 0 (T = 0 is an empty batch).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,   /* bad dims, NULL or misaligned pointer, k > E, ... */
+  MOE_ERR_UNSUPPORTED = -2,   /* valid but not implemented (dtype combination, sizes) */
+  MOE_ERR_WORKSPACE = -3,     /* workspace smaller than moe_workspace_bytes() */
+  MOE_ERR_HIP = -4            /* a HIP launch / runtime call failed */
+};
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype_t;
+
+/* Which entry point a workspace is sized for. */
+typedef enum {
+  MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_LATENT_DOWN = 2, MOE_OP_EXPERT_FFN = 3,
+  MOE_OP_COMBINE = 4, MOE_OP_OUTPUT = 5, MOE_OP_LAYER = 6
+} moe_op_t;
+
+typedef struct {
+  int32_t T;            /* tokens in the batch */
+  int32_t d_model;      /* d */
+  int32_t d_latent;     /* d_lat */
+  int32_t n_experts;    /* E, routed experts */
+  int32_t top_k;        /* k */
+  int32_t d_ff;         /* F, routed expert intermediate */
+  int32_t n_shared;     /* S, shared experts (may be 0) */
+  int32_t d_ff_shared;  /* Fs */
+  float situ_c;         /* SiTU-GLU cap c (> 0) */
+  float rms_eps;        /* RMSNorm epsilon (>= 0) */
+  int32_t act_dtype;      /* x, z, h, o, n, shared h, y: MOE_F32 or MOE_BF16 */
+  int32_t expert_w_dtype; /* W_g, W_v, W_o */
+  int32_t latent_w_dtype; /* W_ld, W_lu */
+  int32_t dense_w_dtype;  /* W_r, W_gs, W_vs, W_os */
+} moe_desc_t;
+
+/* A weight tensor: data (dtype of its class) and, for MXFP4 only, scales. */
+typedef struct {
+  const void* data;
+  const uint8_t* scale;
+} moe_w_t;
+
+typedef struct {
+  moe_w_t router;              /* W_r [E, d] */
+  const float* router_bias;    /* b [E] fp32 */
+  moe_w_t lat_down;            /* W_ld [d_lat, d] */
+  moe_w_t lat_up;              /* W_lu [d, d_lat] */
+  const float* rms_gain;       /* [d_lat] fp32, or NULL for a gain of 1 */
+  moe_w_t exp_gate, exp_up;    /* W_g, W_v [E, F, d_lat] */
+  moe_w_t exp_down;            /* W_o [E, d_lat, F] */
+  moe_w_t sh_gate, sh_up;      /* W_gs, W_vs [S, Fs, d] */
+  moe_w_t sh_down;             /* W_os [S, d, Fs] */
+} moe_weights_t;
+
+/* Bytes of workspace that entry point `op` needs for this descriptor
+   (0 for an invalid descriptor; check moe_check_desc first). */
+size_t moe_workspace_bytes(const moe_desc_t* desc, int op);
+
+/* Host-only validation of a descriptor: MOE_OK, MOE_ERR_INVALID_ARG or
+   MOE_ERR_UNSUPPORTED. Makes no HIP call. */
+int moe_check_desc(const moe_desc_t* desc);
+
+/* Router and top-k ("ルーターは計算の割当器").
+   For each token t: l_e = sum_k x[t][k] W_r[e][k] as the fp32 chain
+   acc = fma(x, w, acc) over k ascending from +0; s_e = sigmoid(l_e) by the
+   library's fixed IEEE-754 fp32 sequence (Cody-Waite reduction + degree-7
+   Taylor polynomial + one correctly rounded division); key_e = s_e + b_e.
+   topk_idx[t] = the k experts with the largest keys (key descending, ties to
+   the lower index); topk_gate[t][j] = s_{idx_j} / (s_{idx_0} + ... + s_{idx_{k-1}})
+   in fp32, summed in slot order. scores_opt: if non-NULL receives s [T, E] fp32.
+   x: act dtype [T, d]; router.data: dense_w dtype [E, d]. */
+int moe_route(const moe_desc_t* desc, const void* x, moe_w_t router, const float* bias,
+              int32_t* topk_idx, float* topk_gate, float* scores_opt,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* Token permutation: group the T*k (token, slot) pairs by expert (the
+   dispatch step of the flowchart: run the chosen experts).
+   counts [E], offsets [E+1], perm_src [T*k], inv_pos [T*k] as described in
+   the layout notes. Deterministic (no order decided by atomics).
+   topk_idx entries outside [0, E) are skipped (they take no row; offsets[E]
+   then counts only the valid entries); if a token lists one expert twice,
+   both entries get rows, in unspecified order between the two. */
+int moe_permute(const moe_desc_t* desc, const int32_t* topk_idx, int32_t* counts,
+                int32_t* offsets, int32_t* perm_src, int32_t* inv_pos,
+                void* ws, size_t ws_bytes, void* stream);
+
+/* Latent down-projection z = W_down x (equation z = W_down x), stored in the
+   act dtype. x [T, d]; z [T, d_lat]; lat_down: latent_w dtype. */
+int moe_latent_down(const moe_desc_t* desc, const void* x, moe_w_t lat_down, void* z,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Routed experts on the permuted rows (E_i(z) of the u equation):
+   for every row r of expert e (offsets[e] <= r < offsets[e+1]) with token
+   t = perm_src[r] / k: h = act(W_g[e] z_t, W_v[e] z_t) (stored in the act
+   dtype), o_perm[r] = W_o[e] h (act dtype, [T*k, d_lat], permuted order).
+   Only exp_gate / exp_up / exp_down of `w` are read. perm_src and offsets as
+   produced by moe_permute (offsets[E] rows are processed). */
+int moe_expert_ffn(const moe_desc_t* desc, const void* z, const int32_t* perm_src,
+                   const int32_t* offsets, const moe_weights_t* w, void* o_perm,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* Weighted combine and RMSNorm (u equation, then RMSNorm of the y equation):
+   u_t = sum_j topk_gate[t][j] * o_perm[inv_pos[t*k + j]] (fp32, j ascending);
+   n_t = u_t / sqrt(mean(u_t^2) + eps) * gain, stored in the act dtype.
+   u_out_opt: if non-NULL receives u [T, d_lat] fp32. */
+int moe_combine(const moe_desc_t* desc, const void* o_perm, const int32_t* inv_pos,
+                const float* topk_gate, const float* rms_gain, void* n_out, float* u_out_opt,
+                void* stream);
+
+/* Output (y equation): y = W_up n + sum_s W_os[s] act(W_gs[s] x, W_vs[s] x),
+   accumulated in fp32, stored in the act dtype. Reads lat_up and sh_* of `w`. */
+int moe_output(const moe_desc_t* desc, const void* x, const void* n, const moe_weights_t* w,
+               void* y, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer: route, permute, latent down, experts, combine, output.
+   y [T, d] act dtype. Optional outputs (NULL to skip): topk_idx [T, k],
+   topk_gate [T, k], counts [E]. */
+int moe_layer_forward(const moe_desc_t* desc, const moe_weights_t* w, const void* x, void* y,
+                      int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* counts_opt,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Static text of a status code. */
+const char* moe_status_string(int status);
+
+/* Thread-local text of the last failure in this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,209 @@
+"""Python binding of libmoe.so, the gfx950 Stable LatentMoE layer (C ABI in include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. PyTorch is used for device memory and the current HIP stream. The
+entry points keep the C names (moe_route, moe_permute, moe_latent_down,
+moe_expert_ffn, moe_combine, moe_output, moe_layer_forward) and take torch
+tensors (or None for optional outputs); a non-zero status raises MoeError.
+
+There is no fallback: if libmoe.so is missing, importing the binding's entry
+points raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from functools import lru_cache
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
+(MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_LATENT_DOWN, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE,
+ MOE_OP_OUTPUT, MOE_OP_LAYER) = range(7)
+
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
+
+EXPORTS = ["moe_workspace_bytes", "moe_check_desc", "moe_route", "moe_permute", "moe_latent_down",
+           "moe_expert_ffn", "moe_combine", "moe_output", "moe_layer_forward",
+           "moe_status_string", "moe_last_error"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{msg} (status {status})")
+        self.status = status
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d_model", ctypes.c_int32), ("d_latent", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("n_shared", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
+                ("situ_c", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                ("act_dtype", ctypes.c_int32), ("expert_w_dtype", ctypes.c_int32),
+                ("latent_w_dtype", ctypes.c_int32), ("dense_w_dtype", ctypes.c_int32)]
+
+
+class MoeW(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p)]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [("router", MoeW), ("router_bias", ctypes.c_void_p),
+                ("lat_down", MoeW), ("lat_up", MoeW), ("rms_gain", ctypes.c_void_p),
+                ("exp_gate", MoeW), ("exp_up", MoeW), ("exp_down", MoeW),
+                ("sh_gate", MoeW), ("sh_up", MoeW), ("sh_down", MoeW)]
+
+
+@lru_cache(maxsize=None)
+def lib():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built (run __graft_entry__.build()); "
+                          "there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    D, W, WS = ctypes.POINTER(MoeDesc), MoeW, ctypes.POINTER(MoeWeights)
+    sigs = {
+        "moe_workspace_bytes": ([D, i32], sz),
+        "moe_check_desc": ([D], i32),
+        "moe_route": ([D, vp, W, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_permute": ([D, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_latent_down": ([D, vp, W, vp, vp, sz, vp], i32),
+        "moe_expert_ffn": ([D, vp, vp, vp, WS, vp, vp, sz, vp], i32),
+        "moe_combine": ([D, vp, vp, vp, vp, vp, vp, vp], i32),
+        "moe_output": ([D, vp, vp, WS, vp, vp, sz, vp], i32),
+        "moe_layer_forward": ([D, WS, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_status_string": ([i32], ctypes.c_char_p),
+        "moe_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sigs.items():
+        fn = getattr(L, name)
+        fn.argtypes = args
+        fn.restype = res
+    return L
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def make_desc(cfg, T=None) -> MoeDesc:
+    """Descriptor from any object with T, d, d_lat, E, k, F, S, Fs, c, eps and the
+    dtype names act, expert_w, latent_w, dense_w ('f32' | 'bf16' | 'mxfp4')."""
+    return MoeDesc(T=cfg.T if T is None else T, d_model=cfg.d, d_latent=cfg.d_lat,
+                   n_experts=cfg.E, top_k=cfg.k, d_ff=cfg.F, n_shared=cfg.S, d_ff_shared=cfg.Fs,
+                   situ_c=cfg.c, rms_eps=cfg.eps, act_dtype=DTYPES[cfg.act],
+                   expert_w_dtype=DTYPES[cfg.expert_w], latent_w_dtype=DTYPES[cfg.latent_w],
+                   dense_w_dtype=DTYPES[cfg.dense_w])
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def make_w(t) -> MoeW:
+    """bf16 / fp32 tensor -> MoeW(data); (packed, scales) pair -> MoeW(data, scale)."""
+    if t is None:
+        return MoeW(None, None)
+    if isinstance(t, (tuple, list)):
+        return MoeW(_ptr(t[0]), _ptr(t[1]))
+    return MoeW(_ptr(t), None)
+
+
+def make_weights(w: dict) -> MoeWeights:
+    """Keys: W_r, b, W_ld, W_lu, gain (optional), W_g, W_v, W_o, W_gs, W_vs, W_os."""
+    return MoeWeights(router=make_w(w.get("W_r")), router_bias=_ptr(w.get("b")),
+                      lat_down=make_w(w.get("W_ld")), lat_up=make_w(w.get("W_lu")),
+                      rms_gain=_ptr(w.get("gain")),
+                      exp_gate=make_w(w.get("W_g")), exp_up=make_w(w.get("W_v")),
+                      exp_down=make_w(w.get("W_o")),
+                      sh_gate=make_w(w.get("W_gs")), sh_up=make_w(w.get("W_vs")),
+                      sh_down=make_w(w.get("W_os")))
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        msg = lib().moe_last_error().decode() or lib().moe_status_string(status).decode()
+        raise MoeError(status, msg)
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return _ptr(ws), ws.numel() * ws.element_size()
+
+
+# --------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# --------------------------------------------------------------------------
+
+def moe_check_desc(desc: MoeDesc) -> int:
+    return lib().moe_check_desc(ctypes.byref(desc))
+
+
+def moe_workspace_bytes(desc: MoeDesc, op: int) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(desc), op))
+
+
+def moe_route(desc, x, router, bias, topk_idx, topk_gate, scores=None, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_route(ctypes.byref(desc), _ptr(x), make_w(router), _ptr(bias), _ptr(topk_idx),
+                           _ptr(topk_gate), _ptr(scores), p, n, _stream(stream)))
+
+
+def moe_permute(desc, topk_idx, counts, offsets, perm_src, inv_pos, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_permute(ctypes.byref(desc), _ptr(topk_idx), _ptr(counts), _ptr(offsets),
+                             _ptr(perm_src), _ptr(inv_pos), p, n, _stream(stream)))
+
+
+def moe_latent_down(desc, x, lat_down, z, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check(lib().moe_latent_down(ctypes.byref(desc), _ptr(x), make_w(lat_down), _ptr(z), p, n,
+                                 _stream(stream)))
+
+
+def moe_expert_ffn(desc, z, perm_src, offsets, weights: dict, o_perm, ws=None, stream=None):
+    p, n = _ws(ws)
+    w = make_weights(weights)
+    _check(lib().moe_expert_ffn(ctypes.byref(desc), _ptr(z), _ptr(perm_src), _ptr(offsets),
+                                ctypes.byref(w), _ptr(o_perm), p, n, _stream(stream)))
+
+
+def moe_combine(desc, o_perm, inv_pos, topk_gate, rms_gain, n_out, u_out=None, stream=None):
+    _check(lib().moe_combine(ctypes.byref(desc), _ptr(o_perm), _ptr(inv_pos), _ptr(topk_gate),
+                             _ptr(rms_gain), _ptr(n_out), _ptr(u_out), _stream(stream)))
+
+
+def moe_output(desc, x, n, weights: dict, y, ws=None, stream=None):
+    p, nb = _ws(ws)
+    w = make_weights(weights)
+    _check(lib().moe_output(ctypes.byref(desc), _ptr(x), _ptr(n), ctypes.byref(w), _ptr(y), p, nb,
+                            _stream(stream)))
+
+
+def moe_layer_forward(desc, weights: dict, x, y, topk_idx=None, topk_gate=None, counts=None,
+                      ws=None, stream=None):
+    p, n = _ws(ws)
+    w = make_weights(weights)
+    _check(lib().moe_layer_forward(ctypes.byref(desc), ctypes.byref(w), _ptr(x), _ptr(y),
+                                   _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), p, n,
+                                   _stream(stream)))
+
+
+def workspace(desc: MoeDesc, op: int, device="cuda:0"):
+    """A device byte tensor of moe_workspace_bytes(desc, op) bytes (at least 1)."""
+    import torch
+    return torch.empty(max(moe_workspace_bytes(desc, op), 1), dtype=torch.uint8, device=device)

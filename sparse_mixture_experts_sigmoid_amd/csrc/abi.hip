@@ -1,0 +1,479 @@
+// C ABI of the Stable LatentMoE layer (declared in include/moe.h): host-side
+// validation, workspace planning and the launch sequence. All validation runs
+// before any HIP call, so every error path is testable without a GPU.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(int hip_status, const char* where) {
+  if (hip_status == -1) return fail(MOE_ERR_UNSUPPORTED, "%s: no kernel for this configuration", where);
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString((hipError_t)hip_status));
+}
+
+#define MOE_LAUNCH(call, where)                  \
+  do {                                           \
+    int st_ = (call);                            \
+    if (st_ != 0) return hip_fail(st_, where);   \
+  } while (0)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t elem_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+constexpr int kMaxExperts = 4096;
+
+int check_desc(const moe_desc_t* d) {
+  if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is NULL");
+  if (d->T < 0) return fail(MOE_ERR_INVALID_ARG, "T = %d < 0", d->T);
+  if (d->d_model <= 0 || d->d_latent <= 0 || d->d_ff <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "d_model, d_latent and d_ff must be > 0");
+  if (d->n_shared < 0) return fail(MOE_ERR_INVALID_ARG, "n_shared < 0");
+  if (d->n_shared > 0 && d->d_ff_shared <= 0)
+    return fail(MOE_ERR_INVALID_ARG, "d_ff_shared must be > 0 when n_shared > 0");
+  if (d->n_experts <= 0) return fail(MOE_ERR_INVALID_ARG, "n_experts must be > 0");
+  if (d->top_k < 1 || d->top_k > d->n_experts)
+    return fail(MOE_ERR_INVALID_ARG, "top_k = %d must be in [1, n_experts = %d]", d->top_k,
+                d->n_experts);
+  if (!(d->situ_c > 0.0f) || !std::isfinite(d->situ_c))
+    return fail(MOE_ERR_INVALID_ARG, "situ_c must be finite and > 0");
+  if (!(d->rms_eps >= 0.0f) || !std::isfinite(d->rms_eps))
+    return fail(MOE_ERR_INVALID_ARG, "rms_eps must be finite and >= 0");
+  const int dts[4] = {d->act_dtype, d->expert_w_dtype, d->latent_w_dtype, d->dense_w_dtype};
+  for (int v : dts)
+    if (v != MOE_F32 && v != MOE_BF16 && v != MOE_MXFP4)
+      return fail(MOE_ERR_INVALID_ARG, "unknown dtype %d", v);
+  if (d->act_dtype == MOE_F32) {
+    if (d->expert_w_dtype != MOE_F32 || d->latent_w_dtype != MOE_F32 || d->dense_w_dtype != MOE_F32)
+      return fail(MOE_ERR_UNSUPPORTED, "fp32 activations need fp32 weights");
+  } else if (d->act_dtype == MOE_BF16) {
+    if (d->dense_w_dtype != MOE_BF16)
+      return fail(MOE_ERR_UNSUPPORTED, "bf16 activations need bf16 router/shared weights");
+    if (d->expert_w_dtype == MOE_F32 || d->latent_w_dtype == MOE_F32)
+      return fail(MOE_ERR_UNSUPPORTED, "bf16 activations need bf16 or MXFP4 expert/latent weights");
+  } else {
+    return fail(MOE_ERR_UNSUPPORTED, "activations must be fp32 or bf16");
+  }
+  if (d->d_model % 32 || d->d_latent % 32 || d->d_ff % 32 ||
+      (d->n_shared > 0 && d->d_ff_shared % 32))
+    return fail(MOE_ERR_UNSUPPORTED, "d_model, d_latent, d_ff, d_ff_shared must be multiples of 32");
+  if (d->n_experts > kMaxExperts)
+    return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", kMaxExperts);
+  if (d->n_shared + 1 > moe::kMaxSegments)
+    return fail(MOE_ERR_UNSUPPORTED, "n_shared > %d", moe::kMaxSegments - 1);
+  const int64_t rows = (int64_t)d->T * d->top_k;
+  if (rows > (int64_t)1 << 30) return fail(MOE_ERR_UNSUPPORTED, "T * top_k too large");
+  if (rows / 128 + d->n_experts > 65535 || (int64_t)d->T / 128 + 1 > 65535)
+    return fail(MOE_ERR_UNSUPPORTED, "batch too large for one launch");
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------------------------------------
+// workspace planning
+// ------------------------------------------------------------------------------------------
+
+struct Plan {
+  size_t total = 0;
+  size_t take(size_t bytes) {
+    size_t off = total;
+    total += (bytes + 255) & ~(size_t)255;
+    return off;
+  }
+};
+
+struct LayerWs {
+  size_t s, key, idx, gate, counts, offsets, perm, inv, blk, z, tile_off, H, O, n, Hs;
+};
+
+int max_tiles(const moe_desc_t* d) {
+  const int bm = moe::grouped_bm(d->act_dtype, (int64_t)d->T * d->top_k, d->n_experts);
+  return (int)(((int64_t)d->T * d->top_k + bm - 1) / bm + d->n_experts);
+}
+
+void plan_route(const moe_desc_t* d, Plan& p, LayerWs& w) {
+  w.s = p.take((size_t)d->T * d->n_experts * 4);
+  w.key = p.take((size_t)d->T * d->n_experts * 4);
+}
+void plan_permute(const moe_desc_t* d, Plan& p, LayerWs& w) {
+  w.blk = p.take((size_t)moe::permute_blocks(d->T) * d->n_experts * 4);
+}
+void plan_expert(const moe_desc_t* d, Plan& p, LayerWs& w) {
+  w.tile_off = p.take((size_t)(d->n_experts + 1) * 4);
+  w.H = p.take((size_t)d->T * d->top_k * d->d_ff * elem_bytes(d->act_dtype));
+}
+void plan_output(const moe_desc_t* d, Plan& p, LayerWs& w) {
+  w.Hs = p.take((size_t)d->T * d->n_shared * d->d_ff_shared * elem_bytes(d->act_dtype));
+}
+
+Plan plan_layer(const moe_desc_t* d, LayerWs& w) {
+  Plan p;
+  plan_route(d, p, w);
+  const size_t tk = (size_t)d->T * d->top_k;
+  w.idx = p.take(tk * 4);
+  w.gate = p.take(tk * 4);
+  w.counts = p.take((size_t)d->n_experts * 4);
+  w.offsets = p.take((size_t)(d->n_experts + 1) * 4);
+  w.perm = p.take(tk * 4);
+  w.inv = p.take(tk * 4);
+  plan_permute(d, p, w);
+  w.z = p.take((size_t)d->T * d->d_latent * elem_bytes(d->act_dtype));
+  plan_expert(d, p, w);
+  w.O = p.take(tk * d->d_latent * elem_bytes(d->act_dtype));
+  w.n = p.take((size_t)d->T * d->d_latent * elem_bytes(d->act_dtype));
+  plan_output(d, p, w);
+  return p;
+}
+
+size_t ws_bytes_for(const moe_desc_t* d, int op) {
+  Plan p;
+  LayerWs w{};
+  switch (op) {
+    case MOE_OP_ROUTE: plan_route(d, p, w); break;
+    case MOE_OP_PERMUTE: plan_permute(d, p, w); break;
+    case MOE_OP_LATENT_DOWN: break;
+    case MOE_OP_EXPERT_FFN: plan_expert(d, p, w); break;
+    case MOE_OP_COMBINE: break;
+    case MOE_OP_OUTPUT: plan_output(d, p, w); break;
+    case MOE_OP_LAYER: p = plan_layer(d, w); break;
+    default: return 0;
+  }
+  return p.total;
+}
+
+int check_ws(const moe_desc_t* d, int op, void* ws, size_t ws_bytes) {
+  const size_t need = ws_bytes_for(d, op);
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", ws_bytes, need);
+  if (need > 0 && (ws == nullptr || !aligned16(ws)))
+    return fail(MOE_ERR_INVALID_ARG, "workspace is NULL or not 16-byte aligned");
+  return MOE_OK;
+}
+
+int need_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+// A buffer whose size scales with T: may be NULL for an empty batch.
+int need_ptr_t(const moe_desc_t* d, const void* p, const char* name) {
+  if (d->T == 0 && p == nullptr) return MOE_OK;
+  return need_ptr(p, name);
+}
+
+int opt_ptr(const void* p, const char* name) {
+  if (p != nullptr && !aligned16(p)) return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+int need_w(const moe_w_t& w, int dtype, const char* name) {
+  if (int st = need_ptr(w.data, name)) return st;
+  if (dtype == MOE_MXFP4 && w.scale == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "%s: MXFP4 weight without scales", name);
+  return MOE_OK;
+}
+
+#define MOE_CHECK(expr)           \
+  do {                            \
+    int st_ = (expr);             \
+    if (st_ != MOE_OK) return st_; \
+  } while (0)
+
+moe::WOperand wop(const moe_w_t& w, int dtype) { return moe::WOperand{w.data, w.scale, dtype}; }
+
+char* at(void* ws, size_t off) { return (char*)ws + off; }
+
+// ------------------------------------------------------------------------------------------
+// stages (arguments already validated)
+// ------------------------------------------------------------------------------------------
+
+int do_route(const moe_desc_t* d, const void* x, moe_w_t router, const float* bias, int32_t* idx,
+             float* gate, float* s, float* key, hipStream_t st) {
+  moe::RouterArgs ra{x, d->act_dtype, router.data, d->dense_w_dtype, bias, d->T, d->d_model,
+                     d->n_experts, s, key};
+  MOE_LAUNCH(moe::launch_router(ra, st), "router");
+  moe::TopkArgs ta{s, key, d->T, d->n_experts, d->top_k, idx, gate};
+  MOE_LAUNCH(moe::launch_topk(ta, st), "topk");
+  return MOE_OK;
+}
+
+int do_permute(const moe_desc_t* d, const int32_t* idx, int32_t* counts, int32_t* offsets,
+               int32_t* perm, int32_t* inv, int32_t* blk, hipStream_t st) {
+  moe::PermuteArgs pa{idx, d->T, d->n_experts, d->top_k, counts, offsets, perm, inv, blk};
+  MOE_LAUNCH(moe::launch_permute(pa, st), "permute");
+  return MOE_OK;
+}
+
+int do_latent_down(const moe_desc_t* d, const void* x, moe_w_t w, void* z, hipStream_t st) {
+  moe::DenseArgs a{x, d->d_model, wop(w, d->latent_w_dtype), d->T, d->d_latent, d->d_model, z,
+                   d->d_latent, d->act_dtype};
+  MOE_LAUNCH(moe::launch_dense(a, st), "latent_down");
+  return MOE_OK;
+}
+
+int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const int32_t* offsets,
+               const moe_weights_t* w, void* o_perm, int32_t* tile_off, void* H, hipStream_t st) {
+  const int bm = moe::grouped_bm(d->act_dtype, (int64_t)d->T * d->top_k, d->n_experts);
+  const int mt = max_tiles(d);
+  const int rows_cap = d->T * d->top_k;
+  if (d->T == 0) return MOE_OK;
+  MOE_LAUNCH(moe::launch_tile_table(offsets, d->n_experts, bm, tile_off, st), "tile_table");
+  moe::GroupedGluArgs g{};
+  g.Z = z; g.ldz = d->d_latent; g.T = d->T; g.rows_cap = rows_cap;
+  g.perm_src = perm; g.topk = d->top_k; g.offsets = offsets; g.tile_off = tile_off;
+  g.max_tiles = mt;
+  g.Wg = wop(w->exp_gate, d->expert_w_dtype);
+  g.Wv = wop(w->exp_up, d->expert_w_dtype);
+  g.E = d->n_experts; g.F = d->d_ff; g.K = d->d_latent;
+  g.H = H; g.c = d->situ_c; g.act_dtype = d->act_dtype;
+  MOE_LAUNCH(moe::launch_grouped_glu(g, st), "expert_gate_up");
+  moe::GroupedDownArgs dn{};
+  dn.H = H; dn.ldh = d->d_ff; dn.rows_cap = rows_cap;
+  dn.offsets = offsets; dn.tile_off = tile_off; dn.max_tiles = mt;
+  dn.Wo = wop(w->exp_down, d->expert_w_dtype);
+  dn.E = d->n_experts; dn.N = d->d_latent; dn.K = d->d_ff;
+  dn.O = o_perm; dn.act_dtype = d->act_dtype;
+  MOE_LAUNCH(moe::launch_grouped_down(dn, st), "expert_down");
+  return MOE_OK;
+}
+
+int do_combine(const moe_desc_t* d, const void* o_perm, const int32_t* inv, const float* gate,
+               const float* gain, void* n, float* u, hipStream_t st) {
+  moe::CombineArgs c{o_perm, inv, gate, gain, d->T, d->top_k, d->d_latent, d->rms_eps,
+                     n, d->d_latent, u, d->act_dtype};
+  MOE_LAUNCH(moe::launch_combine(c, st), "combine");
+  return MOE_OK;
+}
+
+int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weights_t* w, void* y,
+              void* Hs, hipStream_t st) {
+  if (d->T == 0) return MOE_OK;
+  const int S = d->n_shared, Fs = d->d_ff_shared, D = d->d_model;
+  const size_t eb = elem_bytes(d->act_dtype);
+  if (S > 0) {
+    moe::GluArgs g{};
+    g.A = x; g.lda = D;
+    g.Wg = wop(w->sh_gate, d->dense_w_dtype);
+    g.Wv = wop(w->sh_up, d->dense_w_dtype);
+    g.M = d->T; g.F = S * Fs; g.K = D;
+    g.H = Hs; g.ldh = (int64_t)S * Fs; g.c = d->situ_c; g.act_dtype = d->act_dtype;
+    MOE_LAUNCH(moe::launch_glu(g, st), "shared_gate_up");
+  }
+  moe::MultiSegArgs m{};
+  for (int s = 0; s < S; ++s) {
+    m.seg[s].A = (const char*)Hs + (size_t)s * Fs * eb;
+    m.seg[s].lda = (int64_t)S * Fs;
+    m.seg[s].B = moe::WOperand{(const char*)w->sh_down.data + (size_t)s * D * Fs * eb, nullptr,
+                               d->dense_w_dtype};
+    m.seg[s].K = Fs;
+  }
+  m.seg[S].A = n;
+  m.seg[S].lda = d->d_latent;
+  m.seg[S].B = wop(w->lat_up, d->latent_w_dtype);
+  m.seg[S].K = d->d_latent;
+  m.nseg = S + 1;
+  m.M = d->T; m.N = D; m.C = y; m.ldc = D; m.act_dtype = d->act_dtype;
+  MOE_LAUNCH(moe::launch_multiseg(m, st), "output");
+  return MOE_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------
+// exported entry points
+// ------------------------------------------------------------------------------------------
+
+extern "C" {
+
+int moe_check_desc(const moe_desc_t* desc) {
+  g_last_error.clear();
+  return check_desc(desc);
+}
+
+size_t moe_workspace_bytes(const moe_desc_t* desc, int op) {
+  if (check_desc(desc) != MOE_OK) return 0;
+  return ws_bytes_for(desc, op);
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    default: return "MOE_ERR_UNKNOWN";
+  }
+}
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+int moe_route(const moe_desc_t* d, const void* x, moe_w_t router, const float* bias,
+              int32_t* topk_idx, float* topk_gate, float* scores_opt, void* ws, size_t ws_bytes,
+              void* stream) {
+  g_last_error.clear();
+  MOE_CHECK(check_desc(d));
+  MOE_CHECK(need_ptr_t(d, x, "x"));
+  MOE_CHECK(need_w(router, d->dense_w_dtype, "router"));
+  MOE_CHECK(need_ptr(bias, "bias"));
+  MOE_CHECK(need_ptr_t(d, topk_idx, "topk_idx"));
+  MOE_CHECK(need_ptr_t(d, topk_gate, "topk_gate"));
+  MOE_CHECK(opt_ptr(scores_opt, "scores"));
+  MOE_CHECK(check_ws(d, MOE_OP_ROUTE, ws, ws_bytes));
+  Plan p;
+  LayerWs w{};
+  plan_route(d, p, w);
+  float* s = scores_opt ? scores_opt : (float*)at(ws, w.s);
+  return do_route(d, x, router, bias, topk_idx, topk_gate, s, (float*)at(ws, w.key),
+                  (hipStream_t)stream);
+}
+
+int moe_permute(const moe_desc_t* d, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
+                int32_t* perm_src, int32_t* inv_pos, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_CHECK(check_desc(d));
+  MOE_CHECK(need_ptr_t(d, topk_idx, "topk_idx"));
+  MOE_CHECK(need_ptr(counts, "counts"));
+  MOE_CHECK(need_ptr(offsets, "offsets"));
+  MOE_CHECK(need_ptr_t(d, perm_src, "perm_src"));
+  MOE_CHECK(need_ptr_t(d, inv_pos, "inv_pos"));
+  MOE_CHECK(check_ws(d, MOE_OP_PERMUTE, ws, ws_bytes));
+  Plan p;
+  LayerWs w{};
+  plan_permute(d, p, w);
+  return do_permute(d, topk_idx, counts, offsets, perm_src, inv_pos, (int32_t*)at(ws, w.blk),
+                    (hipStream_t)stream);
+}
+
+int moe_latent_down(const moe_desc_t* d, const void* x, moe_w_t lat_down, void* z, void* ws,
+                    size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_CHECK(check_desc(d));
+  MOE_CHECK(need_ptr_t(d, x, "x"));
+  MOE_CHECK(need_w(lat_down, d->latent_w_dtype, "lat_down"));
+  MOE_CHECK(need_ptr_t(d, z, "z"));
+  MOE_CHECK(check_ws(d, MOE_OP_LATENT_DOWN, ws, ws_bytes));
+  return do_latent_down(d, x, lat_down, z, (hipStream_t)stream);
+}
+
+int moe_expert_ffn(const moe_desc_t* d, const void* z, const int32_t* perm_src,
+                   const int32_t* offsets, const moe_weights_t* w, void* o_perm, void* ws,
+                   size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_CHECK(check_desc(d));
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  MOE_CHECK(need_ptr_t(d, z, "z"));
+  MOE_CHECK(need_ptr_t(d, perm_src, "perm_src"));
+  MOE_CHECK(need_ptr(offsets, "offsets"));
+  MOE_CHECK(need_w(w->exp_gate, d->expert_w_dtype, "exp_gate"));
+  MOE_CHECK(need_w(w->exp_up, d->expert_w_dtype, "exp_up"));
+  MOE_CHECK(need_w(w->exp_down, d->expert_w_dtype, "exp_down"));
+  MOE_CHECK(need_ptr_t(d, o_perm, "o_perm"));
+  MOE_CHECK(check_ws(d, MOE_OP_EXPERT_FFN, ws, ws_bytes));
+  Plan p;
+  LayerWs lw{};
+  plan_expert(d, p, lw);
+  return do_experts(d, z, perm_src, offsets, w, o_perm, (int32_t*)at(ws, lw.tile_off),
+                    at(ws, lw.H), (hipStream_t)stream);
+}
+
+int moe_combine(const moe_desc_t* d, const void* o_perm, const int32_t* inv_pos,
+                const float* topk_gate, const float* rms_gain, void* n_out, float* u_out_opt,
+                void* stream) {
+  g_last_error.clear();
+  MOE_CHECK(check_desc(d));
+  MOE_CHECK(need_ptr_t(d, o_perm, "o_perm"));
+  MOE_CHECK(need_ptr_t(d, inv_pos, "inv_pos"));
+  MOE_CHECK(need_ptr_t(d, topk_gate, "topk_gate"));
+  MOE_CHECK(opt_ptr(rms_gain, "rms_gain"));
+  MOE_CHECK(need_ptr_t(d, n_out, "n_out"));
+  MOE_CHECK(opt_ptr(u_out_opt, "u_out"));
+  return do_combine(d, o_perm, inv_pos, topk_gate, rms_gain, n_out, u_out_opt, (hipStream_t)stream);
+}
+
+int moe_output(const moe_desc_t* d, const void* x, const void* n, const moe_weights_t* w, void* y,
+               void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_CHECK(check_desc(d));
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  MOE_CHECK(need_ptr_t(d, x, "x"));
+  MOE_CHECK(need_ptr_t(d, n, "n"));
+  MOE_CHECK(need_w(w->lat_up, d->latent_w_dtype, "lat_up"));
+  if (d->n_shared > 0) {
+    MOE_CHECK(need_w(w->sh_gate, d->dense_w_dtype, "sh_gate"));
+    MOE_CHECK(need_w(w->sh_up, d->dense_w_dtype, "sh_up"));
+    MOE_CHECK(need_w(w->sh_down, d->dense_w_dtype, "sh_down"));
+  }
+  MOE_CHECK(need_ptr_t(d, y, "y"));
+  MOE_CHECK(check_ws(d, MOE_OP_OUTPUT, ws, ws_bytes));
+  Plan p;
+  LayerWs lw{};
+  plan_output(d, p, lw);
+  return do_output(d, x, n, w, y, at(ws, lw.Hs), (hipStream_t)stream);
+}
+
+int moe_layer_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
+                      int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* counts_opt, void* ws,
+                      size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_CHECK(check_desc(d));
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  MOE_CHECK(need_ptr_t(d, x, "x"));
+  MOE_CHECK(need_ptr_t(d, y, "y"));
+  MOE_CHECK(need_w(w->router, d->dense_w_dtype, "router"));
+  MOE_CHECK(need_ptr(w->router_bias, "router_bias"));
+  MOE_CHECK(need_w(w->lat_down, d->latent_w_dtype, "lat_down"));
+  MOE_CHECK(need_w(w->lat_up, d->latent_w_dtype, "lat_up"));
+  MOE_CHECK(opt_ptr(w->rms_gain, "rms_gain"));
+  MOE_CHECK(need_w(w->exp_gate, d->expert_w_dtype, "exp_gate"));
+  MOE_CHECK(need_w(w->exp_up, d->expert_w_dtype, "exp_up"));
+  MOE_CHECK(need_w(w->exp_down, d->expert_w_dtype, "exp_down"));
+  if (d->n_shared > 0) {
+    MOE_CHECK(need_w(w->sh_gate, d->dense_w_dtype, "sh_gate"));
+    MOE_CHECK(need_w(w->sh_up, d->dense_w_dtype, "sh_up"));
+    MOE_CHECK(need_w(w->sh_down, d->dense_w_dtype, "sh_down"));
+  }
+  MOE_CHECK(opt_ptr(topk_idx_opt, "topk_idx"));
+  MOE_CHECK(opt_ptr(topk_gate_opt, "topk_gate"));
+  MOE_CHECK(opt_ptr(counts_opt, "counts"));
+  MOE_CHECK(check_ws(d, MOE_OP_LAYER, ws, ws_bytes));
+  LayerWs lw{};
+  plan_layer(d, lw);
+  hipStream_t st = (hipStream_t)stream;
+  int32_t* idx = topk_idx_opt ? topk_idx_opt : (int32_t*)at(ws, lw.idx);
+  float* gate = topk_gate_opt ? topk_gate_opt : (float*)at(ws, lw.gate);
+  int32_t* counts = counts_opt ? counts_opt : (int32_t*)at(ws, lw.counts);
+  int32_t* offsets = (int32_t*)at(ws, lw.offsets);
+  int32_t* perm = (int32_t*)at(ws, lw.perm);
+  int32_t* inv = (int32_t*)at(ws, lw.inv);
+  MOE_CHECK(do_route(d, x, w->router, w->router_bias, idx, gate, (float*)at(ws, lw.s),
+                     (float*)at(ws, lw.key), st));
+  MOE_CHECK(do_permute(d, idx, counts, offsets, perm, inv, (int32_t*)at(ws, lw.blk), st));
+  MOE_CHECK(do_latent_down(d, x, w->lat_down, at(ws, lw.z), st));
+  MOE_CHECK(do_experts(d, at(ws, lw.z), perm, offsets, w, at(ws, lw.O), (int32_t*)at(ws, lw.tile_off),
+                       at(ws, lw.H), st));
+  MOE_CHECK(do_combine(d, at(ws, lw.O), inv, gate, w->rms_gain, at(ws, lw.n), nullptr, st));
+  MOE_CHECK(do_output(d, x, at(ws, lw.n), w, y, at(ws, lw.Hs), st));
+  return MOE_OK;
+}
+
+}  // extern "C"

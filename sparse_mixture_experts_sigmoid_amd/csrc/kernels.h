@@ -1,0 +1,133 @@
+// Internal launchers of the gfx950 Stable LatentMoE kernels (not part of the ABI).
+// Every launcher only enqueues on `stream`; it returns 0 or a hipError_t value
+// (or -1 for an internal dispatch error). Shapes are checked by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouterArgs {
+  const void* x; int x_dtype;      // [T, d]
+  const void* W; int w_dtype;      // [E, d]
+  const float* bias;               // [E]
+  int T, d, E;
+  float* s;                        // [T, E]
+  float* key;                      // [T, E]
+};
+int launch_router(const RouterArgs& a, hipStream_t stream);
+
+struct TopkArgs {
+  const float* s; const float* key;
+  int T, E, k;
+  int32_t* idx; float* gate;       // [T, k]
+};
+int launch_topk(const TopkArgs& a, hipStream_t stream);
+
+// Permutation. Scratch: block_counts [nblk * E] int32 with nblk = permute_blocks(T).
+int permute_blocks(int T);
+struct PermuteArgs {
+  const int32_t* idx; int T, E, k;
+  int32_t* counts; int32_t* offsets; int32_t* perm_src; int32_t* inv_pos;
+  int32_t* block_counts;
+};
+int launch_permute(const PermuteArgs& a, hipStream_t stream);
+
+// Tile table of a grouped GEMM with BM-row tiles: tile_off[e] = sum_{e'<e}
+// ceil(count_e' / BM), tile_off[E] = total tiles (device side, from offsets).
+int launch_tile_table(const int32_t* offsets, int E, int BM, int32_t* tile_off,
+                      hipStream_t stream);
+
+// A weight operand [rows, K] in bf16, fp32 or MXFP4 (data = packed, scale = e8m0).
+struct WOperand {
+  const void* data;
+  const uint8_t* scale;
+  int dtype;
+};
+
+// C[M, N] = A[M, K] W[N, K]^T, store in the act dtype. (latent down)
+struct DenseArgs {
+  const void* A; int64_t lda;  // act dtype
+  WOperand W;                  // [N, K]
+  int M, N, K;
+  void* C; int64_t ldc;        // act dtype
+  int act_dtype;
+};
+int launch_dense(const DenseArgs& a, hipStream_t stream);
+
+// H[M, F] = act(A Wg^T, A Wv^T), Wg/Wv [F, K]. (shared gate/up)
+struct GluArgs {
+  const void* A; int64_t lda;
+  WOperand Wg, Wv;
+  int M, F, K;
+  void* H; int64_t ldh;
+  float c;
+  int act_dtype;
+};
+int launch_glu(const GluArgs& a, hipStream_t stream);
+
+// Grouped over experts: rows r in [offsets[e], offsets[e+1]) of expert e.
+// gate/up: A row = z[perm_src[r] / k]; H[r] = act(z Wg[e]^T, z Wv[e]^T).
+struct GroupedGluArgs {
+  const void* Z; int64_t ldz;        // [T, K]
+  int T;                             // rows of Z
+  int rows_cap;                      // rows of H (T*k): rows at or past it are skipped
+  const int32_t* perm_src; int topk;
+  const int32_t* offsets;            // [E+1]
+  const int32_t* tile_off;           // [E+1] for BM-row tiles
+  int max_tiles;                     // upper bound of tile_off[E]
+  WOperand Wg, Wv;                   // [E, F, K]
+  int E, F, K;
+  void* H;                           // [rows, F]
+  float c;
+  int act_dtype;
+};
+int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream);
+int grouped_bm(int act_dtype, int64_t rows, int E);  // BM used by the grouped kernels
+
+// down: O[r] = H[r] Wo[e]^T, Wo [E, N, K].
+struct GroupedDownArgs {
+  const void* H; int64_t ldh;
+  int rows_cap;                      // rows of H and O
+  const int32_t* offsets;
+  const int32_t* tile_off;
+  int max_tiles;
+  WOperand Wo;
+  int E, N, K;
+  void* O;
+  int act_dtype;
+};
+int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream);
+
+// y[M, N] = sum over segments s of A_s[M, K_s] B_s[N, K_s]^T (fp32 accumulate).
+struct Segment {
+  const void* A; int64_t lda;
+  WOperand B;
+  int K;
+};
+constexpr int kMaxSegments = 8;
+struct MultiSegArgs {
+  Segment seg[kMaxSegments];
+  int nseg;
+  int M, N;
+  void* C; int64_t ldc;
+  int act_dtype;
+};
+int launch_multiseg(const MultiSegArgs& a, hipStream_t stream);
+
+// Combine + RMSNorm.
+struct CombineArgs {
+  const void* O;                 // [T*k, D] act dtype, permuted rows
+  const int32_t* inv_pos;        // [T*k]
+  const float* gate;             // [T, k]
+  const float* gain;             // [D] or null
+  int T, k, D;
+  float eps;
+  void* n_out; int64_t ldn;      // [T, D] act dtype
+  float* u_out;                  // [T, D] or null
+  int act_dtype;
+};
+int launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace moe
