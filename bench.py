@@ -1,0 +1,182 @@
+#!/usr/bin/env python3
+"""Throughput of the Stable LatentMoE layer forward on one MI355X.
+
+One step = one moe_layer_forward call (router, top-k + gates, permutation,
+latent down, routed experts, combine + RMSNorm, shared experts, latent up) on
+one batch of seeded synthetic inputs already resident in HBM. Prints ONE JSON
+line.
+
+Default workload: the K3-shape decode layer (T = 256 tokens, d = 7168,
+d_lat = 3584, 896 experts, top-16, F = 3072, 2 shared experts with Fs = 3072,
+bf16 weights and activations, fp32 accumulation). Other workloads (--workload
+k3_prefill | k3_skew | k3_prefill_mxfp4 | tiny_f32) are parity cases that can
+also be timed.
+
+roofline: the dominant kernel's algorithmic rate from HIP events recorded by
+the library around every stage of the timed calls (moe_trace_*), on the stream
+the kernels run on. Decode: the expert gate/up grouped GEMM is HBM-bound; its
+algorithmic bytes per launch = (touched experts) x 2*F*d_lat*2 B (W_g and W_v)
++ (T*k routed rows) x (d_lat + F)*2 B (gathered z rows in, h rows out).
+Prefill: the same kernel is MFMA-bound; flops per launch = T*k*2*2*d_lat*F.
+
+cpu_baseline: the CPU oracle (never tuned) on a bounded token sample of the
+same workload, on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix
+METRIC = "tokens/s per K3-shape LatentMoE layer; % MFMA peak (prefill), % HBM BW (decode)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="k3_decode")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample (0 = skip)")
+    ap.add_argument("--quiet", action="store_true")
+    return ap.parse_args()
+
+
+def log(args, *a):
+    if not args.quiet:
+        print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, target_s: float):
+    """Oracle (route + forward) on growing token samples until ~target_s of work."""
+    import numpy as np
+    import oracle
+    import synth
+    w = synth.HostWeights(cfg)
+    rng = np.random.default_rng(1234)
+    order = rng.permutation(cfg.T)
+    done, spent, chunk = 0, 0.0, 1
+    while spent < target_s and done < cfg.T:
+        toks = np.sort(order[done:done + chunk])
+        t0 = time.perf_counter()
+        oracle.forward(cfg, w, tokens=toks)          # routes these tokens, then the layer
+        spent += time.perf_counter() - t0
+        done += len(toks)
+        chunk = min(chunk * 2, 64)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": done / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {cfg.T} tokens of {cfg.name} (routing + full layer per token, "
+                      f"{spent:.1f} s)"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the layer's hot path is "
+                                   "measured on a single MI355X; use --gpus 1"}))
+        return 2
+
+    import numpy as np
+    import torch
+    import synth
+    import sparse_mixture_experts_sigmoid_amd as moe
+
+    dev = "cuda:0"
+    cfg = synth.config(args.workload)
+    log(args, f"[bench] {cfg.name}: generating inputs on {dev}")
+    inp = synth.device_inputs(cfg, dev)
+    desc = moe.make_desc(cfg)
+    act = torch.float32 if cfg.act == "f32" else torch.bfloat16
+    y = torch.empty((cfg.T, cfg.d), dtype=act, device=dev)
+    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
+    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
+    counts = torch.empty((cfg.E,), dtype=torch.int32, device=dev)
+    ws = moe.workspace(desc, moe.MOE_OP_LAYER, dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moe.moe_layer_forward(desc, inp, inp["x"], y, idx, gate, counts, ws, stream)
+
+    log(args, f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    moe.moe_trace_enable(args.steps)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    stages, ncalls = moe.moe_trace_read()
+    moe.moe_trace_enable(0)
+    log(args, f"[bench] {ms:.3f} ms/step; stages " +
+        ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
+
+    cnt = counts.cpu().numpy()
+    touched = int((cnt > 0).sum())
+    rows = cfg.T * cfg.k
+    wbytes = {"bf16": 2.0, "f32": 4.0, "mxfp4": 0.5 + 1.0 / 32}[cfg.expert_w]
+    abytes = 4 if cfg.act == "f32" else 2
+    t_gu = stages["expert_gate_up"] * 1e-3
+    decode = cfg.name == "k3_decode"
+    if decode:
+        algo = touched * 2 * cfg.F * cfg.d_lat * wbytes + rows * (cfg.d_lat + cfg.F) * abytes
+        achieved = algo / t_gu / 1e9
+        roof = {"bound": "hbm", "kernel": "expert_gate_up (grouped GEMM + SiTU-GLU)",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": int(algo), "avg_launch_ms": round(t_gu * 1e3, 4)}
+    else:
+        algo = rows * 2 * 2 * cfg.d_lat * cfg.F
+        achieved = algo / t_gu / 1e12
+        roof = {"bound": "mfma", "kernel": "expert_gate_up (grouped GEMM + SiTU-GLU)",
+                "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "algorithmic_flops_per_launch": int(algo), "avg_launch_ms": round(t_gu * 1e3, 4)}
+
+    touched_bytes = touched * 3 * cfg.F * cfg.d_lat * wbytes
+    layer = {
+        "tflops": round(cfg.flops_per_token * cfg.T / (ms * 1e-3) / 1e12, 2),
+        "touched_expert_GBps": round(touched_bytes / (ms * 1e-3) / 1e9, 1),
+        "touched_experts": touched,
+        "stage_ms": {k: round(v, 4) for k, v in stages.items()},
+        "traced_calls": ncalls,
+    }
+    base = None
+    if args.cpu_seconds > 0:
+        log(args, "[bench] cpu baseline (oracle)")
+        base = cpu_baseline(cfg, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.act,
+        "data": "synthetic: seeded counter-based N(0,1) activations and N(0,1/fan_in) "
+                "random-init weights of the K3 layer shape (no checkpoint)",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} d_lat={cfg.d_lat} E={cfg.E} "
+                               f"k={cfg.k} F={cfg.F} S={cfg.S} Fs={cfg.Fs} act={cfg.act} "
+                               f"expert_w={cfg.expert_w} latent_w={cfg.latent_w}",
+                   "tokens": cfg.T, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": base,
+        "layer": layer,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -178,6 +178,19 @@ int moe_layer_forward(const moe_desc_t* desc, const moe_weights_t* w, const void
                       int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* counts_opt,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* Stage tracing. moe_trace_enable(max_calls) makes the next max_calls calls of
+   moe_layer_forward record a HIP event on their stream before each stage and
+   after the last one (max_calls = 0 turns tracing off). moe_trace_read waits
+   for those events, writes the average milliseconds of each stage over the
+   traced calls into ms[0 .. min(max_stages, MOE_TRACE_STAGES)) and the number
+   of traced calls into *ncalls, then starts a new trace window. Stage i is
+   named by moe_trace_stage_name(i). The events are created by the library on
+   the device current at moe_trace_enable and live until the next enable. */
+#define MOE_TRACE_STAGES 10
+int moe_trace_enable(int max_calls);
+int moe_trace_read(float* ms, int max_stages, int* ncalls);
+const char* moe_trace_stage_name(int stage);
+
 /* Static text of a status code. */
 const char* moe_status_string(int status);
 

@@ -27,7 +27,9 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
 
 EXPORTS = ["moe_workspace_bytes", "moe_check_desc", "moe_route", "moe_permute", "moe_latent_down",
            "moe_expert_ffn", "moe_combine", "moe_output", "moe_layer_forward",
-           "moe_status_string", "moe_last_error"]
+           "moe_status_string", "moe_last_error", "moe_trace_enable", "moe_trace_read",
+           "moe_trace_stage_name"]
+MOE_TRACE_STAGES = 10
 
 
 class MoeError(RuntimeError):
@@ -76,6 +78,9 @@ def lib():
         "moe_layer_forward": ([D, WS, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_status_string": ([i32], ctypes.c_char_p),
         "moe_last_error": ([], ctypes.c_char_p),
+        "moe_trace_enable": ([i32], i32),
+        "moe_trace_read": ([ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(ctypes.c_int)], i32),
+        "moe_trace_stage_name": ([i32], ctypes.c_char_p),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -201,6 +206,19 @@ def moe_layer_forward(desc, weights: dict, x, y, topk_idx=None, topk_gate=None, 
     _check(lib().moe_layer_forward(ctypes.byref(desc), ctypes.byref(w), _ptr(x), _ptr(y),
                                    _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), p, n,
                                    _stream(stream)))
+
+
+def moe_trace_enable(max_calls: int):
+    _check(lib().moe_trace_enable(max_calls))
+
+
+def moe_trace_read() -> tuple[dict, int]:
+    """({stage name: average ms}, number of traced calls) of the current window."""
+    ms = (ctypes.c_float * MOE_TRACE_STAGES)()
+    n = ctypes.c_int(0)
+    _check(lib().moe_trace_read(ms, MOE_TRACE_STAGES, ctypes.byref(n)))
+    names = [lib().moe_trace_stage_name(i).decode() for i in range(MOE_TRACE_STAGES)]
+    return dict(zip(names, [float(v) for v in ms])), int(n.value)
 
 
 def workspace(desc: MoeDesc, op: int, device="cuda:0"):

@@ -5,7 +5,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/moe.h"
 #include "common.h"
@@ -203,14 +205,47 @@ moe::WOperand wop(const moe_w_t& w, int dtype) { return moe::WOperand{w.data, w.
 char* at(void* ws, size_t off) { return (char*)ws + off; }
 
 // ------------------------------------------------------------------------------------------
+// stage tracing: per traced call, MOE_TRACE_STAGES + 1 events recorded on the call's stream
+// ------------------------------------------------------------------------------------------
+
+const char* const kStageNames[MOE_TRACE_STAGES] = {
+    "router", "topk", "permute", "latent_down", "tile_table",
+    "expert_gate_up", "expert_down", "combine", "shared_gate_up", "output"};
+
+struct Trace {
+  std::mutex mu;
+  int max_calls = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;  // max_calls * (MOE_TRACE_STAGES + 1)
+};
+Trace g_trace;
+
+// A slot for one traced call, or -1.
+int trace_begin() {
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  if (g_trace.used >= g_trace.max_calls) return -1;
+  return g_trace.used++;
+}
+
+struct Marker {
+  int slot;
+  hipStream_t st;
+  void operator()(int boundary) const {
+    if (slot >= 0) hipEventRecord(g_trace.ev[(size_t)slot * (MOE_TRACE_STAGES + 1) + boundary], st);
+  }
+};
+
+// ------------------------------------------------------------------------------------------
 // stages (arguments already validated)
 // ------------------------------------------------------------------------------------------
 
 int do_route(const moe_desc_t* d, const void* x, moe_w_t router, const float* bias, int32_t* idx,
-             float* gate, float* s, float* key, hipStream_t st) {
+             float* gate, float* s, float* key, hipStream_t st, Marker mk = {-1, nullptr}) {
   moe::RouterArgs ra{x, d->act_dtype, router.data, d->dense_w_dtype, bias, d->T, d->d_model,
                      d->n_experts, s, key};
+  mk(0);
   MOE_LAUNCH(moe::launch_router(ra, st), "router");
+  mk(1);
   moe::TopkArgs ta{s, key, d->T, d->n_experts, d->top_k, idx, gate};
   MOE_LAUNCH(moe::launch_topk(ta, st), "topk");
   return MOE_OK;
@@ -231,12 +266,15 @@ int do_latent_down(const moe_desc_t* d, const void* x, moe_w_t w, void* z, hipSt
 }
 
 int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const int32_t* offsets,
-               const moe_weights_t* w, void* o_perm, int32_t* tile_off, void* H, hipStream_t st) {
+               const moe_weights_t* w, void* o_perm, int32_t* tile_off, void* H, hipStream_t st,
+               Marker mk = {-1, nullptr}) {
   const int bm = moe::grouped_bm(d->act_dtype, (int64_t)d->T * d->top_k, d->n_experts);
   const int mt = max_tiles(d);
   const int rows_cap = d->T * d->top_k;
-  if (d->T == 0) return MOE_OK;
-  MOE_LAUNCH(moe::launch_tile_table(offsets, d->n_experts, bm, tile_off, st), "tile_table");
+  mk(4);
+  if (d->T > 0)
+    MOE_LAUNCH(moe::launch_tile_table(offsets, d->n_experts, bm, tile_off, st), "tile_table");
+  mk(5);
   moe::GroupedGluArgs g{};
   g.Z = z; g.ldz = d->d_latent; g.T = d->T; g.rows_cap = rows_cap;
   g.perm_src = perm; g.topk = d->top_k; g.offsets = offsets; g.tile_off = tile_off;
@@ -245,14 +283,15 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
   g.Wv = wop(w->exp_up, d->expert_w_dtype);
   g.E = d->n_experts; g.F = d->d_ff; g.K = d->d_latent;
   g.H = H; g.c = d->situ_c; g.act_dtype = d->act_dtype;
-  MOE_LAUNCH(moe::launch_grouped_glu(g, st), "expert_gate_up");
+  if (d->T > 0) MOE_LAUNCH(moe::launch_grouped_glu(g, st), "expert_gate_up");
+  mk(6);
   moe::GroupedDownArgs dn{};
   dn.H = H; dn.ldh = d->d_ff; dn.rows_cap = rows_cap;
   dn.offsets = offsets; dn.tile_off = tile_off; dn.max_tiles = mt;
   dn.Wo = wop(w->exp_down, d->expert_w_dtype);
   dn.E = d->n_experts; dn.N = d->d_latent; dn.K = d->d_ff;
   dn.O = o_perm; dn.act_dtype = d->act_dtype;
-  MOE_LAUNCH(moe::launch_grouped_down(dn, st), "expert_down");
+  if (d->T > 0) MOE_LAUNCH(moe::launch_grouped_down(dn, st), "expert_down");
   return MOE_OK;
 }
 
@@ -265,8 +304,8 @@ int do_combine(const moe_desc_t* d, const void* o_perm, const int32_t* inv, cons
 }
 
 int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weights_t* w, void* y,
-              void* Hs, hipStream_t st) {
-  if (d->T == 0) return MOE_OK;
+              void* Hs, hipStream_t st, Marker mk = {-1, nullptr}) {
+  mk(8);
   const int S = d->n_shared, Fs = d->d_ff_shared, D = d->d_model;
   const size_t eb = elem_bytes(d->act_dtype);
   if (S > 0) {
@@ -278,6 +317,7 @@ int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weigh
     g.H = Hs; g.ldh = (int64_t)S * Fs; g.c = d->situ_c; g.act_dtype = d->act_dtype;
     MOE_LAUNCH(moe::launch_glu(g, st), "shared_gate_up");
   }
+  mk(9);
   moe::MultiSegArgs m{};
   for (int s = 0; s < S; ++s) {
     m.seg[s].A = (const char*)Hs + (size_t)s * Fs * eb;
@@ -293,6 +333,7 @@ int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weigh
   m.nseg = S + 1;
   m.M = d->T; m.N = D; m.C = y; m.ldc = D; m.act_dtype = d->act_dtype;
   MOE_LAUNCH(moe::launch_multiseg(m, st), "output");
+  mk(10);
   return MOE_OK;
 }
 
@@ -326,6 +367,54 @@ const char* moe_status_string(int status) {
 }
 
 const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+const char* moe_trace_stage_name(int stage) {
+  return (stage >= 0 && stage < MOE_TRACE_STAGES) ? kStageNames[stage] : "";
+}
+
+int moe_trace_enable(int max_calls) {
+  g_last_error.clear();
+  if (max_calls < 0 || max_calls > 100000) return fail(MOE_ERR_INVALID_ARG, "max_calls out of range");
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  for (hipEvent_t e : g_trace.ev) hipEventDestroy(e);
+  g_trace.ev.clear();
+  g_trace.max_calls = 0;
+  g_trace.used = 0;
+  const size_t n = (size_t)max_calls * (MOE_TRACE_STAGES + 1);
+  g_trace.ev.resize(n);
+  for (size_t i = 0; i < n; ++i) {
+    hipError_t e = hipEventCreate(&g_trace.ev[i]);
+    if (e != hipSuccess) {
+      g_trace.ev.resize(i);
+      return hip_fail((int)e, "trace_enable");
+    }
+  }
+  g_trace.max_calls = max_calls;
+  return MOE_OK;
+}
+
+int moe_trace_read(float* ms, int max_stages, int* ncalls) {
+  g_last_error.clear();
+  if (ms == nullptr && max_stages > 0) return fail(MOE_ERR_INVALID_ARG, "ms is NULL");
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  const int used = g_trace.used;
+  const int ns = max_stages < MOE_TRACE_STAGES ? max_stages : MOE_TRACE_STAGES;
+  for (int i = 0; i < ns; ++i) ms[i] = 0.0f;
+  for (int c = 0; c < used; ++c) {
+    hipEvent_t* ev = &g_trace.ev[(size_t)c * (MOE_TRACE_STAGES + 1)];
+    hipError_t e = hipEventSynchronize(ev[MOE_TRACE_STAGES]);
+    if (e != hipSuccess) return hip_fail((int)e, "trace_read");
+    for (int i = 0; i < ns; ++i) {
+      float t = 0.0f;
+      e = hipEventElapsedTime(&t, ev[i], ev[i + 1]);
+      if (e != hipSuccess) return hip_fail((int)e, "trace_read");
+      ms[i] += t / (float)used;
+    }
+  }
+  if (ncalls) *ncalls = used;
+  g_trace.used = 0;
+  return MOE_OK;
+}
 
 int moe_route(const moe_desc_t* d, const void* x, moe_w_t router, const float* bias,
               int32_t* topk_idx, float* topk_gate, float* scores_opt, void* ws, size_t ws_bytes,
@@ -465,14 +554,18 @@ int moe_layer_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x
   int32_t* offsets = (int32_t*)at(ws, lw.offsets);
   int32_t* perm = (int32_t*)at(ws, lw.perm);
   int32_t* inv = (int32_t*)at(ws, lw.inv);
+  const Marker mk{trace_begin(), st};
   MOE_CHECK(do_route(d, x, w->router, w->router_bias, idx, gate, (float*)at(ws, lw.s),
-                     (float*)at(ws, lw.key), st));
+                     (float*)at(ws, lw.key), st, mk));
+  mk(2);
   MOE_CHECK(do_permute(d, idx, counts, offsets, perm, inv, (int32_t*)at(ws, lw.blk), st));
+  mk(3);
   MOE_CHECK(do_latent_down(d, x, w->lat_down, at(ws, lw.z), st));
   MOE_CHECK(do_experts(d, at(ws, lw.z), perm, offsets, w, at(ws, lw.O), (int32_t*)at(ws, lw.tile_off),
-                       at(ws, lw.H), st));
+                       at(ws, lw.H), st, mk));
+  mk(7);
   MOE_CHECK(do_combine(d, at(ws, lw.O), inv, gate, w->rms_gain, at(ws, lw.n), nullptr, st));
-  MOE_CHECK(do_output(d, x, at(ws, lw.n), w, y, at(ws, lw.Hs), st));
+  MOE_CHECK(do_output(d, x, at(ws, lw.n), w, y, at(ws, lw.Hs), st, mk));
   return MOE_OK;
 }
 
