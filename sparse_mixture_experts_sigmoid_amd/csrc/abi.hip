@@ -282,7 +282,7 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
   g.Wg = wop(w->exp_gate, d->expert_w_dtype);
   g.Wv = wop(w->exp_up, d->expert_w_dtype);
   g.E = d->n_experts; g.F = d->d_ff; g.K = d->d_latent;
-  g.H = H; g.c = d->situ_c; g.act_dtype = d->act_dtype;
+  g.H = H; g.c = d->situ_c; g.act_dtype = d->act_dtype; g.bm = bm;
   if (d->T > 0) MOE_LAUNCH(moe::launch_grouped_glu(g, st), "expert_gate_up");
   mk(6);
   moe::GroupedDownArgs dn{};
@@ -290,7 +290,7 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
   dn.offsets = offsets; dn.tile_off = tile_off; dn.max_tiles = mt;
   dn.Wo = wop(w->exp_down, d->expert_w_dtype);
   dn.E = d->n_experts; dn.N = d->d_latent; dn.K = d->d_ff;
-  dn.O = o_perm; dn.act_dtype = d->act_dtype;
+  dn.O = o_perm; dn.act_dtype = d->act_dtype; dn.bm = bm;
   if (d->T > 0) MOE_LAUNCH(moe::launch_grouped_down(dn, st), "expert_down");
   return MOE_OK;
 }

@@ -464,6 +464,224 @@ __global__ __launch_bounds__(256) void multiseg_kernel(MultiSegArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// weight-streaming grouped kernels (few rows per expert, e.g. decode)
+//
+// With ~5 rows per expert the expert GEMMs are bound by reading each touched
+// expert's weights from HBM once. A block owns one expert tile of up to 32
+// rows (two 16-row v_mfma_f32_16x16x32_bf16 tiles) and 64 weight rows (four
+// 16-column tiles: for gate/up two gate + the two matching up tiles), and the
+// four waves split K: each wave streams its quarter of the 64 weight rows
+// straight from global memory into MFMA operand registers (no LDS staging;
+// the next 64-k chunk is in flight while the current one is multiplied), and
+// the partial sums are reduced through LDS in a fixed wave order.
+//
+// k assignment inside a 64-k chunk: lane group g = lane/16 takes k = g*16 ..
+// g*16+15, 8 per MFMA step. A and B use the same assignment, so every MFMA
+// still sums over its 32 k values, and the 4 lanes of a weight row read the
+// row's whole 128-byte segment.
+// ---------------------------------------------------------------------------
+
+constexpr int SK_BM = 32;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8 zero_frag() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return __builtin_bit_cast(bf16x8, z);
+}
+
+__device__ __forceinline__ bf16x8 ld_frag(const bf16_t* row, int k, int K) {
+  if (row == nullptr || k >= K) return zero_frag();
+  return *(const bf16x8*)(row + k);
+}
+
+// 8 MXFP4 elements k..k+7 (k a multiple of 8) of one packed row, decoded to bf16.
+__device__ __forceinline__ bf16x8 ld_frag_mx(const uint8_t* prow, const uint8_t* srow, int k, int K) {
+  if (prow == nullptr || k >= K) return zero_frag();
+  const uint32_t q = *(const uint32_t*)(prow + k / 2);
+  const uint32_t sb = srow[k / 32];
+  const float scale = sb == 0u ? 0x1p-127f : __uint_as_float(sb << 23);
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t byte = (q >> (8 * i)) & 0xFFu;
+    w[i] = scale_bf16(e2m1_bf16(byte & 0xFu), scale) | (scale_bf16(e2m1_bf16(byte >> 4), scale) << 16);
+  }
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+struct SkRows {
+  const bf16_t* a[2];      // A rows of m-tiles 0, 1 (nullptr: zero row)
+  const void* b[4];        // B rows of n-tiles 0..3 (bf16 row, or packed MXFP4 row)
+  const uint8_t* bs[4];    // MXFP4 scale rows
+};
+
+struct SkFrag {
+  bf16x8 a[2][2];          // [m][step]
+  bf16x8 b[4][2];          // [n][step]
+};
+
+template <bool MX>
+__device__ __forceinline__ void sk_load(const SkRows& r, int k0, int K, SkFrag& f) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const int k = k0 + g * 16 + st * 8;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) f.a[m][st] = ld_frag(r.a[m], k, K);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      if constexpr (MX) f.b[n][st] = ld_frag_mx((const uint8_t*)r.b[n], r.bs[n], k, K);
+      else f.b[n][st] = ld_frag((const bf16_t*)r.b[n], k, K);
+    }
+  }
+}
+
+// acc[m][n] over this wave's share of K, then a fixed-order reduction over
+// the four waves into red (LDS, 4 x 32 x 64 floats).
+template <bool MX>
+__device__ void sk_mainloop(const SkRows& r, int K, float* red) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nchunk = (int)ceil_div(K, 64);
+  const int c0 = (wv * nchunk) / 4, c1 = ((wv + 1) * nchunk) / 4;
+  if (c0 < c1) {
+    SkFrag cur, nxt;
+    sk_load<MX>(r, c0 * 64, K, cur);
+    for (int c = c0; c < c1; ++c) {
+      if (c + 1 < c1) sk_load<MX>(r, (c + 1) * 64, K, nxt);
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[m][st], cur.b[n][st],
+                                                                acc[m][n], 0, 0, 0);
+      cur = nxt;
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) red[(wv * 32 + m * 16 + n * 4 + q) * 64 + lane] = acc[m][n][q];
+  __syncthreads();
+}
+
+// Sum of value i (= m*16 + n*4 + q) of `lane` over the four waves, in order.
+__device__ __forceinline__ float sk_sum(const float* red, int i, int lane) {
+  float s = red[(0 * 32 + i) * 64 + lane];
+  s += red[(1 * 32 + i) * 64 + lane];
+  s += red[(2 * 32 + i) * 64 + lane];
+  s += red[(3 * 32 + i) * 64 + lane];
+  return s;
+}
+
+// Output position of value (m, n, q) of `lane`: tile row m*16 + 4*(lane/16) + q,
+// tile column n*16 + lane%16 (the 16x16 accumulator layout).
+template <bool MX>
+__global__ __launch_bounds__(256) void skinny_glu_kernel(GroupedGluArgs a) {
+  __shared__ float red[4 * 32 * 64];
+  const int tile = blockIdx.y;
+  if (tile >= a.tile_off[a.E]) return;
+  const int e = expert_of_tile(a.tile_off, a.E, tile);
+  const int row_lo = a.offsets[e] + (tile - a.tile_off[e]) * SK_BM;
+  const int row_hi = min(min(a.offsets[e + 1], row_lo + SK_BM), a.rows_cap);
+  const int f0 = blockIdx.x * 32;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15;
+
+  SkRows r;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int row = row_lo + m * 16 + l16;
+    const bf16_t* p = nullptr;
+    if (row >= 0 && row < row_hi) {
+      const int src = a.perm_src[row];
+      const int t = src / a.topk;
+      if (src >= 0 && t < a.T) p = (const bf16_t*)a.Z + (int64_t)t * a.ldz;
+    }
+    r.a[m] = p;
+  }
+  const int64_t wrow = (int64_t)e * a.F;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int f = f0 + (n & 1) * 16 + l16;
+    const WOperand& w = (n < 2) ? a.Wg : a.Wv;
+    const bool ok = f < a.F;
+    if constexpr (MX) {
+      r.b[n] = ok ? (const void*)((const uint8_t*)w.data + (wrow + f) * (a.K / 2)) : nullptr;
+      r.bs[n] = ok ? w.scale + (wrow + f) * (a.K / 32) : nullptr;
+    } else {
+      r.b[n] = ok ? (const void*)((const bf16_t*)w.data + (wrow + f) * a.K) : nullptr;
+      r.bs[n] = nullptr;
+    }
+  }
+  sk_mainloop<MX>(r, a.K, red);
+
+  const float inv_c = 1.0f / a.c;
+  bf16_t* H = (bf16_t*)a.H;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int pidx = wv * 4 + j;              // 16 (gate, up) pairs per lane
+    const int m = pidx >> 3, n = (pidx >> 2) & 1, q = pidx & 3;
+    const float g = sk_sum(red, m * 16 + n * 4 + q, lane);
+    const float v = sk_sum(red, m * 16 + (n + 2) * 4 + q, lane);
+    const int row = row_lo + m * 16 + 4 * (lane >> 4) + q;
+    const int f = f0 + n * 16 + l16;
+    if (row < row_hi && f < a.F) H[(int64_t)row * a.F + f] = f32_to_bf16(situ_glu(g, v, a.c, inv_c));
+  }
+}
+
+template <bool MX>
+__global__ __launch_bounds__(256) void skinny_down_kernel(GroupedDownArgs a) {
+  __shared__ float red[4 * 32 * 64];
+  const int tile = blockIdx.y;
+  if (tile >= a.tile_off[a.E]) return;
+  const int e = expert_of_tile(a.tile_off, a.E, tile);
+  const int row_lo = a.offsets[e] + (tile - a.tile_off[e]) * SK_BM;
+  const int row_hi = min(min(a.offsets[e + 1], row_lo + SK_BM), a.rows_cap);
+  const int n0 = blockIdx.x * 64;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15;
+
+  SkRows r;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int row = row_lo + m * 16 + l16;
+    r.a[m] = (row >= 0 && row < row_hi) ? (const bf16_t*)a.H + (int64_t)row * a.ldh : nullptr;
+  }
+  const int64_t wrow = (int64_t)e * a.N;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int col = n0 + n * 16 + l16;
+    const bool ok = col < a.N;
+    if constexpr (MX) {
+      r.b[n] = ok ? (const void*)((const uint8_t*)a.Wo.data + (wrow + col) * (a.K / 2)) : nullptr;
+      r.bs[n] = ok ? a.Wo.scale + (wrow + col) * (a.K / 32) : nullptr;
+    } else {
+      r.b[n] = ok ? (const void*)((const bf16_t*)a.Wo.data + (wrow + col) * a.K) : nullptr;
+      r.bs[n] = nullptr;
+    }
+  }
+  sk_mainloop<MX>(r, a.K, red);
+
+  bf16_t* O = (bf16_t*)a.O;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = wv * 8 + j;                 // 32 values per lane
+    const int m = i >> 4, n = (i >> 2) & 3, q = i & 3;
+    const float v = sk_sum(red, i, lane);
+    const int row = row_lo + m * 16 + 4 * (lane >> 4) + q;
+    const int col = n0 + n * 16 + l16;
+    if (row < row_hi && col < a.N) O[(int64_t)row * a.N + col] = f32_to_bf16(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // kernels (fp32 activations and weights): one thread per output
 // ---------------------------------------------------------------------------
 
@@ -562,7 +780,10 @@ unsigned blocks_for(int64_t n) { return (unsigned)ceil_div(n, 256); }
 
 }  // namespace
 
-int grouped_bm(int act_dtype, int64_t, int) { return act_dtype == DT_F32 ? 1 : BM; }
+int grouped_bm(int act_dtype, int64_t rows, int E) {
+  if (act_dtype == DT_F32) return 1;
+  return rows <= (int64_t)SK_BM * E ? SK_BM : BM;
+}
 
 int launch_dense(const DenseArgs& a, hipStream_t stream) {
   if (a.M == 0) return 0;
@@ -611,6 +832,13 @@ int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream) {
                        stream, a);
     return (int)hipGetLastError();
   }
+  if (a.bm == SK_BM) {
+    dim3 g((unsigned)ceil_div(a.F, 32), (unsigned)a.max_tiles);
+    if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(skinny_glu_kernel<true>, g, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(skinny_glu_kernel<false>, g, dim3(256), 0, stream, a);
+    return (int)hipGetLastError();
+  }
+  if (a.bm != BM) return -1;
   dim3 grid((unsigned)ceil_div(a.F, BN / 2), (unsigned)a.max_tiles);
   if (a.Wg.dtype == DT_MXFP4) {
     hipLaunchKernelGGL(grouped_glu_kernel<true>, grid, dim3(256), LDS_BYTES, stream, a);
@@ -630,6 +858,13 @@ int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream) {
                        stream, a);
     return (int)hipGetLastError();
   }
+  if (a.bm == SK_BM) {
+    dim3 g((unsigned)ceil_div(a.N, 64), (unsigned)a.max_tiles);
+    if (a.Wo.dtype == DT_MXFP4) hipLaunchKernelGGL(skinny_down_kernel<true>, g, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(skinny_down_kernel<false>, g, dim3(256), 0, stream, a);
+    return (int)hipGetLastError();
+  }
+  if (a.bm != BM) return -1;
   dim3 grid((unsigned)ceil_div(a.N, BN), (unsigned)a.max_tiles);
   if (a.Wo.dtype == DT_MXFP4) {
     hipLaunchKernelGGL(grouped_down_kernel<true>, grid, dim3(256), LDS_BYTES, stream, a);

@@ -82,9 +82,12 @@ struct GroupedGluArgs {
   void* H;                           // [rows, F]
   float c;
   int act_dtype;
+  int bm;                            // tile rows (grouped_bm)
 };
 int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream);
-int grouped_bm(int act_dtype, int64_t rows, int E);  // BM used by the grouped kernels
+// Tile rows of the grouped expert kernels: 1 (fp32 path), 32 (few rows per
+// expert: the weight-streaming kernel) or 128 (the LDS-tiled MFMA kernel).
+int grouped_bm(int act_dtype, int64_t rows, int E);
 
 // down: O[r] = H[r] Wo[e]^T, Wo [E, N, K].
 struct GroupedDownArgs {
@@ -97,6 +100,7 @@ struct GroupedDownArgs {
   int E, N, K;
   void* O;
   int act_dtype;
+  int bm;                            // tile rows (grouped_bm)
 };
 int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream);
 

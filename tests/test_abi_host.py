@@ -1,0 +1,185 @@
+"""Host-side contract of the C ABI (no GPU needed): the library loads, exports
+every symbol include/moe.h declares, and every validation error is returned
+before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+import sparse_mixture_experts_sigmoid_amd as moe
+from synth.configs import LayerConfig
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 14
+    L = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(moe.EXPORTS) == set(names)
+
+
+def test_status_strings():
+    L = moe.lib()
+    assert L.moe_status_string(0) == b"MOE_OK"
+    assert L.moe_status_string(-3) == b"MOE_ERR_WORKSPACE"
+    assert L.moe_status_string(42) == b"MOE_ERR_UNKNOWN"
+    assert L.moe_trace_stage_name(5) == b"expert_gate_up"
+    assert L.moe_trace_stage_name(99) == b""
+
+
+@pytest.mark.parametrize("cfg", synth.CONFIGS, ids=lambda c: c.name)
+def test_configs_are_valid(cfg):
+    assert moe.moe_check_desc(moe.make_desc(cfg)) == moe.MOE_OK
+
+
+def _desc(**kw):
+    d = moe.make_desc(synth.config("k3_decode"))
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(top_k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(top_k=897), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(d_model=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_experts=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_shared=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(situ_c=0.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(situ_c=float("nan")), moe.MOE_ERR_INVALID_ARG),
+    (dict(rms_eps=-1.0), moe.MOE_ERR_INVALID_ARG),
+    (dict(act_dtype=7), moe.MOE_ERR_INVALID_ARG),
+    (dict(d_model=7160), moe.MOE_ERR_UNSUPPORTED),          # not a multiple of 32
+    (dict(d_ff=3000), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=moe.MOE_MXFP4), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype=moe.MOE_F32), moe.MOE_ERR_UNSUPPORTED),   # bf16 weights with fp32 act
+    (dict(dense_w_dtype=moe.MOE_MXFP4), moe.MOE_ERR_UNSUPPORTED),
+    (dict(expert_w_dtype=moe.MOE_F32), moe.MOE_ERR_UNSUPPORTED),
+    (dict(n_experts=5000, top_k=16), moe.MOE_ERR_UNSUPPORTED),
+    (dict(n_shared=8), moe.MOE_ERR_UNSUPPORTED),
+])
+def test_invalid_descriptors(kw, status):
+    d = _desc(**kw)
+    assert moe.moe_check_desc(d) == status
+    assert moe.lib().moe_last_error() != b""
+    assert moe.moe_workspace_bytes(d, moe.MOE_OP_LAYER) == 0
+
+
+def test_workspace_sizes():
+    cfg = synth.config("k3_prefill")
+    d = moe.make_desc(cfg)
+    ws = [moe.moe_workspace_bytes(d, op) for op in range(7)]
+    assert ws[moe.MOE_OP_LATENT_DOWN] == 0 and ws[moe.MOE_OP_COMBINE] == 0
+    assert ws[moe.MOE_OP_ROUTE] == 2 * cfg.T * cfg.E * 4
+    assert ws[moe.MOE_OP_EXPERT_FFN] >= cfg.T * cfg.k * cfg.F * 2
+    assert ws[moe.MOE_OP_LAYER] >= sum(ws[:6])
+    d2 = moe.make_desc(cfg, T=cfg.T // 2)
+    assert moe.moe_workspace_bytes(d2, moe.MOE_OP_LAYER) < ws[moe.MOE_OP_LAYER]
+    assert moe.moe_workspace_bytes(d, 99) == 0
+
+
+FAKE = 0x7f0000001000          # a 16-byte-aligned address that is never dereferenced
+MIS = FAKE + 4                 # misaligned
+
+
+def _weights(**over):
+    keys = ("W_r", "b", "W_ld", "W_lu", "W_g", "W_v", "W_o", "W_gs", "W_vs", "W_os")
+    w = {k: FAKE for k in keys}
+    w.update(over)
+    return w
+
+
+def _call_layer(d, w, ws_bytes=None, x=FAKE, y=FAKE):
+    L = moe.lib()
+    n = moe.moe_workspace_bytes(d, moe.MOE_OP_LAYER) if ws_bytes is None else ws_bytes
+    mw = moe.make_weights(w)
+    return L.moe_layer_forward(ctypes.byref(d), ctypes.byref(mw), x, y, None, None, None,
+                               FAKE, n, None)
+
+
+def test_layer_rejects_bad_pointers_before_any_launch():
+    d = moe.make_desc(synth.config("k3_decode"))
+    assert _call_layer(d, _weights(), x=None) == moe.MOE_ERR_INVALID_ARG
+    assert b"x is NULL" in moe.lib().moe_last_error()
+    assert _call_layer(d, _weights(), y=MIS) == moe.MOE_ERR_INVALID_ARG
+    assert b"aligned" in moe.lib().moe_last_error()
+    assert _call_layer(d, _weights(W_g=None)) == moe.MOE_ERR_INVALID_ARG
+    assert _call_layer(d, _weights(b=None)) == moe.MOE_ERR_INVALID_ARG
+    assert _call_layer(d, _weights(W_os=None)) == moe.MOE_ERR_INVALID_ARG
+    assert _call_layer(d, _weights(), ws_bytes=1024) == moe.MOE_ERR_WORKSPACE
+    assert b"workspace" in moe.lib().moe_last_error()
+    L = moe.lib()
+    assert L.moe_layer_forward(ctypes.byref(d), None, FAKE, FAKE, None, None, None, FAKE, 1 << 40,
+                               None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_layer_forward(None, None, FAKE, FAKE, None, None, None, FAKE, 0, None) \
+        == moe.MOE_ERR_INVALID_ARG
+
+
+def test_shared_weights_not_needed_without_shared_experts():
+    cfg = synth.config("k3_decode").replace(S=0)
+    d = moe.make_desc(cfg)
+    # with S = 0 a NULL shared weight is fine: the call gets past validation and
+    # then fails on the workspace check we force
+    assert _call_layer(d, _weights(W_gs=None, W_vs=None, W_os=None), ws_bytes=16) \
+        == moe.MOE_ERR_WORKSPACE
+
+
+def test_mxfp4_weights_need_scales():
+    d = moe.make_desc(synth.config("k3_prefill_mxfp4"))
+    w = _weights(W_g=(FAKE, None))
+    assert _call_layer(d, w) == moe.MOE_ERR_INVALID_ARG
+    assert b"scales" in moe.lib().moe_last_error()
+
+
+def test_staged_entry_points_validate():
+    L = moe.lib()
+    d = moe.make_desc(synth.config("k3_decode"))
+    rw = moe.MoeW(FAKE, None)
+    assert L.moe_route(ctypes.byref(d), FAKE, rw, None, FAKE, FAKE, None, FAKE, 1 << 40, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route(ctypes.byref(d), FAKE, rw, FAKE, FAKE, FAKE, MIS, FAKE, 1 << 40, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route(ctypes.byref(d), FAKE, rw, FAKE, FAKE, FAKE, None, FAKE, 8, None) \
+        == moe.MOE_ERR_WORKSPACE
+    assert L.moe_permute(ctypes.byref(d), FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_latent_down(ctypes.byref(d), FAKE, moe.MoeW(None, None), FAKE, None, 0, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    mw = moe.make_weights(_weights(W_o=None))
+    assert L.moe_expert_ffn(ctypes.byref(d), FAKE, FAKE, FAKE, ctypes.byref(mw), FAKE, FAKE,
+                            1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(ctypes.byref(d), FAKE, FAKE, FAKE, MIS, FAKE, None, None) \
+        == moe.MOE_ERR_INVALID_ARG
+    mw = moe.make_weights(_weights(W_lu=None))
+    assert L.moe_output(ctypes.byref(d), FAKE, FAKE, ctypes.byref(mw), FAKE, FAKE, 1 << 40, None) \
+        == moe.MOE_ERR_INVALID_ARG
+
+
+def test_empty_batch_allows_null_token_buffers():
+    """T = 0: token-sized buffers may be NULL; validation passes (and the
+    forced tiny workspace is still enough, since nothing token-sized is needed
+    beyond the per-expert tables)."""
+    cfg = synth.config("tiny_f32").replace(T=0)
+    d = moe.make_desc(cfg)
+    need = moe.moe_workspace_bytes(d, moe.MOE_OP_LAYER)
+    assert need > 0          # per-expert tables
+    assert _call_layer(d, _weights(), ws_bytes=need - 1, x=None, y=None) == moe.MOE_ERR_WORKSPACE
+
+
+def test_trace_read_argument_checks():
+    L = moe.lib()
+    assert L.moe_trace_read(None, 3, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_trace_enable(-1) == moe.MOE_ERR_INVALID_ARG

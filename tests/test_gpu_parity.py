@@ -22,6 +22,7 @@ SMALL_MX = SMALL_BF16.replace(name="small_mxfp4", expert_w="mxfp4", latent_w="mx
 # several 128-row tiles per expert, ragged in M, N and K
 MID_BF16 = LayerConfig("mid_bf16", T=700, d=320, d_lat=192, E=6, k=2, F=224, S=1, Fs=160, seed=13,
                        bias=("uniform", 0.05))
+MID_MX = MID_BF16.replace(name="mid_mxfp4", expert_w="mxfp4", latent_w="mxfp4", seed=14)
 
 
 # ---------------------------------------------------------------------------
@@ -149,7 +150,7 @@ def test_permute_skewed_and_empty(device):
 # the whole layer
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cfg", [synth.config("tiny_f32"), SMALL_BF16, SMALL_MX, MID_BF16],
+@pytest.mark.parametrize("cfg", [synth.config("tiny_f32"), SMALL_BF16, SMALL_MX, MID_BF16, MID_MX],
                          ids=lambda c: c.name)
 def test_layer_small_full_parity(cfg, device):
     say(f"layer {cfg.name}")
@@ -198,10 +199,12 @@ def test_staged_entry_points_equal_layer(device):
     assert np.abs(u.cpu().numpy() - u_ref).max() <= 2e-2 * np.sqrt((u_ref ** 2).mean())
 
 
-def test_mxfp4_path_equals_bf16_path_on_decoded_weights(device):
+@pytest.mark.parametrize("cfg", [SMALL_MX, MID_MX], ids=lambda c: c.name)
+def test_mxfp4_path_equals_bf16_path_on_decoded_weights(cfg, device):
     """MXFP4 decoding is exact: the MXFP4 layer must equal, bit for bit, the bf16
-    layer run on the decoded weights (same kernels, same accumulation order)."""
-    cfg = SMALL_MX
+    layer run on the decoded weights (same kernels, same accumulation order).
+    The small layer takes the weight-streaming expert kernels, the mid one the
+    LDS-tiled ones."""
     inp = synth.device_inputs(cfg, device)
     y_mx, _, _, _ = run_layer(cfg, inp, device)
     dec = dict(inp)
