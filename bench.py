@@ -47,7 +47,31 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample (0 = skip)")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-probe", type=float, default=0.0, metavar="GB",
+                    help="instead of the layer: time a plain device-to-device copy of GB "
+                         "gigabytes (the reference for HBM rates and PMC byte counters)")
     return ap.parse_args()
+
+
+def copy_probe(gb: float, steps: int):
+    """Plain copy kernel of known size: read gb GB + write gb GB per launch."""
+    import torch
+    n = int(gb * 1e9) // 16 * 16
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    print(json.dumps({"probe": "device copy", "bytes_read_per_launch": n,
+                      "bytes_written_per_launch": n, "ms_per_launch": round(ms, 4),
+                      "read_plus_write_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def log(args, *a):
@@ -84,6 +108,10 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only: the layer's hot path is "
                                    "measured on a single MI355X; use --gpus 1"}))
         return 2
+
+    if args.copy_probe > 0:
+        copy_probe(args.copy_probe, args.steps)
+        return 0
 
     import numpy as np
     import torch

@@ -2,338 +2,510 @@
 //
 // Equations on "Kimi K3の896エキスパートを「896人の専門家」と呼ぶと何がズレるか"
 // (lilting.ch, section "K3のエキスパートは896個の小型LLMではない"):
-//   z = W_down x                       -> dense   (latent down)
-//   E_i(z) = W_o act(W_g z, W_v z)     -> grouped_glu + grouped_down (routed experts)
-//   E_s(x)                             -> glu (shared gate/up) + multiseg
-//   y = sum_s E_s(x) + W_up RMSNorm(u) -> multiseg: one GEMM whose K runs over the
-//                                          shared experts' down projections and
-//                                          then over W_up (sums over experts are
-//                                          concatenations along K)
+//   z = W_down x                       -> dense_kernel      (latent down)
+//   E_i(z) = W_o act(W_g z, W_v z)     -> grouped_glu_kernel + grouped_down_kernel
+//   E_s(x), shared gate/up             -> glu_kernel
+//   y = sum_s E_s(x) + W_up RMSNorm(u) -> multiseg_kernel: one GEMM whose K runs
+//                                         over the shared experts' down projections
+//                                         and then over W_up (a sum over experts
+//                                         is a concatenation along K)
 // Activation SiTU-GLU ("Kimi K3 テクニカルレポート", jiwasawa.github.io, section
-// "幅のスケーリング: Stable LatentMoE"): act(g, v) = c tanh(SiLU(g)/c) c tanh(v/c).
-// MXFP4 weights ("Kimi K3 ... Open Frontier Intelligence", ai-tech-express.jp,
-// section "MXFP4 Quantization-Aware Training") are decoded to bf16 while they
-// are staged into LDS; decoding is exact, so the MFMA itself stays bf16.
+// "幅のスケーリング: Stable LatentMoE"): act(g, v) = c tanh(SiLU(g)/c) c tanh(v/c),
+// fused into the gate/up epilogue. MXFP4 weights ("Kimi K3 ... Open Frontier
+// Intelligence", ai-tech-express.jp, section "MXFP4 Quantization-Aware
+// Training") are decoded exactly to bf16 while they are staged into LDS, so
+// the MFMA itself stays bf16.
 //
-// Engine (bf16): block tile 128 x 128 x 64, 256 threads = 4 wave64 in a 2 x 2
-// grid, each wave 64 x 64 = 2 x 2 tiles of v_mfma_f32_32x32x16_bf16, fp32
-// accumulators. Operands are staged global -> registers -> LDS (row stride 72
-// bf16: 16-byte reads of 8 consecutive rows hit distinct banks), double
-// buffered: the next K-tile's global loads are in flight while the MFMAs run.
-// Every weight row is K-contiguous ([out, in] layout), so A and B tiles are
-// both "rows x K" and load the same way.
-//
-// fp32 activations (the small fp32 layer) use plain one-thread-per-output
-// kernels: that layer is a parity case, not a throughput target.
+// Engine: 256 threads = 4 wave64 in a 2 x 2 grid; a wave owns WM x WN tiles of
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulators), so the block tile is
+// (64 WM) x (64 WN) x 64. Dense GEMMs use 256 x 256 tiles (each wave 128 x 128:
+// LDS traffic per MFMA low enough for the matrix cores to be the limit);
+// grouped expert GEMMs use 128 x 256 (an expert's row count is rarely a
+// multiple of 256). bf16 operands go straight from global memory into LDS
+// (buffer_load ... lds, 16 bytes per lane, no register staging), into an
+// unpadded layout of 128-byte rows whose 16-byte chunk c of row r sits in slot
+// c ^ ((r >> 1) & 7): the MFMA operand reads (16 consecutive rows, same chunk,
+// per LDS cycle) then hit distinct banks. MXFP4 weights are loaded to registers, decoded, and written
+// to the same layout. Double buffered: the next K-tile's loads are in flight
+// during this tile's MFMAs. Loads are raw buffer loads from per-block bases:
+// an offset past the buffer (rows past M, k past K, masked rows) returns
+// zeros, so no load sits behind a branch. Every weight row is K-contiguous
+// ([out, in] layout), so A and B tiles are both "rows x K" and stage the same
+// way.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDK = BK + 8;                         // LDS row stride (bf16 elements)
-constexpr int STAGE = (BM + BN) * LDK;              // elements per pipeline stage
-constexpr size_t LDS_BYTES = 2 * STAGE * sizeof(bf16_t);
+constexpr int BK = 64;
+constexpr int LDK = BK;  // LDS row stride (bf16 elements): 128 bytes, swizzled chunks
+
+template <int WM_, int WN_, int NS_>
+struct Cfg {
+  static constexpr int WM = WM_, WN = WN_, NS = NS_;
+  static constexpr int BM = 64 * WM, BN = 64 * WN;
+  static constexpr int AR = BM / 32;          // A: 8-row DMA loads per wave per stage
+  static constexpr int BR = BN / 32;          // B: 8-row DMA loads per wave per stage
+  static constexpr int MXU = BN / 128;        // MXFP4 (row, 32-k half) units per thread
+  static constexpr int STAGE = (BM + BN) * LDK;
+  static constexpr size_t LDS = NS * STAGE * sizeof(bf16_t);
+};
+using DenseCfg = Cfg<4, 2, 3>;   // 256 x 128, 3 LDS stages of 48 KB
+using GroupCfg = Cfg<2, 4, 3>;   // 128 x 256, 3 LDS stages of 48 KB
+
+// ---------------------------------------------------------------------------
+// buffer loads
+// ---------------------------------------------------------------------------
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;  // past every buffer (each is < 2^31 bytes)
+
+// Every resource is built from block-uniform values; readfirstlane states that
+// to the compiler so the descriptor lives in scalar registers (a descriptor in
+// vector registers turns each load into a waterfall loop).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
 
 // ---------------------------------------------------------------------------
 // operand staging
 // ---------------------------------------------------------------------------
 
-// This thread's share of a 128-row x 64-k bf16 tile: rows r0 + 32 i (i < 4),
-// k-chunk kc (8 elements = 16 bytes); 8 consecutive threads cover one row's
-// 128 bytes.
-struct RowSet {
-  const bf16_t* row[4];  // start of each row in global memory (nullptr: zero row)
+// bf16 rows by DMA: wave w fills tile rows w*8N .. w*8N + 8N-1, one 8-row
+// (1 KB) buffer_load ... lds per q < N; lane i of load q takes tile row
+// w*8N + 8q + i/8 and writes LDS slot i%8 of it, so it fetches global chunk
+// (i%8) ^ (i/8) of that row. Rows of one wave come through resource r[sel]
+// (gate or up weights of a GLU tile; sel is wave-uniform).
+template <int N>
+struct Rows {
+  rsrc_t r[2];
+  int sel;
+  uint32_t off[N];  // byte offset of this lane's row of load q, or kOOB
 };
 
-__device__ __forceinline__ void load_rows(const RowSet& rs, int kc, int k0, int K, uint4 (&v)[4]) {
-  const int k = k0 + kc * 8;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS layout of a 128-byte tile row r: its 16-byte chunk c sits in slot
+// c ^ swz(r). 16 lanes of a b128 read (16 consecutive rows, one chunk) then
+// cover all 64 banks: rows r and r^1 differ in bank half, and swz takes 8
+// distinct values over the even (odd) rows of any aligned 16-row group.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+template <int N>
+__device__ __forceinline__ void dma_rows(const Rows<N>& rs, bf16_t* tile, int k0, int K) {
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: LDS base in M0
+  const rsrc_t r = rs.sel ? rs.r[1] : rs.r[0];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (rs.row[i] != nullptr && k < K) v[i] = *(const uint4*)(rs.row[i] + k);
-    else v[i] = make_uint4(0, 0, 0, 0);
+  for (int q = 0; q < N; ++q) {
+    const int row0 = wv * 8 * N + 8 * q;
+    const int c = (lane & 7) ^ swz(row0 + (lane >> 3));  // global chunk for LDS slot lane % 8
+    const int k = k0 + c * 8;
+    const uint32_t o = rs.off[q];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(tile + row0 * LDK), 16,
+                                             (k < K && o != kOOB) ? o + 2u * (uint32_t)k : kOOB,
+                                             0, 0, 0);
   }
 }
 
-__device__ __forceinline__ void store_rows(bf16_t* tile, int r0, int kc, const uint4 (&v)[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *(uint4*)(tile + (r0 + 32 * i) * LDK + kc * 8) = v[i];
+// tile row of this lane's load q
+template <int N>
+__device__ __forceinline__ int dma_row(int q) {
+  return (threadIdx.x >> 6) * 8 * N + 8 * q + ((threadIdx.x & 63) >> 3);
 }
 
-// MXFP4 rows: this thread owns one (row, 32-element half) unit of the
-// 128-row x 64-k tile: row = tid / 2, half = tid % 2.
-struct MxRow {
-  const uint8_t* packed;  // row start (K/2 bytes), nullptr: zero row
-  const uint8_t* scale;   // row start (K/32 bytes)
+// MXFP4 rows: unit j of thread t is tile row (t >> 1) + 128 j, 32-k half (t & 1).
+template <int N>
+struct MxRows {
+  rsrc_t rp[2], rs[2];   // packed bytes, e8m0 scales (gate / up for the GLU tile)
+  int sel[N];            // resource of unit j (wave-uniform)
+  uint32_t poff[N];      // packed-row byte offset, or kOOB
+  uint32_t soff[N];      // scale-row byte offset
 };
 
 struct MxStage {
-  uint4 q;       // 32 e2m1 codes
-  uint32_t s;    // e8m0 scale byte (256 = zero block)
+  uint4 q;      // 32 e2m1 codes
+  uint32_t s;   // e8m0 scale byte
 };
 
-__device__ __forceinline__ void load_mx(const MxRow& m, int half, int k0, int K, MxStage& st) {
-  const int k = k0 + half * 32;
-  if (m.packed != nullptr && k < K) {
-    st.q = *(const uint4*)(m.packed + k / 2);
-    st.s = m.scale[k / 32];
-  } else {
-    st.q = make_uint4(0, 0, 0, 0);
-    st.s = 256;
+template <int N>
+__device__ __forceinline__ void load_mx(const MxRows<N>& m, int k0, int K, MxStage (&st)[N]) {
+  const int k = k0 + (threadIdx.x & 1) * 32;
+  const bool kin = k < K;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const bool ok = kin && m.poff[j] != kOOB;
+    const rsrc_t rp = m.sel[j] ? m.rp[1] : m.rp[0];
+    const rsrc_t rsc = m.sel[j] ? m.rs[1] : m.rs[0];
+    st[j].q = bload16(rp, ok ? m.poff[j] + (uint32_t)(k / 2) : kOOB);
+    st[j].s = __builtin_amdgcn_raw_buffer_load_b8(rsc, ok ? m.soff[j] + (uint32_t)(k / 32) : kOOB, 0, 0);
   }
 }
 
 // e2m1 code (4 bits) -> bf16 bits of its value (OCP MX: 0, .5, 1, 1.5, 2, 3, 4, 6).
 __device__ __forceinline__ uint32_t e2m1_bf16(uint32_t c) {
-  uint32_t m = c & 7u;
-  uint32_t b = (m >= 2u) ? (0x3F80u + ((m - 2u) << 6)) : (m == 1u ? 0x3F00u : 0u);
+  const uint32_t m = c & 7u;
+  const uint32_t b = (m >= 2u) ? (0x3F80u + ((m - 2u) << 6)) : (m == 1u ? 0x3F00u : 0u);
   return b | ((c & 8u) << 12);
 }
 
-// value * 2^(s-127) exactly (power-of-two scaling of a 2-significant-bit value).
+// value * 2^(s-127), exact (power-of-two scaling of a 2-significant-bit value).
 __device__ __forceinline__ uint32_t scale_bf16(uint32_t b, float scale) {
-  float v = __uint_as_float(b << 16) * scale;
-  return __float_as_uint(v) >> 16;
+  return __float_as_uint(__uint_as_float(b << 16) * scale) >> 16;
 }
 
-__device__ __forceinline__ void store_mx(bf16_t* tile, int row, int half, const MxStage& st) {
-  uint32_t w[16];
-  if (st.s == 256u) {
+template <int N>
+__device__ __forceinline__ void store_mx(bf16_t* tile, const MxStage (&st)[N]) {
+  const int half = threadIdx.x & 1;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) w[i] = 0;
-  } else {
-    const float scale = st.s == 0u ? 0x1p-127f : __uint_as_float(st.s << 23);
-    const uint32_t q[4] = {st.q.x, st.q.y, st.q.z, st.q.w};
+  for (int j = 0; j < N; ++j) {
+    const int row = (threadIdx.x >> 1) + 128 * j;
+    // a zero-filled (out-of-range) block decodes to zeros whatever its scale byte
+    const float scale = st[j].s == 0u ? 0x1p-127f : __uint_as_float(st[j].s << 23);
+    const uint32_t q[4] = {st[j].q.x, st[j].q.y, st[j].q.z, st[j].q.w};
+    uint32_t w[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t byte = (q[i / 4] >> (8 * (i % 4))) & 0xFFu;
-      const uint32_t lo = scale_bf16(e2m1_bf16(byte & 0xFu), scale);
-      const uint32_t hi = scale_bf16(e2m1_bf16(byte >> 4), scale);
-      w[i] = lo | (hi << 16);
+      w[i] = scale_bf16(e2m1_bf16(byte & 0xFu), scale) |
+             (scale_bf16(e2m1_bf16(byte >> 4), scale) << 16);
     }
-  }
-  bf16_t* dst = tile + row * LDK + half * 32;
+    bf16_t* dst = tile + row * LDK;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *(uint4*)(dst + 8 * i) = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    for (int i = 0; i < 4; ++i)
+      *(uint4*)(dst + 8 * ((half * 4 + i) ^ swz(row))) =
+          make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// the MFMA main loop over one K range
+// the MFMA main loop
 // ---------------------------------------------------------------------------
 
+template <class C>
 struct Acc {
-  f32x16 c[2][2];
+  f32x16 c[C::WM][C::WN];
 };
 
-__device__ __forceinline__ void acc_zero(Acc& acc) {
+template <class C>
+__device__ __forceinline__ void acc_zero(Acc<C>& acc) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < C::WN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc.c[i][j][r] = 0.0f;
 }
 
-__device__ __forceinline__ void mma_stage(const bf16_t* As, const bf16_t* Bs, int wm, int wn,
-                                          int lane, Acc& acc) {
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
+template <class C>
+__device__ __forceinline__ void mma_stage(const bf16_t* As, const bf16_t* Bs, Acc<C>& acc) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, wm = wv >> 1, wn = wv & 1;
+  const int lr = lane & 31, lh = lane >> 5;
+  // row R = base + lr (base a multiple of 32): chunk kc sits in slot kc ^ swz(lr)
+  const bf16_t* Aw = As + (wm * (C::BM / 2) + lr) * LDK;
+  const bf16_t* Bw = Bs + (wn * (C::BN / 2) + lr) * LDK;
 #pragma unroll
   for (int ks = 0; ks < BK / 16; ++ks) {
-    bf16x8 a[2], b[2];
+    const int slot = 8 * ((2 * ks + lh) ^ swz(lr));
+    bf16x8 a[C::WM], b[C::WN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      a[i] = *(const bf16x8*)(As + (wm * 64 + i * 32 + lr) * LDK + ks * 16 + lk);
+    for (int i = 0; i < C::WM; ++i) a[i] = *(const bf16x8*)(Aw + i * 32 * LDK + slot);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      b[j] = *(const bf16x8*)(Bs + (wn * 64 + j * 32 + lr) * LDK + ks * 16 + lk);
+    for (int j = 0; j < C::WN; ++j) b[j] = *(const bf16x8*)(Bw + j * 32 * LDK + slot);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::WM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < C::WN; ++j)
         acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
   }
 }
 
-// acc += A_tile(rows of `ar`) * B_tile(rows of `br` / `bm`)^T over k in [0, K).
-template <bool B_MX>
-__device__ void mainloop(bf16_t* lds, const RowSet& ar, const RowSet& br, const MxRow& bm, int K,
-                         Acc& acc) {
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
-  const int r0 = tid >> 3, kc = tid & 7;
-  const int mrow = tid >> 1, mhalf = tid & 1;
+// s_waitcnt with only the vector-memory counter limited to n.
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Workgroup barrier without __syncthreads()'s release fence (that fence waits
+// for every outstanding load, which would empty the DMA ring each K-tile).
+// LDS needs no fence: each wave waits for its own DMA before it arrives here.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Three LDS stages, each its own array: the compiler tracks DMA writes per
+// array, so reading stage J waits only for the loads that fill stage J.
+constexpr int kStageElems = 384 * LDK;   // (BM + BN) rows of both tile shapes
+#define MOE_LDS_RING                                                                  \
+  __shared__ __align__(16) bf16_t lds0[kStageElems];                                \
+  __shared__ __align__(16) bf16_t lds1[kStageElems];                                \
+  __shared__ __align__(16) bf16_t lds2[kStageElems]
+
+// Issue the loads of K-tile kt into stage buffer buf. Every load is
+// unconditional (past K it reads zeros), so each stage issues the same number.
+template <class C, bool B_MX>
+__device__ __forceinline__ void stage_issue(bf16_t* buf, const Rows<C::AR>& ar, const Rows<C::BR>& br,
+                                            const MxRows<C::MXU>& bm, int kt, int K) {
+  if constexpr (B_MX) {
+    // MXFP4 B: register loads first (the decode waits only for these), then A's DMA
+    MxStage mx[C::MXU];
+    load_mx(bm, kt * BK, K, mx);
+    dma_rows(ar, buf, kt * BK, K);
+    store_mx(buf + C::BM * LDK, mx);
+  } else {
+    dma_rows(ar, buf, kt * BK, K);
+    dma_rows(br, buf + C::BM * LDK, kt * BK, K);
+  }
+}
+
+// One K-tile: stage kt (in R) has landed once only the next stage's loads are
+// outstanding; after the barrier every wave is done with W (read one tile ago),
+// which receives K-tile kt + 2.
+template <class C, bool B_MX>
+__device__ __forceinline__ void ring_step(bf16_t* R, bf16_t* W, const Rows<C::AR>& ar,
+                                          const Rows<C::BR>& br, const MxRows<C::MXU>& bm, int kt,
+                                          int K, Acc<C>& acc) {
+  constexpr int kLoads = B_MX ? C::AR : C::AR + C::BR;  // DMA loads per thread per stage
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads));
+  wg_barrier();
+  stage_issue<C, B_MX>(W, ar, br, bm, kt + 2, K);
+  mma_stage<C>(R, R + C::BM * LDK, acc);
+}
+
+// acc += A_tile B_tile^T over k in [0, K) through the three-stage ring (two
+// K-tiles in flight). The K-tile count is rounded up to a multiple of 3; the
+// extra tiles read zeros. A rows: `ar` (bf16 DMA); B rows: `br` (bf16 DMA) or
+// `bm` (MXFP4, decoded through registers).
+template <class C, bool B_MX>
+__device__ __forceinline__ void mainloop(bf16_t* s0, bf16_t* s1, bf16_t* s2, const Rows<C::AR>& ar,
+                                         const Rows<C::BR>& br, const MxRows<C::MXU>& bm, int K,
+                                         Acc<C>& acc) {
+  static_assert((C::BM + C::BN) * LDK == kStageElems, "stage size");
   const int nk = (int)ceil_div(K, BK);
-
-  uint4 va[4], vb[4];
-  MxStage mx;
-  load_rows(ar, kc, 0, K, va);
-  if constexpr (B_MX) load_mx(bm, mhalf, 0, K, mx); else load_rows(br, kc, 0, K, vb);
-  store_rows(lds, r0, kc, va);
-  if constexpr (B_MX) store_mx(lds + BM * LDK, mrow, mhalf, mx);
-  else store_rows(lds + BM * LDK, r0, kc, vb);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    bf16_t* cur = lds + (kt & 1) * STAGE;
-    bf16_t* nxt = lds + ((kt + 1) & 1) * STAGE;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_rows(ar, kc, (kt + 1) * BK, K, va);
-      if constexpr (B_MX) load_mx(bm, mhalf, (kt + 1) * BK, K, mx);
-      else load_rows(br, kc, (kt + 1) * BK, K, vb);
-    }
-    mma_stage(cur, cur + BM * LDK, wm, wn, lane, acc);
-    if (more) {
-      store_rows(nxt, r0, kc, va);
-      if constexpr (B_MX) store_mx(nxt + BM * LDK, mrow, mhalf, mx);
-      else store_rows(nxt + BM * LDK, r0, kc, vb);
-    }
-    __syncthreads();
+  stage_issue<C, B_MX>(s0, ar, br, bm, 0, K);
+  stage_issue<C, B_MX>(s1, ar, br, bm, 1, K);
+  for (int kt = 0; kt < nk; kt += 3) {
+    ring_step<C, B_MX>(s0, s2, ar, br, bm, kt, K, acc);
+    ring_step<C, B_MX>(s1, s0, ar, br, bm, kt + 1, K, acc);
+    ring_step<C, B_MX>(s2, s1, ar, br, bm, kt + 2, K, acc);
   }
+  // drain the trailing (zero) loads before the buffers are reused
+  __builtin_amdgcn_s_waitcnt(0);
+  wg_barrier();
 }
 
-// Element (i, j, r) of this lane's accumulators sits at tile row / column:
-//   row = wm*64 + i*32 + 8*(r/4) + 4*(lane/32) + r%4,  col = wn*64 + j*32 + lane%32.
-__device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
-  return wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+// Element (i, j, r) of this lane's accumulators sits at tile row / column
+//   row = wm*BM/2 + i*32 + 8*(r/4) + 4*(lane/32) + r%4,  col = wn*BN/2 + j*32 + lane%32.
+template <class C>
+__device__ __forceinline__ int acc_row(int i, int r) {
+  const int lane = threadIdx.x & 63, wm = threadIdx.x >> 7;
+  return wm * (C::BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
-__device__ __forceinline__ int acc_col(int wn, int j, int lane) { return wn * 64 + j * 32 + (lane & 31); }
+template <class C>
+__device__ __forceinline__ int acc_col(int j) {
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+  return wn * (C::BN / 2) + j * 32 + (lane & 31);
+}
 
-// Row set for B rows n0 + tile_row of a [N, K] bf16 matrix (rows >= N: zero).
-__device__ __forceinline__ RowSet b_rows_plain(const bf16_t* W, int64_t ldw, int n0, int N) {
-  RowSet rs;
-  const int r0 = threadIdx.x >> 3;
+// ---------------------------------------------------------------------------
+// operand set-up helpers
+// ---------------------------------------------------------------------------
+
+// A rows m0 + tile_row of a row-major [M, lda] bf16 matrix (rows >= M read zeros).
+template <int N>
+__device__ __forceinline__ Rows<N> a_rows_dense(const void* A, int64_t lda, int m0, int M) {
+  Rows<N> rs;
+  const int nrows = max(0, min(M - m0, 32 * N));
+  rs.r[0] = rs.r[1] = make_rsrc((const bf16_t*)A + (int64_t)m0 * lda, (int64_t)nrows * lda * 2);
+  rs.sel = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int n = n0 + r0 + 32 * i;
-    rs.row[i] = n < N ? W + (int64_t)n * ldw : nullptr;
+  for (int q = 0; q < N; ++q) {
+    const int r = dma_row<N>(q);
+    rs.off[q] = r < nrows ? (uint32_t)((int64_t)r * lda * 2) : kOOB;
   }
   return rs;
 }
 
-__device__ __forceinline__ MxRow b_mx_plain(const uint8_t* P, const uint8_t* S, int K, int n0, int N) {
-  MxRow m;
-  int n = n0 + (threadIdx.x >> 1);
-  m.packed = n < N ? P + (int64_t)n * (K / 2) : nullptr;
-  m.scale = n < N ? S + (int64_t)n * (K / 32) : nullptr;
+// B rows n0 + tile_row of a [N, K] bf16 matrix.
+template <int NR>
+__device__ __forceinline__ Rows<NR> b_rows_plain(const void* W, int K, int n0, int N) {
+  return a_rows_dense<NR>(W, K, n0, N);
+}
+
+template <int NU>
+__device__ __forceinline__ MxRows<NU> b_mx_plain(const WOperand& w, int64_t row_base, int K, int n0,
+                                                 int N) {
+  MxRows<NU> m;
+  const int nrows = max(0, min(N - n0, 128 * NU));
+  const int64_t r0 = row_base + n0;
+  m.rp[0] = m.rp[1] = make_rsrc((const uint8_t*)w.data + r0 * (K / 2), (int64_t)nrows * (K / 2));
+  m.rs[0] = m.rs[1] = make_rsrc(w.scale + r0 * (K / 32), (int64_t)nrows * (K / 32));
+#pragma unroll
+  for (int j = 0; j < NU; ++j) {
+    const int row = (threadIdx.x >> 1) + 128 * j;
+    m.sel[j] = 0;
+    m.poff[j] = row < nrows ? (uint32_t)(row * (K / 2)) : kOOB;
+    m.soff[j] = row < nrows ? (uint32_t)(row * (K / 32)) : kOOB;
+  }
   return m;
 }
 
-// GLU B tile: wave column wn covers tile rows wn*64 .. +63 = gate rows f0 + wn*32 + (0..31)
-// then up rows f0 + wn*32 + (0..31).
-__device__ __forceinline__ void glu_row_of(int tile_row, int f0, int& f, bool& up) {
-  const int wn = tile_row >> 6, w = tile_row & 63;
-  up = w >= 32;
-  f = f0 + wn * 32 + (w & 31);
-}
-
-__device__ __forceinline__ RowSet b_rows_glu(const bf16_t* Wg, const bf16_t* Wv, int64_t ldw, int f0,
-                                             int F) {
-  RowSet rs;
-  const int r0 = threadIdx.x >> 3;
+// GLU B tile: wave column wn covers tile rows wn*BN/2 .. +BN/2: first the gate
+// rows f0 + wn*BN/4 + (0 .. BN/4-1) of Wg, then the same rows of Wv. The block
+// produces BN/2 outputs f0 .. f0 + BN/2 - 1.
+// Wave w fills tile rows w*BN/4 .. +BN/4, i.e. the gate half (w even) or the
+// up half (w odd) of wave column w/2.
+template <class C>
+__device__ __forceinline__ Rows<C::BR> b_rows_glu(const WOperand& g, const WOperand& v,
+                                                  int64_t row_base, int K, int f0, int F) {
+  static_assert(8 * C::BR == C::BN / 4, "one DMA wave per gate / up half");
+  Rows<C::BR> rs;
+  const int nf = max(0, min(F - f0, C::BN / 2));  // valid outputs of this block
+  rs.r[0] = make_rsrc((const bf16_t*)g.data + (row_base + f0) * K, (int64_t)nf * K * 2);
+  rs.r[1] = make_rsrc((const bf16_t*)v.data + (row_base + f0) * K, (int64_t)nf * K * 2);
+  const int wv = threadIdx.x >> 6;
+  rs.sel = __builtin_amdgcn_readfirstlane(wv & 1);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int f;
-    bool up;
-    glu_row_of(r0 + 32 * i, f0, f, up);
-    rs.row[i] = f < F ? (up ? Wv : Wg) + (int64_t)f * ldw : nullptr;
+  for (int q = 0; q < C::BR; ++q) {
+    const int fl = (wv >> 1) * (C::BN / 4) + 8 * q + ((threadIdx.x & 63) >> 3);
+    rs.off[q] = fl < nf ? (uint32_t)((int64_t)fl * K * 2) : kOOB;
   }
   return rs;
 }
 
-__device__ __forceinline__ MxRow b_mx_glu(const WOperand& g, const WOperand& v, int64_t row_base,
-                                          int K, int f0, int F) {
-  int f;
-  bool up;
-  glu_row_of(threadIdx.x >> 1, f0, f, up);
-  MxRow m;
-  const WOperand& w = up ? v : g;
-  m.packed = f < F ? (const uint8_t*)w.data + (row_base + f) * (K / 2) : nullptr;
-  m.scale = f < F ? w.scale + (row_base + f) * (K / 32) : nullptr;
+template <class C>
+__device__ __forceinline__ MxRows<C::MXU> b_mx_glu(const WOperand& g, const WOperand& v,
+                                                   int64_t row_base, int K, int f0, int F) {
+  MxRows<C::MXU> m;
+  const int nf = max(0, min(F - f0, C::BN / 2));
+  m.rp[0] = make_rsrc((const uint8_t*)g.data + (row_base + f0) * (K / 2), (int64_t)nf * (K / 2));
+  m.rs[0] = make_rsrc(g.scale + (row_base + f0) * (K / 32), (int64_t)nf * (K / 32));
+  m.rp[1] = make_rsrc((const uint8_t*)v.data + (row_base + f0) * (K / 2), (int64_t)nf * (K / 2));
+  m.rs[1] = make_rsrc(v.scale + (row_base + f0) * (K / 32), (int64_t)nf * (K / 32));
+#pragma unroll
+  for (int j = 0; j < C::MXU; ++j) {
+    const int row = (threadIdx.x >> 1) + 128 * j;          // tile row
+    const int wn = row / (C::BN / 2), w = row % (C::BN / 2);
+    // up-ness depends on bits of threadIdx that are uniform across the wave
+    m.sel[j] = __builtin_amdgcn_readfirstlane(w >= C::BN / 4 ? 1 : 0);
+    const int fl = wn * (C::BN / 4) + (w % (C::BN / 4));
+    m.poff[j] = fl < nf ? (uint32_t)(fl * (K / 2)) : kOOB;
+    m.soff[j] = fl < nf ? (uint32_t)(fl * (K / 32)) : kOOB;
+  }
   return m;
 }
 
-template <typename OT>
-__device__ __forceinline__ void store_tile(const Acc& acc, OT* C, int64_t ldc, int m0, int n0, int M,
-                                           int N) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, wm = wv >> 1, wn = wv & 1;
+// ---------------------------------------------------------------------------
+// epilogues
+// ---------------------------------------------------------------------------
+
+template <class C>
+__device__ __forceinline__ void store_tile(const Acc<C>& acc, bf16_t* Cm, int64_t ldc, int m0, int n0,
+                                           int M, int N) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + acc_col(wn, j, lane);
+    for (int j = 0; j < C::WN; ++j) {
+      const int n = n0 + acc_col<C>(j);
       if (n >= N) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int m = m0 + acc_row(wm, i, r, lane);
-        if (m < M) store_f32(C, (int64_t)m * ldc + n, acc.c[i][j][r]);
+        const int m = m0 + acc_row<C>(i, r);
+        if (m < M) Cm[(int64_t)m * ldc + n] = f32_to_bf16(acc.c[i][j][r]);
       }
     }
 }
 
-// rows: output row index of tile row (m0 + tr) is out_row(tr) (or < 0: skip)
-template <typename OT, typename RowMap>
-__device__ __forceinline__ void store_glu(const Acc& acc, OT* H, int64_t ldh, int f0, int F, float c,
-                                          RowMap out_row) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, wm = wv >> 1, wn = wv & 1;
+// out_row(tile_row) -> output row index, or < 0 to skip
+template <class C, typename RowMap>
+__device__ __forceinline__ void store_glu(const Acc<C>& acc, bf16_t* H, int64_t ldh, int f0, int F,
+                                          float c, RowMap out_row) {
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
   const float inv_c = 1.0f / c;
-  const int f = f0 + wn * 32 + (lane & 31);
-  if (f >= F) return;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int j = 0; j < C::WN / 2; ++j) {
+    const int f = f0 + wn * (C::BN / 4) + j * 32 + (lane & 31);
+    if (f >= F) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t orow = out_row(acc_row(wm, i, r, lane));
-      if (orow < 0) continue;
-      store_f32(H, orow * ldh + f, situ_glu(acc.c[i][0][r], acc.c[i][1][r], c, inv_c));
-    }
+    for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t orow = out_row(acc_row<C>(i, r));
+        if (orow < 0) continue;
+        H[orow * ldh + f] = f32_to_bf16(situ_glu(acc.c[i][j][r], acc.c[i][j + C::WN / 2][r], c, inv_c));
+      }
+  }
+}
+
+// XCD-aware block order. Workgroups are handed to the 8 XCDs round-robin
+// (hardware id h runs on XCD h % 8), and each XCD has its own L2. Logical work
+// item L = (h % 8) * chunk + h / 8, chunk = ceil(live / 8), gives every XCD one
+// contiguous slice of the logical order, so blocks that share operands (the
+// n-tiles of one row tile, the row tiles of one expert) run on the same XCD and
+// share its L2. The 1-D grid holds at least 8 * ceil(live_max / 8) blocks;
+// returns false for a block with nothing to do. (The mapping is a bijection
+// onto [0, live) whatever the dispatch order; only the speed depends on it.)
+constexpr int64_t xcd_grid(int64_t live_max) { return (live_max + 7) / 8 * 8; }
+
+__device__ __forceinline__ bool xcd_item(int64_t live, int64_t& L) {
+  const int64_t h = blockIdx.x;
+  const int64_t chunk = (live + 7) / 8;
+  const int64_t slot = h / 8;
+  if (slot >= chunk) return false;
+  L = (h % 8) * chunk + slot;
+  return L < live;
 }
 
 // ---------------------------------------------------------------------------
-// kernels (bf16 activations)
+// kernels
 // ---------------------------------------------------------------------------
 
 template <bool B_MX>
 __global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
-  extern __shared__ __align__(16) bf16_t lds[];
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  RowSet ar;
-  const int r0 = threadIdx.x >> 3;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int m = m0 + r0 + 32 * i;
-    ar.row[i] = m < a.M ? (const bf16_t*)a.A + (int64_t)m * a.lda : nullptr;
-  }
-  RowSet br{};
-  MxRow bm{};
-  if constexpr (B_MX) bm = b_mx_plain((const uint8_t*)a.W.data, a.W.scale, a.K, n0, a.N);
-  else br = b_rows_plain((const bf16_t*)a.W.data, a.K, n0, a.N);
-  Acc acc;
+  using C = DenseCfg;
+  MOE_LDS_RING;
+  const int ntn = (int)ceil_div(a.N, C::BN);
+  int64_t L;
+  if (!xcd_item(ceil_div(a.M, C::BM) * ntn, L)) return;
+  const int m0 = (int)(L / ntn) * C::BM, n0 = (int)(L % ntn) * C::BN;
+  const Rows<C::AR> ar = a_rows_dense<C::AR>(a.A, a.lda, m0, a.M);
+  Rows<C::BR> br{};
+  MxRows<C::MXU> bm{};
+  if constexpr (B_MX) bm = b_mx_plain<C::MXU>(a.W, 0, a.K, n0, a.N);
+  else br = b_rows_plain<C::BR>(a.W.data, a.K, n0, a.N);
+  Acc<C> acc;
   acc_zero(acc);
-  mainloop<B_MX>(lds, ar, br, bm, a.K, acc);
+  mainloop<C, B_MX>(lds0, lds1, lds2, ar, br, bm, a.K, acc);
   store_tile(acc, (bf16_t*)a.C, a.ldc, m0, n0, a.M, a.N);
 }
 
 template <bool B_MX>
 __global__ __launch_bounds__(256) void glu_kernel(GluArgs a) {
-  extern __shared__ __align__(16) bf16_t lds[];
-  const int m0 = blockIdx.y * BM, f0 = blockIdx.x * (BN / 2);
-  RowSet ar;
-  const int r0 = threadIdx.x >> 3;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int m = m0 + r0 + 32 * i;
-    ar.row[i] = m < a.M ? (const bf16_t*)a.A + (int64_t)m * a.lda : nullptr;
-  }
-  RowSet br{};
-  MxRow bm{};
-  if constexpr (B_MX) bm = b_mx_glu(a.Wg, a.Wv, 0, a.K, f0, a.F);
-  else br = b_rows_glu((const bf16_t*)a.Wg.data, (const bf16_t*)a.Wv.data, a.K, f0, a.F);
-  Acc acc;
+  using C = DenseCfg;
+  MOE_LDS_RING;
+  const int ntn = (int)ceil_div(a.F, C::BN / 2);
+  int64_t L;
+  if (!xcd_item(ceil_div(a.M, C::BM) * ntn, L)) return;
+  const int m0 = (int)(L / ntn) * C::BM, f0 = (int)(L % ntn) * (C::BN / 2);
+  const Rows<C::AR> ar = a_rows_dense<C::AR>(a.A, a.lda, m0, a.M);
+  Rows<C::BR> br{};
+  MxRows<C::MXU> bm{};
+  if constexpr (B_MX) bm = b_mx_glu<C>(a.Wg, a.Wv, 0, a.K, f0, a.F);
+  else br = b_rows_glu<C>(a.Wg, a.Wv, 0, a.K, f0, a.F);
+  Acc<C> acc;
   acc_zero(acc);
-  mainloop<B_MX>(lds, ar, br, bm, a.K, acc);
+  mainloop<C, B_MX>(lds0, lds1, lds2, ar, br, bm, a.K, acc);
   const int M = a.M;
   store_glu(acc, (bf16_t*)a.H, a.ldh, f0, a.F, a.c,
             [=](int tr) -> int64_t { return m0 + tr < M ? (int64_t)(m0 + tr) : -1; });
@@ -341,550 +513,196 @@ __global__ __launch_bounds__(256) void glu_kernel(GluArgs a) {
 
 // Which expert owns grouped tile `tile`: the e with tile_off[e] <= tile < tile_off[e+1].
 __device__ __forceinline__ int expert_of_tile(const int32_t* tile_off, int E, int tile) {
-  int lo = 0, hi = E;  // invariant: tile_off[lo] <= tile < tile_off[hi]
+  int lo = 0, hi = E;
   while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
+    const int mid = (lo + hi) >> 1;
     if (tile_off[mid] <= tile) lo = mid; else hi = mid;
   }
   return lo;
 }
 
+// Expert and row range of grouped tile `tile` (false: past the last tile). The
+// values are read from memory but are the same for every lane: readfirstlane
+// makes that visible to the compiler, so addresses built from them stay scalar
+// (otherwise every buffer load would be wrapped in a waterfall loop).
+template <int BM_>
+__device__ __forceinline__ bool tile_rows(const int32_t* tile_off, const int32_t* offsets, int E,
+                                          int rows_cap, int tile, int& e, int& row_lo, int& row_hi) {
+  if (tile >= __builtin_amdgcn_readfirstlane(tile_off[E])) return false;
+  e = __builtin_amdgcn_readfirstlane(expert_of_tile(tile_off, E, tile));
+  const int t0 = __builtin_amdgcn_readfirstlane(tile_off[e]);
+  const int o0 = __builtin_amdgcn_readfirstlane(offsets[e]);
+  const int o1 = __builtin_amdgcn_readfirstlane(offsets[e + 1]);
+  row_lo = o0 + (tile - t0) * BM_;
+  row_hi = min(min(o1, row_lo + BM_), rows_cap);
+  return true;
+}
+
+// Logical order of grouped work: expert by expert; inside an expert, n-tile
+// major and row tile minor, so the row tiles that share one weight slice run
+// side by side and read it through L2 once (the expert's gathered rows are
+// small and stay in L2). Expert e owns items [tile_off[e], tile_off[e+1]) * ntn.
+__device__ __forceinline__ void grouped_order(const int32_t* tile_off, int E, int ntn, int64_t L,
+                                              int& tile, int& nt) {
+  const int e = __builtin_amdgcn_readfirstlane(expert_of_tile(tile_off, E, (int)(L / ntn)));
+  const int t0 = __builtin_amdgcn_readfirstlane(tile_off[e]);
+  const int mt = __builtin_amdgcn_readfirstlane(tile_off[e + 1]) - t0;
+  const int64_t local = L - (int64_t)t0 * ntn;
+  nt = (int)(local / mt);
+  tile = t0 + (int)(local % mt);
+}
+
 template <bool B_MX>
 __global__ __launch_bounds__(256) void grouped_glu_kernel(GroupedGluArgs a) {
-  extern __shared__ __align__(16) bf16_t lds[];
-  const int tile = blockIdx.y;
-  if (tile >= a.tile_off[a.E]) return;
-  const int e = expert_of_tile(a.tile_off, a.E, tile);
-  const int row_lo = a.offsets[e] + (tile - a.tile_off[e]) * BM;
-  const int row_hi = min(min(a.offsets[e + 1], row_lo + BM), a.rows_cap);
-  const int f0 = blockIdx.x * (BN / 2);
-  RowSet ar;
-  const int r0 = threadIdx.x >> 3;
+  using C = GroupCfg;
+  MOE_LDS_RING;
+  const int ntn = (int)ceil_div(a.F, C::BN / 2);
+  int64_t L;
+  if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, L)) return;
+  int tile, nt;
+  grouped_order(a.tile_off, a.E, ntn, L, tile, nt);
+  int e, row_lo, row_hi;
+  if (!tile_rows<C::BM>(a.tile_off, a.offsets, a.E, a.rows_cap, tile, e, row_lo, row_hi)) return;
+  const int f0 = nt * (C::BN / 2);
+  // A: z rows of the tile's (token, slot) pairs, gathered through perm_src
+  Rows<C::AR> ar;
+  ar.r[0] = ar.r[1] = make_rsrc(a.Z, (int64_t)a.T * a.ldz * 2);
+  ar.sel = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int r = row_lo + r0 + 32 * i;
-    const bf16_t* p = nullptr;
-    if (r >= 0 && r < row_hi) {
-      const int src = a.perm_src[r];
+  for (int q = 0; q < C::AR; ++q) {
+    const int row = row_lo + dma_row<C::AR>(q);
+    uint32_t off = kOOB;
+    if (row >= 0 && row < row_hi) {
+      const int src = a.perm_src[row];
       const int t = src / a.topk;
-      if (src >= 0 && t < a.T) p = (const bf16_t*)a.Z + (int64_t)t * a.ldz;
+      if (src >= 0 && t < a.T) off = (uint32_t)((int64_t)t * a.ldz * 2);
     }
-    ar.row[i] = p;
+    ar.off[q] = off;
   }
-  RowSet br{};
-  MxRow bm{};
+  Rows<C::BR> br{};
+  MxRows<C::MXU> bm{};
   const int64_t wrow = (int64_t)e * a.F;
-  if constexpr (B_MX) {
-    bm = b_mx_glu(a.Wg, a.Wv, wrow, a.K, f0, a.F);
-  } else {
-    br = b_rows_glu((const bf16_t*)a.Wg.data + wrow * a.K, (const bf16_t*)a.Wv.data + wrow * a.K,
-                    a.K, f0, a.F);
-  }
-  Acc acc;
+  if constexpr (B_MX) bm = b_mx_glu<C>(a.Wg, a.Wv, wrow, a.K, f0, a.F);
+  else br = b_rows_glu<C>(a.Wg, a.Wv, wrow, a.K, f0, a.F);
+  Acc<C> acc;
   acc_zero(acc);
-  mainloop<B_MX>(lds, ar, br, bm, a.K, acc);
-  store_glu(acc, (bf16_t*)a.H, a.F, f0, a.F, a.c,
-            [=](int tr) -> int64_t {
-              const int r = row_lo + tr;
-              return (r >= 0 && r < row_hi) ? (int64_t)r : -1;
-            });
+  mainloop<C, B_MX>(lds0, lds1, lds2, ar, br, bm, a.K, acc);
+  store_glu(acc, (bf16_t*)a.H, a.F, f0, a.F, a.c, [=](int tr) -> int64_t {
+    const int r = row_lo + tr;
+    return (r >= 0 && r < row_hi) ? (int64_t)r : -1;
+  });
 }
 
 template <bool B_MX>
 __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedDownArgs a) {
-  extern __shared__ __align__(16) bf16_t lds[];
-  const int tile = blockIdx.y;
-  if (tile >= a.tile_off[a.E]) return;
-  const int e = expert_of_tile(a.tile_off, a.E, tile);
-  const int row_lo = a.offsets[e] + (tile - a.tile_off[e]) * BM;
-  const int row_hi = min(min(a.offsets[e + 1], row_lo + BM), a.rows_cap);
-  const int n0 = blockIdx.x * BN;
-  RowSet ar;
-  const int r0 = threadIdx.x >> 3;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int r = row_lo + r0 + 32 * i;
-    ar.row[i] = (r >= 0 && r < row_hi) ? (const bf16_t*)a.H + (int64_t)r * a.ldh : nullptr;
-  }
-  RowSet br{};
-  MxRow bm{};
+  using C = GroupCfg;
+  MOE_LDS_RING;
+  const int ntn = (int)ceil_div(a.N, C::BN);
+  int64_t L;
+  if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, L)) return;
+  int tile, nt;
+  grouped_order(a.tile_off, a.E, ntn, L, tile, nt);
+  int e, row_lo, row_hi;
+  if (!tile_rows<C::BM>(a.tile_off, a.offsets, a.E, a.rows_cap, tile, e, row_lo, row_hi)) return;
+  const int n0 = nt * C::BN;
+  const Rows<C::AR> ar = a_rows_dense<C::AR>(a.H, a.ldh, max(row_lo, 0), max(row_hi, 0));
+  Rows<C::BR> br{};
+  MxRows<C::MXU> bm{};
   const int64_t wrow = (int64_t)e * a.N;
-  if constexpr (B_MX) {
-    bm = b_mx_plain((const uint8_t*)a.Wo.data + wrow * (a.K / 2), a.Wo.scale + wrow * (a.K / 32),
-                    a.K, n0, a.N);
-  } else {
-    br = b_rows_plain((const bf16_t*)a.Wo.data + wrow * a.K, a.K, n0, a.N);
-  }
-  Acc acc;
+  if constexpr (B_MX) bm = b_mx_plain<C::MXU>(a.Wo, wrow, a.K, n0, a.N);
+  else br = b_rows_plain<C::BR>((const bf16_t*)a.Wo.data + wrow * a.K, a.K, n0, a.N);
+  Acc<C> acc;
   acc_zero(acc);
-  mainloop<B_MX>(lds, ar, br, bm, a.K, acc);
-  // rows row_lo.. of O (ld = N)
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, wm = wv >> 1, wn = wv & 1;
-  bf16_t* O = (bf16_t*)a.O;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + acc_col(wn, j, lane);
-      if (n >= a.N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_lo + acc_row(wm, i, r, lane);
-        if (row >= 0 && row < row_hi) O[(int64_t)row * a.N + n] = f32_to_bf16(acc.c[i][j][r]);
-      }
-    }
+  mainloop<C, B_MX>(lds0, lds1, lds2, ar, br, bm, a.K, acc);
+  store_tile(acc, (bf16_t*)a.O, a.N, row_lo, n0, row_hi, a.N);
 }
 
-// Segments are visited in order; each segment's B is bf16 or MXFP4.
+// Segments are visited in order; every B is bf16 except, when LAST_MX, the last
+// one (W_up in MXFP4).
+template <bool LAST_MX>
 __global__ __launch_bounds__(256) void multiseg_kernel(MultiSegArgs a) {
-  extern __shared__ __align__(16) bf16_t lds[];
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  Acc acc;
+  using C = DenseCfg;
+  MOE_LDS_RING;
+  const int ntn = (int)ceil_div(a.N, C::BN);
+  int64_t L;
+  if (!xcd_item(ceil_div(a.M, C::BM) * ntn, L)) return;
+  const int m0 = (int)(L / ntn) * C::BM, n0 = (int)(L % ntn) * C::BN;
+  Acc<C> acc;
   acc_zero(acc);
-  const int r0 = threadIdx.x >> 3;
-  for (int s = 0; s < a.nseg; ++s) {
+  const int nplain = LAST_MX ? a.nseg - 1 : a.nseg;
+  for (int s = 0; s < nplain; ++s) {
     const Segment& sg = a.seg[s];
-    RowSet ar;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int m = m0 + r0 + 32 * i;
-      ar.row[i] = m < a.M ? (const bf16_t*)sg.A + (int64_t)m * sg.lda : nullptr;
-    }
-    if (sg.B.dtype == DT_MXFP4) {
-      MxRow bm = b_mx_plain((const uint8_t*)sg.B.data, sg.B.scale, sg.K, n0, a.N);
-      RowSet br{};
-      mainloop<true>(lds, ar, br, bm, sg.K, acc);
-    } else {
-      RowSet br = b_rows_plain((const bf16_t*)sg.B.data, sg.K, n0, a.N);
-      MxRow bm{};
-      mainloop<false>(lds, ar, br, bm, sg.K, acc);
-    }
+    const Rows<C::AR> ar = a_rows_dense<C::AR>(sg.A, sg.lda, m0, a.M);
+    const Rows<C::BR> br = b_rows_plain<C::BR>(sg.B.data, sg.K, n0, a.N);
+    mainloop<C, false>(lds0, lds1, lds2, ar, br, MxRows<C::MXU>{}, sg.K, acc);
+  }
+  if constexpr (LAST_MX) {
+    const Segment& sg = a.seg[a.nseg - 1];
+    const Rows<C::AR> ar = a_rows_dense<C::AR>(sg.A, sg.lda, m0, a.M);
+    const MxRows<C::MXU> bm = b_mx_plain<C::MXU>(sg.B, 0, sg.K, n0, a.N);
+    mainloop<C, true>(lds0, lds1, lds2, ar, Rows<C::BR>{}, bm, sg.K, acc);
   }
   store_tile(acc, (bf16_t*)a.C, a.ldc, m0, n0, a.M, a.N);
 }
 
-// ---------------------------------------------------------------------------
-// weight-streaming grouped kernels (few rows per expert, e.g. decode)
-//
-// With ~5 rows per expert the expert GEMMs are bound by reading each touched
-// expert's weights from HBM once. A block owns one expert tile of up to 32
-// rows (two 16-row v_mfma_f32_16x16x32_bf16 tiles) and 64 weight rows (four
-// 16-column tiles: for gate/up two gate + the two matching up tiles), and the
-// four waves split K: each wave streams its quarter of the 64 weight rows
-// straight from global memory into MFMA operand registers (no LDS staging;
-// the next 64-k chunk is in flight while the current one is multiplied), and
-// the partial sums are reduced through LDS in a fixed wave order.
-//
-// k assignment inside a 64-k chunk: lane group g = lane/16 takes k = g*16 ..
-// g*16+15, 8 per MFMA step. A and B use the same assignment, so every MFMA
-// still sums over its 32 k values, and the 4 lanes of a weight row read the
-// row's whole 128-byte segment.
-// ---------------------------------------------------------------------------
-
-constexpr int SK_BM = 32;
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ bf16x8 zero_frag() {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  return __builtin_bit_cast(bf16x8, z);
-}
-
-__device__ __forceinline__ bf16x8 ld_frag(const bf16_t* row, int k, int K) {
-  if (row == nullptr || k >= K) return zero_frag();
-  return *(const bf16x8*)(row + k);
-}
-
-// 8 MXFP4 elements k..k+7 (k a multiple of 8) of one packed row, decoded to bf16.
-__device__ __forceinline__ bf16x8 ld_frag_mx(const uint8_t* prow, const uint8_t* srow, int k, int K) {
-  if (prow == nullptr || k >= K) return zero_frag();
-  const uint32_t q = *(const uint32_t*)(prow + k / 2);
-  const uint32_t sb = srow[k / 32];
-  const float scale = sb == 0u ? 0x1p-127f : __uint_as_float(sb << 23);
-  u32x4 w;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t byte = (q >> (8 * i)) & 0xFFu;
-    w[i] = scale_bf16(e2m1_bf16(byte & 0xFu), scale) | (scale_bf16(e2m1_bf16(byte >> 4), scale) << 16);
-  }
-  return __builtin_bit_cast(bf16x8, w);
-}
-
-struct SkRows {
-  const bf16_t* a[2];      // A rows of m-tiles 0, 1 (nullptr: zero row)
-  const void* b[4];        // B rows of n-tiles 0..3 (bf16 row, or packed MXFP4 row)
-  const uint8_t* bs[4];    // MXFP4 scale rows
-};
-
-struct SkFrag {
-  bf16x8 a[2][2];          // [m][step]
-  bf16x8 b[4][2];          // [n][step]
-};
-
-template <bool MX>
-__device__ __forceinline__ void sk_load(const SkRows& r, int k0, int K, SkFrag& f) {
-  const int g = (threadIdx.x & 63) >> 4;
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    const int k = k0 + g * 16 + st * 8;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) f.a[m][st] = ld_frag(r.a[m], k, K);
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      if constexpr (MX) f.b[n][st] = ld_frag_mx((const uint8_t*)r.b[n], r.bs[n], k, K);
-      else f.b[n][st] = ld_frag((const bf16_t*)r.b[n], k, K);
-    }
-  }
-}
-
-// acc[m][n] over this wave's share of K, then a fixed-order reduction over
-// the four waves into red (LDS, 4 x 32 x 64 floats).
-template <bool MX>
-__device__ void sk_mainloop(const SkRows& r, int K, float* red) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  f32x4 acc[2][4];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int nchunk = (int)ceil_div(K, 64);
-  const int c0 = (wv * nchunk) / 4, c1 = ((wv + 1) * nchunk) / 4;
-  if (c0 < c1) {
-    SkFrag cur, nxt;
-    sk_load<MX>(r, c0 * 64, K, cur);
-    for (int c = c0; c < c1; ++c) {
-      if (c + 1 < c1) sk_load<MX>(r, (c + 1) * 64, K, nxt);
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int n = 0; n < 4; ++n)
-            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[m][st], cur.b[n][st],
-                                                                acc[m][n], 0, 0, 0);
-      cur = nxt;
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) red[(wv * 32 + m * 16 + n * 4 + q) * 64 + lane] = acc[m][n][q];
-  __syncthreads();
-}
-
-// Sum of value i (= m*16 + n*4 + q) of `lane` over the four waves, in order.
-__device__ __forceinline__ float sk_sum(const float* red, int i, int lane) {
-  float s = red[(0 * 32 + i) * 64 + lane];
-  s += red[(1 * 32 + i) * 64 + lane];
-  s += red[(2 * 32 + i) * 64 + lane];
-  s += red[(3 * 32 + i) * 64 + lane];
-  return s;
-}
-
-// Output position of value (m, n, q) of `lane`: tile row m*16 + 4*(lane/16) + q,
-// tile column n*16 + lane%16 (the 16x16 accumulator layout).
-template <bool MX>
-__global__ __launch_bounds__(256) void skinny_glu_kernel(GroupedGluArgs a) {
-  __shared__ float red[4 * 32 * 64];
-  const int tile = blockIdx.y;
-  if (tile >= a.tile_off[a.E]) return;
-  const int e = expert_of_tile(a.tile_off, a.E, tile);
-  const int row_lo = a.offsets[e] + (tile - a.tile_off[e]) * SK_BM;
-  const int row_hi = min(min(a.offsets[e + 1], row_lo + SK_BM), a.rows_cap);
-  const int f0 = blockIdx.x * 32;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15;
-
-  SkRows r;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int row = row_lo + m * 16 + l16;
-    const bf16_t* p = nullptr;
-    if (row >= 0 && row < row_hi) {
-      const int src = a.perm_src[row];
-      const int t = src / a.topk;
-      if (src >= 0 && t < a.T) p = (const bf16_t*)a.Z + (int64_t)t * a.ldz;
-    }
-    r.a[m] = p;
-  }
-  const int64_t wrow = (int64_t)e * a.F;
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int f = f0 + (n & 1) * 16 + l16;
-    const WOperand& w = (n < 2) ? a.Wg : a.Wv;
-    const bool ok = f < a.F;
-    if constexpr (MX) {
-      r.b[n] = ok ? (const void*)((const uint8_t*)w.data + (wrow + f) * (a.K / 2)) : nullptr;
-      r.bs[n] = ok ? w.scale + (wrow + f) * (a.K / 32) : nullptr;
-    } else {
-      r.b[n] = ok ? (const void*)((const bf16_t*)w.data + (wrow + f) * a.K) : nullptr;
-      r.bs[n] = nullptr;
-    }
-  }
-  sk_mainloop<MX>(r, a.K, red);
-
-  const float inv_c = 1.0f / a.c;
-  bf16_t* H = (bf16_t*)a.H;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int pidx = wv * 4 + j;              // 16 (gate, up) pairs per lane
-    const int m = pidx >> 3, n = (pidx >> 2) & 1, q = pidx & 3;
-    const float g = sk_sum(red, m * 16 + n * 4 + q, lane);
-    const float v = sk_sum(red, m * 16 + (n + 2) * 4 + q, lane);
-    const int row = row_lo + m * 16 + 4 * (lane >> 4) + q;
-    const int f = f0 + n * 16 + l16;
-    if (row < row_hi && f < a.F) H[(int64_t)row * a.F + f] = f32_to_bf16(situ_glu(g, v, a.c, inv_c));
-  }
-}
-
-template <bool MX>
-__global__ __launch_bounds__(256) void skinny_down_kernel(GroupedDownArgs a) {
-  __shared__ float red[4 * 32 * 64];
-  const int tile = blockIdx.y;
-  if (tile >= a.tile_off[a.E]) return;
-  const int e = expert_of_tile(a.tile_off, a.E, tile);
-  const int row_lo = a.offsets[e] + (tile - a.tile_off[e]) * SK_BM;
-  const int row_hi = min(min(a.offsets[e + 1], row_lo + SK_BM), a.rows_cap);
-  const int n0 = blockIdx.x * 64;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, l16 = lane & 15;
-
-  SkRows r;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const int row = row_lo + m * 16 + l16;
-    r.a[m] = (row >= 0 && row < row_hi) ? (const bf16_t*)a.H + (int64_t)row * a.ldh : nullptr;
-  }
-  const int64_t wrow = (int64_t)e * a.N;
-#pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int col = n0 + n * 16 + l16;
-    const bool ok = col < a.N;
-    if constexpr (MX) {
-      r.b[n] = ok ? (const void*)((const uint8_t*)a.Wo.data + (wrow + col) * (a.K / 2)) : nullptr;
-      r.bs[n] = ok ? a.Wo.scale + (wrow + col) * (a.K / 32) : nullptr;
-    } else {
-      r.b[n] = ok ? (const void*)((const bf16_t*)a.Wo.data + (wrow + col) * a.K) : nullptr;
-      r.bs[n] = nullptr;
-    }
-  }
-  sk_mainloop<MX>(r, a.K, red);
-
-  bf16_t* O = (bf16_t*)a.O;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int i = wv * 8 + j;                 // 32 values per lane
-    const int m = i >> 4, n = (i >> 2) & 3, q = i & 3;
-    const float v = sk_sum(red, i, lane);
-    const int row = row_lo + m * 16 + 4 * (lane >> 4) + q;
-    const int col = n0 + n * 16 + l16;
-    if (row < row_hi && col < a.N) O[(int64_t)row * a.N + col] = f32_to_bf16(v);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// kernels (fp32 activations and weights): one thread per output
-// ---------------------------------------------------------------------------
-
-__device__ __forceinline__ float dot_f32(const float* a, const float* b, int K) {
-  float acc = 0.0f;
-  for (int k = 0; k < K; ++k) acc = __builtin_fmaf(a[k], b[k], acc);
-  return acc;
-}
-
-__global__ void dense_f32(DenseArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)a.M * a.N) return;
-  const int m = (int)(i / a.N), n = (int)(i % a.N);
-  ((float*)a.C)[(int64_t)m * a.ldc + n] =
-      dot_f32((const float*)a.A + (int64_t)m * a.lda, (const float*)a.W.data + (int64_t)n * a.K, a.K);
-}
-
-__global__ void glu_f32(GluArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)a.M * a.F) return;
-  const int m = (int)(i / a.F), f = (int)(i % a.F);
-  const float* x = (const float*)a.A + (int64_t)m * a.lda;
-  float g = dot_f32(x, (const float*)a.Wg.data + (int64_t)f * a.K, a.K);
-  float v = dot_f32(x, (const float*)a.Wv.data + (int64_t)f * a.K, a.K);
-  ((float*)a.H)[(int64_t)m * a.ldh + f] = situ_glu(g, v, a.c, 1.0f / a.c);
-}
-
-__device__ __forceinline__ int expert_of_row(const int32_t* offsets, int E, int r) {
-  int lo = 0, hi = E;  // offsets[lo] <= r < offsets[hi]
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (offsets[mid] <= r) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
-__global__ void grouped_glu_f32(GroupedGluArgs a) {
-  const int64_t rows = min((int64_t)a.offsets[a.E], (int64_t)a.rows_cap);
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= rows * a.F) return;
-  const int r = (int)(i / a.F), f = (int)(i % a.F);
-  const int e = expert_of_row(a.offsets, a.E, r);
-  const int src = a.perm_src[r];
-  if (src < 0 || src / a.topk >= a.T) return;
-  const float* z = (const float*)a.Z + (int64_t)(src / a.topk) * a.ldz;
-  const int64_t wrow = (int64_t)e * a.F + f;
-  float g = dot_f32(z, (const float*)a.Wg.data + wrow * a.K, a.K);
-  float v = dot_f32(z, (const float*)a.Wv.data + wrow * a.K, a.K);
-  ((float*)a.H)[(int64_t)r * a.F + f] = situ_glu(g, v, a.c, 1.0f / a.c);
-}
-
-__global__ void grouped_down_f32(GroupedDownArgs a) {
-  const int64_t rows = min((int64_t)a.offsets[a.E], (int64_t)a.rows_cap);
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= rows * a.N) return;
-  const int r = (int)(i / a.N), n = (int)(i % a.N);
-  const int e = expert_of_row(a.offsets, a.E, r);
-  ((float*)a.O)[(int64_t)r * a.N + n] =
-      dot_f32((const float*)a.H + (int64_t)r * a.ldh,
-              (const float*)a.Wo.data + ((int64_t)e * a.N + n) * a.K, a.K);
-}
-
-__global__ void multiseg_f32(MultiSegArgs a) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (int64_t)a.M * a.N) return;
-  const int m = (int)(i / a.N), n = (int)(i % a.N);
-  float acc = 0.0f;
-  for (int s = 0; s < a.nseg; ++s) {
-    const Segment& sg = a.seg[s];
-    const float* x = (const float*)sg.A + (int64_t)m * sg.lda;
-    const float* w = (const float*)sg.B.data + (int64_t)n * sg.K;
-    for (int k = 0; k < sg.K; ++k) acc = __builtin_fmaf(x[k], w[k], acc);
-  }
-  ((float*)a.C)[(int64_t)m * a.ldc + n] = acc;
-}
-
-// The bf16 kernels use 72 KB of dynamic LDS (above the 64 KB default cap):
-// raise the cap once per process for every instantiation.
-int init_lds_caps() {
-  static int status = -1;
-  if (status >= 0) return status;
-  const void* ks[] = {(const void*)dense_kernel<true>,        (const void*)dense_kernel<false>,
-                      (const void*)glu_kernel<true>,          (const void*)glu_kernel<false>,
-                      (const void*)grouped_glu_kernel<true>,  (const void*)grouped_glu_kernel<false>,
-                      (const void*)grouped_down_kernel<true>, (const void*)grouped_down_kernel<false>,
-                      (const void*)multiseg_kernel};
-  status = 0;
-  for (const void* k : ks) {
-    hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)LDS_BYTES);
-    if (e != hipSuccess) { status = (int)e; break; }
-  }
-  return status;
-}
-
-unsigned blocks_for(int64_t n) { return (unsigned)ceil_div(n, 256); }
-
 }  // namespace
 
-int grouped_bm(int act_dtype, int64_t rows, int E) {
-  if (act_dtype == DT_F32) return 1;
-  return rows <= (int64_t)SK_BM * E ? SK_BM : BM;
-}
+int grouped_bm(int act_dtype, int64_t, int) { return act_dtype == DT_F32 ? 1 : GroupCfg::BM; }
 
 int launch_dense(const DenseArgs& a, hipStream_t stream) {
+  if (a.act_dtype == DT_F32) return launch_dense_f32(a, stream);
   if (a.M == 0) return 0;
-  if (a.act_dtype != DT_F32) {
-    if (int e = init_lds_caps()) return e;
-  }
-  if (a.act_dtype == DT_F32) {
-    hipLaunchKernelGGL(dense_f32, dim3(blocks_for((int64_t)a.M * a.N)), dim3(256), 0, stream, a);
-    return (int)hipGetLastError();
-  }
-  dim3 grid((unsigned)ceil_div(a.N, BN), (unsigned)ceil_div(a.M, BM));
-  if (a.W.dtype == DT_MXFP4) {
-    hipLaunchKernelGGL(dense_kernel<true>, grid, dim3(256), LDS_BYTES, stream, a);
-  } else {
-    hipLaunchKernelGGL(dense_kernel<false>, grid, dim3(256), LDS_BYTES, stream, a);
-  }
+  using C = DenseCfg;
+  dim3 grid((unsigned)xcd_grid(ceil_div(a.N, C::BN) * ceil_div(a.M, C::BM)));
+  if (a.W.dtype == DT_MXFP4) hipLaunchKernelGGL(dense_kernel<true>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(dense_kernel<false>, grid, dim3(256), 0, stream, a);
   return (int)hipGetLastError();
 }
 
 int launch_glu(const GluArgs& a, hipStream_t stream) {
+  if (a.act_dtype == DT_F32) return launch_glu_f32(a, stream);
   if (a.M == 0) return 0;
-  if (a.act_dtype != DT_F32) {
-    if (int e = init_lds_caps()) return e;
-  }
-  if (a.act_dtype == DT_F32) {
-    hipLaunchKernelGGL(glu_f32, dim3(blocks_for((int64_t)a.M * a.F)), dim3(256), 0, stream, a);
-    return (int)hipGetLastError();
-  }
-  dim3 grid((unsigned)ceil_div(a.F, BN / 2), (unsigned)ceil_div(a.M, BM));
-  if (a.Wg.dtype == DT_MXFP4) {
-    hipLaunchKernelGGL(glu_kernel<true>, grid, dim3(256), LDS_BYTES, stream, a);
-  } else {
-    hipLaunchKernelGGL(glu_kernel<false>, grid, dim3(256), LDS_BYTES, stream, a);
-  }
+  using C = DenseCfg;
+  dim3 grid((unsigned)xcd_grid(ceil_div(a.F, C::BN / 2) * ceil_div(a.M, C::BM)));
+  if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(glu_kernel<true>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(glu_kernel<false>, grid, dim3(256), 0, stream, a);
   return (int)hipGetLastError();
 }
 
 int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream) {
+  if (a.act_dtype == DT_F32) return launch_grouped_glu_f32(a, stream);
   if (a.max_tiles == 0) return 0;
-  if (a.act_dtype != DT_F32) {
-    if (int e = init_lds_caps()) return e;
-  }
-  if (a.act_dtype == DT_F32) {
-    // rows <= max_tiles when BM = 1 (the fp32 path uses one-row "tiles")
-    hipLaunchKernelGGL(grouped_glu_f32, dim3(blocks_for((int64_t)a.max_tiles * a.F)), dim3(256), 0,
-                       stream, a);
-    return (int)hipGetLastError();
-  }
-  if (a.bm == SK_BM) {
-    dim3 g((unsigned)ceil_div(a.F, 32), (unsigned)a.max_tiles);
-    if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(skinny_glu_kernel<true>, g, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(skinny_glu_kernel<false>, g, dim3(256), 0, stream, a);
-    return (int)hipGetLastError();
-  }
-  if (a.bm != BM) return -1;
-  dim3 grid((unsigned)ceil_div(a.F, BN / 2), (unsigned)a.max_tiles);
-  if (a.Wg.dtype == DT_MXFP4) {
-    hipLaunchKernelGGL(grouped_glu_kernel<true>, grid, dim3(256), LDS_BYTES, stream, a);
-  } else {
-    hipLaunchKernelGGL(grouped_glu_kernel<false>, grid, dim3(256), LDS_BYTES, stream, a);
-  }
+  if (a.bm != GroupCfg::BM) return -1;
+  using C = GroupCfg;
+  dim3 grid((unsigned)xcd_grid(ceil_div(a.F, C::BN / 2) * a.max_tiles));
+  if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(grouped_glu_kernel<true>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(grouped_glu_kernel<false>, grid, dim3(256), 0, stream, a);
   return (int)hipGetLastError();
 }
 
 int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream) {
+  if (a.act_dtype == DT_F32) return launch_grouped_down_f32(a, stream);
   if (a.max_tiles == 0) return 0;
-  if (a.act_dtype != DT_F32) {
-    if (int e = init_lds_caps()) return e;
-  }
-  if (a.act_dtype == DT_F32) {
-    hipLaunchKernelGGL(grouped_down_f32, dim3(blocks_for((int64_t)a.max_tiles * a.N)), dim3(256), 0,
-                       stream, a);
-    return (int)hipGetLastError();
-  }
-  if (a.bm == SK_BM) {
-    dim3 g((unsigned)ceil_div(a.N, 64), (unsigned)a.max_tiles);
-    if (a.Wo.dtype == DT_MXFP4) hipLaunchKernelGGL(skinny_down_kernel<true>, g, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(skinny_down_kernel<false>, g, dim3(256), 0, stream, a);
-    return (int)hipGetLastError();
-  }
-  if (a.bm != BM) return -1;
-  dim3 grid((unsigned)ceil_div(a.N, BN), (unsigned)a.max_tiles);
-  if (a.Wo.dtype == DT_MXFP4) {
-    hipLaunchKernelGGL(grouped_down_kernel<true>, grid, dim3(256), LDS_BYTES, stream, a);
-  } else {
-    hipLaunchKernelGGL(grouped_down_kernel<false>, grid, dim3(256), LDS_BYTES, stream, a);
-  }
+  if (a.bm != GroupCfg::BM) return -1;
+  using C = GroupCfg;
+  dim3 grid((unsigned)xcd_grid(ceil_div(a.N, C::BN) * a.max_tiles));
+  if (a.Wo.dtype == DT_MXFP4) hipLaunchKernelGGL(grouped_down_kernel<true>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(grouped_down_kernel<false>, grid, dim3(256), 0, stream, a);
   return (int)hipGetLastError();
 }
 
 int launch_multiseg(const MultiSegArgs& a, hipStream_t stream) {
+  if (a.act_dtype == DT_F32) return launch_multiseg_f32(a, stream);
   if (a.M == 0) return 0;
-  if (a.act_dtype != DT_F32) {
-    if (int e = init_lds_caps()) return e;
-  }
-  if (a.act_dtype == DT_F32) {
-    hipLaunchKernelGGL(multiseg_f32, dim3(blocks_for((int64_t)a.M * a.N)), dim3(256), 0, stream, a);
-    return (int)hipGetLastError();
-  }
-  dim3 grid((unsigned)ceil_div(a.N, BN), (unsigned)ceil_div(a.M, BM));
-  hipLaunchKernelGGL(multiseg_kernel, grid, dim3(256), LDS_BYTES, stream, a);
+  using C = DenseCfg;
+  dim3 grid((unsigned)xcd_grid(ceil_div(a.N, C::BN) * ceil_div(a.M, C::BM)));
+  // only the last segment (W_up) may be MXFP4
+  for (int i = 0; i + 1 < a.nseg; ++i)
+    if (a.seg[i].B.dtype == DT_MXFP4) return -1;
+  if (a.nseg > 0 && a.seg[a.nseg - 1].B.dtype == DT_MXFP4)
+    hipLaunchKernelGGL(multiseg_kernel<true>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(multiseg_kernel<false>, grid, dim3(256), 0, stream, a);
   return (int)hipGetLastError();
 }
 

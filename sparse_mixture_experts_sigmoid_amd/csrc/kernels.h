@@ -120,6 +120,13 @@ struct MultiSegArgs {
 };
 int launch_multiseg(const MultiSegArgs& a, hipStream_t stream);
 
+// fp32-activation variants of the GEMM launchers (gemm_f32.hip).
+int launch_dense_f32(const DenseArgs& a, hipStream_t stream);
+int launch_glu_f32(const GluArgs& a, hipStream_t stream);
+int launch_grouped_glu_f32(const GroupedGluArgs& a, hipStream_t stream);
+int launch_grouped_down_f32(const GroupedDownArgs& a, hipStream_t stream);
+int launch_multiseg_f32(const MultiSegArgs& a, hipStream_t stream);
+
 // Combine + RMSNorm.
 struct CombineArgs {
   const void* O;                 // [T*k, D] act dtype, permuted rows
