@@ -103,7 +103,7 @@ struct Plan {
 };
 
 struct LayerWs {
-  size_t s, key, idx, gate, counts, offsets, perm, inv, blk, z, tile_off, H, O, n, Hs;
+  size_t s, key, norms, idx, gate, counts, offsets, perm, inv, blk, z, tile_off, H, O, n, Hs;
 };
 
 int max_tiles(const moe_desc_t* d) {
@@ -114,6 +114,7 @@ int max_tiles(const moe_desc_t* d) {
 void plan_route(const moe_desc_t* d, Plan& p, LayerWs& w) {
   w.s = p.take((size_t)d->T * d->n_experts * 4);
   w.key = p.take((size_t)d->T * d->n_experts * 4);
+  w.norms = p.take((size_t)(d->T + d->n_experts) * 4);
 }
 void plan_permute(const moe_desc_t* d, Plan& p, LayerWs& w) {
   w.blk = p.take((size_t)moe::permute_blocks(d->T) * d->n_experts * 4);
@@ -239,8 +240,28 @@ struct Marker {
 // stages (arguments already validated)
 // ------------------------------------------------------------------------------------------
 
+// bf16 x and W_r without a request for all scores: matrix-core logits, then
+// the exact fixed-order recheck of the near-boundary experts only (same result
+// bit for bit). Otherwise every (token, expert) logit in fixed order on VALU.
 int do_route(const moe_desc_t* d, const void* x, moe_w_t router, const float* bias, int32_t* idx,
-             float* gate, float* s, float* key, hipStream_t st, Marker mk = {-1, nullptr}) {
+             float* gate, float* s, float* key, float* norms, bool want_scores, hipStream_t st,
+             Marker mk = {-1, nullptr}) {
+  if (!want_scores && d->act_dtype == MOE_BF16 && d->dense_w_dtype == MOE_BF16 &&
+      moe::router_select_supported(d->n_experts, d->d_model)) {
+    float* xn = norms;
+    float* wn = norms + d->T;
+    mk(0);
+    MOE_LAUNCH(moe::launch_row_norms(x, d->T, d->d_model, xn, st), "row_norms");
+    MOE_LAUNCH(moe::launch_row_norms(router.data, d->n_experts, d->d_model, wn, st), "row_norms");
+    moe::LogitsArgs la{x, router.data, d->T, d->n_experts, d->d_model,
+                       moe::router_logit_splits(d->T, d->n_experts, d->d_model), s};
+    MOE_LAUNCH(moe::launch_router_logits(la, st), "router_logits");
+    mk(1);
+    moe::SelectArgs sa{s, x, router.data, bias, xn, wn, d->T, d->n_experts, d->d_model,
+                       d->top_k, idx, gate};
+    MOE_LAUNCH(moe::launch_router_select(sa, st), "router_select");
+    return MOE_OK;
+  }
   moe::RouterArgs ra{x, d->act_dtype, router.data, d->dense_w_dtype, bias, d->T, d->d_model,
                      d->n_experts, s, key};
   mk(0);
@@ -433,7 +454,7 @@ int moe_route(const moe_desc_t* d, const void* x, moe_w_t router, const float* b
   plan_route(d, p, w);
   float* s = scores_opt ? scores_opt : (float*)at(ws, w.s);
   return do_route(d, x, router, bias, topk_idx, topk_gate, s, (float*)at(ws, w.key),
-                  (hipStream_t)stream);
+                  (float*)at(ws, w.norms), scores_opt != nullptr, (hipStream_t)stream);
 }
 
 int moe_permute(const moe_desc_t* d, const int32_t* topk_idx, int32_t* counts, int32_t* offsets,
@@ -556,7 +577,7 @@ int moe_layer_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x
   int32_t* inv = (int32_t*)at(ws, lw.inv);
   const Marker mk{trace_begin(), st};
   MOE_CHECK(do_route(d, x, w->router, w->router_bias, idx, gate, (float*)at(ws, lw.s),
-                     (float*)at(ws, lw.key), st, mk));
+                     (float*)at(ws, lw.key), (float*)at(ws, lw.norms), false, st, mk));
   mk(2);
   MOE_CHECK(do_permute(d, idx, counts, offsets, perm, inv, (int32_t*)at(ws, lw.blk), st));
   mk(3);

@@ -65,6 +65,26 @@ __device__ __forceinline__ float situ_glu(float g, float v, float c, float inv_c
   return (c * tanh_fast(silu * inv_c)) * (c * tanh_fast(v * inv_c));
 }
 
+// Buffer resources: loads at offsets past num_records return zeros (no fault).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;  // past every buffer (each is < 2^31 bytes)
+
+// Every resource is built from block-uniform values; readfirstlane states that
+// to the compiler so the descriptor lives in scalar registers (a descriptor in
+// vector registers turns each load into a waterfall loop).
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 __host__ __device__ __forceinline__ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace moe

@@ -58,25 +58,6 @@ using GroupCfg = Cfg<2, 4, 3>;   // 128 x 256, 3 LDS stages of 48 KB
 // buffer loads
 // ---------------------------------------------------------------------------
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr uint32_t kOOB = 0x80000000u;  // past every buffer (each is < 2^31 bytes)
-
-// Every resource is built from block-uniform values; readfirstlane states that
-// to the compiler so the descriptor lives in scalar registers (a descriptor in
-// vector registers turns each load into a waterfall loop).
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const uint64_t b = (uint64_t)base;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
-  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n,
-                                           0x00020000);
-}
-
-__device__ __forceinline__ uint4 bload16(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
 // ---------------------------------------------------------------------------
 // operand staging
 // ---------------------------------------------------------------------------
@@ -208,25 +189,46 @@ __device__ __forceinline__ void acc_zero(Acc<C>& acc) {
 }
 
 template <class C>
+__device__ __forceinline__ void load_frags(const bf16_t* Aw, const bf16_t* Bw, int ks, int slot_base,
+                                           bf16x8 (&a)[C::WM], bf16x8 (&b)[C::WN]) {
+  const int slot = 8 * ((2 * ks + (slot_base >> 3)) ^ (slot_base & 7));
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i) a[i] = *(const bf16x8*)(Aw + i * 32 * LDK + slot);
+#pragma unroll
+  for (int j = 0; j < C::WN; ++j) b[j] = *(const bf16x8*)(Bw + j * 32 * LDK + slot);
+}
+
+// One 64-k LDS stage: 4 k-steps of WM x WN MFMAs. The operand reads of step
+// ks+1 are issued before the MFMAs of step ks (two fragment sets) and
+// interleaved with them, so LDS latency hides behind the matrix cores.
+template <class C>
 __device__ __forceinline__ void mma_stage(const bf16_t* As, const bf16_t* Bs, Acc<C>& acc) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, wm = wv >> 1, wn = wv & 1;
   const int lr = lane & 31, lh = lane >> 5;
   // row R = base + lr (base a multiple of 32): chunk kc sits in slot kc ^ swz(lr)
   const bf16_t* Aw = As + (wm * (C::BM / 2) + lr) * LDK;
   const bf16_t* Bw = Bs + (wn * (C::BN / 2) + lr) * LDK;
+  const int slot_base = (lh << 3) | swz(lr);
+  bf16x8 a[2][C::WM], b[2][C::WN];
+  load_frags<C>(Aw, Bw, 0, slot_base, a[0], b[0]);
 #pragma unroll
   for (int ks = 0; ks < BK / 16; ++ks) {
-    const int slot = 8 * ((2 * ks + lh) ^ swz(lr));
-    bf16x8 a[C::WM], b[C::WN];
-#pragma unroll
-    for (int i = 0; i < C::WM; ++i) a[i] = *(const bf16x8*)(Aw + i * 32 * LDK + slot);
-#pragma unroll
-    for (int j = 0; j < C::WN; ++j) b[j] = *(const bf16x8*)(Bw + j * 32 * LDK + slot);
+    const int cur = ks & 1;
+    if (ks + 1 < BK / 16) load_frags<C>(Aw, Bw, ks + 1, slot_base, a[cur ^ 1], b[cur ^ 1]);
 #pragma unroll
     for (int i = 0; i < C::WM; ++i)
 #pragma unroll
       for (int j = 0; j < C::WN; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc.c[i][j], 0, 0, 0);
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc.c[i][j], 0, 0, 0);
+    if (ks + 1 < BK / 16) {
+      // interleave: one LDS read after each of the first WM+WN MFMAs
+#pragma unroll
+      for (int q = 0; q < C::WM + C::WN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, C::WM * C::WN - (C::WM + C::WN), 0);
+    }
   }
 }
 
@@ -291,7 +293,7 @@ template <class C, bool B_MX>
 __device__ __forceinline__ void mainloop(bf16_t* s0, bf16_t* s1, bf16_t* s2, const Rows<C::AR>& ar,
                                          const Rows<C::BR>& br, const MxRows<C::MXU>& bm, int K,
                                          Acc<C>& acc) {
-  static_assert((C::BM + C::BN) * LDK == kStageElems, "stage size");
+  static_assert((C::BM + C::BN) * LDK <= kStageElems, "stage size");
   const int nk = (int)ceil_div(K, BK);
   stage_issue<C, B_MX>(s0, ar, br, bm, 0, K);
   stage_issue<C, B_MX>(s1, ar, br, bm, 1, K);
@@ -645,6 +647,53 @@ __global__ __launch_bounds__(256) void multiseg_kernel(MultiSegArgs a) {
   store_tile(acc, (bf16_t*)a.C, a.ldc, m0, n0, a.M, a.N);
 }
 
+// Approximate router logits (the exact routing is decided in router.hip):
+// 128 x 128 tiles of x W_r^T, K split over `splits` blocks whose fp32 partial
+// sums are added atomically (their order does not matter: the logits only
+// bound the fixed-order ones).
+using LogitCfg = Cfg<2, 2, 3>;
+
+__global__ __launch_bounds__(256) void logits_kernel(LogitsArgs a) {
+  using C = LogitCfg;
+  MOE_LDS_RING;
+  const int ntn = (int)ceil_div(a.E, C::BN), ntm = (int)ceil_div(a.T, C::BM);
+  int64_t L;
+  if (!xcd_item((int64_t)ntm * ntn * a.splits, L)) return;
+  const int sp = (int)(L % a.splits);
+  const int64_t rest = L / a.splits;
+  const int m0 = (int)(rest / ntn) * C::BM, n0 = (int)(rest % ntn) * C::BN;
+  const int kchunk = (int)ceil_div(ceil_div(a.d, a.splits), BK) * BK;
+  const int k0 = sp * kchunk;
+  const int klen = min(a.d - k0, kchunk);
+  if (klen <= 0) return;
+  const Rows<C::AR> ar = a_rows_dense<C::AR>((const bf16_t*)a.x + k0, a.d, m0, a.T);
+  const Rows<C::BR> br = a_rows_dense<C::BR>((const bf16_t*)a.W + k0, a.d, n0, a.E);
+  Acc<C> acc;
+  acc_zero(acc);
+  mainloop<C, false>(lds0, lds1, lds2, ar, br, MxRows<C::MXU>{}, klen, acc);
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const int n = n0 + acc_col<C>(j);
+      if (n >= a.E) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + acc_row<C>(i, r);
+        if (m >= a.T) continue;
+        float* dst = a.L + (int64_t)m * a.E + n;
+        if (a.splits == 1) *dst = acc.c[i][j][r];
+        else atomicAdd(dst, acc.c[i][j][r]);
+      }
+    }
+}
+
+__global__ void zero_f32(float* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+
 }  // namespace
 
 int grouped_bm(int act_dtype, int64_t, int) { return act_dtype == DT_F32 ? 1 : GroupCfg::BM; }
@@ -703,6 +752,26 @@ int launch_multiseg(const MultiSegArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(multiseg_kernel<true>, grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(multiseg_kernel<false>, grid, dim3(256), 0, stream, a);
+  return (int)hipGetLastError();
+}
+
+// Split K until the grid has about two blocks per CU (small batches).
+int router_logit_splits(int T, int E, int d) {
+  const int64_t tiles = ceil_div(T, LogitCfg::BM) * ceil_div(E, LogitCfg::BN);
+  int splits = 1;
+  while (tiles * splits < 512 && d / (splits * 2) >= 4 * BK) splits *= 2;
+  return splits;
+}
+
+int launch_router_logits(const LogitsArgs& a, hipStream_t stream) {
+  if (a.T == 0) return 0;
+  if (a.splits > 1) {
+    const int64_t n = (int64_t)a.T * a.E;
+    const int64_t blocks = ceil_div(n, 256) < 4096 ? ceil_div(n, 256) : 4096;
+    hipLaunchKernelGGL(zero_f32, dim3((unsigned)blocks), dim3(256), 0, stream, a.L, n);
+  }
+  const int64_t items = ceil_div(a.T, LogitCfg::BM) * ceil_div(a.E, LogitCfg::BN) * a.splits;
+  hipLaunchKernelGGL(logits_kernel, dim3((unsigned)xcd_grid(items)), dim3(256), 0, stream, a);
   return (int)hipGetLastError();
 }
 

@@ -18,6 +18,33 @@ struct RouterArgs {
 };
 int launch_router(const RouterArgs& a, hipStream_t stream);
 
+// Router on the matrix cores with an exact recheck (bf16 x and W_r):
+//   1. row norms of x and W_r (upper bounds, fp32)
+//   2. approximate logits L = x W_r^T (bf16 MFMA, fp32 accumulate; split-K
+//      partial sums added atomically: the values only bound the exact ones)
+//   3. per token: interval keys from L +- beta, the candidate set that
+//      provably holds the top-k, the fixed-order fp32 logit / sigmoid / key of
+//      each candidate, and the exact top-k and gates.
+int launch_row_norms(const void* A, int rows, int K, float* out, hipStream_t stream);
+struct LogitsArgs {
+  const void* x; const void* W;      // [T, d], [E, d] bf16
+  int T, E, d;
+  int splits;                        // K splits (atomic accumulation when > 1)
+  float* L;                          // [T, E] fp32 (zeroed by the launcher when splits > 1)
+};
+int launch_router_logits(const LogitsArgs& a, hipStream_t stream);
+int router_logit_splits(int T, int E, int d);
+struct SelectArgs {
+  const float* L;                    // [T, E] approximate logits
+  const void* x; const void* W;      // [T, d], [E, d] bf16
+  const float* bias;                 // [E]
+  const float* xn; const float* wn;  // [T], [E] row norms
+  int T, E, d, k;
+  int32_t* idx; float* gate;         // [T, k]
+};
+int launch_router_select(const SelectArgs& a, hipStream_t stream);
+bool router_select_supported(int E, int d);  // shapes the select kernel takes
+
 struct TopkArgs {
   const float* s; const float* key;
   int T, E, k;

@@ -184,6 +184,228 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ s,
   for (int j = lane; j < k; j += 64) gr[j] = __fdiv_rn(sr[ir[j]], total);
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core router with an exact recheck (bf16 x and W_r).
+//
+// The bf16 products x_k w_k are exact in fp32, so both the fixed fp32 chain
+// and the matrix cores' fp32 accumulation are sums of the same d exact terms,
+// each within gamma_d * sum_k |x_k w_k| <= gamma_d * |x| |w| of the exact sum
+// (gamma_d = d u / (1 - d u), u = 2^-24, any summation order and rounding to
+// nearest or toward zero at most doubles it). Hence the fixed-order logit lies
+// in [L - beta, L + beta] with beta = 6 gamma_d |x_t| |w_e| for the matrix-core
+// logit L. The sigmoid and "+ b_e" are monotone, so the fixed-order key lies in
+// [key_lo, key_hi]. With L_k the k-th largest key_lo, any expert with
+// key_hi < L_k is beaten by k experts and cannot be chosen: the candidates
+// {e : key_hi >= L_k} hold the top-k. For them the fixed-order logit, sigmoid
+// and key are computed exactly as the VALU router does, and the top-k and
+// gates are taken among them: bit for bit the same result.
+// ---------------------------------------------------------------------------
+
+// Upper bounds of the row norms |A_r| (bf16 rows of K): the fp32 sum of
+// squares is within gamma_K (about K 2^-24) of the exact one; the factor
+// 1 + K 2^-22 covers that, and 1 + 2^-20 the rounding of the square root.
+__global__ __launch_bounds__(256) void row_norms_kernel(const bf16_t* __restrict__ A, int rows, int K,
+                                                        float* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const bf16_t* row = A + (int64_t)r * K;
+  float ss = 0.0f;
+  for (int k = lane * 8; k < K; k += 64 * 8) {
+    const uint4 v = *(const uint4*)(row + k);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = __uint_as_float(w[j] << 16), hi = __uint_as_float(w[j] & 0xFFFF0000u);
+      ss = __builtin_fmaf(lo, lo, ss);
+      ss = __builtin_fmaf(hi, hi, ss);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  if (lane == 0) out[r] = sqrtf(ss * (1.0f + (float)K * 0x1p-22f)) * (1.0f + 0x1p-20f);
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One 64-thread block (one wave) per token; d % 64 == 0 and E d 2 < 2^31.
+//  1. From the matrix-core logits: the interval [key_lo, key_hi] that holds
+//     each expert's fixed-order key, and L_k, the k-th largest key_lo.
+//  2. The candidates {e : key_hi >= L_k} (compacted in LDS), their fixed-order
+//     logits 64 at a time, one per lane: the W rows of the 64 candidates pass
+//     through LDS in chunks of kChunk k (coalesced loads of the next chunk run
+//     while the lanes walk the current one); x goes to LDS widened to fp32.
+//  3. The top-k of the exact keys (key descending, ties to the lower index)
+//     and the gates s_j / sum_slots s, the sum in slot order.
+template <int NPER>
+__global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coef) {
+  constexpr int kChunk = 64;                 // k per staged chunk
+  constexpr int kRowBytes = kChunk * 2 + 16; // LDS row stride (16 B pad: conflict-free reads)
+  __shared__ int32_t cand_e[NPER * 64];
+  __shared__ __align__(16) uint8_t wst[64 * kRowBytes];
+  __shared__ __align__(16) float xst[kChunk];
+  __shared__ float sel_s[64];
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x;
+  const float* Lr = a.L + (int64_t)t * a.E;
+  const float xn = a.xn[t];
+
+  // 1. interval keys; L_k
+  uint64_t lo_code[NPER];
+  float key_hi[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = lane + 64 * i;
+    lo_code[i] = 0ull;
+    key_hi[i] = -INFINITY;
+    if (e < a.E) {
+      const float l = Lr[e];
+      const float beta = beta_coef * xn * a.wn[e] + 1e-30f;
+      const float s_lo = sigmoid_fixed(l - beta) * (1.0f - 0x1p-20f);
+      const float s_hi = sigmoid_fixed(l + beta) * (1.0f + 0x1p-20f);
+      const float b = a.bias[e];
+      lo_code[i] = ((uint64_t)key_code(__fadd_rn(s_lo, b)) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+      key_hi[i] = __fadd_rn(s_hi, b);
+    }
+  }
+  uint64_t kth = 0;
+  for (int j = 0; j < a.k; ++j) {
+    uint64_t m = 0;
+#pragma unroll
+    for (int i = 0; i < NPER; ++i) m = lo_code[i] > m ? lo_code[i] : m;
+    m = wave_max_u64(m);
+    const int e = (int)(0xFFFFFFFFu - (uint32_t)m);
+#pragma unroll
+    for (int i = 0; i < NPER; ++i)
+      if (lo_code[i] == m) lo_code[i] = 0ull;   // codes are unique: one owner
+    kth = m;
+    (void)e;
+  }
+  const uint32_t kc = (uint32_t)(kth >> 32);  // invert the order-preserving code of L_k
+  const float Lk = __uint_as_float((kc & 0x80000000u) ? (kc & 0x7FFFFFFFu) : ~kc);
+
+  // 2a. candidates, in expert order
+  int ncand = 0;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int e = lane + 64 * i;
+    const bool is_c = e < a.E && key_hi[i] >= Lk;
+    const uint64_t mask = __ballot(is_c);
+    if (is_c) cand_e[ncand + __popcll(mask & ((1ull << lane) - 1ull))] = e;
+    ncand += __popcll(mask);
+  }
+  wave_sync();
+
+  // 2b. fixed-order logits of the candidates; candidate p = 64 r + lane ends
+  //     in code[r], sc[r] of this lane
+  const rsrc_t wres = make_rsrc(a.W, (int64_t)a.E * a.d * 2);
+  const rsrc_t xres = make_rsrc((const bf16_t*)a.x + (int64_t)t * a.d, (int64_t)a.d * 2);
+  const int nchunks = a.d / kChunk;         // d % kChunk == 0 (checked by the launcher)
+  uint64_t code[NPER];
+  float sc[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) { code[i] = 0ull; sc[i] = 0.0f; }
+  const int npass = (int)ceil_div(ncand, 64);
+  for (int r = 0; r < npass; ++r) {
+    // rows this lane loads: (lane >> 3) + 8 j, 16-byte piece lane & 7
+    uint32_t roff[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = 64 * r + (lane >> 3) + 8 * j;
+      roff[j] = p < ncand ? (uint32_t)cand_e[p] * (uint32_t)a.d * 2u + (uint32_t)(lane & 7) * 16u
+                          : kOOB;
+    }
+    const uint32_t xoff = lane < 8 ? (uint32_t)lane * 16u : kOOB;
+    uint4 pw[8], px;
+    auto load_chunk = [&](int c) {
+      const uint32_t k0b = 2u * (uint32_t)(c * kChunk);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pw[j] = bload16(wres, roff[j] != kOOB ? roff[j] + k0b : kOOB);
+      px = bload16(xres, xoff != kOOB ? xoff + k0b : kOOB);
+    };
+    load_chunk(0);
+    float acc = 0.0f;
+    for (int c = 0; c < nchunks; ++c) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        *(uint4*)(wst + ((lane >> 3) + 8 * j) * kRowBytes + (lane & 7) * 16) = pw[j];
+      if (lane < 8) {
+        const uint32_t xv[4] = {px.x, px.y, px.z, px.w};
+        float4 lo4, hi4;
+        lo4.x = __uint_as_float(xv[0] << 16); lo4.y = __uint_as_float(xv[0] & 0xFFFF0000u);
+        lo4.z = __uint_as_float(xv[1] << 16); lo4.w = __uint_as_float(xv[1] & 0xFFFF0000u);
+        hi4.x = __uint_as_float(xv[2] << 16); hi4.y = __uint_as_float(xv[2] & 0xFFFF0000u);
+        hi4.z = __uint_as_float(xv[3] << 16); hi4.w = __uint_as_float(xv[3] & 0xFFFF0000u);
+        *(float4*)(xst + lane * 8) = lo4;
+        *(float4*)(xst + lane * 8 + 4) = hi4;
+      }
+      wave_sync();
+      if (c + 1 < nchunks) load_chunk(c + 1);
+      const uint8_t* row = wst + lane * kRowBytes;
+#pragma unroll
+      for (int st = 0; st < kChunk / 8; ++st) {
+        const uint4 wv = *(const uint4*)(row + st * 16);
+        const float4 x0 = *(const float4*)(xst + st * 8);
+        const float4 x1 = *(const float4*)(xst + st * 8 + 4);
+        acc = __builtin_fmaf(x0.x, __uint_as_float(wv.x << 16), acc);
+        acc = __builtin_fmaf(x0.y, __uint_as_float(wv.x & 0xFFFF0000u), acc);
+        acc = __builtin_fmaf(x0.z, __uint_as_float(wv.y << 16), acc);
+        acc = __builtin_fmaf(x0.w, __uint_as_float(wv.y & 0xFFFF0000u), acc);
+        acc = __builtin_fmaf(x1.x, __uint_as_float(wv.z << 16), acc);
+        acc = __builtin_fmaf(x1.y, __uint_as_float(wv.z & 0xFFFF0000u), acc);
+        acc = __builtin_fmaf(x1.z, __uint_as_float(wv.w << 16), acc);
+        acc = __builtin_fmaf(x1.w, __uint_as_float(wv.w & 0xFFFF0000u), acc);
+      }
+      wave_sync();
+    }
+    const int p = 64 * r + lane;
+    if (p < ncand) {
+      const int e = cand_e[p];
+      const float sv = sigmoid_fixed(acc);
+      const uint64_t cd = ((uint64_t)key_code(__fadd_rn(sv, a.bias[e])) << 32) |
+                          (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
+#pragma unroll
+      for (int i = 0; i < NPER; ++i)
+        if (i == r) { code[i] = cd; sc[i] = sv; }
+    }
+  }
+
+  // 3. top-k of the exact keys; gates
+  int32_t* ir = a.idx + (int64_t)t * a.k;
+  float* gr = a.gate + (int64_t)t * a.k;
+  float total = 0.0f;
+  for (int j0 = 0; j0 < a.k; j0 += 64) {
+    const int jn = min(64, a.k - j0);
+    int my_e = 0;
+    for (int j = 0; j < jn; ++j) {
+      uint64_t m = 0;
+#pragma unroll
+      for (int i = 0; i < NPER; ++i) m = code[i] > m ? code[i] : m;
+      const uint64_t wmax = wave_max_u64(m);
+      if (wmax != 0ull) {
+#pragma unroll
+        for (int i = 0; i < NPER; ++i)
+          if (code[i] == wmax) { sel_s[j] = sc[i]; code[i] = 0ull; }
+      }
+      if (lane == j) my_e = (int)(0xFFFFFFFFu - (uint32_t)wmax);
+    }
+    wave_sync();
+    const float my_s = lane < jn ? sel_s[lane] : 0.0f;
+    if (lane < jn) {
+      ir[j0 + lane] = my_e;
+      gr[j0 + lane] = my_s;  // the score for now; divided by the sum below
+    }
+    for (int j = 0; j < jn; ++j) total = __fadd_rn(total, __shfl(my_s, j, 64));
+    wave_sync();
+  }
+  // slot j was written by lane j % 64 above (the same thread reads it back)
+  for (int j = lane; j < a.k; j += 64) gr[j] = __fdiv_rn(gr[j], total);
+}
+
 }  // namespace
 
 template <int TMN, typename XT, typename WT>
@@ -224,6 +446,39 @@ int launch_topk(const TopkArgs& a, hipStream_t stream) {
   else if (nper <= 64) MOE_TOPK(64);
   else return -1;
 #undef MOE_TOPK
+  return (int)hipGetLastError();
+}
+
+int launch_row_norms(const void* A, int rows, int K, float* out, hipStream_t stream) {
+  if (rows == 0) return 0;
+  hipLaunchKernelGGL(row_norms_kernel, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, stream,
+                     (const bf16_t*)A, rows, K, out);
+  return (int)hipGetLastError();
+}
+
+bool router_select_supported(int E, int d) {
+  return d % 64 == 0 && (int64_t)E * d * 2 < ((int64_t)1 << 31) && E <= 64 * 64;
+}
+
+int launch_router_select(const SelectArgs& a, hipStream_t stream) {
+  if (a.T == 0) return 0;
+  if (!router_select_supported(a.E, a.d)) return -1;
+  // beta = 6 gamma_d |x| |w|: 4 gamma_d bounds the two sums' distance (rounding
+  // to nearest or toward zero), the rest covers the fp32 evaluation of beta
+  const double du = (double)a.d * 0x1p-24;
+  const float beta_coef = (float)(6.0 * du / (1.0 - du));
+  const int nper = (int)ceil_div(a.E, 64);
+#define MOE_SEL(N) \
+  hipLaunchKernelGGL(select_kernel<N>, dim3((unsigned)a.T), dim3(64), 0, stream, a, beta_coef)
+  if (nper <= 1) MOE_SEL(1);
+  else if (nper <= 2) MOE_SEL(2);
+  else if (nper <= 4) MOE_SEL(4);
+  else if (nper <= 8) MOE_SEL(8);
+  else if (nper <= 16) MOE_SEL(16);
+  else if (nper <= 32) MOE_SEL(32);
+  else if (nper <= 64) MOE_SEL(64);
+  else return -1;
+#undef MOE_SEL
   return (int)hipGetLastError();
 }
 

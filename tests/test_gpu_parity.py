@@ -53,15 +53,17 @@ def test_device_generator_matches_host(device):
 # routing
 # ---------------------------------------------------------------------------
 
-def _route_gpu(cfg, inp, dev):
+def _route_gpu(cfg, inp, dev, want_scores=True):
+    """moe_route with the score output (every logit in fixed order on VALU) or
+    without it (bf16: matrix-core logits + exact recheck near the boundary)."""
     desc = moe.make_desc(cfg)
-    idx = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=dev)
-    gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
-    s = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev)
+    idx = torch.full((cfg.T, cfg.k), -5, dtype=torch.int32, device=dev)
+    gate = torch.full((cfg.T, cfg.k), -5.0, dtype=torch.float32, device=dev)
+    s = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device=dev) if want_scores else None
     ws = moe.workspace(desc, moe.MOE_OP_ROUTE, dev)
     moe.moe_route(desc, inp["x"], inp["W_r"], inp["b"], idx, gate, s, ws)
     torch.cuda.synchronize()
-    return idx.cpu().numpy(), gate.cpu().numpy(), s.cpu().numpy()
+    return idx.cpu().numpy(), gate.cpu().numpy(), (s.cpu().numpy() if want_scores else None)
 
 
 ROUTE_CASES = [
@@ -86,6 +88,10 @@ def test_route_bit_exact(cfg, device):
     assert np.array_equal(idx, ref["idx"]), "expert indices differ"
     check_gates(gate, ref["p"])
     assert np.array_equal(gate, ref["p"])
+    say(f"route {cfg.name}: without the score output")
+    idx2, gate2, _ = _route_gpu(cfg, inp, device, want_scores=False)
+    assert np.array_equal(idx2, ref["idx"]), "expert indices differ (no score output)"
+    assert np.array_equal(gate2, ref["p"]), "gates differ (no score output)"
 
 
 def test_route_ties_go_to_lower_index(device):
@@ -102,6 +108,29 @@ def test_route_ties_go_to_lower_index(device):
     assert np.array_equal(s[:, :6], s[:, 6:])
     assert np.array_equal(idx, ref["idx"])
     assert np.array_equal(gate, ref["p"])
+    idx2, gate2, _ = _route_gpu(cfg, {"x": x, "W_r": W, "b": b}, device, want_scores=False)
+    assert np.array_equal(idx2, ref["idx"])
+    assert np.array_equal(gate2, ref["p"])
+
+
+@pytest.mark.parametrize("shift", [10, 16])
+def test_route_near_ties(shift, device):
+    """Router rows scaled by 2^-shift (exact in bf16): every logit is tiny, all
+    sigmoid scores sit within a few ulp of 1/2 and the keys of most experts tie
+    or nearly tie, so the rounding of the logit sums decides the selection.
+    With and without the score output the routing must equal the oracle's."""
+    cfg = LayerConfig("near_ties", T=96, d=7168, d_lat=32, E=896, k=16, F=32, S=0, Fs=32, seed=26)
+    x = synth.device_tensor(cfg, "x", device)
+    W = synth.device_tensor(cfg, "W_r", device) * (2.0 ** -shift)
+    b = torch.zeros(cfg.E, dtype=torch.float32, device=device)
+    ref = oracle.route(oracle.widen(("bf16", x.view(torch.int16).cpu().numpy().view(np.uint16))),
+                       oracle.widen(("bf16", W.view(torch.int16).cpu().numpy().view(np.uint16))),
+                       b.cpu().numpy(), cfg.k)
+    say(f"near ties 2^-{shift}: {len(np.unique(ref['key']))} distinct keys of {ref['key'].size}")
+    for want in (True, False):
+        idx, gate, _ = _route_gpu(cfg, {"x": x, "W_r": W, "b": b}, device, want_scores=want)
+        assert np.array_equal(idx, ref["idx"]), f"indices differ (score output {want})"
+        assert np.array_equal(gate, ref["p"]), f"gates differ (score output {want})"
 
 
 # ---------------------------------------------------------------------------
