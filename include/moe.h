@@ -144,7 +144,11 @@ int moe_permute(const moe_desc_t* desc, const int32_t* topk_idx, int32_t* counts
                 void* ws, size_t ws_bytes, void* stream);
 
 /* Latent down-projection z = W_down x (equation z = W_down x), stored in the
-   act dtype. x [T, d]; z [T, d_lat]; lat_down: latent_w dtype. */
+   act dtype. x [T, d]; z [T, d_lat]; lat_down: latent_w dtype.
+   ws: moe_workspace_bytes(desc, MOE_OP_LATENT_DOWN) bytes, which is 0 unless
+   the batch is too small to fill the GPU with output tiles; then K is split
+   and the fp32 partial sums pass through the workspace (added in a fixed
+   order, so results stay deterministic). */
 int moe_latent_down(const moe_desc_t* desc, const void* x, moe_w_t lat_down, void* z,
                     void* ws, size_t ws_bytes, void* stream);
 
@@ -167,7 +171,9 @@ int moe_combine(const moe_desc_t* desc, const void* o_perm, const int32_t* inv_p
                 void* stream);
 
 /* Output (y equation): y = W_up n + sum_s W_os[s] act(W_gs[s] x, W_vs[s] x),
-   accumulated in fp32, stored in the act dtype. Reads lat_up and sh_* of `w`. */
+   accumulated in fp32, stored in the act dtype. Reads lat_up and sh_* of `w`.
+   ws holds the shared hidden rows and, for small batches, fp32 split-K
+   partials (see moe_latent_down). */
 int moe_output(const moe_desc_t* desc, const void* x, const void* n, const moe_weights_t* w,
                void* y, void* ws, size_t ws_bytes, void* stream);
 

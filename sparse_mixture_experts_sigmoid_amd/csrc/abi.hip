@@ -103,7 +103,7 @@ struct Plan {
 };
 
 struct LayerWs {
-  size_t s, key, norms, idx, gate, counts, offsets, perm, inv, blk, z, tile_off, H, O, n, Hs;
+  size_t s, key, norms, idx, gate, counts, offsets, perm, inv, blk, z, tile_off, H, O, n, Hs, P;
 };
 
 int max_tiles(const moe_desc_t* d) {
@@ -123,8 +123,27 @@ void plan_expert(const moe_desc_t* d, Plan& p, LayerWs& w) {
   w.tile_off = p.take((size_t)(d->n_experts + 1) * 4);
   w.H = p.take((size_t)d->T * d->top_k * d->d_ff * elem_bytes(d->act_dtype));
 }
+// fp32 split-K partials of the dense GEMMs that run with few tokens
+moe::SplitK latent_split(const moe_desc_t* d) {
+  return moe::plan_split(d->act_dtype, d->T, d->d_latent, d->d_model);
+}
+moe::SplitK shared_split(const moe_desc_t* d) {
+  return moe::plan_split(d->act_dtype, d->T, 2 * d->n_shared * d->d_ff_shared, d->d_model);
+}
+size_t latent_partial_bytes(const moe_desc_t* d) {
+  return (size_t)latent_split(d).partial_bytes(d->T, d->d_latent);
+}
+size_t output_partial_bytes(const moe_desc_t* d) {
+  const size_t glu = d->n_shared > 0
+      ? (size_t)shared_split(d).partial_bytes(d->T, 2 * (int64_t)d->n_shared * d->d_ff_shared) : 0;
+  const size_t out = (size_t)moe::multiseg_slices(d->act_dtype, d->T, d->d_model, d->n_shared + 1) *
+                     d->T * d->d_model * 4;
+  return glu > out ? glu : out;
+}
+void plan_latent(const moe_desc_t* d, Plan& p, LayerWs& w) { w.P = p.take(latent_partial_bytes(d)); }
 void plan_output(const moe_desc_t* d, Plan& p, LayerWs& w) {
   w.Hs = p.take((size_t)d->T * d->n_shared * d->d_ff_shared * elem_bytes(d->act_dtype));
+  w.P = p.take(output_partial_bytes(d));
 }
 
 Plan plan_layer(const moe_desc_t* d, LayerWs& w) {
@@ -142,7 +161,10 @@ Plan plan_layer(const moe_desc_t* d, LayerWs& w) {
   plan_expert(d, p, w);
   w.O = p.take(tk * d->d_latent * elem_bytes(d->act_dtype));
   w.n = p.take((size_t)d->T * d->d_latent * elem_bytes(d->act_dtype));
-  plan_output(d, p, w);
+  w.Hs = p.take((size_t)d->T * d->n_shared * d->d_ff_shared * elem_bytes(d->act_dtype));
+  // one partial buffer serves latent down, shared gate/up and the output GEMM (in turn)
+  const size_t lp = latent_partial_bytes(d), op = output_partial_bytes(d);
+  w.P = p.take(lp > op ? lp : op);
   return p;
 }
 
@@ -152,7 +174,7 @@ size_t ws_bytes_for(const moe_desc_t* d, int op) {
   switch (op) {
     case MOE_OP_ROUTE: plan_route(d, p, w); break;
     case MOE_OP_PERMUTE: plan_permute(d, p, w); break;
-    case MOE_OP_LATENT_DOWN: break;
+    case MOE_OP_LATENT_DOWN: plan_latent(d, p, w); break;
     case MOE_OP_EXPERT_FFN: plan_expert(d, p, w); break;
     case MOE_OP_COMBINE: break;
     case MOE_OP_OUTPUT: plan_output(d, p, w); break;
@@ -279,9 +301,9 @@ int do_permute(const moe_desc_t* d, const int32_t* idx, int32_t* counts, int32_t
   return MOE_OK;
 }
 
-int do_latent_down(const moe_desc_t* d, const void* x, moe_w_t w, void* z, hipStream_t st) {
+int do_latent_down(const moe_desc_t* d, const void* x, moe_w_t w, void* z, float* P, hipStream_t st) {
   moe::DenseArgs a{x, d->d_model, wop(w, d->latent_w_dtype), d->T, d->d_latent, d->d_model, z,
-                   d->d_latent, d->act_dtype};
+                   d->d_latent, d->act_dtype, latent_split(d), P};
   MOE_LAUNCH(moe::launch_dense(a, st), "latent_down");
   return MOE_OK;
 }
@@ -325,7 +347,7 @@ int do_combine(const moe_desc_t* d, const void* o_perm, const int32_t* inv, cons
 }
 
 int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weights_t* w, void* y,
-              void* Hs, hipStream_t st, Marker mk = {-1, nullptr}) {
+              void* Hs, float* P, hipStream_t st, Marker mk = {-1, nullptr}) {
   mk(8);
   const int S = d->n_shared, Fs = d->d_ff_shared, D = d->d_model;
   const size_t eb = elem_bytes(d->act_dtype);
@@ -336,6 +358,7 @@ int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weigh
     g.Wv = wop(w->sh_up, d->dense_w_dtype);
     g.M = d->T; g.F = S * Fs; g.K = D;
     g.H = Hs; g.ldh = (int64_t)S * Fs; g.c = d->situ_c; g.act_dtype = d->act_dtype;
+    g.split = shared_split(d); g.P = P;
     MOE_LAUNCH(moe::launch_glu(g, st), "shared_gate_up");
   }
   mk(9);
@@ -352,7 +375,7 @@ int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weigh
   m.seg[S].B = wop(w->lat_up, d->latent_w_dtype);
   m.seg[S].K = d->d_latent;
   m.nseg = S + 1;
-  m.M = d->T; m.N = D; m.C = y; m.ldc = D; m.act_dtype = d->act_dtype;
+  m.M = d->T; m.N = D; m.C = y; m.ldc = D; m.act_dtype = d->act_dtype; m.P = P;
   MOE_LAUNCH(moe::launch_multiseg(m, st), "output");
   mk(10);
   return MOE_OK;
@@ -482,7 +505,10 @@ int moe_latent_down(const moe_desc_t* d, const void* x, moe_w_t lat_down, void* 
   MOE_CHECK(need_w(lat_down, d->latent_w_dtype, "lat_down"));
   MOE_CHECK(need_ptr_t(d, z, "z"));
   MOE_CHECK(check_ws(d, MOE_OP_LATENT_DOWN, ws, ws_bytes));
-  return do_latent_down(d, x, lat_down, z, (hipStream_t)stream);
+  Plan p;
+  LayerWs lw{};
+  plan_latent(d, p, lw);
+  return do_latent_down(d, x, lat_down, z, (float*)at(ws, lw.P), (hipStream_t)stream);
 }
 
 int moe_expert_ffn(const moe_desc_t* d, const void* z, const int32_t* perm_src,
@@ -538,7 +564,7 @@ int moe_output(const moe_desc_t* d, const void* x, const void* n, const moe_weig
   Plan p;
   LayerWs lw{};
   plan_output(d, p, lw);
-  return do_output(d, x, n, w, y, at(ws, lw.Hs), (hipStream_t)stream);
+  return do_output(d, x, n, w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), (hipStream_t)stream);
 }
 
 int moe_layer_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
@@ -581,12 +607,12 @@ int moe_layer_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x
   mk(2);
   MOE_CHECK(do_permute(d, idx, counts, offsets, perm, inv, (int32_t*)at(ws, lw.blk), st));
   mk(3);
-  MOE_CHECK(do_latent_down(d, x, w->lat_down, at(ws, lw.z), st));
+  MOE_CHECK(do_latent_down(d, x, w->lat_down, at(ws, lw.z), (float*)at(ws, lw.P), st));
   MOE_CHECK(do_experts(d, at(ws, lw.z), perm, offsets, w, at(ws, lw.O), (int32_t*)at(ws, lw.tile_off),
                        at(ws, lw.H), st, mk));
   mk(7);
   MOE_CHECK(do_combine(d, at(ws, lw.O), inv, gate, w->rms_gain, at(ws, lw.n), nullptr, st));
-  MOE_CHECK(do_output(d, x, at(ws, lw.n), w, y, at(ws, lw.Hs), st, mk));
+  MOE_CHECK(do_output(d, x, at(ws, lw.n), w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), st, mk));
   return MOE_OK;
 }
 

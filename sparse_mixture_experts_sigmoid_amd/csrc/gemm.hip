@@ -647,6 +647,183 @@ __global__ __launch_bounds__(256) void multiseg_kernel(MultiSegArgs a) {
   store_tile(acc, (bf16_t*)a.C, a.ldc, m0, n0, a.M, a.N);
 }
 
+// ---------------------------------------------------------------------------
+// split-K path (few output rows: too few tiles to fill 256 CUs)
+// ---------------------------------------------------------------------------
+
+using SplitCfg = Cfg<2, 2, 3>;   // 128 x 128
+
+template <class C>
+__device__ __forceinline__ void store_partial(const Acc<C>& acc, float* P, int64_t ldp, int m0, int n0,
+                                              int M, int N) {
+#pragma unroll
+  for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) {
+      const int n = n0 + acc_col<C>(j);
+      if (n >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + acc_row<C>(i, r);
+        if (m < M) P[(int64_t)m * ldp + n] = acc.c[i][j][r];
+      }
+    }
+}
+
+// GLU partial row: gate sums at [0, F), up sums at [F, 2F).
+template <class C>
+__device__ __forceinline__ void store_partial_glu(const Acc<C>& acc, float* P, int F, int f0, int m0,
+                                                  int M) {
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+#pragma unroll
+  for (int j = 0; j < C::WN / 2; ++j) {
+    const int f = f0 + wn * (C::BN / 4) + j * 32 + (lane & 31);
+    if (f >= F) continue;
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + acc_row<C>(i, r);
+        if (m >= M) continue;
+        float* row = P + (int64_t)m * 2 * F;
+        row[f] = acc.c[i][j][r];
+        row[F + f] = acc.c[i][j + C::WN / 2][r];
+      }
+  }
+}
+
+// Work item L -> (split, tile): split-major, so blocks that run together on
+// one XCD read the same K range of A.
+__device__ __forceinline__ void split_item(int64_t L, int64_t tiles, int ntn, int& sp, int& m0,
+                                           int& n0, int BM, int BN) {
+  sp = (int)(L / tiles);
+  const int64_t tile = L % tiles;
+  m0 = (int)(tile / ntn) * BM;
+  n0 = (int)(tile % ntn) * BN;
+}
+
+// bf16 row operand shifted to column kb (row stride unchanged)
+__device__ __forceinline__ WOperand shift_k(const WOperand& w, int kb) {
+  if (w.dtype == DT_MXFP4) return WOperand{(const uint8_t*)w.data + kb / 2, w.scale + kb / 32, w.dtype};
+  return WOperand{(const bf16_t*)w.data + kb, w.scale, w.dtype};
+}
+
+template <bool B_MX>
+__global__ __launch_bounds__(256) void dense_split_kernel(DenseArgs a) {
+  using C = SplitCfg;
+  MOE_LDS_RING;
+  const int ntn = (int)ceil_div(a.N, C::BN);
+  const int64_t tiles = ceil_div(a.M, C::BM) * ntn;
+  int64_t L;
+  if (!xcd_item(tiles * a.split.splits, L)) return;
+  int sp, m0, n0;
+  split_item(L, tiles, ntn, sp, m0, n0, C::BM, C::BN);
+  const int kb = sp * a.split.kchunk, klen = min(a.K - kb, a.split.kchunk);
+  const WOperand W = shift_k(a.W, kb);
+  const Rows<C::AR> ar = a_rows_dense<C::AR>((const bf16_t*)a.A + kb, a.lda, m0, a.M);
+  Rows<C::BR> br{};
+  MxRows<C::MXU> bm{};
+  if constexpr (B_MX) bm = b_mx_plain<C::MXU>(W, 0, a.K, n0, a.N);
+  else br = b_rows_plain<C::BR>(W.data, a.K, n0, a.N);
+  Acc<C> acc;
+  acc_zero(acc);
+  mainloop<C, B_MX>(lds0, lds1, lds2, ar, br, bm, klen, acc);
+  store_partial(acc, a.P + (int64_t)sp * a.M * a.N, a.N, m0, n0, a.M, a.N);
+}
+
+template <bool B_MX>
+__global__ __launch_bounds__(256) void glu_split_kernel(GluArgs a) {
+  using C = SplitCfg;
+  MOE_LDS_RING;
+  const int ntn = (int)ceil_div(a.F, C::BN / 2);
+  const int64_t tiles = ceil_div(a.M, C::BM) * ntn;
+  int64_t L;
+  if (!xcd_item(tiles * a.split.splits, L)) return;
+  int sp, m0, f0;
+  split_item(L, tiles, ntn, sp, m0, f0, C::BM, C::BN / 2);
+  const int kb = sp * a.split.kchunk, klen = min(a.K - kb, a.split.kchunk);
+  const WOperand Wg = shift_k(a.Wg, kb), Wv = shift_k(a.Wv, kb);
+  const Rows<C::AR> ar = a_rows_dense<C::AR>((const bf16_t*)a.A + kb, a.lda, m0, a.M);
+  Rows<C::BR> br{};
+  MxRows<C::MXU> bm{};
+  if constexpr (B_MX) bm = b_mx_glu<C>(Wg, Wv, 0, a.K, f0, a.F);
+  else br = b_rows_glu<C>(Wg, Wv, 0, a.K, f0, a.F);
+  Acc<C> acc;
+  acc_zero(acc);
+  mainloop<C, B_MX>(lds0, lds1, lds2, ar, br, bm, klen, acc);
+  store_partial_glu(acc, a.P + (int64_t)sp * a.M * 2 * a.F, a.F, f0, m0, a.M);
+}
+
+// One work item per (segment, tile); segment s writes partial slice s.
+template <bool LAST_MX>
+__global__ __launch_bounds__(256) void multiseg_split_kernel(MultiSegArgs a) {
+  using C = SplitCfg;
+  MOE_LDS_RING;
+  const int ntn = (int)ceil_div(a.N, C::BN);
+  const int64_t tiles = ceil_div(a.M, C::BM) * ntn;
+  int64_t L;
+  if (!xcd_item(tiles * a.nseg, L)) return;
+  int s, m0, n0;
+  split_item(L, tiles, ntn, s, m0, n0, C::BM, C::BN);
+  const Segment& sg = a.seg[s];
+  const Rows<C::AR> ar = a_rows_dense<C::AR>(sg.A, sg.lda, m0, a.M);
+  Acc<C> acc;
+  acc_zero(acc);
+  if (LAST_MX && s == a.nseg - 1) {
+    const MxRows<C::MXU> bm = b_mx_plain<C::MXU>(sg.B, 0, sg.K, n0, a.N);
+    mainloop<C, true>(lds0, lds1, lds2, ar, Rows<C::BR>{}, bm, sg.K, acc);
+  } else {
+    const Rows<C::BR> br = b_rows_plain<C::BR>(sg.B.data, sg.K, n0, a.N);
+    mainloop<C, false>(lds0, lds1, lds2, ar, br, MxRows<C::MXU>{}, sg.K, acc);
+  }
+  store_partial(acc, a.P + (int64_t)s * a.M * a.N, a.N, m0, n0, a.M, a.N);
+}
+
+// C[m, n] = bf16(sum over slices in ascending order); 4 columns per thread.
+__global__ __launch_bounds__(256) void reduce_store_kernel(const float* __restrict__ P, int slices,
+                                                           int M, int N, bf16_t* __restrict__ Cm,
+                                                           int64_t ldc) {
+  const int64_t stride = (int64_t)M * N, n4 = stride / 4;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    float4 v = ((const float4*)P)[q];
+    for (int s = 1; s < slices; ++s) {
+      const float4 w = ((const float4*)(P + s * stride))[q];
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    const int64_t e = q * 4, m = e / N, n = e % N;
+    const uint32_t lo = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    *(uint2*)(Cm + m * ldc + n) = make_uint2(lo, hi);
+  }
+}
+
+// H[m, f] = bf16(act(sum gate, sum up)) from GLU partial rows [gate F | up F].
+__global__ __launch_bounds__(256) void reduce_glu_kernel(const float* __restrict__ P, int slices, int M,
+                                                         int F, float c, bf16_t* __restrict__ H,
+                                                         int64_t ldh) {
+  const int64_t stride = (int64_t)M * 2 * F, n4 = (int64_t)M * F / 4;
+  const float inv_c = 1.0f / c;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = q * 4, m = e / F, f = e % F;
+    const float* g0 = P + m * 2 * F + f;
+    float4 g = *(const float4*)g0, u = *(const float4*)(g0 + F);
+    for (int s = 1; s < slices; ++s) {
+      const float4 wg = *(const float4*)(g0 + s * stride), wu = *(const float4*)(g0 + s * stride + F);
+      g.x += wg.x; g.y += wg.y; g.z += wg.z; g.w += wg.w;
+      u.x += wu.x; u.y += wu.y; u.z += wu.z; u.w += wu.w;
+    }
+    const uint32_t lo = (uint32_t)f32_to_bf16(situ_glu(g.x, u.x, c, inv_c)) |
+                        ((uint32_t)f32_to_bf16(situ_glu(g.y, u.y, c, inv_c)) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(situ_glu(g.z, u.z, c, inv_c)) |
+                        ((uint32_t)f32_to_bf16(situ_glu(g.w, u.w, c, inv_c)) << 16);
+    *(uint2*)(H + m * ldh + f) = make_uint2(lo, hi);
+  }
+}
+
+int reduce_blocks(int64_t n4) { return (int)(ceil_div(n4, 256) < 2048 ? ceil_div(n4, 256) : 2048); }
+
 // Approximate router logits (the exact routing is decided in router.hip):
 // 128 x 128 tiles of x W_r^T, K split over `splits` blocks whose fp32 partial
 // sums are added atomically (their order does not matter: the logits only
@@ -696,11 +873,42 @@ __global__ void zero_f32(float* p, int64_t n) {
 
 }  // namespace
 
+// Below 256 single-pass tiles the chip is not full: take 128 x 128 tiles and
+// split K until about 256 blocks run, each over at least 6 K-tiles.
+SplitK plan_split(int act_dtype, int M, int ncols, int K) {
+  SplitK p;
+  if (act_dtype != DT_BF16 || M == 0) return p;
+  if (ceil_div(M, DenseCfg::BM) * ceil_div(ncols, DenseCfg::BN) >= 256) return p;
+  const int64_t tiles = ceil_div(M, SplitCfg::BM) * ceil_div(ncols, SplitCfg::BN);
+  int s = 1;
+  while (s < 16 && tiles * s < 256 && K / (2 * s) >= 6 * BK) s *= 2;
+  const int unit = 3 * BK;  // the ring walks K-tiles in threes
+  p.kchunk = (int)(ceil_div(ceil_div(K, s), unit) * unit);
+  p.splits = (int)ceil_div(K, p.kchunk);
+  return p;
+}
+
+int multiseg_slices(int act_dtype, int M, int N, int nseg) {
+  if (act_dtype != DT_BF16 || M == 0 || nseg < 2) return 0;
+  if (ceil_div(M, DenseCfg::BM) * ceil_div(N, DenseCfg::BN) >= 256) return 0;
+  return nseg;
+}
+
 int grouped_bm(int act_dtype, int64_t, int) { return act_dtype == DT_F32 ? 1 : GroupCfg::BM; }
 
 int launch_dense(const DenseArgs& a, hipStream_t stream) {
   if (a.act_dtype == DT_F32) return launch_dense_f32(a, stream);
   if (a.M == 0) return 0;
+  if (a.split.splits > 0) {
+    using C = SplitCfg;
+    dim3 grid((unsigned)xcd_grid(ceil_div(a.N, C::BN) * ceil_div(a.M, C::BM) * a.split.splits));
+    if (a.W.dtype == DT_MXFP4) hipLaunchKernelGGL(dense_split_kernel<true>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(dense_split_kernel<false>, grid, dim3(256), 0, stream, a);
+    const int64_t n4 = (int64_t)a.M * a.N / 4;
+    hipLaunchKernelGGL(reduce_store_kernel, dim3(reduce_blocks(n4)), dim3(256), 0, stream, a.P,
+                       a.split.splits, a.M, a.N, (bf16_t*)a.C, a.ldc);
+    return (int)hipGetLastError();
+  }
   using C = DenseCfg;
   dim3 grid((unsigned)xcd_grid(ceil_div(a.N, C::BN) * ceil_div(a.M, C::BM)));
   if (a.W.dtype == DT_MXFP4) hipLaunchKernelGGL(dense_kernel<true>, grid, dim3(256), 0, stream, a);
@@ -711,6 +919,16 @@ int launch_dense(const DenseArgs& a, hipStream_t stream) {
 int launch_glu(const GluArgs& a, hipStream_t stream) {
   if (a.act_dtype == DT_F32) return launch_glu_f32(a, stream);
   if (a.M == 0) return 0;
+  if (a.split.splits > 0) {
+    using C = SplitCfg;
+    dim3 grid((unsigned)xcd_grid(ceil_div(a.F, C::BN / 2) * ceil_div(a.M, C::BM) * a.split.splits));
+    if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(glu_split_kernel<true>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(glu_split_kernel<false>, grid, dim3(256), 0, stream, a);
+    const int64_t n4 = (int64_t)a.M * a.F / 4;
+    hipLaunchKernelGGL(reduce_glu_kernel, dim3(reduce_blocks(n4)), dim3(256), 0, stream, a.P,
+                       a.split.splits, a.M, a.F, a.c, (bf16_t*)a.H, a.ldh);
+    return (int)hipGetLastError();
+  }
   using C = DenseCfg;
   dim3 grid((unsigned)xcd_grid(ceil_div(a.F, C::BN / 2) * ceil_div(a.M, C::BM)));
   if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(glu_kernel<true>, grid, dim3(256), 0, stream, a);
@@ -748,7 +966,18 @@ int launch_multiseg(const MultiSegArgs& a, hipStream_t stream) {
   // only the last segment (W_up) may be MXFP4
   for (int i = 0; i + 1 < a.nseg; ++i)
     if (a.seg[i].B.dtype == DT_MXFP4) return -1;
-  if (a.nseg > 0 && a.seg[a.nseg - 1].B.dtype == DT_MXFP4)
+  const bool last_mx = a.nseg > 0 && a.seg[a.nseg - 1].B.dtype == DT_MXFP4;
+  if (multiseg_slices(a.act_dtype, a.M, a.N, a.nseg) > 0) {
+    using CS = SplitCfg;
+    dim3 g2((unsigned)xcd_grid(ceil_div(a.N, CS::BN) * ceil_div(a.M, CS::BM) * a.nseg));
+    if (last_mx) hipLaunchKernelGGL(multiseg_split_kernel<true>, g2, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(multiseg_split_kernel<false>, g2, dim3(256), 0, stream, a);
+    const int64_t n4 = (int64_t)a.M * a.N / 4;
+    hipLaunchKernelGGL(reduce_store_kernel, dim3(reduce_blocks(n4)), dim3(256), 0, stream, a.P,
+                       a.nseg, a.M, a.N, (bf16_t*)a.C, a.ldc);
+    return (int)hipGetLastError();
+  }
+  if (last_mx)
     hipLaunchKernelGGL(multiseg_kernel<true>, grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(multiseg_kernel<false>, grid, dim3(256), 0, stream, a);

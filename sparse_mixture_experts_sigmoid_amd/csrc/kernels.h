@@ -73,6 +73,20 @@ struct WOperand {
   int dtype;
 };
 
+// Split-K plan of a dense bf16 GEMM with few output rows: K is cut into
+// `splits` ranges of `kchunk` (the last may be shorter); each (tile, range)
+// block writes its fp32 partial tile to P[split][M][ncols], and a reduce kernel
+// sums the splits in ascending order and applies the epilogue. splits == 0:
+// the single-pass kernel (enough tiles to fill the chip; no partials).
+struct SplitK {
+  int splits = 0, kchunk = 0;
+  int64_t partial_bytes(int64_t M, int64_t ncols) const { return (int64_t)splits * M * ncols * 4; }
+};
+SplitK plan_split(int act_dtype, int M, int ncols, int K);
+// Partial slices of the output GEMM (one per segment) when it takes the split
+// path, else 0.
+int multiseg_slices(int act_dtype, int M, int N, int nseg);
+
 // C[M, N] = A[M, K] W[N, K]^T, store in the act dtype. (latent down)
 struct DenseArgs {
   const void* A; int64_t lda;  // act dtype
@@ -80,6 +94,8 @@ struct DenseArgs {
   int M, N, K;
   void* C; int64_t ldc;        // act dtype
   int act_dtype;
+  SplitK split;                // plan_split(act_dtype, M, N, K)
+  float* P;                    // split.partial_bytes(M, N) bytes when split.splits > 0
 };
 int launch_dense(const DenseArgs& a, hipStream_t stream);
 
@@ -91,6 +107,8 @@ struct GluArgs {
   void* H; int64_t ldh;
   float c;
   int act_dtype;
+  SplitK split;                // plan_split(act_dtype, M, 2 F, K)
+  float* P;                    // split.partial_bytes(M, 2 F) bytes when split.splits > 0
 };
 int launch_glu(const GluArgs& a, hipStream_t stream);
 
@@ -144,6 +162,7 @@ struct MultiSegArgs {
   int M, N;
   void* C; int64_t ldc;
   int act_dtype;
+  float* P;                    // multiseg_slices(...) * M * N fp32 when that is > 0
 };
 int launch_multiseg(const MultiSegArgs& a, hipStream_t stream);
 

@@ -89,6 +89,12 @@ def test_workspace_sizes():
     d2 = moe.make_desc(cfg, T=cfg.T // 2)
     assert moe.moe_workspace_bytes(d2, moe.MOE_OP_LAYER) < ws[moe.MOE_OP_LAYER]
     assert moe.moe_workspace_bytes(d, 99) == 0
+    # few tokens: the dense GEMMs split K and keep fp32 partials in the workspace
+    dec = synth.config("k3_decode")
+    dd = moe.make_desc(dec)
+    assert moe.moe_workspace_bytes(dd, moe.MOE_OP_LATENT_DOWN) >= 2 * dec.T * dec.d_lat * 4
+    hs = dec.T * dec.S * dec.Fs * 2
+    assert moe.moe_workspace_bytes(dd, moe.MOE_OP_OUTPUT) >= hs + 2 * dec.T * dec.d * 4
 
 
 FAKE = 0x7f0000001000          # a 16-byte-aligned address that is never dereferenced

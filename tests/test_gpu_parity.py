@@ -209,7 +209,7 @@ def test_staged_entry_points_equal_layer(device):
     inv = torch.empty(T * k, dtype=torch.int32, device=device)
     moe.moe_permute(desc, idx, counts, offsets, perm, inv, moe.workspace(desc, moe.MOE_OP_PERMUTE, device))
     z = torch.empty((T, cfg.d_lat), dtype=dt, device=device)
-    moe.moe_latent_down(desc, inp["x"], inp["W_ld"], z)
+    moe.moe_latent_down(desc, inp["x"], inp["W_ld"], z, moe.workspace(desc, moe.MOE_OP_LATENT_DOWN, device))
     o = torch.empty((T * k, cfg.d_lat), dtype=dt, device=device)
     moe.moe_expert_ffn(desc, z, perm, offsets, inp, o, moe.workspace(desc, moe.MOE_OP_EXPERT_FFN, device))
     n = torch.empty((T, cfg.d_lat), dtype=dt, device=device)
