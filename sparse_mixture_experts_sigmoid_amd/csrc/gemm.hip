@@ -16,57 +16,64 @@
 // Training") are decoded exactly to bf16 while they are staged into LDS, so
 // the MFMA itself stays bf16.
 //
-// Engine: 256 threads = 4 wave64 in a 2 x 2 grid; a wave owns WM x WN tiles of
-// v_mfma_f32_32x32x16_bf16 (fp32 accumulators), so the block tile is
-// (64 WM) x (64 WN) x 64. Dense GEMMs use 256 x 256 tiles (each wave 128 x 128:
-// LDS traffic per MFMA low enough for the matrix cores to be the limit);
-// grouped expert GEMMs use 128 x 256 (an expert's row count is rarely a
-// multiple of 256). bf16 operands go straight from global memory into LDS
-// (buffer_load ... lds, 16 bytes per lane, no register staging), into an
-// unpadded layout of 128-byte rows whose 16-byte chunk c of row r sits in slot
+// Engine: a block of WGM x WGN wave64s; each wave owns WM x WN tiles of
+// v_mfma_f32_32x32x16_bf16 (fp32 accumulators). Dense GEMMs: 256 x 128 blocks
+// of 4 waves (each 128 x 64). Grouped expert GEMMs: 128 x 256 blocks of 8
+// waves (each 64 x 64, two waves per SIMD), since an expert's row count is
+// rarely a multiple of 256; a wave whose rows are all padding skips its reads
+// and MFMAs. bf16 operands go straight from global memory into LDS
+// (buffer_load ... lds, 16 bytes per lane, no register staging) through a
+// ring of NS stages of 64-k tiles (NS - 1 tiles in flight), into an unpadded
+// layout of 128-byte rows whose 16-byte chunk c of row r sits in slot
 // c ^ ((r >> 1) & 7): the MFMA operand reads (16 consecutive rows, same chunk,
-// per LDS cycle) then hit distinct banks. MXFP4 weights are loaded to registers, decoded, and written
-// to the same layout. Double buffered: the next K-tile's loads are in flight
-// during this tile's MFMAs. Loads are raw buffer loads from per-block bases:
-// an offset past the buffer (rows past M, k past K, masked rows) returns
-// zeros, so no load sits behind a branch. Every weight row is K-contiguous
-// ([out, in] layout), so A and B tiles are both "rows x K" and stage the same
-// way.
+// per LDS cycle) then hit distinct banks. Per K-tile a wave reads all its
+// operand fragments into registers, then issues its MFMAs with the loads of a
+// later tile spread between them (a load can stall the wave's issue while the
+// address unit is busy; between MFMAs that time overlaps matrix work). MXFP4
+// weights are loaded to registers, decoded, and written to the same layout.
+// Loads are raw buffer loads from per-block bases: an offset past the buffer
+// (rows past M, k past K, masked rows) returns zeros, so no load sits behind a
+// branch. Every weight row is K-contiguous ([out, in] layout), so A and B
+// tiles are both "rows x K" and stage the same way.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int BK = 64;
-constexpr int LDK = BK;  // LDS row stride (bf16 elements): 128 bytes, swizzled chunks
-
-template <int WM_, int WN_, int NS_>
+// WGM x WGN waves (NT = 64 WGM WGN threads); a wave owns WM x WN tiles of
+// 32x32 MFMA, so the block tile is (32 WM WGM) x (32 WN WGN). K is staged BK
+// (32 or 64) at a time through an NS-stage LDS ring (NS - 1 K-tiles in flight).
+template <int WGM_, int WGN_, int WM_, int WN_, int BK_, int NS_>
 struct Cfg {
-  static constexpr int WM = WM_, WN = WN_, NS = NS_;
-  static constexpr int BM = 64 * WM, BN = 64 * WN;
-  static constexpr int AR = BM / 32;          // A: 8-row DMA loads per wave per stage
-  static constexpr int BR = BN / 32;          // B: 8-row DMA loads per wave per stage
-  static constexpr int MXU = BN / 128;        // MXFP4 (row, 32-k half) units per thread
-  static constexpr int STAGE = (BM + BN) * LDK;
-  static constexpr size_t LDS = NS * STAGE * sizeof(bf16_t);
+  static constexpr int WGM = WGM_, WGN = WGN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+  static constexpr int NW = WGM * WGN, NT = 64 * NW;
+  static constexpr int BM = 32 * WM * WGM, BN = 32 * WN * WGN;
+  static constexpr int CH = BK / 8;            // 16-byte chunks per LDS row
+  static constexpr int RPI = 64 / CH;          // tile rows per DMA instruction (1 KB)
+  static constexpr int AR = BM / (NW * RPI);   // A: DMA loads per wave per stage
+  static constexpr int BR = BN / (NW * RPI);   // B: DMA loads per wave per stage
+  static constexpr int UR = BK / 32;           // MXFP4 32-element blocks per row per stage
+  static constexpr int MXU = BN * UR / NT;     // MXFP4 (row, block) units per thread per stage
+  static constexpr int STAGE = (BM + BN) * BK;   // bf16 elements per LDS stage
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(AR >= 1 && BR >= 1 && MXU >= 1, "tile too small for the DMA pattern");
+  static_assert(AR * NW * RPI == BM && BR * NW * RPI == BN && MXU * NT == BN * UR, "DMA cover");
+  static_assert(NS >= 2 && NS <= 5, "ring depth");
 };
-using DenseCfg = Cfg<4, 2, 3>;   // 256 x 128, 3 LDS stages of 48 KB
-using GroupCfg = Cfg<2, 4, 3>;   // 128 x 256, 3 LDS stages of 48 KB
-
-// ---------------------------------------------------------------------------
-// buffer loads
-// ---------------------------------------------------------------------------
+using DenseCfg = Cfg<2, 2, 4, 2, 64, 3>;   // 256 x 128, 4 waves, 3 stages of 48 KB
+using GroupCfg = Cfg<2, 4, 2, 2, 64, 3>;   // 128 x 256, 8 waves, 3 stages of 48 KB
+using SplitCfg = Cfg<2, 2, 2, 2, 64, 3>;   // 128 x 128 (small batches, split K)
 
 // ---------------------------------------------------------------------------
 // operand staging
 // ---------------------------------------------------------------------------
 
-// bf16 rows by DMA: wave w fills tile rows w*8N .. w*8N + 8N-1, one 8-row
-// (1 KB) buffer_load ... lds per q < N; lane i of load q takes tile row
-// w*8N + 8q + i/8 and writes LDS slot i%8 of it, so it fetches global chunk
-// (i%8) ^ (i/8) of that row. Rows of one wave come through resource r[sel]
-// (gate or up weights of a GLU tile; sel is wave-uniform).
+// bf16 rows by DMA: wave w fills tile rows w*RPI*N .. + RPI*N - 1 with one
+// 1 KB buffer_load ... lds per q < N; lane i of load q takes tile row
+// w*RPI*N + RPI*q + i/CH and writes LDS slot i%CH of it. Rows of one wave come
+// through resource r[sel] (gate or up weights of a GLU tile; sel is
+// wave-uniform).
 template <int N>
 struct Rows {
   rsrc_t r[2];
@@ -76,36 +83,49 @@ struct Rows {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// LDS layout of a 128-byte tile row r: its 16-byte chunk c sits in slot
-// c ^ swz(r). 16 lanes of a b128 read (16 consecutive rows, one chunk) then
-// cover all 64 banks: rows r and r^1 differ in bank half, and swz takes 8
-// distinct values over the even (odd) rows of any aligned 16-row group.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// LDS layout of a tile row r (BK elements, CH chunks of 16 bytes): chunk c sits
+// in slot c ^ swz(r). The MFMA operand reads take 16 consecutive rows at one
+// chunk per LDS cycle; with the swizzle they cover all 64 banks.
+//   BK = 64 (128-byte rows): rows r and r^1 differ in bank half and (r>>1)&7
+//     takes 8 distinct values over the even (odd) rows of an aligned 16-row group.
+//   BK = 32 (64-byte rows): rows r, r+4, r+8, r+12 share banks and (r>>2)&3
+//     gives them 4 distinct slots.
+template <class C>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (C::BK == 64) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
 
-template <int N>
+// tile row of this lane's load q
+template <class C, int N>
+__device__ __forceinline__ int dma_row(int q) {
+  return (threadIdx.x >> 6) * C::RPI * N + C::RPI * q + (threadIdx.x & 63) / C::CH;
+}
+// (wave row, wave column) of this thread in the WGM x WGN wave grid
+template <class C>
+__device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) / C::WGN; }
+template <class C>
+__device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % C::WGN; }
+
+template <class C, int N>
 __device__ __forceinline__ void dma_rows(const Rows<N>& rs, bf16_t* tile, int k0, int K) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: LDS base in M0
   const rsrc_t r = rs.sel ? rs.r[1] : rs.r[0];
 #pragma unroll
   for (int q = 0; q < N; ++q) {
-    const int row0 = wv * 8 * N + 8 * q;
-    const int c = (lane & 7) ^ swz(row0 + (lane >> 3));  // global chunk for LDS slot lane % 8
+    const int row0 = wv * C::RPI * N + C::RPI * q;
+    const int c = (lane % C::CH) ^ swz<C>(row0 + lane / C::CH);  // global chunk for this slot
     const int k = k0 + c * 8;
     const uint32_t o = rs.off[q];
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(tile + row0 * LDK), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(tile + row0 * C::BK), 16,
                                              (k < K && o != kOOB) ? o + 2u * (uint32_t)k : kOOB,
                                              0, 0, 0);
   }
 }
 
-// tile row of this lane's load q
-template <int N>
-__device__ __forceinline__ int dma_row(int q) {
-  return (threadIdx.x >> 6) * 8 * N + 8 * q + ((threadIdx.x & 63) >> 3);
-}
-
-// MXFP4 rows: unit j of thread t is tile row (t >> 1) + 128 j, 32-k half (t & 1).
+// MXFP4 rows: unit j of thread t is tile row t / UR + (NT / UR) j and 32-element
+// block t % UR of the stage.
 template <int N>
 struct MxRows {
   rsrc_t rp[2], rs[2];   // packed bytes, e8m0 scales (gate / up for the GLU tile)
@@ -119,12 +139,16 @@ struct MxStage {
   uint32_t s;   // e8m0 scale byte
 };
 
-template <int N>
-__device__ __forceinline__ void load_mx(const MxRows<N>& m, int k0, int K, MxStage (&st)[N]) {
-  const int k = k0 + (threadIdx.x & 1) * 32;
+template <class C>
+__device__ __forceinline__ int mx_row(int j) { return threadIdx.x / C::UR + (C::NT / C::UR) * j; }
+
+template <class C>
+__device__ __forceinline__ void load_mx(const MxRows<C::MXU>& m, int k0, int K,
+                                        MxStage (&st)[C::MXU]) {
+  const int k = k0 + (threadIdx.x % C::UR) * 32;
   const bool kin = k < K;
 #pragma unroll
-  for (int j = 0; j < N; ++j) {
+  for (int j = 0; j < C::MXU; ++j) {
     const bool ok = kin && m.poff[j] != kOOB;
     const rsrc_t rp = m.sel[j] ? m.rp[1] : m.rp[0];
     const rsrc_t rsc = m.sel[j] ? m.rs[1] : m.rs[0];
@@ -145,12 +169,12 @@ __device__ __forceinline__ uint32_t scale_bf16(uint32_t b, float scale) {
   return __float_as_uint(__uint_as_float(b << 16) * scale) >> 16;
 }
 
-template <int N>
-__device__ __forceinline__ void store_mx(bf16_t* tile, const MxStage (&st)[N]) {
-  const int half = threadIdx.x & 1;
+template <class C>
+__device__ __forceinline__ void store_mx(bf16_t* tile, const MxStage (&st)[C::MXU]) {
+  const int part = threadIdx.x % C::UR;
 #pragma unroll
-  for (int j = 0; j < N; ++j) {
-    const int row = (threadIdx.x >> 1) + 128 * j;
+  for (int j = 0; j < C::MXU; ++j) {
+    const int row = mx_row<C>(j);
     // a zero-filled (out-of-range) block decodes to zeros whatever its scale byte
     const float scale = st[j].s == 0u ? 0x1p-127f : __uint_as_float(st[j].s << 23);
     const uint32_t q[4] = {st[j].q.x, st[j].q.y, st[j].q.z, st[j].q.w};
@@ -161,10 +185,10 @@ __device__ __forceinline__ void store_mx(bf16_t* tile, const MxStage (&st)[N]) {
       w[i] = scale_bf16(e2m1_bf16(byte & 0xFu), scale) |
              (scale_bf16(e2m1_bf16(byte >> 4), scale) << 16);
     }
-    bf16_t* dst = tile + row * LDK;
+    bf16_t* dst = tile + row * C::BK;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *(uint4*)(dst + 8 * ((half * 4 + i) ^ swz(row))) =
+      *(uint4*)(dst + 8 * ((part * 4 + i) ^ swz<C>(row))) =
           make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
   }
 }
@@ -188,50 +212,6 @@ __device__ __forceinline__ void acc_zero(Acc<C>& acc) {
       for (int r = 0; r < 16; ++r) acc.c[i][j][r] = 0.0f;
 }
 
-template <class C>
-__device__ __forceinline__ void load_frags(const bf16_t* Aw, const bf16_t* Bw, int ks, int slot_base,
-                                           bf16x8 (&a)[C::WM], bf16x8 (&b)[C::WN]) {
-  const int slot = 8 * ((2 * ks + (slot_base >> 3)) ^ (slot_base & 7));
-#pragma unroll
-  for (int i = 0; i < C::WM; ++i) a[i] = *(const bf16x8*)(Aw + i * 32 * LDK + slot);
-#pragma unroll
-  for (int j = 0; j < C::WN; ++j) b[j] = *(const bf16x8*)(Bw + j * 32 * LDK + slot);
-}
-
-// One 64-k LDS stage: 4 k-steps of WM x WN MFMAs. The operand reads of step
-// ks+1 are issued before the MFMAs of step ks (two fragment sets) and
-// interleaved with them, so LDS latency hides behind the matrix cores.
-template <class C>
-__device__ __forceinline__ void mma_stage(const bf16_t* As, const bf16_t* Bs, Acc<C>& acc) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, wm = wv >> 1, wn = wv & 1;
-  const int lr = lane & 31, lh = lane >> 5;
-  // row R = base + lr (base a multiple of 32): chunk kc sits in slot kc ^ swz(lr)
-  const bf16_t* Aw = As + (wm * (C::BM / 2) + lr) * LDK;
-  const bf16_t* Bw = Bs + (wn * (C::BN / 2) + lr) * LDK;
-  const int slot_base = (lh << 3) | swz(lr);
-  bf16x8 a[2][C::WM], b[2][C::WN];
-  load_frags<C>(Aw, Bw, 0, slot_base, a[0], b[0]);
-#pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    const int cur = ks & 1;
-    if (ks + 1 < BK / 16) load_frags<C>(Aw, Bw, ks + 1, slot_base, a[cur ^ 1], b[cur ^ 1]);
-#pragma unroll
-    for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::WN; ++j)
-        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][i], b[cur][j], acc.c[i][j], 0, 0, 0);
-    if (ks + 1 < BK / 16) {
-      // interleave: one LDS read after each of the first WM+WN MFMAs
-#pragma unroll
-      for (int q = 0; q < C::WM + C::WN; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, C::WM * C::WN - (C::WM + C::WN), 0);
-    }
-  }
-}
-
 // s_waitcnt with only the vector-memory counter limited to n.
 constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
@@ -246,13 +226,15 @@ __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Three LDS stages, each its own array: the compiler tracks DMA writes per
-// array, so reading stage J waits only for the loads that fill stage J.
-constexpr int kStageElems = 384 * LDK;   // (BM + BN) rows of both tile shapes
-#define MOE_LDS_RING                                                                  \
-  __shared__ __align__(16) bf16_t lds0[kStageElems];                                \
-  __shared__ __align__(16) bf16_t lds1[kStageElems];                                \
-  __shared__ __align__(16) bf16_t lds2[kStageElems]
+// The LDS ring: one static array per stage (the compiler tracks DMA writes per
+// array, so reading stage J waits only for the loads that fill stage J).
+#define MOE_LDS_RING(C)                                                   \
+  __shared__ __align__(16) bf16_t lds0[(C::NS > 0) ? C::STAGE : 1];    \
+  __shared__ __align__(16) bf16_t lds1[(C::NS > 1) ? C::STAGE : 1];    \
+  __shared__ __align__(16) bf16_t lds2[(C::NS > 2) ? C::STAGE : 1];    \
+  __shared__ __align__(16) bf16_t lds3[(C::NS > 3) ? C::STAGE : 1];    \
+  __shared__ __align__(16) bf16_t lds4[(C::NS > 4) ? C::STAGE : 1]
+#define MOE_RING lds0, lds1, lds2, lds3, lds4
 
 // Issue the loads of K-tile kt into stage buffer buf. Every load is
 // unconditional (past K it reads zeros), so each stage issues the same number.
@@ -262,62 +244,162 @@ __device__ __forceinline__ void stage_issue(bf16_t* buf, const Rows<C::AR>& ar, 
   if constexpr (B_MX) {
     // MXFP4 B: register loads first (the decode waits only for these), then A's DMA
     MxStage mx[C::MXU];
-    load_mx(bm, kt * BK, K, mx);
-    dma_rows(ar, buf, kt * BK, K);
-    store_mx(buf + C::BM * LDK, mx);
+    load_mx<C>(bm, kt * C::BK, K, mx);
+    dma_rows<C>(ar, buf, kt * C::BK, K);
+    store_mx<C>(buf + C::BM * C::BK, mx);
   } else {
-    dma_rows(ar, buf, kt * BK, K);
-    dma_rows(br, buf + C::BM * LDK, kt * BK, K);
+    dma_rows<C>(ar, buf, kt * C::BK, K);
+    dma_rows<C>(br, buf + C::BM * C::BK, kt * C::BK, K);
   }
 }
 
-// One K-tile: stage kt (in R) has landed once only the next stage's loads are
+// Operand fragments of a whole stage, in registers.
+template <class C>
+struct Frags {
+  bf16x8 a[C::BK / 16][C::WM], b[C::BK / 16][C::WN];
+};
+
+// NV: A fragments of this wave that hold rows of the problem (the others are
+// all padding: no reads, no MFMAs). NV = 0 reads nothing.
+template <class C, int NV>
+__device__ __forceinline__ void read_frags(const bf16_t* As, const bf16_t* Bs, Frags<C>& f) {
+  if constexpr (NV > 0) {
+    const int lane = threadIdx.x & 63, wm = wave_m<C>(), wn = wave_n<C>();
+    const int lr = lane & 31, lh = lane >> 5;
+    // fragment rows start at multiples of 32, so the swizzle of row base + lr is swz(lr)
+    const bf16_t* Aw = As + (wm * (C::BM / C::WGM) + lr) * C::BK;
+    const bf16_t* Bw = Bs + (wn * (C::BN / C::WGN) + lr) * C::BK;
+    const int sw = swz<C>(lr);
+#pragma unroll
+    for (int ks = 0; ks < C::BK / 16; ++ks) {
+      const int slot = 8 * ((2 * ks + lh) ^ sw);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) f.a[ks][i] = *(const bf16x8*)(Aw + i * 32 * C::BK + slot);
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j) f.b[ks][j] = *(const bf16x8*)(Bw + j * 32 * C::BK + slot);
+    }
+  }
+}
+
+template <class C, int NV>
+__device__ __forceinline__ void mma_frags(const Frags<C>& f, Acc<C>& acc) {
+#pragma unroll
+  for (int ks = 0; ks < C::BK / 16; ++ks)
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < C::WN; ++j)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[ks][i], f.b[ks][j], acc.c[i][j], 0, 0, 0);
+}
+
+// One K-tile: stage kt (in R) has landed once only the later stages' loads are
 // outstanding; after the barrier every wave is done with W (read one tile ago),
-// which receives K-tile kt + 2.
-template <class C, bool B_MX>
+// which receives K-tile kt + NS - 1. The wave issues its fragment reads first,
+// then the MFMAs with the next stage's loads spread between them: a load
+// instruction can hold the wave's issue for a long time when the address unit
+// is busy, and placed between MFMAs that time overlaps matrix work instead of
+// adding to it.
+template <class C, bool B_MX, int NV>
 __device__ __forceinline__ void ring_step(bf16_t* R, bf16_t* W, const Rows<C::AR>& ar,
                                           const Rows<C::BR>& br, const MxRows<C::MXU>& bm, int kt,
                                           int K, Acc<C>& acc) {
   constexpr int kLoads = B_MX ? C::AR : C::AR + C::BR;  // DMA loads per thread per stage
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads));
+  static_assert(kLoads * (C::NS - 2) < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads * (C::NS - 2)));
   wg_barrier();
-  stage_issue<C, B_MX>(W, ar, br, bm, kt + 2, K);
-  mma_stage<C>(R, R + C::BM * LDK, acc);
+  Frags<C> f;
+  // (NS = 2: the single buffer in flight is W itself, written after this barrier)
+  read_frags<C, NV>(R, R + C::BM * C::BK, f);
+  stage_issue<C, B_MX>(W, ar, br, bm, kt + C::NS - 1, K);
+  mma_frags<C, NV>(f, acc);
+  constexpr int kReads = NV > 0 ? C::BK / 16 * (NV + C::WN) : 0;
+  constexpr int kMfma = C::BK / 16 * NV * C::WN;
+  constexpr int kVmem = B_MX ? C::AR + 2 * C::MXU : C::AR + C::BR;
+  constexpr int kPer = kMfma / kVmem > 0 ? kMfma / kVmem : 1;  // MFMAs between two loads
+  if constexpr (kMfma == 0) return;
+  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);      // the stage's fragment reads
+#pragma unroll
+  for (int q = 0; q < kVmem; ++q) {
+    __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);      // kPer MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);         // one load
+  }
+  if constexpr (kMfma > kPer * kVmem)
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPer * kVmem, 0);
 }
 
-// acc += A_tile B_tile^T over k in [0, K) through the three-stage ring (two
-// K-tiles in flight). The K-tile count is rounded up to a multiple of 3; the
-// extra tiles read zeros. A rows: `ar` (bf16 DMA); B rows: `br` (bf16 DMA) or
-// `bm` (MXFP4, decoded through registers).
-template <class C, bool B_MX>
-__device__ __forceinline__ void mainloop(bf16_t* s0, bf16_t* s1, bf16_t* s2, const Rows<C::AR>& ar,
-                                         const Rows<C::BR>& br, const MxRows<C::MXU>& bm, int K,
-                                         Acc<C>& acc) {
-  static_assert((C::BM + C::BN) * LDK <= kStageElems, "stage size");
-  const int nk = (int)ceil_div(K, BK);
-  stage_issue<C, B_MX>(s0, ar, br, bm, 0, K);
-  stage_issue<C, B_MX>(s1, ar, br, bm, 1, K);
-  for (int kt = 0; kt < nk; kt += 3) {
-    ring_step<C, B_MX>(s0, s2, ar, br, bm, kt, K, acc);
-    ring_step<C, B_MX>(s1, s0, ar, br, bm, kt + 1, K, acc);
-    ring_step<C, B_MX>(s2, s1, ar, br, bm, kt + 2, K, acc);
+// acc += A_tile B_tile^T over k in [0, K) through the NS-stage ring. The
+// K-tile count is rounded up to a multiple of NS; the extra tiles read zeros.
+// A rows: `ar` (bf16 DMA); B rows: `br` (bf16 DMA) or `bm` (MXFP4, decoded
+// through registers).
+template <class C, bool B_MX, int NV = C::WM>
+__device__ __forceinline__ void mainloop(bf16_t* s0, bf16_t* s1, bf16_t* s2, bf16_t* s3, bf16_t* s4,
+                                         const Rows<C::AR>& ar, const Rows<C::BR>& br,
+                                         const MxRows<C::MXU>& bm, int K, Acc<C>& acc) {
+  {
+    const int nk = (int)ceil_div(K, C::BK);
+    stage_issue<C, B_MX>(s0, ar, br, bm, 0, K);
+    if constexpr (C::NS > 2) stage_issue<C, B_MX>(s1, ar, br, bm, 1, K);
+    if constexpr (C::NS > 3) stage_issue<C, B_MX>(s2, ar, br, bm, 2, K);
+    if constexpr (C::NS > 4) stage_issue<C, B_MX>(s3, ar, br, bm, 3, K);
+    for (int kt = 0; kt < nk; kt += C::NS) {
+      if constexpr (C::NS == 2) {
+        ring_step<C, B_MX, NV>(s0, s1, ar, br, bm, kt, K, acc);
+        ring_step<C, B_MX, NV>(s1, s0, ar, br, bm, kt + 1, K, acc);
+      } else if constexpr (C::NS == 3) {
+        ring_step<C, B_MX, NV>(s0, s2, ar, br, bm, kt, K, acc);
+        ring_step<C, B_MX, NV>(s1, s0, ar, br, bm, kt + 1, K, acc);
+        ring_step<C, B_MX, NV>(s2, s1, ar, br, bm, kt + 2, K, acc);
+      } else if constexpr (C::NS == 4) {
+        ring_step<C, B_MX, NV>(s0, s3, ar, br, bm, kt, K, acc);
+        ring_step<C, B_MX, NV>(s1, s0, ar, br, bm, kt + 1, K, acc);
+        ring_step<C, B_MX, NV>(s2, s1, ar, br, bm, kt + 2, K, acc);
+        ring_step<C, B_MX, NV>(s3, s2, ar, br, bm, kt + 3, K, acc);
+      } else {
+        ring_step<C, B_MX, NV>(s0, s4, ar, br, bm, kt, K, acc);
+        ring_step<C, B_MX, NV>(s1, s0, ar, br, bm, kt + 1, K, acc);
+        ring_step<C, B_MX, NV>(s2, s1, ar, br, bm, kt + 2, K, acc);
+        ring_step<C, B_MX, NV>(s3, s2, ar, br, bm, kt + 3, K, acc);
+        ring_step<C, B_MX, NV>(s4, s3, ar, br, bm, kt + 4, K, acc);
+      }
+    }
+    // drain the trailing (zero) loads before the buffers are reused
+    __builtin_amdgcn_s_waitcnt(0);
+    wg_barrier();
   }
-  // drain the trailing (zero) loads before the buffers are reused
-  __builtin_amdgcn_s_waitcnt(0);
-  wg_barrier();
+}
+
+// mainloop for a tile whose rows at or past `valid_rows` are padding: each wave
+// runs only the A fragments that hold real rows (wave-uniform choice).
+template <class C, bool B_MX>
+__device__ __forceinline__ void mainloop_rows(bf16_t* s0, bf16_t* s1, bf16_t* s2, bf16_t* s3, bf16_t* s4,
+                                              const Rows<C::AR>& ar, const Rows<C::BR>& br,
+                                              const MxRows<C::MXU>& bm, int K, int valid_rows,
+                                              Acc<C>& acc) {
+  static_assert(C::WM <= 4, "fragment dispatch");
+  const int first = wave_m<C>() * (C::BM / C::WGM);
+  const int nv = __builtin_amdgcn_readfirstlane(max(0, min(C::WM, (valid_rows - first + 31) / 32)));
+  if (nv >= C::WM) mainloop<C, B_MX, C::WM>(s0, s1, s2, s3, s4, ar, br, bm, K, acc);
+  else if (nv == 0) mainloop<C, B_MX, 0>(s0, s1, s2, s3, s4, ar, br, bm, K, acc);
+  else if constexpr (C::WM > 1) {
+    if (nv == 1) mainloop<C, B_MX, 1>(s0, s1, s2, s3, s4, ar, br, bm, K, acc);
+    else if constexpr (C::WM > 2) {
+      if (nv == 2) mainloop<C, B_MX, 2>(s0, s1, s2, s3, s4, ar, br, bm, K, acc);
+      else if constexpr (C::WM > 3) mainloop<C, B_MX, 3>(s0, s1, s2, s3, s4, ar, br, bm, K, acc);
+    }
+  }
 }
 
 // Element (i, j, r) of this lane's accumulators sits at tile row / column
-//   row = wm*BM/2 + i*32 + 8*(r/4) + 4*(lane/32) + r%4,  col = wn*BN/2 + j*32 + lane%32.
+//   row = wm*BM/WGM + i*32 + 8*(r/4) + 4*(lane/32) + r%4,  col = wn*BN/WGN + j*32 + lane%32.
 template <class C>
 __device__ __forceinline__ int acc_row(int i, int r) {
-  const int lane = threadIdx.x & 63, wm = threadIdx.x >> 7;
-  return wm * (C::BM / 2) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  const int lane = threadIdx.x & 63;
+  return wave_m<C>() * (C::BM / C::WGM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 template <class C>
 __device__ __forceinline__ int acc_col(int j) {
-  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
-  return wn * (C::BN / 2) + j * 32 + (lane & 31);
+  const int lane = threadIdx.x & 63;
+  return wave_n<C>() * (C::BN / C::WGN) + j * 32 + (lane & 31);
 }
 
 // ---------------------------------------------------------------------------
@@ -325,37 +407,37 @@ __device__ __forceinline__ int acc_col(int j) {
 // ---------------------------------------------------------------------------
 
 // A rows m0 + tile_row of a row-major [M, lda] bf16 matrix (rows >= M read zeros).
-template <int N>
+template <class C, int N>
 __device__ __forceinline__ Rows<N> a_rows_dense(const void* A, int64_t lda, int m0, int M) {
   Rows<N> rs;
-  const int nrows = max(0, min(M - m0, 32 * N));
+  const int nrows = max(0, min(M - m0, C::NW * C::RPI * N));
   rs.r[0] = rs.r[1] = make_rsrc((const bf16_t*)A + (int64_t)m0 * lda, (int64_t)nrows * lda * 2);
   rs.sel = 0;
 #pragma unroll
   for (int q = 0; q < N; ++q) {
-    const int r = dma_row<N>(q);
+    const int r = dma_row<C, N>(q);
     rs.off[q] = r < nrows ? (uint32_t)((int64_t)r * lda * 2) : kOOB;
   }
   return rs;
 }
 
 // B rows n0 + tile_row of a [N, K] bf16 matrix.
-template <int NR>
-__device__ __forceinline__ Rows<NR> b_rows_plain(const void* W, int K, int n0, int N) {
-  return a_rows_dense<NR>(W, K, n0, N);
+template <class C>
+__device__ __forceinline__ Rows<C::BR> b_rows_plain(const void* W, int K, int n0, int N) {
+  return a_rows_dense<C, C::BR>(W, K, n0, N);
 }
 
-template <int NU>
-__device__ __forceinline__ MxRows<NU> b_mx_plain(const WOperand& w, int64_t row_base, int K, int n0,
-                                                 int N) {
-  MxRows<NU> m;
-  const int nrows = max(0, min(N - n0, 128 * NU));
+template <class C>
+__device__ __forceinline__ MxRows<C::MXU> b_mx_plain(const WOperand& w, int64_t row_base, int K, int n0,
+                                                     int N) {
+  MxRows<C::MXU> m;
+  const int nrows = max(0, min(N - n0, C::BN));
   const int64_t r0 = row_base + n0;
   m.rp[0] = m.rp[1] = make_rsrc((const uint8_t*)w.data + r0 * (K / 2), (int64_t)nrows * (K / 2));
   m.rs[0] = m.rs[1] = make_rsrc(w.scale + r0 * (K / 32), (int64_t)nrows * (K / 32));
 #pragma unroll
-  for (int j = 0; j < NU; ++j) {
-    const int row = (threadIdx.x >> 1) + 128 * j;
+  for (int j = 0; j < C::MXU; ++j) {
+    const int row = mx_row<C>(j);
     m.sel[j] = 0;
     m.poff[j] = row < nrows ? (uint32_t)(row * (K / 2)) : kOOB;
     m.soff[j] = row < nrows ? (uint32_t)(row * (K / 32)) : kOOB;
@@ -363,24 +445,30 @@ __device__ __forceinline__ MxRows<NU> b_mx_plain(const WOperand& w, int64_t row_
   return m;
 }
 
-// GLU B tile: wave column wn covers tile rows wn*BN/2 .. +BN/2: first the gate
-// rows f0 + wn*BN/4 + (0 .. BN/4-1) of Wg, then the same rows of Wv. The block
-// produces BN/2 outputs f0 .. f0 + BN/2 - 1.
-// Wave w fills tile rows w*BN/4 .. +BN/4, i.e. the gate half (w even) or the
-// up half (w odd) of wave column w/2.
+// GLU B tile: wave column wn covers tile rows wn*BN/WGN .. + BN/WGN: first the
+// gate rows f0 + wn*H + (0 .. H-1) of Wg, then the same rows of Wv, with
+// H = BN/(2 WGN). The block produces BN/2 outputs f0 .. f0 + BN/2 - 1. Wave w
+// DMAs tile rows w*BN/NW .. + BN/NW, which lie inside one gate or up half
+// (WGM even), so its resource choice is wave-uniform.
+template <class C>
+__device__ __forceinline__ int glu_half_rows() { return C::BN / (2 * C::WGN); }
+
 template <class C>
 __device__ __forceinline__ Rows<C::BR> b_rows_glu(const WOperand& g, const WOperand& v,
                                                   int64_t row_base, int K, int f0, int F) {
-  static_assert(8 * C::BR == C::BN / 4, "one DMA wave per gate / up half");
+  static_assert(C::WGM % 2 == 0, "each wave's B rows must be all gate or all up");
+  constexpr int H = C::BN / (2 * C::WGN);
   Rows<C::BR> rs;
   const int nf = max(0, min(F - f0, C::BN / 2));  // valid outputs of this block
   rs.r[0] = make_rsrc((const bf16_t*)g.data + (row_base + f0) * K, (int64_t)nf * K * 2);
   rs.r[1] = make_rsrc((const bf16_t*)v.data + (row_base + f0) * K, (int64_t)nf * K * 2);
   const int wv = threadIdx.x >> 6;
-  rs.sel = __builtin_amdgcn_readfirstlane(wv & 1);
+  const int tr0 = wv * (C::BN / C::NW);                      // this wave's first tile row
+  rs.sel = __builtin_amdgcn_readfirstlane((tr0 % (2 * H)) >= H ? 1 : 0);
 #pragma unroll
   for (int q = 0; q < C::BR; ++q) {
-    const int fl = (wv >> 1) * (C::BN / 4) + 8 * q + ((threadIdx.x & 63) >> 3);
+    const int tr = tr0 + C::RPI * q + (threadIdx.x & 63) / C::CH;
+    const int fl = (tr / (2 * H)) * H + (tr % H);
     rs.off[q] = fl < nf ? (uint32_t)((int64_t)fl * K * 2) : kOOB;
   }
   return rs;
@@ -389,6 +477,9 @@ __device__ __forceinline__ Rows<C::BR> b_rows_glu(const WOperand& g, const WOper
 template <class C>
 __device__ __forceinline__ MxRows<C::MXU> b_mx_glu(const WOperand& g, const WOperand& v,
                                                    int64_t row_base, int K, int f0, int F) {
+  constexpr int H = C::BN / (2 * C::WGN);
+  // a wave's units cover 64 / UR consecutive tile rows: all gate or all up
+  static_assert(H % (64 / C::UR) == 0, "gate/up split must be wave-uniform");
   MxRows<C::MXU> m;
   const int nf = max(0, min(F - f0, C::BN / 2));
   m.rp[0] = make_rsrc((const uint8_t*)g.data + (row_base + f0) * (K / 2), (int64_t)nf * (K / 2));
@@ -397,11 +488,9 @@ __device__ __forceinline__ MxRows<C::MXU> b_mx_glu(const WOperand& g, const WOpe
   m.rs[1] = make_rsrc(v.scale + (row_base + f0) * (K / 32), (int64_t)nf * (K / 32));
 #pragma unroll
   for (int j = 0; j < C::MXU; ++j) {
-    const int row = (threadIdx.x >> 1) + 128 * j;          // tile row
-    const int wn = row / (C::BN / 2), w = row % (C::BN / 2);
-    // up-ness depends on bits of threadIdx that are uniform across the wave
-    m.sel[j] = __builtin_amdgcn_readfirstlane(w >= C::BN / 4 ? 1 : 0);
-    const int fl = wn * (C::BN / 4) + (w % (C::BN / 4));
+    const int tr = mx_row<C>(j);                            // tile row
+    m.sel[j] = __builtin_amdgcn_readfirstlane((tr % (2 * H)) >= H ? 1 : 0);
+    const int fl = (tr / (2 * H)) * H + (tr % H);
     m.poff[j] = fl < nf ? (uint32_t)(fl * (K / 2)) : kOOB;
     m.soff[j] = fl < nf ? (uint32_t)(fl * (K / 32)) : kOOB;
   }
@@ -433,11 +522,11 @@ __device__ __forceinline__ void store_tile(const Acc<C>& acc, bf16_t* Cm, int64_
 template <class C, typename RowMap>
 __device__ __forceinline__ void store_glu(const Acc<C>& acc, bf16_t* H, int64_t ldh, int f0, int F,
                                           float c, RowMap out_row) {
-  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+  const int lane = threadIdx.x & 63, wn = wave_n<C>();
   const float inv_c = 1.0f / c;
 #pragma unroll
   for (int j = 0; j < C::WN / 2; ++j) {
-    const int f = f0 + wn * (C::BN / 4) + j * 32 + (lane & 31);
+    const int f = f0 + wn * glu_half_rows<C>() + j * 32 + (lane & 31);
     if (f >= F) continue;
 #pragma unroll
     for (int i = 0; i < C::WM; ++i)
@@ -474,40 +563,40 @@ __device__ __forceinline__ bool xcd_item(int64_t live, int64_t& L) {
 // ---------------------------------------------------------------------------
 
 template <bool B_MX>
-__global__ __launch_bounds__(256) void dense_kernel(DenseArgs a) {
+__global__ __launch_bounds__(DenseCfg::NT) void dense_kernel(DenseArgs a) {
   using C = DenseCfg;
-  MOE_LDS_RING;
+  MOE_LDS_RING(C);
   const int ntn = (int)ceil_div(a.N, C::BN);
   int64_t L;
   if (!xcd_item(ceil_div(a.M, C::BM) * ntn, L)) return;
   const int m0 = (int)(L / ntn) * C::BM, n0 = (int)(L % ntn) * C::BN;
-  const Rows<C::AR> ar = a_rows_dense<C::AR>(a.A, a.lda, m0, a.M);
-  Rows<C::BR> br{};
-  MxRows<C::MXU> bm{};
-  if constexpr (B_MX) bm = b_mx_plain<C::MXU>(a.W, 0, a.K, n0, a.N);
-  else br = b_rows_plain<C::BR>(a.W.data, a.K, n0, a.N);
+  const Rows<C::AR> ar = a_rows_dense<C, C::AR>(a.A, a.lda, m0, a.M);
   Acc<C> acc;
   acc_zero(acc);
-  mainloop<C, B_MX>(lds0, lds1, lds2, ar, br, bm, a.K, acc);
+  Rows<C::BR> br{};
+  MxRows<C::MXU> bm{};
+  if constexpr (B_MX) bm = b_mx_plain<C>(a.W, 0, a.K, n0, a.N);
+  else br = b_rows_plain<C>(a.W.data, a.K, n0, a.N);
+  mainloop<C, B_MX>(MOE_RING, ar, br, bm, a.K, acc);
   store_tile(acc, (bf16_t*)a.C, a.ldc, m0, n0, a.M, a.N);
 }
 
 template <bool B_MX>
-__global__ __launch_bounds__(256) void glu_kernel(GluArgs a) {
+__global__ __launch_bounds__(DenseCfg::NT) void glu_kernel(GluArgs a) {
   using C = DenseCfg;
-  MOE_LDS_RING;
+  MOE_LDS_RING(C);
   const int ntn = (int)ceil_div(a.F, C::BN / 2);
   int64_t L;
   if (!xcd_item(ceil_div(a.M, C::BM) * ntn, L)) return;
   const int m0 = (int)(L / ntn) * C::BM, f0 = (int)(L % ntn) * (C::BN / 2);
-  const Rows<C::AR> ar = a_rows_dense<C::AR>(a.A, a.lda, m0, a.M);
+  const Rows<C::AR> ar = a_rows_dense<C, C::AR>(a.A, a.lda, m0, a.M);
+  Acc<C> acc;
+  acc_zero(acc);
   Rows<C::BR> br{};
   MxRows<C::MXU> bm{};
   if constexpr (B_MX) bm = b_mx_glu<C>(a.Wg, a.Wv, 0, a.K, f0, a.F);
   else br = b_rows_glu<C>(a.Wg, a.Wv, 0, a.K, f0, a.F);
-  Acc<C> acc;
-  acc_zero(acc);
-  mainloop<C, B_MX>(lds0, lds1, lds2, ar, br, bm, a.K, acc);
+  mainloop<C, B_MX>(MOE_RING, ar, br, bm, a.K, acc);
   const int M = a.M;
   store_glu(acc, (bf16_t*)a.H, a.ldh, f0, a.F, a.c,
             [=](int tr) -> int64_t { return m0 + tr < M ? (int64_t)(m0 + tr) : -1; });
@@ -555,9 +644,9 @@ __device__ __forceinline__ void grouped_order(const int32_t* tile_off, int E, in
 }
 
 template <bool B_MX>
-__global__ __launch_bounds__(256) void grouped_glu_kernel(GroupedGluArgs a) {
+__global__ __launch_bounds__(GroupCfg::NT) void grouped_glu_kernel(GroupedGluArgs a) {
   using C = GroupCfg;
-  MOE_LDS_RING;
+  MOE_LDS_RING(C);
   const int ntn = (int)ceil_div(a.F, C::BN / 2);
   int64_t L;
   if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, L)) return;
@@ -572,7 +661,7 @@ __global__ __launch_bounds__(256) void grouped_glu_kernel(GroupedGluArgs a) {
   ar.sel = 0;
 #pragma unroll
   for (int q = 0; q < C::AR; ++q) {
-    const int row = row_lo + dma_row<C::AR>(q);
+    const int row = row_lo + dma_row<C, C::AR>(q);
     uint32_t off = kOOB;
     if (row >= 0 && row < row_hi) {
       const int src = a.perm_src[row];
@@ -581,14 +670,14 @@ __global__ __launch_bounds__(256) void grouped_glu_kernel(GroupedGluArgs a) {
     }
     ar.off[q] = off;
   }
-  Rows<C::BR> br{};
-  MxRows<C::MXU> bm{};
   const int64_t wrow = (int64_t)e * a.F;
-  if constexpr (B_MX) bm = b_mx_glu<C>(a.Wg, a.Wv, wrow, a.K, f0, a.F);
-  else br = b_rows_glu<C>(a.Wg, a.Wv, wrow, a.K, f0, a.F);
   Acc<C> acc;
   acc_zero(acc);
-  mainloop<C, B_MX>(lds0, lds1, lds2, ar, br, bm, a.K, acc);
+  Rows<C::BR> br{};
+  MxRows<C::MXU> bm{};
+  if constexpr (B_MX) bm = b_mx_glu<C>(a.Wg, a.Wv, wrow, a.K, f0, a.F);
+  else br = b_rows_glu<C>(a.Wg, a.Wv, wrow, a.K, f0, a.F);
+  mainloop_rows<C, B_MX>(MOE_RING, ar, br, bm, a.K, row_hi - row_lo, acc);
   store_glu(acc, (bf16_t*)a.H, a.F, f0, a.F, a.c, [=](int tr) -> int64_t {
     const int r = row_lo + tr;
     return (r >= 0 && r < row_hi) ? (int64_t)r : -1;
@@ -596,9 +685,9 @@ __global__ __launch_bounds__(256) void grouped_glu_kernel(GroupedGluArgs a) {
 }
 
 template <bool B_MX>
-__global__ __launch_bounds__(256) void grouped_down_kernel(GroupedDownArgs a) {
+__global__ __launch_bounds__(GroupCfg::NT) void grouped_down_kernel(GroupedDownArgs a) {
   using C = GroupCfg;
-  MOE_LDS_RING;
+  MOE_LDS_RING(C);
   const int ntn = (int)ceil_div(a.N, C::BN);
   int64_t L;
   if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, L)) return;
@@ -607,24 +696,24 @@ __global__ __launch_bounds__(256) void grouped_down_kernel(GroupedDownArgs a) {
   int e, row_lo, row_hi;
   if (!tile_rows<C::BM>(a.tile_off, a.offsets, a.E, a.rows_cap, tile, e, row_lo, row_hi)) return;
   const int n0 = nt * C::BN;
-  const Rows<C::AR> ar = a_rows_dense<C::AR>(a.H, a.ldh, max(row_lo, 0), max(row_hi, 0));
-  Rows<C::BR> br{};
-  MxRows<C::MXU> bm{};
+  const Rows<C::AR> ar = a_rows_dense<C, C::AR>(a.H, a.ldh, max(row_lo, 0), max(row_hi, 0));
   const int64_t wrow = (int64_t)e * a.N;
-  if constexpr (B_MX) bm = b_mx_plain<C::MXU>(a.Wo, wrow, a.K, n0, a.N);
-  else br = b_rows_plain<C::BR>((const bf16_t*)a.Wo.data + wrow * a.K, a.K, n0, a.N);
   Acc<C> acc;
   acc_zero(acc);
-  mainloop<C, B_MX>(lds0, lds1, lds2, ar, br, bm, a.K, acc);
+  Rows<C::BR> br{};
+  MxRows<C::MXU> bm{};
+  if constexpr (B_MX) bm = b_mx_plain<C>(a.Wo, wrow, a.K, n0, a.N);
+  else br = b_rows_plain<C>((const bf16_t*)a.Wo.data + wrow * a.K, a.K, n0, a.N);
+  mainloop_rows<C, B_MX>(MOE_RING, ar, br, bm, a.K, row_hi - row_lo, acc);
   store_tile(acc, (bf16_t*)a.O, a.N, row_lo, n0, row_hi, a.N);
 }
 
 // Segments are visited in order; every B is bf16 except, when LAST_MX, the last
 // one (W_up in MXFP4).
 template <bool LAST_MX>
-__global__ __launch_bounds__(256) void multiseg_kernel(MultiSegArgs a) {
+__global__ __launch_bounds__(DenseCfg::NT) void multiseg_kernel(MultiSegArgs a) {
   using C = DenseCfg;
-  MOE_LDS_RING;
+  MOE_LDS_RING(C);
   const int ntn = (int)ceil_div(a.N, C::BN);
   int64_t L;
   if (!xcd_item(ceil_div(a.M, C::BM) * ntn, L)) return;
@@ -634,15 +723,15 @@ __global__ __launch_bounds__(256) void multiseg_kernel(MultiSegArgs a) {
   const int nplain = LAST_MX ? a.nseg - 1 : a.nseg;
   for (int s = 0; s < nplain; ++s) {
     const Segment& sg = a.seg[s];
-    const Rows<C::AR> ar = a_rows_dense<C::AR>(sg.A, sg.lda, m0, a.M);
-    const Rows<C::BR> br = b_rows_plain<C::BR>(sg.B.data, sg.K, n0, a.N);
-    mainloop<C, false>(lds0, lds1, lds2, ar, br, MxRows<C::MXU>{}, sg.K, acc);
+    const Rows<C::AR> ar = a_rows_dense<C, C::AR>(sg.A, sg.lda, m0, a.M);
+    const Rows<C::BR> br = b_rows_plain<C>(sg.B.data, sg.K, n0, a.N);
+    mainloop<C, false>(MOE_RING, ar, br, MxRows<C::MXU>{}, sg.K, acc);
   }
   if constexpr (LAST_MX) {
     const Segment& sg = a.seg[a.nseg - 1];
-    const Rows<C::AR> ar = a_rows_dense<C::AR>(sg.A, sg.lda, m0, a.M);
-    const MxRows<C::MXU> bm = b_mx_plain<C::MXU>(sg.B, 0, sg.K, n0, a.N);
-    mainloop<C, true>(lds0, lds1, lds2, ar, Rows<C::BR>{}, bm, sg.K, acc);
+    const Rows<C::AR> ar = a_rows_dense<C, C::AR>(sg.A, sg.lda, m0, a.M);
+    const MxRows<C::MXU> bm = b_mx_plain<C>(sg.B, 0, sg.K, n0, a.N);
+    mainloop<C, true>(MOE_RING, ar, Rows<C::BR>{}, bm, sg.K, acc);
   }
   store_tile(acc, (bf16_t*)a.C, a.ldc, m0, n0, a.M, a.N);
 }
@@ -651,7 +740,6 @@ __global__ __launch_bounds__(256) void multiseg_kernel(MultiSegArgs a) {
 // split-K path (few output rows: too few tiles to fill 256 CUs)
 // ---------------------------------------------------------------------------
 
-using SplitCfg = Cfg<2, 2, 3>;   // 128 x 128
 
 template <class C>
 __device__ __forceinline__ void store_partial(const Acc<C>& acc, float* P, int64_t ldp, int m0, int n0,
@@ -674,10 +762,10 @@ __device__ __forceinline__ void store_partial(const Acc<C>& acc, float* P, int64
 template <class C>
 __device__ __forceinline__ void store_partial_glu(const Acc<C>& acc, float* P, int F, int f0, int m0,
                                                   int M) {
-  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+  const int lane = threadIdx.x & 63, wn = wave_n<C>();
 #pragma unroll
   for (int j = 0; j < C::WN / 2; ++j) {
-    const int f = f0 + wn * (C::BN / 4) + j * 32 + (lane & 31);
+    const int f = f0 + wn * glu_half_rows<C>() + j * 32 + (lane & 31);
     if (f >= F) continue;
 #pragma unroll
     for (int i = 0; i < C::WM; ++i)
@@ -709,9 +797,9 @@ __device__ __forceinline__ WOperand shift_k(const WOperand& w, int kb) {
 }
 
 template <bool B_MX>
-__global__ __launch_bounds__(256) void dense_split_kernel(DenseArgs a) {
+__global__ __launch_bounds__(SplitCfg::NT) void dense_split_kernel(DenseArgs a) {
   using C = SplitCfg;
-  MOE_LDS_RING;
+  MOE_LDS_RING(C);
   const int ntn = (int)ceil_div(a.N, C::BN);
   const int64_t tiles = ceil_div(a.M, C::BM) * ntn;
   int64_t L;
@@ -720,21 +808,21 @@ __global__ __launch_bounds__(256) void dense_split_kernel(DenseArgs a) {
   split_item(L, tiles, ntn, sp, m0, n0, C::BM, C::BN);
   const int kb = sp * a.split.kchunk, klen = min(a.K - kb, a.split.kchunk);
   const WOperand W = shift_k(a.W, kb);
-  const Rows<C::AR> ar = a_rows_dense<C::AR>((const bf16_t*)a.A + kb, a.lda, m0, a.M);
+  const Rows<C::AR> ar = a_rows_dense<C, C::AR>((const bf16_t*)a.A + kb, a.lda, m0, a.M);
   Rows<C::BR> br{};
   MxRows<C::MXU> bm{};
-  if constexpr (B_MX) bm = b_mx_plain<C::MXU>(W, 0, a.K, n0, a.N);
-  else br = b_rows_plain<C::BR>(W.data, a.K, n0, a.N);
+  if constexpr (B_MX) bm = b_mx_plain<C>(W, 0, a.K, n0, a.N);
+  else br = b_rows_plain<C>(W.data, a.K, n0, a.N);
   Acc<C> acc;
   acc_zero(acc);
-  mainloop<C, B_MX>(lds0, lds1, lds2, ar, br, bm, klen, acc);
+  mainloop<C, B_MX>(MOE_RING, ar, br, bm, klen, acc);
   store_partial(acc, a.P + (int64_t)sp * a.M * a.N, a.N, m0, n0, a.M, a.N);
 }
 
 template <bool B_MX>
-__global__ __launch_bounds__(256) void glu_split_kernel(GluArgs a) {
+__global__ __launch_bounds__(SplitCfg::NT) void glu_split_kernel(GluArgs a) {
   using C = SplitCfg;
-  MOE_LDS_RING;
+  MOE_LDS_RING(C);
   const int ntn = (int)ceil_div(a.F, C::BN / 2);
   const int64_t tiles = ceil_div(a.M, C::BM) * ntn;
   int64_t L;
@@ -743,22 +831,22 @@ __global__ __launch_bounds__(256) void glu_split_kernel(GluArgs a) {
   split_item(L, tiles, ntn, sp, m0, f0, C::BM, C::BN / 2);
   const int kb = sp * a.split.kchunk, klen = min(a.K - kb, a.split.kchunk);
   const WOperand Wg = shift_k(a.Wg, kb), Wv = shift_k(a.Wv, kb);
-  const Rows<C::AR> ar = a_rows_dense<C::AR>((const bf16_t*)a.A + kb, a.lda, m0, a.M);
+  const Rows<C::AR> ar = a_rows_dense<C, C::AR>((const bf16_t*)a.A + kb, a.lda, m0, a.M);
   Rows<C::BR> br{};
   MxRows<C::MXU> bm{};
   if constexpr (B_MX) bm = b_mx_glu<C>(Wg, Wv, 0, a.K, f0, a.F);
   else br = b_rows_glu<C>(Wg, Wv, 0, a.K, f0, a.F);
   Acc<C> acc;
   acc_zero(acc);
-  mainloop<C, B_MX>(lds0, lds1, lds2, ar, br, bm, klen, acc);
+  mainloop<C, B_MX>(MOE_RING, ar, br, bm, klen, acc);
   store_partial_glu(acc, a.P + (int64_t)sp * a.M * 2 * a.F, a.F, f0, m0, a.M);
 }
 
 // One work item per (segment, tile); segment s writes partial slice s.
 template <bool LAST_MX>
-__global__ __launch_bounds__(256) void multiseg_split_kernel(MultiSegArgs a) {
+__global__ __launch_bounds__(SplitCfg::NT) void multiseg_split_kernel(MultiSegArgs a) {
   using C = SplitCfg;
-  MOE_LDS_RING;
+  MOE_LDS_RING(C);
   const int ntn = (int)ceil_div(a.N, C::BN);
   const int64_t tiles = ceil_div(a.M, C::BM) * ntn;
   int64_t L;
@@ -766,15 +854,15 @@ __global__ __launch_bounds__(256) void multiseg_split_kernel(MultiSegArgs a) {
   int s, m0, n0;
   split_item(L, tiles, ntn, s, m0, n0, C::BM, C::BN);
   const Segment& sg = a.seg[s];
-  const Rows<C::AR> ar = a_rows_dense<C::AR>(sg.A, sg.lda, m0, a.M);
+  const Rows<C::AR> ar = a_rows_dense<C, C::AR>(sg.A, sg.lda, m0, a.M);
   Acc<C> acc;
   acc_zero(acc);
   if (LAST_MX && s == a.nseg - 1) {
-    const MxRows<C::MXU> bm = b_mx_plain<C::MXU>(sg.B, 0, sg.K, n0, a.N);
-    mainloop<C, true>(lds0, lds1, lds2, ar, Rows<C::BR>{}, bm, sg.K, acc);
+    const MxRows<C::MXU> bm = b_mx_plain<C>(sg.B, 0, sg.K, n0, a.N);
+    mainloop<C, true>(MOE_RING, ar, Rows<C::BR>{}, bm, sg.K, acc);
   } else {
-    const Rows<C::BR> br = b_rows_plain<C::BR>(sg.B.data, sg.K, n0, a.N);
-    mainloop<C, false>(lds0, lds1, lds2, ar, br, MxRows<C::MXU>{}, sg.K, acc);
+    const Rows<C::BR> br = b_rows_plain<C>(sg.B.data, sg.K, n0, a.N);
+    mainloop<C, false>(MOE_RING, ar, br, MxRows<C::MXU>{}, sg.K, acc);
   }
   store_partial(acc, a.P + (int64_t)s * a.M * a.N, a.N, m0, n0, a.M, a.N);
 }
@@ -828,26 +916,26 @@ int reduce_blocks(int64_t n4) { return (int)(ceil_div(n4, 256) < 2048 ? ceil_div
 // 128 x 128 tiles of x W_r^T, K split over `splits` blocks whose fp32 partial
 // sums are added atomically (their order does not matter: the logits only
 // bound the fixed-order ones).
-using LogitCfg = Cfg<2, 2, 3>;
+using LogitCfg = Cfg<2, 2, 2, 2, 64, 3>;
 
-__global__ __launch_bounds__(256) void logits_kernel(LogitsArgs a) {
+__global__ __launch_bounds__(LogitCfg::NT) void logits_kernel(LogitsArgs a) {
   using C = LogitCfg;
-  MOE_LDS_RING;
+  MOE_LDS_RING(C);
   const int ntn = (int)ceil_div(a.E, C::BN), ntm = (int)ceil_div(a.T, C::BM);
   int64_t L;
   if (!xcd_item((int64_t)ntm * ntn * a.splits, L)) return;
   const int sp = (int)(L % a.splits);
   const int64_t rest = L / a.splits;
   const int m0 = (int)(rest / ntn) * C::BM, n0 = (int)(rest % ntn) * C::BN;
-  const int kchunk = (int)ceil_div(ceil_div(a.d, a.splits), BK) * BK;
+  const int kchunk = (int)ceil_div(ceil_div(a.d, a.splits), LogitCfg::BK) * LogitCfg::BK;
   const int k0 = sp * kchunk;
   const int klen = min(a.d - k0, kchunk);
   if (klen <= 0) return;
-  const Rows<C::AR> ar = a_rows_dense<C::AR>((const bf16_t*)a.x + k0, a.d, m0, a.T);
-  const Rows<C::BR> br = a_rows_dense<C::BR>((const bf16_t*)a.W + k0, a.d, n0, a.E);
+  const Rows<C::AR> ar = a_rows_dense<C, C::AR>((const bf16_t*)a.x + k0, a.d, m0, a.T);
+  const Rows<C::BR> br = a_rows_dense<C, C::BR>((const bf16_t*)a.W + k0, a.d, n0, a.E);
   Acc<C> acc;
   acc_zero(acc);
-  mainloop<C, false>(lds0, lds1, lds2, ar, br, MxRows<C::MXU>{}, klen, acc);
+  mainloop<C, false>(MOE_RING, ar, br, MxRows<C::MXU>{}, klen, acc);
 #pragma unroll
   for (int i = 0; i < C::WM; ++i)
 #pragma unroll
@@ -881,8 +969,8 @@ SplitK plan_split(int act_dtype, int M, int ncols, int K) {
   if (ceil_div(M, DenseCfg::BM) * ceil_div(ncols, DenseCfg::BN) >= 256) return p;
   const int64_t tiles = ceil_div(M, SplitCfg::BM) * ceil_div(ncols, SplitCfg::BN);
   int s = 1;
-  while (s < 16 && tiles * s < 256 && K / (2 * s) >= 6 * BK) s *= 2;
-  const int unit = 3 * BK;  // the ring walks K-tiles in threes
+  while (s < 16 && tiles * s < 256 && K / (2 * s) >= 6 * SplitCfg::BK) s *= 2;
+  const int unit = SplitCfg::NS * SplitCfg::BK;  // the ring walks K-tiles NS at a time
   p.kchunk = (int)(ceil_div(ceil_div(K, s), unit) * unit);
   p.splits = (int)ceil_div(K, p.kchunk);
   return p;
@@ -902,8 +990,8 @@ int launch_dense(const DenseArgs& a, hipStream_t stream) {
   if (a.split.splits > 0) {
     using C = SplitCfg;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.N, C::BN) * ceil_div(a.M, C::BM) * a.split.splits));
-    if (a.W.dtype == DT_MXFP4) hipLaunchKernelGGL(dense_split_kernel<true>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(dense_split_kernel<false>, grid, dim3(256), 0, stream, a);
+    if (a.W.dtype == DT_MXFP4) hipLaunchKernelGGL(dense_split_kernel<true>, grid, dim3(SplitCfg::NT), 0, stream, a);
+    else hipLaunchKernelGGL(dense_split_kernel<false>, grid, dim3(SplitCfg::NT), 0, stream, a);
     const int64_t n4 = (int64_t)a.M * a.N / 4;
     hipLaunchKernelGGL(reduce_store_kernel, dim3(reduce_blocks(n4)), dim3(256), 0, stream, a.P,
                        a.split.splits, a.M, a.N, (bf16_t*)a.C, a.ldc);
@@ -911,8 +999,8 @@ int launch_dense(const DenseArgs& a, hipStream_t stream) {
   }
   using C = DenseCfg;
   dim3 grid((unsigned)xcd_grid(ceil_div(a.N, C::BN) * ceil_div(a.M, C::BM)));
-  if (a.W.dtype == DT_MXFP4) hipLaunchKernelGGL(dense_kernel<true>, grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(dense_kernel<false>, grid, dim3(256), 0, stream, a);
+  if (a.W.dtype == DT_MXFP4) hipLaunchKernelGGL(dense_kernel<true>, grid, dim3(DenseCfg::NT), 0, stream, a);
+  else hipLaunchKernelGGL(dense_kernel<false>, grid, dim3(DenseCfg::NT), 0, stream, a);
   return (int)hipGetLastError();
 }
 
@@ -922,8 +1010,8 @@ int launch_glu(const GluArgs& a, hipStream_t stream) {
   if (a.split.splits > 0) {
     using C = SplitCfg;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.F, C::BN / 2) * ceil_div(a.M, C::BM) * a.split.splits));
-    if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(glu_split_kernel<true>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(glu_split_kernel<false>, grid, dim3(256), 0, stream, a);
+    if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(glu_split_kernel<true>, grid, dim3(SplitCfg::NT), 0, stream, a);
+    else hipLaunchKernelGGL(glu_split_kernel<false>, grid, dim3(SplitCfg::NT), 0, stream, a);
     const int64_t n4 = (int64_t)a.M * a.F / 4;
     hipLaunchKernelGGL(reduce_glu_kernel, dim3(reduce_blocks(n4)), dim3(256), 0, stream, a.P,
                        a.split.splits, a.M, a.F, a.c, (bf16_t*)a.H, a.ldh);
@@ -931,8 +1019,8 @@ int launch_glu(const GluArgs& a, hipStream_t stream) {
   }
   using C = DenseCfg;
   dim3 grid((unsigned)xcd_grid(ceil_div(a.F, C::BN / 2) * ceil_div(a.M, C::BM)));
-  if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(glu_kernel<true>, grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(glu_kernel<false>, grid, dim3(256), 0, stream, a);
+  if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(glu_kernel<true>, grid, dim3(DenseCfg::NT), 0, stream, a);
+  else hipLaunchKernelGGL(glu_kernel<false>, grid, dim3(DenseCfg::NT), 0, stream, a);
   return (int)hipGetLastError();
 }
 
@@ -942,8 +1030,8 @@ int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream) {
   if (a.bm != GroupCfg::BM) return -1;
   using C = GroupCfg;
   dim3 grid((unsigned)xcd_grid(ceil_div(a.F, C::BN / 2) * a.max_tiles));
-  if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(grouped_glu_kernel<true>, grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(grouped_glu_kernel<false>, grid, dim3(256), 0, stream, a);
+  if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(grouped_glu_kernel<true>, grid, dim3(C::NT), 0, stream, a);
+  else hipLaunchKernelGGL(grouped_glu_kernel<false>, grid, dim3(C::NT), 0, stream, a);
   return (int)hipGetLastError();
 }
 
@@ -953,8 +1041,8 @@ int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream) {
   if (a.bm != GroupCfg::BM) return -1;
   using C = GroupCfg;
   dim3 grid((unsigned)xcd_grid(ceil_div(a.N, C::BN) * a.max_tiles));
-  if (a.Wo.dtype == DT_MXFP4) hipLaunchKernelGGL(grouped_down_kernel<true>, grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(grouped_down_kernel<false>, grid, dim3(256), 0, stream, a);
+  if (a.Wo.dtype == DT_MXFP4) hipLaunchKernelGGL(grouped_down_kernel<true>, grid, dim3(C::NT), 0, stream, a);
+  else hipLaunchKernelGGL(grouped_down_kernel<false>, grid, dim3(C::NT), 0, stream, a);
   return (int)hipGetLastError();
 }
 
@@ -970,17 +1058,17 @@ int launch_multiseg(const MultiSegArgs& a, hipStream_t stream) {
   if (multiseg_slices(a.act_dtype, a.M, a.N, a.nseg) > 0) {
     using CS = SplitCfg;
     dim3 g2((unsigned)xcd_grid(ceil_div(a.N, CS::BN) * ceil_div(a.M, CS::BM) * a.nseg));
-    if (last_mx) hipLaunchKernelGGL(multiseg_split_kernel<true>, g2, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(multiseg_split_kernel<false>, g2, dim3(256), 0, stream, a);
+    if (last_mx) hipLaunchKernelGGL(multiseg_split_kernel<true>, g2, dim3(SplitCfg::NT), 0, stream, a);
+    else hipLaunchKernelGGL(multiseg_split_kernel<false>, g2, dim3(SplitCfg::NT), 0, stream, a);
     const int64_t n4 = (int64_t)a.M * a.N / 4;
     hipLaunchKernelGGL(reduce_store_kernel, dim3(reduce_blocks(n4)), dim3(256), 0, stream, a.P,
                        a.nseg, a.M, a.N, (bf16_t*)a.C, a.ldc);
     return (int)hipGetLastError();
   }
   if (last_mx)
-    hipLaunchKernelGGL(multiseg_kernel<true>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(multiseg_kernel<true>, grid, dim3(DenseCfg::NT), 0, stream, a);
   else
-    hipLaunchKernelGGL(multiseg_kernel<false>, grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(multiseg_kernel<false>, grid, dim3(DenseCfg::NT), 0, stream, a);
   return (int)hipGetLastError();
 }
 
@@ -988,7 +1076,7 @@ int launch_multiseg(const MultiSegArgs& a, hipStream_t stream) {
 int router_logit_splits(int T, int E, int d) {
   const int64_t tiles = ceil_div(T, LogitCfg::BM) * ceil_div(E, LogitCfg::BN);
   int splits = 1;
-  while (tiles * splits < 512 && d / (splits * 2) >= 4 * BK) splits *= 2;
+  while (tiles * splits < 512 && d / (splits * 2) >= 4 * LogitCfg::BK) splits *= 2;
   return splits;
 }
 
@@ -1000,7 +1088,7 @@ int launch_router_logits(const LogitsArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(zero_f32, dim3((unsigned)blocks), dim3(256), 0, stream, a.L, n);
   }
   const int64_t items = ceil_div(a.T, LogitCfg::BM) * ceil_div(a.E, LogitCfg::BN) * a.splits;
-  hipLaunchKernelGGL(logits_kernel, dim3((unsigned)xcd_grid(items)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(logits_kernel, dim3((unsigned)xcd_grid(items)), dim3(LogitCfg::NT), 0, stream, a);
   return (int)hipGetLastError();
 }
 
