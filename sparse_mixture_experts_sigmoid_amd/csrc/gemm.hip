@@ -157,39 +157,30 @@ __device__ __forceinline__ void load_mx(const MxRows<C::MXU>& m, int k0, int K,
   }
 }
 
-// e2m1 code (4 bits) -> bf16 bits of its value (OCP MX: 0, .5, 1, 1.5, 2, 3, 4, 6).
-__device__ __forceinline__ uint32_t e2m1_bf16(uint32_t c) {
-  const uint32_t m = c & 7u;
-  const uint32_t b = (m >= 2u) ? (0x3F80u + ((m - 2u) << 6)) : (m == 1u ? 0x3F00u : 0u);
-  return b | ((c & 8u) << 12);
-}
-
-// value * 2^(s-127), exact (power-of-two scaling of a 2-significant-bit value).
-__device__ __forceinline__ uint32_t scale_bf16(uint32_t b, float scale) {
-  return __float_as_uint(__uint_as_float(b << 16) * scale) >> 16;
-}
-
+// Decode of one 32-element MXFP4 block: gfx950's v_cvt_scalef32_pk_bf16_fp4
+// turns the two e2m1 codes of one byte (low nibble first) into two bf16 scaled
+// by an fp32 factor; with the factor 2^(s-127) of the e8m0 byte s the result is
+// exact (a power-of-two scaling of a 2-significant-bit value; checked bit for
+// bit against the value table for every code and every finite scale byte).
+// Scale byte 255 (NaN in e8m0) is not supported.
 template <class C>
 __device__ __forceinline__ void store_mx(bf16_t* tile, const MxStage (&st)[C::MXU]) {
   const int part = threadIdx.x % C::UR;
 #pragma unroll
   for (int j = 0; j < C::MXU; ++j) {
     const int row = mx_row<C>(j);
-    // a zero-filled (out-of-range) block decodes to zeros whatever its scale byte
     const float scale = st[j].s == 0u ? 0x1p-127f : __uint_as_float(st[j].s << 23);
     const uint32_t q[4] = {st[j].q.x, st[j].q.y, st[j].q.z, st[j].q.w};
-    uint32_t w[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t byte = (q[i / 4] >> (8 * (i % 4))) & 0xFFu;
-      w[i] = scale_bf16(e2m1_bf16(byte & 0xFu), scale) |
-             (scale_bf16(e2m1_bf16(byte >> 4), scale) << 16);
-    }
     bf16_t* dst = tile + row * C::BK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *(uint4*)(dst + 8 * ((part * 4 + i) ^ swz<C>(row))) =
-          make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    for (int i = 0; i < 4; ++i) {
+      // the byte selector of the conversion is an immediate
+      const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], scale, 0));
+      const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], scale, 1));
+      const uint32_t w2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], scale, 2));
+      const uint32_t w3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q[i], scale, 3));
+      *(uint4*)(dst + 8 * ((part * 4 + i) ^ swz<C>(row))) = make_uint4(w0, w1, w2, w3);
+    }
   }
 }
 
@@ -327,6 +318,62 @@ __device__ __forceinline__ void ring_step(bf16_t* R, bf16_t* W, const Rows<C::AR
     __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPer * kVmem, 0);
 }
 
+// MXFP4 B through registers, three K-tiles ahead of its LDS stage (NS = 3):
+// step kt stores the decoded B of tile kt + 2 (loaded three steps ago, in q)
+// into the free stage W next to A's DMA, then reloads q with tile kt + 5.
+template <class C, int NV>
+__device__ __forceinline__ void ring_step_mx(bf16_t* R, bf16_t* W, const Rows<C::AR>& ar,
+                                             const MxRows<C::MXU>& bm, int kt, int K, Acc<C>& acc,
+                                             MxStage (&q)[C::MXU]) {
+  static_assert(C::NS == 3, "MXFP4 ring");
+  constexpr int kMx = 2 * C::MXU;   // packed + scale load per unit
+  // A of tile kt has landed once only A of kt+1 and B of kt+3, kt+4 are outstanding
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(C::AR + 2 * kMx));
+  wg_barrier();
+  Frags<C> f;
+  read_frags<C, NV>(R, R + C::BM * C::BK, f);
+  dma_rows<C>(ar, W, (kt + 2) * C::BK, K);
+  store_mx<C>(W + C::BM * C::BK, q);
+  load_mx<C>(bm, (kt + 5) * C::BK, K, q);
+  mma_frags<C, NV>(f, acc);
+  constexpr int kReads = NV > 0 ? C::BK / 16 * (NV + C::WN) : 0;
+  constexpr int kMfma = C::BK / 16 * NV * C::WN;
+  constexpr int kVmem = C::AR + kMx;
+  constexpr int kPer = kMfma / kVmem > 0 ? kMfma / kVmem : 1;
+  if constexpr (kMfma == 0) return;
+  __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+#pragma unroll
+  for (int v = 0; v < kVmem; ++v) {
+    __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+  if constexpr (kMfma > kPer * kVmem)
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPer * kVmem, 0);
+}
+
+template <class C, int NV>
+__device__ __forceinline__ void mainloop_mx(bf16_t* s0, bf16_t* s1, bf16_t* s2, const Rows<C::AR>& ar,
+                                            const MxRows<C::MXU>& bm, int K, Acc<C>& acc) {
+  const int nk = (int)ceil_div(K, C::BK);
+  MxStage t[C::MXU], q0[C::MXU], q1[C::MXU], q2[C::MXU];   // q_i: B of tiles = i (mod 3)
+  load_mx<C>(bm, 0, K, t);
+  dma_rows<C>(ar, s0, 0, K);
+  store_mx<C>(s0 + C::BM * C::BK, t);
+  load_mx<C>(bm, C::BK, K, t);
+  dma_rows<C>(ar, s1, C::BK, K);
+  store_mx<C>(s1 + C::BM * C::BK, t);
+  load_mx<C>(bm, 2 * C::BK, K, q2);
+  load_mx<C>(bm, 3 * C::BK, K, q0);
+  load_mx<C>(bm, 4 * C::BK, K, q1);
+  for (int kt = 0; kt < nk; kt += 3) {
+    ring_step_mx<C, NV>(s0, s2, ar, bm, kt, K, acc, q2);
+    ring_step_mx<C, NV>(s1, s0, ar, bm, kt + 1, K, acc, q0);
+    ring_step_mx<C, NV>(s2, s1, ar, bm, kt + 2, K, acc, q1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  wg_barrier();
+}
+
 // acc += A_tile B_tile^T over k in [0, K) through the NS-stage ring. The
 // K-tile count is rounded up to a multiple of NS; the extra tiles read zeros.
 // A rows: `ar` (bf16 DMA); B rows: `br` (bf16 DMA) or `bm` (MXFP4, decoded
@@ -335,7 +382,9 @@ template <class C, bool B_MX, int NV = C::WM>
 __device__ __forceinline__ void mainloop(bf16_t* s0, bf16_t* s1, bf16_t* s2, bf16_t* s3, bf16_t* s4,
                                          const Rows<C::AR>& ar, const Rows<C::BR>& br,
                                          const MxRows<C::MXU>& bm, int K, Acc<C>& acc) {
-  {
+  if constexpr (B_MX && C::NS == 3) {
+    mainloop_mx<C, NV>(s0, s1, s2, ar, bm, K, acc);
+  } else {
     const int nk = (int)ceil_div(K, C::BK);
     stage_issue<C, B_MX>(s0, ar, br, bm, 0, K);
     if constexpr (C::NS > 2) stage_issue<C, B_MX>(s1, ar, br, bm, 1, K);
