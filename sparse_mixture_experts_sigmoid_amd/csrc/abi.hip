@@ -103,7 +103,7 @@ struct Plan {
 };
 
 struct LayerWs {
-  size_t s, key, norms, idx, gate, counts, offsets, perm, inv, blk, z, tile_off, H, O, n, Hs, P;
+  size_t s, key, norms, idx, gate, counts, offsets, perm, inv, blk, z, tile_off, tile_info, H, O, n, Hs, P;
 };
 
 int max_tiles(const moe_desc_t* d) {
@@ -121,6 +121,7 @@ void plan_permute(const moe_desc_t* d, Plan& p, LayerWs& w) {
 }
 void plan_expert(const moe_desc_t* d, Plan& p, LayerWs& w) {
   w.tile_off = p.take((size_t)(d->n_experts + 1) * 4);
+  w.tile_info = p.take((size_t)max_tiles(d) * 16);
   w.H = p.take((size_t)d->T * d->top_k * d->d_ff * elem_bytes(d->act_dtype));
 }
 // fp32 split-K partials of the dense GEMMs that run with few tokens
@@ -309,18 +310,21 @@ int do_latent_down(const moe_desc_t* d, const void* x, moe_w_t w, void* z, float
 }
 
 int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const int32_t* offsets,
-               const moe_weights_t* w, void* o_perm, int32_t* tile_off, void* H, hipStream_t st,
+               const moe_weights_t* w, void* o_perm, int32_t* tile_off, int32_t* tile_info, void* H,
+               hipStream_t st,
                Marker mk = {-1, nullptr}) {
   const int bm = moe::grouped_bm(d->act_dtype, (int64_t)d->T * d->top_k, d->n_experts);
   const int mt = max_tiles(d);
   const int rows_cap = d->T * d->top_k;
   mk(4);
   if (d->T > 0)
-    MOE_LAUNCH(moe::launch_tile_table(offsets, d->n_experts, bm, tile_off, st), "tile_table");
+    MOE_LAUNCH(moe::launch_tile_table(offsets, d->n_experts, bm, tile_off, tile_info, st),
+               "tile_table");
   mk(5);
   moe::GroupedGluArgs g{};
   g.Z = z; g.ldz = d->d_latent; g.T = d->T; g.rows_cap = rows_cap;
   g.perm_src = perm; g.topk = d->top_k; g.offsets = offsets; g.tile_off = tile_off;
+  g.tile_info = tile_info;
   g.max_tiles = mt;
   g.Wg = wop(w->exp_gate, d->expert_w_dtype);
   g.Wv = wop(w->exp_up, d->expert_w_dtype);
@@ -330,7 +334,7 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
   mk(6);
   moe::GroupedDownArgs dn{};
   dn.H = H; dn.ldh = d->d_ff; dn.rows_cap = rows_cap;
-  dn.offsets = offsets; dn.tile_off = tile_off; dn.max_tiles = mt;
+  dn.offsets = offsets; dn.tile_off = tile_off; dn.tile_info = tile_info; dn.max_tiles = mt;
   dn.Wo = wop(w->exp_down, d->expert_w_dtype);
   dn.E = d->n_experts; dn.N = d->d_latent; dn.K = d->d_ff;
   dn.O = o_perm; dn.act_dtype = d->act_dtype; dn.bm = bm;
@@ -529,6 +533,7 @@ int moe_expert_ffn(const moe_desc_t* d, const void* z, const int32_t* perm_src,
   LayerWs lw{};
   plan_expert(d, p, lw);
   return do_experts(d, z, perm_src, offsets, w, o_perm, (int32_t*)at(ws, lw.tile_off),
+                    (int32_t*)at(ws, lw.tile_info),
                     at(ws, lw.H), (hipStream_t)stream);
 }
 
@@ -609,6 +614,7 @@ int moe_layer_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x
   mk(3);
   MOE_CHECK(do_latent_down(d, x, w->lat_down, at(ws, lw.z), (float*)at(ws, lw.P), st));
   MOE_CHECK(do_experts(d, at(ws, lw.z), perm, offsets, w, at(ws, lw.O), (int32_t*)at(ws, lw.tile_off),
+                       (int32_t*)at(ws, lw.tile_info),
                        at(ws, lw.H), st, mk));
   mk(7);
   MOE_CHECK(do_combine(d, at(ws, lw.O), inv, gate, w->rms_gain, at(ws, lw.n), nullptr, st));

@@ -71,13 +71,13 @@ using SplitCfg = Cfg<2, 2, 2, 2, 64, 3>;   // 128 x 128 (small batches, split K)
 
 // bf16 rows by DMA: wave w fills tile rows w*RPI*N .. + RPI*N - 1 with one
 // 1 KB buffer_load ... lds per q < N; lane i of load q takes tile row
-// w*RPI*N + RPI*q + i/CH and writes LDS slot i%CH of it. Rows of one wave come
-// through resource r[sel] (gate or up weights of a GLU tile; sel is
-// wave-uniform).
+// w*RPI*N + RPI*q + i/CH and writes LDS slot i%CH of it. The rows of load q
+// come through resource r[sel[q]] (gate or up weights of a GLU tile; sel[q]
+// is wave-uniform).
 template <int N>
 struct Rows {
   rsrc_t r[2];
-  int sel;
+  int sel[N];
   uint32_t off[N];  // byte offset of this lane's row of load q, or kOOB
 };
 
@@ -111,9 +111,9 @@ template <class C, int N>
 __device__ __forceinline__ void dma_rows(const Rows<N>& rs, bf16_t* tile, int k0, int K) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: LDS base in M0
-  const rsrc_t r = rs.sel ? rs.r[1] : rs.r[0];
 #pragma unroll
   for (int q = 0; q < N; ++q) {
+    const rsrc_t r = rs.sel[q] ? rs.r[1] : rs.r[0];
     const int row0 = wv * C::RPI * N + C::RPI * q;
     const int c = (lane % C::CH) ^ swz<C>(row0 + lane / C::CH);  // global chunk for this slot
     const int k = k0 + c * 8;
@@ -461,9 +461,9 @@ __device__ __forceinline__ Rows<N> a_rows_dense(const void* A, int64_t lda, int 
   Rows<N> rs;
   const int nrows = max(0, min(M - m0, C::NW * C::RPI * N));
   rs.r[0] = rs.r[1] = make_rsrc((const bf16_t*)A + (int64_t)m0 * lda, (int64_t)nrows * lda * 2);
-  rs.sel = 0;
 #pragma unroll
   for (int q = 0; q < N; ++q) {
+    rs.sel[q] = 0;
     const int r = dma_row<C, N>(q);
     rs.off[q] = r < nrows ? (uint32_t)((int64_t)r * lda * 2) : kOOB;
   }
@@ -497,25 +497,25 @@ __device__ __forceinline__ MxRows<C::MXU> b_mx_plain(const WOperand& w, int64_t 
 // GLU B tile: wave column wn covers tile rows wn*BN/WGN .. + BN/WGN: first the
 // gate rows f0 + wn*H + (0 .. H-1) of Wg, then the same rows of Wv, with
 // H = BN/(2 WGN). The block produces BN/2 outputs f0 .. f0 + BN/2 - 1. Wave w
-// DMAs tile rows w*BN/NW .. + BN/NW, which lie inside one gate or up half
-// (WGM even), so its resource choice is wave-uniform.
+// DMAs tile rows w*BN/NW .. + BN/NW in loads of RPI rows; each load lies inside
+// one gate or up half (H is a multiple of RPI), so its resource is wave-uniform.
 template <class C>
 __device__ __forceinline__ int glu_half_rows() { return C::BN / (2 * C::WGN); }
 
 template <class C>
 __device__ __forceinline__ Rows<C::BR> b_rows_glu(const WOperand& g, const WOperand& v,
                                                   int64_t row_base, int K, int f0, int F) {
-  static_assert(C::WGM % 2 == 0, "each wave's B rows must be all gate or all up");
   constexpr int H = C::BN / (2 * C::WGN);
+  static_assert(H % C::RPI == 0, "each load's B rows must be all gate or all up");
   Rows<C::BR> rs;
   const int nf = max(0, min(F - f0, C::BN / 2));  // valid outputs of this block
   rs.r[0] = make_rsrc((const bf16_t*)g.data + (row_base + f0) * K, (int64_t)nf * K * 2);
   rs.r[1] = make_rsrc((const bf16_t*)v.data + (row_base + f0) * K, (int64_t)nf * K * 2);
   const int wv = threadIdx.x >> 6;
   const int tr0 = wv * (C::BN / C::NW);                      // this wave's first tile row
-  rs.sel = __builtin_amdgcn_readfirstlane((tr0 % (2 * H)) >= H ? 1 : 0);
 #pragma unroll
   for (int q = 0; q < C::BR; ++q) {
+    rs.sel[q] = __builtin_amdgcn_readfirstlane(((tr0 + C::RPI * q) % (2 * H)) >= H ? 1 : 0);
     const int tr = tr0 + C::RPI * q + (threadIdx.x & 63) / C::CH;
     const int fl = (tr / (2 * H)) * H + (tr % H);
     rs.off[q] = fl < nf ? (uint32_t)((int64_t)fl * K * 2) : kOOB;
@@ -651,45 +651,28 @@ __global__ __launch_bounds__(DenseCfg::NT) void glu_kernel(GluArgs a) {
             [=](int tr) -> int64_t { return m0 + tr < M ? (int64_t)(m0 + tr) : -1; });
 }
 
-// Which expert owns grouped tile `tile`: the e with tile_off[e] <= tile < tile_off[e+1].
-__device__ __forceinline__ int expert_of_tile(const int32_t* tile_off, int E, int tile) {
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (tile_off[mid] <= tile) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
-// Expert and row range of grouped tile `tile` (false: past the last tile). The
-// values are read from memory but are the same for every lane: readfirstlane
-// makes that visible to the compiler, so addresses built from them stay scalar
+// Work item L of a grouped GEMM -> expert e, n-tile nt and row range
+// [row_lo, row_hi). Logical order: expert by expert; inside an expert, n-tile
+// major and row tile minor, so the row tiles that share one weight slice run
+// side by side and read it through L2 once. Expert e owns items
+// [tile_off[e], tile_off[e+1]) * ntn, so item L lies in the expert of tile
+// L / ntn, whose tile_info entry {e, tile_off[e], count_e, offsets[e]} is the
+// only table read. The values are the same for every lane: readfirstlane makes
+// that visible to the compiler, so addresses built from them stay scalar
 // (otherwise every buffer load would be wrapped in a waterfall loop).
 template <int BM_>
-__device__ __forceinline__ bool tile_rows(const int32_t* tile_off, const int32_t* offsets, int E,
-                                          int rows_cap, int tile, int& e, int& row_lo, int& row_hi) {
-  if (tile >= __builtin_amdgcn_readfirstlane(tile_off[E])) return false;
-  e = __builtin_amdgcn_readfirstlane(expert_of_tile(tile_off, E, tile));
-  const int t0 = __builtin_amdgcn_readfirstlane(tile_off[e]);
-  const int o0 = __builtin_amdgcn_readfirstlane(offsets[e]);
-  const int o1 = __builtin_amdgcn_readfirstlane(offsets[e + 1]);
-  row_lo = o0 + (tile - t0) * BM_;
-  row_hi = min(min(o1, row_lo + BM_), rows_cap);
-  return true;
-}
-
-// Logical order of grouped work: expert by expert; inside an expert, n-tile
-// major and row tile minor, so the row tiles that share one weight slice run
-// side by side and read it through L2 once (the expert's gathered rows are
-// small and stay in L2). Expert e owns items [tile_off[e], tile_off[e+1]) * ntn.
-__device__ __forceinline__ void grouped_order(const int32_t* tile_off, int E, int ntn, int64_t L,
-                                              int& tile, int& nt) {
-  const int e = __builtin_amdgcn_readfirstlane(expert_of_tile(tile_off, E, (int)(L / ntn)));
-  const int t0 = __builtin_amdgcn_readfirstlane(tile_off[e]);
-  const int mt = __builtin_amdgcn_readfirstlane(tile_off[e + 1]) - t0;
+__device__ __forceinline__ void grouped_item(const int32_t* tile_info, int ntn, int rows_cap, int64_t L,
+                                             int& e, int& nt, int& row_lo, int& row_hi) {
+  const int32_t* ti = tile_info + 4 * (L / ntn);
+  e = __builtin_amdgcn_readfirstlane(ti[0]);
+  const int t0 = __builtin_amdgcn_readfirstlane(ti[1]);
+  const int cnt = __builtin_amdgcn_readfirstlane(ti[2]);
+  const int r0 = __builtin_amdgcn_readfirstlane(ti[3]);
+  const int mt = (cnt + BM_ - 1) / BM_;
   const int64_t local = L - (int64_t)t0 * ntn;
   nt = (int)(local / mt);
-  tile = t0 + (int)(local % mt);
+  row_lo = r0 + (int)(local % mt) * BM_;
+  row_hi = min(min(r0 + cnt, row_lo + BM_), rows_cap);
 }
 
 template <bool B_MX>
@@ -699,17 +682,15 @@ __global__ __launch_bounds__(GroupCfg::NT) void grouped_glu_kernel(GroupedGluArg
   const int ntn = (int)ceil_div(a.F, C::BN / 2);
   int64_t L;
   if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, L)) return;
-  int tile, nt;
-  grouped_order(a.tile_off, a.E, ntn, L, tile, nt);
-  int e, row_lo, row_hi;
-  if (!tile_rows<C::BM>(a.tile_off, a.offsets, a.E, a.rows_cap, tile, e, row_lo, row_hi)) return;
+  int e, nt, row_lo, row_hi;
+  grouped_item<C::BM>(a.tile_info, ntn, a.rows_cap, L, e, nt, row_lo, row_hi);
   const int f0 = nt * (C::BN / 2);
   // A: z rows of the tile's (token, slot) pairs, gathered through perm_src
   Rows<C::AR> ar;
   ar.r[0] = ar.r[1] = make_rsrc(a.Z, (int64_t)a.T * a.ldz * 2);
-  ar.sel = 0;
 #pragma unroll
   for (int q = 0; q < C::AR; ++q) {
+    ar.sel[q] = 0;
     const int row = row_lo + dma_row<C, C::AR>(q);
     uint32_t off = kOOB;
     if (row >= 0 && row < row_hi) {
@@ -740,10 +721,8 @@ __global__ __launch_bounds__(GroupCfg::NT) void grouped_down_kernel(GroupedDownA
   const int ntn = (int)ceil_div(a.N, C::BN);
   int64_t L;
   if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, L)) return;
-  int tile, nt;
-  grouped_order(a.tile_off, a.E, ntn, L, tile, nt);
-  int e, row_lo, row_hi;
-  if (!tile_rows<C::BM>(a.tile_off, a.offsets, a.E, a.rows_cap, tile, e, row_lo, row_hi)) return;
+  int e, nt, row_lo, row_hi;
+  grouped_item<C::BM>(a.tile_info, ntn, a.rows_cap, L, e, nt, row_lo, row_hi);
   const int n0 = nt * C::BN;
   const Rows<C::AR> ar = a_rows_dense<C, C::AR>(a.H, a.ldh, max(row_lo, 0), max(row_hi, 0));
   const int64_t wrow = (int64_t)e * a.N;

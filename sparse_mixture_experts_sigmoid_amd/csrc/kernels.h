@@ -61,9 +61,11 @@ struct PermuteArgs {
 };
 int launch_permute(const PermuteArgs& a, hipStream_t stream);
 
-// Tile table of a grouped GEMM with BM-row tiles: tile_off[e] = sum_{e'<e}
-// ceil(count_e' / BM), tile_off[E] = total tiles (device side, from offsets).
-int launch_tile_table(const int32_t* offsets, int E, int BM, int32_t* tile_off,
+// Tile table of a grouped GEMM with BM-row tiles (device side, from offsets):
+// tile_off[e] = sum_{e'<e} ceil(count_e' / BM), tile_off[E] = total tiles, and
+// for each tile t of expert e, tile_info[4t .. 4t+3] = {e, tile_off[e],
+// count_e, offsets[e]} (tile_info holds max_tiles entries).
+int launch_tile_table(const int32_t* offsets, int E, int BM, int32_t* tile_off, int32_t* tile_info,
                       hipStream_t stream);
 
 // A weight operand [rows, K] in bf16, fp32 or MXFP4 (data = packed, scale = e8m0).
@@ -121,6 +123,7 @@ struct GroupedGluArgs {
   const int32_t* perm_src; int topk;
   const int32_t* offsets;            // [E+1]
   const int32_t* tile_off;           // [E+1] for BM-row tiles
+  const int32_t* tile_info;          // [max_tiles][4] (launch_tile_table)
   int max_tiles;                     // upper bound of tile_off[E]
   WOperand Wg, Wv;                   // [E, F, K]
   int E, F, K;
@@ -140,6 +143,7 @@ struct GroupedDownArgs {
   int rows_cap;                      // rows of H and O
   const int32_t* offsets;
   const int32_t* tile_off;
+  const int32_t* tile_info;
   int max_tiles;
   WOperand Wo;
   int E, N, K;

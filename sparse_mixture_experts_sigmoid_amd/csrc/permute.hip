@@ -123,7 +123,8 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ 
 }
 
 __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restrict__ offsets, int E,
-                                                          int BM, int32_t* __restrict__ tile_off) {
+                                                          int BM, int32_t* __restrict__ tile_off,
+                                                          int32_t* __restrict__ tile_info) {
   __shared__ int32_t sh[4096];
   __shared__ int32_t part[1024];
   __shared__ int32_t total;
@@ -133,7 +134,13 @@ __global__ __launch_bounds__(1024) void tile_table_kernel(const int32_t* __restr
   }
   __syncthreads();
   block_exclusive_scan(sh, E, part, &total);
-  for (int e = threadIdx.x; e < E; e += blockDim.x) tile_off[e] = sh[e];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    tile_off[e] = sh[e];
+    const int32_t o0 = offsets[e], c = offsets[e + 1] - o0;
+    const int n = c > 0 ? (c + BM - 1) / BM : 0;
+    for (int i = 0; i < n; ++i)
+      *(int4*)(tile_info + 4 * (int64_t)(sh[e] + i)) = make_int4(e, sh[e], c, o0);
+  }
   if (threadIdx.x == 0) tile_off[E] = total;
 }
 
@@ -165,9 +172,10 @@ int launch_permute(const PermuteArgs& a, hipStream_t stream) {
   return (int)hipGetLastError();
 }
 
-int launch_tile_table(const int32_t* offsets, int E, int BM, int32_t* tile_off,
+int launch_tile_table(const int32_t* offsets, int E, int BM, int32_t* tile_off, int32_t* tile_info,
                       hipStream_t stream) {
-  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream, offsets, E, BM, tile_off);
+  hipLaunchKernelGGL(tile_table_kernel, dim3(1), dim3(1024), 0, stream, offsets, E, BM, tile_off,
+                     tile_info);
   return (int)hipGetLastError();
 }
 
