@@ -179,19 +179,26 @@ int moe_output(const moe_desc_t* desc, const void* x, const void* n, const moe_w
 
 /* The whole layer: route, permute, latent down, experts, combine, output.
    y [T, d] act dtype. Optional outputs (NULL to skip): topk_idx [T, k],
-   topk_gate [T, k], counts [E]. */
+   topk_gate [T, k], counts [E]. The latent down-projection and the shared
+   experts' gate/up do not depend on the routing: they run on a second stream
+   that the library keeps per device (created on the first call, default
+   priority), forked from `stream` with an event at the start of the call and
+   joined back into it before the routed experts, so the call remains ordered
+   on `stream` like any other work there (and can be captured into a graph). */
 int moe_layer_forward(const moe_desc_t* desc, const moe_weights_t* w, const void* x, void* y,
                       int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* counts_opt,
                       void* ws, size_t ws_bytes, void* stream);
 
 /* Stage tracing. moe_trace_enable(max_calls) makes the next max_calls calls of
-   moe_layer_forward record a HIP event on their stream before each stage and
-   after the last one (max_calls = 0 turns tracing off). moe_trace_read waits
-   for those events, writes the average milliseconds of each stage over the
-   traced calls into ms[0 .. min(max_stages, MOE_TRACE_STAGES)) and the number
-   of traced calls into *ncalls, then starts a new trace window. Stage i is
-   named by moe_trace_stage_name(i). The events are created by the library on
-   the device current at moe_trace_enable and live until the next enable. */
+   moe_layer_forward record a HIP event before and after each stage, on the
+   stream the stage runs on (max_calls = 0 turns tracing off). moe_trace_read
+   waits for those events, writes the average milliseconds of each stage over
+   the traced calls into ms[0 .. min(max_stages, MOE_TRACE_STAGES)) and the
+   number of traced calls into *ncalls, then starts a new trace window. Stage i
+   is named by moe_trace_stage_name(i). Stages on the second stream (latent
+   down, shared gate/up) overlap the routing stages, so the stage times can add
+   up to more than the call. The events are created by the library on the
+   device current at moe_trace_enable and live until the next enable. */
 #define MOE_TRACE_STAGES 10
 int moe_trace_enable(int max_calls);
 int moe_trace_read(float* ms, int max_stages, int* ncalls);

@@ -229,7 +229,8 @@ moe::WOperand wop(const moe_w_t& w, int dtype) { return moe::WOperand{w.data, w.
 char* at(void* ws, size_t off) { return (char*)ws + off; }
 
 // ------------------------------------------------------------------------------------------
-// stage tracing: per traced call, MOE_TRACE_STAGES + 1 events recorded on the call's stream
+// stage tracing: per traced call and stage, a start and an end event recorded on the stream
+// the stage runs on
 // ------------------------------------------------------------------------------------------
 
 const char* const kStageNames[MOE_TRACE_STAGES] = {
@@ -240,7 +241,7 @@ struct Trace {
   std::mutex mu;
   int max_calls = 0;
   int used = 0;
-  std::vector<hipEvent_t> ev;  // max_calls * (MOE_TRACE_STAGES + 1)
+  std::vector<hipEvent_t> ev;  // max_calls * 2 * MOE_TRACE_STAGES
 };
 Trace g_trace;
 
@@ -251,11 +252,15 @@ int trace_begin() {
   return g_trace.used++;
 }
 
+constexpr size_t kTraceEvents = 2 * MOE_TRACE_STAGES;   // per traced call
+
 struct Marker {
   int slot;
-  hipStream_t st;
-  void operator()(int boundary) const {
-    if (slot >= 0) hipEventRecord(g_trace.ev[(size_t)slot * (MOE_TRACE_STAGES + 1) + boundary], st);
+  void beg(int stage, hipStream_t s) const {
+    if (slot >= 0) hipEventRecord(g_trace.ev[(size_t)slot * kTraceEvents + 2 * stage], s);
+  }
+  void end(int stage, hipStream_t s) const {
+    if (slot >= 0) hipEventRecord(g_trace.ev[(size_t)slot * kTraceEvents + 2 * stage + 1], s);
   }
 };
 
@@ -268,30 +273,34 @@ struct Marker {
 // bit for bit). Otherwise every (token, expert) logit in fixed order on VALU.
 int do_route(const moe_desc_t* d, const void* x, moe_w_t router, const float* bias, int32_t* idx,
              float* gate, float* s, float* key, float* norms, bool want_scores, hipStream_t st,
-             Marker mk = {-1, nullptr}) {
+             Marker mk = {-1}) {
   if (!want_scores && d->act_dtype == MOE_BF16 && d->dense_w_dtype == MOE_BF16 &&
       moe::router_select_supported(d->n_experts, d->d_model)) {
     float* xn = norms;
     float* wn = norms + d->T;
-    mk(0);
+    mk.beg(0, st);
     MOE_LAUNCH(moe::launch_row_norms(x, d->T, d->d_model, xn, st), "row_norms");
     MOE_LAUNCH(moe::launch_row_norms(router.data, d->n_experts, d->d_model, wn, st), "row_norms");
     moe::LogitsArgs la{x, router.data, d->T, d->n_experts, d->d_model,
                        moe::router_logit_splits(d->T, d->n_experts, d->d_model), s};
     MOE_LAUNCH(moe::launch_router_logits(la, st), "router_logits");
-    mk(1);
+    mk.end(0, st);
+    mk.beg(1, st);
     moe::SelectArgs sa{s, x, router.data, bias, xn, wn, d->T, d->n_experts, d->d_model,
                        d->top_k, idx, gate};
     MOE_LAUNCH(moe::launch_router_select(sa, st), "router_select");
+    mk.end(1, st);
     return MOE_OK;
   }
   moe::RouterArgs ra{x, d->act_dtype, router.data, d->dense_w_dtype, bias, d->T, d->d_model,
                      d->n_experts, s, key};
-  mk(0);
+  mk.beg(0, st);
   MOE_LAUNCH(moe::launch_router(ra, st), "router");
-  mk(1);
+  mk.end(0, st);
+  mk.beg(1, st);
   moe::TopkArgs ta{s, key, d->T, d->n_experts, d->top_k, idx, gate};
   MOE_LAUNCH(moe::launch_topk(ta, st), "topk");
+  mk.end(1, st);
   return MOE_OK;
 }
 
@@ -312,15 +321,16 @@ int do_latent_down(const moe_desc_t* d, const void* x, moe_w_t w, void* z, float
 int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const int32_t* offsets,
                const moe_weights_t* w, void* o_perm, int32_t* tile_off, int32_t* tile_info, void* H,
                hipStream_t st,
-               Marker mk = {-1, nullptr}) {
+               Marker mk = {-1}) {
   const int bm = moe::grouped_bm(d->act_dtype, (int64_t)d->T * d->top_k, d->n_experts);
   const int mt = max_tiles(d);
   const int rows_cap = d->T * d->top_k;
-  mk(4);
+  mk.beg(4, st);
   if (d->T > 0)
     MOE_LAUNCH(moe::launch_tile_table(offsets, d->n_experts, bm, tile_off, tile_info, st),
                "tile_table");
-  mk(5);
+  mk.end(4, st);
+  mk.beg(5, st);
   moe::GroupedGluArgs g{};
   g.Z = z; g.ldz = d->d_latent; g.T = d->T; g.rows_cap = rows_cap;
   g.perm_src = perm; g.topk = d->top_k; g.offsets = offsets; g.tile_off = tile_off;
@@ -331,7 +341,8 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
   g.E = d->n_experts; g.F = d->d_ff; g.K = d->d_latent;
   g.H = H; g.c = d->situ_c; g.act_dtype = d->act_dtype; g.bm = bm;
   if (d->T > 0) MOE_LAUNCH(moe::launch_grouped_glu(g, st), "expert_gate_up");
-  mk(6);
+  mk.end(5, st);
+  mk.beg(6, st);
   moe::GroupedDownArgs dn{};
   dn.H = H; dn.ldh = d->d_ff; dn.rows_cap = rows_cap;
   dn.offsets = offsets; dn.tile_off = tile_off; dn.tile_info = tile_info; dn.max_tiles = mt;
@@ -339,6 +350,7 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
   dn.E = d->n_experts; dn.N = d->d_latent; dn.K = d->d_ff;
   dn.O = o_perm; dn.act_dtype = d->act_dtype; dn.bm = bm;
   if (d->T > 0) MOE_LAUNCH(moe::launch_grouped_down(dn, st), "expert_down");
+  mk.end(6, st);
   return MOE_OK;
 }
 
@@ -350,22 +362,34 @@ int do_combine(const moe_desc_t* d, const void* o_perm, const int32_t* inv, cons
   return MOE_OK;
 }
 
-int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weights_t* w, void* y,
-              void* Hs, float* P, hipStream_t st, Marker mk = {-1, nullptr}) {
-  mk(8);
+// Shared experts' gate/up + SiTU-GLU: Hs = act(x W_g^s^T, x W_v^s^T), all S at once.
+int do_shared_glu(const moe_desc_t* d, const void* x, const moe_weights_t* w, void* Hs, float* P,
+                  hipStream_t st, Marker mk = {-1}) {
+  const int S = d->n_shared, Fs = d->d_ff_shared, D = d->d_model;
+  mk.beg(8, st);
+  if (S == 0) {
+    mk.end(8, st);
+    return MOE_OK;
+  }
+  moe::GluArgs g{};
+  g.A = x; g.lda = D;
+  g.Wg = wop(w->sh_gate, d->dense_w_dtype);
+  g.Wv = wop(w->sh_up, d->dense_w_dtype);
+  g.M = d->T; g.F = S * Fs; g.K = D;
+  g.H = Hs; g.ldh = (int64_t)S * Fs; g.c = d->situ_c; g.act_dtype = d->act_dtype;
+  g.split = shared_split(d); g.P = P;
+  MOE_LAUNCH(moe::launch_glu(g, st), "shared_gate_up");
+  mk.end(8, st);
+  return MOE_OK;
+}
+
+// y = sum_s Hs_s W_o^s^T + n W_up^T: one GEMM whose K runs over the shared
+// experts' down projections and then W_up.
+int do_output_gemm(const moe_desc_t* d, const void* n, const moe_weights_t* w, void* y,
+                   const void* Hs, float* P, hipStream_t st, Marker mk = {-1}) {
+  mk.beg(9, st);
   const int S = d->n_shared, Fs = d->d_ff_shared, D = d->d_model;
   const size_t eb = elem_bytes(d->act_dtype);
-  if (S > 0) {
-    moe::GluArgs g{};
-    g.A = x; g.lda = D;
-    g.Wg = wop(w->sh_gate, d->dense_w_dtype);
-    g.Wv = wop(w->sh_up, d->dense_w_dtype);
-    g.M = d->T; g.F = S * Fs; g.K = D;
-    g.H = Hs; g.ldh = (int64_t)S * Fs; g.c = d->situ_c; g.act_dtype = d->act_dtype;
-    g.split = shared_split(d); g.P = P;
-    MOE_LAUNCH(moe::launch_glu(g, st), "shared_gate_up");
-  }
-  mk(9);
   moe::MultiSegArgs m{};
   for (int s = 0; s < S; ++s) {
     m.seg[s].A = (const char*)Hs + (size_t)s * Fs * eb;
@@ -381,7 +405,54 @@ int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weigh
   m.nseg = S + 1;
   m.M = d->T; m.N = D; m.C = y; m.ldc = D; m.act_dtype = d->act_dtype; m.P = P;
   MOE_LAUNCH(moe::launch_multiseg(m, st), "output");
-  mk(10);
+  mk.end(9, st);
+  return MOE_OK;
+}
+
+int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weights_t* w, void* y,
+              void* Hs, float* P, hipStream_t st) {
+  MOE_CHECK(do_shared_glu(d, x, w, Hs, P, st));
+  return do_output_gemm(d, n, w, y, Hs, P, st);
+}
+
+// A second stream per device for the work of moe_layer_forward that does not
+// depend on the routing (latent down, shared experts' gate/up): forked from
+// and joined back into the caller's stream with events, so the caller sees one
+// stream-ordered call. Created on first use (default priority), kept for the
+// life of the process; `mu` serialises the fork / join of concurrent callers.
+struct SideStream {
+  std::mutex mu;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_init;
+
+int side_stream(SideStream** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail((int)e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_side_init);
+  SideStream& sd = g_side[dev];
+  if (sd.s == nullptr) {
+    hipStream_t s = nullptr;
+    hipEvent_t f = nullptr, j = nullptr;
+    e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      if (j) hipEventDestroy(j);
+      if (f) hipEventDestroy(f);
+      if (s) hipStreamDestroy(s);
+      return hip_fail((int)e, "side stream");
+    }
+    sd.fork = f;
+    sd.join = j;
+    sd.s = s;
+  }
+  *out = &sd;
   return MOE_OK;
 }
 
@@ -428,7 +499,7 @@ int moe_trace_enable(int max_calls) {
   g_trace.ev.clear();
   g_trace.max_calls = 0;
   g_trace.used = 0;
-  const size_t n = (size_t)max_calls * (MOE_TRACE_STAGES + 1);
+  const size_t n = (size_t)max_calls * kTraceEvents;
   g_trace.ev.resize(n);
   for (size_t i = 0; i < n; ++i) {
     hipError_t e = hipEventCreate(&g_trace.ev[i]);
@@ -449,12 +520,12 @@ int moe_trace_read(float* ms, int max_stages, int* ncalls) {
   const int ns = max_stages < MOE_TRACE_STAGES ? max_stages : MOE_TRACE_STAGES;
   for (int i = 0; i < ns; ++i) ms[i] = 0.0f;
   for (int c = 0; c < used; ++c) {
-    hipEvent_t* ev = &g_trace.ev[(size_t)c * (MOE_TRACE_STAGES + 1)];
-    hipError_t e = hipEventSynchronize(ev[MOE_TRACE_STAGES]);
-    if (e != hipSuccess) return hip_fail((int)e, "trace_read");
+    hipEvent_t* ev = &g_trace.ev[(size_t)c * kTraceEvents];
     for (int i = 0; i < ns; ++i) {
+      hipError_t e = hipEventSynchronize(ev[2 * i + 1]);
+      if (e != hipSuccess) return hip_fail((int)e, "trace_read");
       float t = 0.0f;
-      e = hipEventElapsedTime(&t, ev[i], ev[i + 1]);
+      e = hipEventElapsedTime(&t, ev[2 * i], ev[2 * i + 1]);
       if (e != hipSuccess) return hip_fail((int)e, "trace_read");
       ms[i] += t / (float)used;
     }
@@ -606,19 +677,31 @@ int moe_layer_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x
   int32_t* offsets = (int32_t*)at(ws, lw.offsets);
   int32_t* perm = (int32_t*)at(ws, lw.perm);
   int32_t* inv = (int32_t*)at(ws, lw.inv);
-  const Marker mk{trace_begin(), st};
+  SideStream* sd = nullptr;
+  MOE_CHECK(side_stream(&sd));
+  std::lock_guard<std::mutex> lk(sd->mu);
+  const Marker mk{trace_begin()};
+  // side stream: the routing-independent GEMMs (z and the shared experts' H)
+  MOE_LAUNCH((int)hipEventRecord(sd->fork, st), "fork");
+  MOE_LAUNCH((int)hipStreamWaitEvent(sd->s, sd->fork, 0), "fork");
+  mk.beg(3, sd->s);
+  MOE_CHECK(do_latent_down(d, x, w->lat_down, at(ws, lw.z), (float*)at(ws, lw.P), sd->s));
+  mk.end(3, sd->s);
+  MOE_CHECK(do_shared_glu(d, x, w, at(ws, lw.Hs), (float*)at(ws, lw.P), sd->s, mk));
+  MOE_LAUNCH((int)hipEventRecord(sd->join, sd->s), "join");
+  // caller's stream: routing and permutation, then (after the join) the experts
   MOE_CHECK(do_route(d, x, w->router, w->router_bias, idx, gate, (float*)at(ws, lw.s),
                      (float*)at(ws, lw.key), (float*)at(ws, lw.norms), false, st, mk));
-  mk(2);
+  mk.beg(2, st);
   MOE_CHECK(do_permute(d, idx, counts, offsets, perm, inv, (int32_t*)at(ws, lw.blk), st));
-  mk(3);
-  MOE_CHECK(do_latent_down(d, x, w->lat_down, at(ws, lw.z), (float*)at(ws, lw.P), st));
+  mk.end(2, st);
+  MOE_LAUNCH((int)hipStreamWaitEvent(st, sd->join, 0), "join");
   MOE_CHECK(do_experts(d, at(ws, lw.z), perm, offsets, w, at(ws, lw.O), (int32_t*)at(ws, lw.tile_off),
-                       (int32_t*)at(ws, lw.tile_info),
-                       at(ws, lw.H), st, mk));
-  mk(7);
+                       (int32_t*)at(ws, lw.tile_info), at(ws, lw.H), st, mk));
+  mk.beg(7, st);
   MOE_CHECK(do_combine(d, at(ws, lw.O), inv, gate, w->rms_gain, at(ws, lw.n), nullptr, st));
-  MOE_CHECK(do_output(d, x, at(ws, lw.n), w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), st, mk));
+  mk.end(7, st);
+  MOE_CHECK(do_output_gemm(d, at(ws, lw.n), w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), st, mk));
   return MOE_OK;
 }
 
