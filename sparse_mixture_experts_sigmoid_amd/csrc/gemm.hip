@@ -607,6 +607,24 @@ __device__ __forceinline__ bool xcd_item(int64_t live, int64_t& L) {
   return L < live;
 }
 
+// Tile order of a dense GEMM with mtn x ntn tiles: groups of kGroupM row
+// tiles, and inside a group n-tile major, so the blocks that run together on
+// one XCD (a contiguous run of work items) share a few A row tiles and a few B
+// column tiles instead of one A tile and many B tiles: both stay in that XCD's
+// L2 while the blocks walk K side by side.
+// (The output GEMM, whose K runs over several segments, keeps row-major order:
+// GM = 1.)
+template <int GM>
+__device__ __forceinline__ void dense_tile(int64_t L, int mtn, int ntn, int& mt, int& nt) {
+  const int64_t per = (int64_t)GM * ntn;
+  const int g = (int)(L / per);
+  const int rows = min(GM, mtn - g * GM);   // row tiles in this group
+  const int r = (int)(L - (int64_t)g * per);
+  nt = r / rows;
+  mt = g * GM + r % rows;
+}
+constexpr int kGroupM = 8;
+
 // ---------------------------------------------------------------------------
 // kernels
 // ---------------------------------------------------------------------------
@@ -618,7 +636,9 @@ __global__ __launch_bounds__(DenseCfg::NT) void dense_kernel(DenseArgs a) {
   const int ntn = (int)ceil_div(a.N, C::BN);
   int64_t L;
   if (!xcd_item(ceil_div(a.M, C::BM) * ntn, L)) return;
-  const int m0 = (int)(L / ntn) * C::BM, n0 = (int)(L % ntn) * C::BN;
+  int mt, nt;
+  dense_tile<kGroupM>(L, (int)ceil_div(a.M, C::BM), ntn, mt, nt);
+  const int m0 = mt * C::BM, n0 = nt * C::BN;
   const Rows<C::AR> ar = a_rows_dense<C, C::AR>(a.A, a.lda, m0, a.M);
   Acc<C> acc;
   acc_zero(acc);
@@ -637,7 +657,9 @@ __global__ __launch_bounds__(DenseCfg::NT) void glu_kernel(GluArgs a) {
   const int ntn = (int)ceil_div(a.F, C::BN / 2);
   int64_t L;
   if (!xcd_item(ceil_div(a.M, C::BM) * ntn, L)) return;
-  const int m0 = (int)(L / ntn) * C::BM, f0 = (int)(L % ntn) * (C::BN / 2);
+  int mt, nt;
+  dense_tile<kGroupM>(L, (int)ceil_div(a.M, C::BM), ntn, mt, nt);
+  const int m0 = mt * C::BM, f0 = nt * (C::BN / 2);
   const Rows<C::AR> ar = a_rows_dense<C, C::AR>(a.A, a.lda, m0, a.M);
   Acc<C> acc;
   acc_zero(acc);
@@ -745,7 +767,9 @@ __global__ __launch_bounds__(DenseCfg::NT) void multiseg_kernel(MultiSegArgs a) 
   const int ntn = (int)ceil_div(a.N, C::BN);
   int64_t L;
   if (!xcd_item(ceil_div(a.M, C::BM) * ntn, L)) return;
-  const int m0 = (int)(L / ntn) * C::BM, n0 = (int)(L % ntn) * C::BN;
+  int mt, nt;
+  dense_tile<1>(L, (int)ceil_div(a.M, C::BM), ntn, mt, nt);
+  const int m0 = mt * C::BM, n0 = nt * C::BN;
   Acc<C> acc;
   acc_zero(acc);
   const int nplain = LAST_MX ? a.nseg - 1 : a.nseg;
