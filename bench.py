@@ -19,14 +19,22 @@ algorithmic bytes per launch = (touched experts) x 2*F*d_lat*2 B (W_g and W_v)
 + (T*k routed rows) x (d_lat + F)*2 B (gathered z rows in, h rows out).
 Prefill: the same kernel is MFMA-bound; flops per launch = T*k*2*2*d_lat*F.
 
+roofline.traffic: HBM bytes per launch of that kernel from rocprofv3 PMC
+counters (FETCH_SIZE and WRITE_SIZE, each scaled by what the counter reads for
+a plain copy of known size), as recorded in profiles/hbm_traffic.md together
+with the hash of the GEMM source they were taken on; null when that source has
+changed since.
+
 cpu_baseline: the CPU oracle (never tuned) on a bounded token sample of the
 same workload, on this host's cores.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -72,6 +80,25 @@ def copy_probe(gb: float, steps: int):
     print(json.dumps({"probe": "device copy", "bytes_read_per_launch": n,
                       "bytes_written_per_launch": n, "ms_per_launch": round(ms, 4),
                       "read_plus_write_GBps": round(2 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
+GEMM_SRC = os.path.join(ROOT, "sparse_mixture_experts_sigmoid_amd", "csrc", "gemm.hip")
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel recorded for `workload`, or
+    None if not recorded or recorded on another version of the GEMM source."""
+    try:
+        text = open(TRAFFIC_MD).read()
+        sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    m = re.search(r"traffic-record workload=%s kernel=\S+ gemm_sha=(\w+) bytes=(\d+)" % re.escape(workload),
+                  text)
+    if not m or m.group(1) != sha:
+        return None
+    return int(m.group(2))
 
 
 def log(args, *a):
@@ -165,14 +192,15 @@ def main():
         achieved = algo / t_gu / 1e9
         roof = {"bound": "hbm", "kernel": "expert_gate_up (grouped GEMM + SiTU-GLU)",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name),
                 "algorithmic_bytes_per_launch": int(algo), "avg_launch_ms": round(t_gu * 1e3, 4)}
     else:
         algo = rows * 2 * 2 * cfg.d_lat * cfg.F
         achieved = algo / t_gu / 1e12
         roof = {"bound": "mfma", "kernel": "expert_gate_up (grouped GEMM + SiTU-GLU)",
                 "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": measured_traffic(cfg.name),
                 "algorithmic_flops_per_launch": int(algo), "avg_launch_ms": round(t_gu * 1e3, 4)}
 
     touched_bytes = touched * 3 * cfg.F * cfg.d_lat * wbytes
