@@ -189,6 +189,24 @@ int moe_layer_forward(const moe_desc_t* desc, const moe_weights_t* w, const void
                       int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* counts_opt,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* Quantile Balancing: the per-expert selection bias from quantiles of the
+   router scores ("Kimi K3の896エキスパートを「896人の専門家」と呼ぶと何がズレるか",
+   section "ルーター専用の独立訓練はない": the boundary at which each expert
+   receives its target number of tokens is a quantile of its score
+   distribution, and the selection bias is updated from it; "Kimi K3
+   テクニカルレポート", section "幅のスケーリング: Stable LatentMoE": quantiles
+   taken directly from score histograms). For a batch of T = desc->T tokens
+   and target c = round(T k / E) (ties up, clamped to [1, T]):
+     quantile_out[e] = the c-th largest scores[t][e] over t   (exact),
+     tau             = fp32(sum_e quantile_out[e] / E)         (fp64 sum, e ascending),
+     bias_out[e]     = fp32(tau - quantile_out[e]).
+   scores [T, E] fp32 (the unbiased sigmoid scores, e.g. moe_route's scores
+   output), bias_out [E] and quantile_out [E] fp32: device pointers owned by
+   the caller. T must be > 0 (MOE_ERR_INVALID_ARG otherwise). Non-finite
+   scores are not supported. Asynchronous on stream; allocates nothing. */
+int moe_qb_bias(const moe_desc_t* desc, const float* scores, float* bias_out, float* quantile_out,
+                void* stream);
+
 /* Stage tracing. moe_trace_enable(max_calls) makes the next max_calls calls of
    moe_layer_forward record a HIP event before and after each stage, on the
    stream the stage runs on (max_calls = 0 turns tracing off). moe_trace_read

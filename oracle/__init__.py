@@ -193,6 +193,35 @@ def permute(idx: np.ndarray, E: int):
 # fp64 forward
 # --------------------------------------------------------------------------
 
+def qb_target(T: int, E: int, k: int) -> int:
+    """Target tokens per expert: round(T k / E) (ties up), clamped to [1, T]."""
+    c = (T * k + E // 2) // E
+    return max(1, min(T, c))
+
+
+def qb_bias(scores: np.ndarray, k: int):
+    """Quantile Balancing ("Kimi K3の896エキスパートを「896人の専門家」と呼ぶと何が
+    ズレるか", section "ルーター専用の独立訓練はない"; "Kimi K3 テクニカルレポート",
+    section "幅のスケーリング: Stable LatentMoE"): each expert's boundary is the
+    quantile of its score distribution at which it receives its target number
+    of tokens, and the selection bias is set from it.
+
+    scores [T, E] float32 -> (q [E], b [E]) float32: q[e] = the c-th largest
+    scores[:, e] (c = qb_target), tau = fp32(sequential fp64 sum of q over e
+    ascending / E), b[e] = fp32(tau - q[e])."""
+    T, E = scores.shape
+    c = qb_target(T, E, k)
+    q = np.empty(E, np.float32)
+    for e in range(E):
+        q[e] = np.sort(scores[:, e])[::-1][c - 1]
+    total = 0.0
+    for e in range(E):
+        total += float(q[e])
+    tau = np.float32(total / E)
+    b = (tau - q).astype(np.float32)
+    return q, b
+
+
 def linear(A: np.ndarray, W: np.ndarray) -> np.ndarray:
     """A [n, K] (fp64) times W^T, W [N, K] fp32 -> [n, N] fp64 (plain sums)."""
     A = _c(A, np.float64)

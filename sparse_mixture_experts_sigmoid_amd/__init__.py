@@ -28,7 +28,7 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
 EXPORTS = ["moe_workspace_bytes", "moe_check_desc", "moe_route", "moe_permute", "moe_latent_down",
            "moe_expert_ffn", "moe_combine", "moe_output", "moe_layer_forward",
            "moe_status_string", "moe_last_error", "moe_trace_enable", "moe_trace_read",
-           "moe_trace_stage_name"]
+           "moe_trace_stage_name", "moe_qb_bias"]
 MOE_TRACE_STAGES = 10
 
 
@@ -81,6 +81,7 @@ def lib():
         "moe_trace_enable": ([i32], i32),
         "moe_trace_read": ([ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(ctypes.c_int)], i32),
         "moe_trace_stage_name": ([i32], ctypes.c_char_p),
+        "moe_qb_bias": ([D, vp, vp, vp, vp], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -206,6 +207,12 @@ def moe_layer_forward(desc, weights: dict, x, y, topk_idx=None, topk_gate=None, 
     _check(lib().moe_layer_forward(ctypes.byref(desc), ctypes.byref(w), _ptr(x), _ptr(y),
                                    _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), p, n,
                                    _stream(stream)))
+
+
+def moe_qb_bias(desc, scores, bias_out, quantile_out, stream=None):
+    """Quantile Balancing bias from router scores [T, E] (fp32 device tensors)."""
+    _check(lib().moe_qb_bias(ctypes.byref(desc), _ptr(scores), _ptr(bias_out), _ptr(quantile_out),
+                             _stream(stream)))
 
 
 def moe_trace_enable(max_calls: int):

@@ -643,6 +643,20 @@ int moe_output(const moe_desc_t* d, const void* x, const void* n, const moe_weig
   return do_output(d, x, n, w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), (hipStream_t)stream);
 }
 
+int moe_qb_bias(const moe_desc_t* d, const float* scores, float* bias_out, float* quantile_out,
+                void* stream) {
+  g_last_error.clear();
+  MOE_CHECK(check_desc(d));
+  if (d->T == 0) return fail(MOE_ERR_INVALID_ARG, "moe_qb_bias needs T > 0");
+  MOE_CHECK(need_ptr(scores, "scores"));
+  MOE_CHECK(need_ptr(bias_out, "bias_out"));
+  MOE_CHECK(need_ptr(quantile_out, "quantile_out"));
+  MOE_LAUNCH(moe::launch_qb_bias(scores, d->T, d->n_experts, d->top_k, quantile_out, bias_out,
+                                 (hipStream_t)stream),
+             "qb_bias");
+  return MOE_OK;
+}
+
 int moe_layer_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
                       int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* counts_opt, void* ws,
                       size_t ws_bytes, void* stream) {

@@ -177,6 +177,13 @@ int launch_grouped_glu_f32(const GroupedGluArgs& a, hipStream_t stream);
 int launch_grouped_down_f32(const GroupedDownArgs& a, hipStream_t stream);
 int launch_multiseg_f32(const MultiSegArgs& a, hipStream_t stream);
 
+// Quantile Balancing bias: q[e] = the c-th largest scores[t][e] over t with
+// c = qb_target(T, E, k); bias[e] = fp32(tau - q[e]), tau = fp32(mean of q)
+// (fp64 sum, e ascending). T > 0.
+int qb_target(int T, int E, int k);
+int launch_qb_bias(const float* scores, int T, int E, int k, float* q, float* bias,
+                   hipStream_t stream);
+
 // Combine + RMSNorm.
 struct CombineArgs {
   const void* O;                 // [T*k, D] act dtype, permuted rows

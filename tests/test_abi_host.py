@@ -189,3 +189,14 @@ def test_trace_read_argument_checks():
     L = moe.lib()
     assert L.moe_trace_read(None, 3, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_trace_enable(-1) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_qb_bias_validates_before_any_launch():
+    L = moe.lib()
+    d = moe.make_desc(synth.config("k3_prefill"))
+    assert L.moe_qb_bias(ctypes.byref(d), None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_qb_bias(ctypes.byref(d), FAKE, MIS, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_qb_bias(ctypes.byref(d), FAKE, FAKE, None, None) == moe.MOE_ERR_INVALID_ARG
+    d0 = moe.make_desc(synth.config("k3_prefill").replace(T=0))
+    assert L.moe_qb_bias(ctypes.byref(d0), FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert b"T > 0" in L.moe_last_error()

@@ -409,3 +409,58 @@ def test_k3_table_shapes():
     per_layer2 = (cfg.E * 2 * cfg.d_lat * cfg.F + cfg.S * 2 * cfg.d * cfg.Fs
                   + 2 * cfg.d * cfg.d_lat + cfg.E * cfg.d)
     assert abs(t["layers"] * per_layer2 - t["total_params"]) / t["total_params"] > 0.3
+
+
+# ---------------------------------------------------------------------------
+# Quantile Balancing bias
+# ---------------------------------------------------------------------------
+
+def test_qb_target_hand_values():
+    # 16384 tokens x top-16 over 896 experts: 292.57 tokens per expert -> 293
+    assert oracle.qb_target(16384, 896, 16) == 293
+    assert oracle.qb_target(64, 32, 4) == 8          # exactly 8
+    assert oracle.qb_target(1, 4, 2) == 1            # 0.5 rounds up
+    assert oracle.qb_target(3, 1, 1) == 3            # one expert takes every token
+    assert oracle.qb_target(2, 64, 1) == 1           # never below one token
+
+
+@pytest.mark.parametrize("T,E,k,grid", [(50, 7, 3, None), (40, 5, 2, 8), (9, 3, 1, 2), (1, 4, 4, None)])
+def test_qb_quantile_is_the_order_statistic(T, E, k, grid):
+    """q[e] is the c-th largest score: fewer than c scores lie strictly above
+    it and at least c lie at or above it (checked by counting, with heavy ties
+    when the scores sit on a coarse grid)."""
+    rng = np.random.default_rng(T * 100 + E)
+    s = rng.random((T, E)).astype(np.float32)
+    if grid:
+        s = (np.floor(s * grid) / grid + 1.0 / (2 * grid)).astype(np.float32)
+    q, b = oracle.qb_bias(s, k)
+    c = oracle.qb_target(T, E, k)
+    for e in range(E):
+        above = int((s[:, e] > q[e]).sum())
+        at_or_above = int((s[:, e] >= q[e]).sum())
+        assert above < c <= at_or_above, (e, above, c, at_or_above)
+        assert q[e] in s[:, e]
+
+
+def test_qb_bias_centred_and_shifts_quantiles_to_one_boundary():
+    rng = np.random.default_rng(7)
+    s = (1.0 / (1.0 + np.exp(-rng.standard_normal((300, 40))))).astype(np.float32)
+    q, b = oracle.qb_bias(s, 4)
+    tau = np.float32(sum(float(v) for v in q) / 40)
+    # every expert's boundary lands on the common value tau (up to one rounding)
+    assert np.all(np.abs((q + b).astype(np.float64) - float(tau)) <= np.spacing(np.float32(1.0)))
+    assert abs(float(b.astype(np.float64).mean())) < 1e-6
+    # experts with higher quantiles get lower bias, in the same order
+    assert np.array_equal(np.argsort(q, kind="stable"), np.argsort(-b, kind="stable"))
+
+
+def test_qb_hand_example():
+    # 4 tokens, 2 experts, k = 1: target round(4/2) = 2 tokens per expert
+    s = np.array([[0.9, 0.1], [0.8, 0.2], [0.7, 0.6], [0.3, 0.4]], np.float32)
+    q, b = oracle.qb_bias(s, 1)
+    assert q.tolist() == [np.float32(0.8), np.float32(0.4)]
+    tau = np.float32((float(np.float32(0.8)) + float(np.float32(0.4))) / 2)
+    assert b.tolist() == [np.float32(tau - np.float32(0.8)), np.float32(tau - np.float32(0.4))]
+    # with the bias, each expert's top-2 scores are the ones at or above its boundary
+    key = s + b
+    assert ((key >= tau).sum(axis=0) == 2).all()
