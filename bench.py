@@ -43,6 +43,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix (the scaled MXFP8 x MXFP4 expert path)
 METRIC = "tokens/s per K3-shape LatentMoE layer; % MFMA peak (prefill), % HBM BW (decode)"
 
 
@@ -197,9 +198,13 @@ def main():
     else:
         algo = rows * 2 * 2 * cfg.d_lat * cfg.F
         achieved = algo / t_gu / 1e12
-        roof = {"bound": "mfma", "kernel": "expert_gate_up (grouped GEMM + SiTU-GLU)",
-                "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+        mx8 = cfg.expert_act == "mxfp8"
+        peak = MFMA_FP8_PEAK_TFLOPS if mx8 else MFMA_BF16_PEAK_TFLOPS
+        roof = {"bound": "mfma",
+                "kernel": ("expert_gate_up (MXFP8 quantise of z + scaled-MFMA grouped GEMM + SiTU-GLU)"
+                           if mx8 else "expert_gate_up (grouped GEMM + SiTU-GLU)"),
+                "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4),
                 "traffic": measured_traffic(cfg.name),
                 "algorithmic_flops_per_launch": int(algo), "avg_launch_ms": round(t_gu * 1e3, 4)}
 
@@ -219,12 +224,14 @@ def main():
     out = {
         "metric": METRIC, "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.act,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "mxfp8 x mxfp4 experts, bf16 rest" if cfg.expert_act == "mxfp8" else cfg.act,
         "data": "synthetic: seeded counter-based N(0,1) activations and N(0,1/fan_in) "
                 "random-init weights of the K3 layer shape (no checkpoint)",
         "config": {"workload": f"{cfg.name}: T={cfg.T} d={cfg.d} d_lat={cfg.d_lat} E={cfg.E} "
                                f"k={cfg.k} F={cfg.F} S={cfg.S} Fs={cfg.Fs} act={cfg.act} "
-                               f"expert_w={cfg.expert_w} latent_w={cfg.latent_w}",
+                               f"expert_w={cfg.expert_w} latent_w={cfg.latent_w}"
+                               + (" expert_act=mxfp8" if cfg.expert_act == "mxfp8" else ""),
                    "tokens": cfg.T, "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": base,

@@ -91,6 +91,14 @@ typedef struct {
   int32_t expert_w_dtype; /* W_g, W_v, W_o */
   int32_t latent_w_dtype; /* W_ld, W_lu */
   int32_t dense_w_dtype;  /* W_r, W_gs, W_vs, W_os */
+  /* 0: the routed experts' GEMMs take z and h in act_dtype (bf16 MFMA on the
+     decoded weights). 1: they take z and h quantised to MXFP8 (OCP MX, E4M3
+     elements with one e8m0 scale per 32 along K: X = floor(log2 amax) - 8,
+     round to nearest even, saturating) and run on gfx950's scaled MFMA
+     (MXFP8 x MXFP4); needs act_dtype MOE_BF16, expert_w_dtype MOE_MXFP4 and
+     d_latent, d_ff multiples of 128. Changes the numerics (the oracle quantises
+     the same way). */
+  int32_t expert_act_mxfp8;
 } moe_desc_t;
 
 /* A weight tensor: data (dtype of its class) and, for MXFP4 only, scales. */
@@ -188,6 +196,18 @@ int moe_output(const moe_desc_t* desc, const void* x, const void* n, const moe_w
 int moe_layer_forward(const moe_desc_t* desc, const moe_weights_t* w, const void* x, void* y,
                       int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* counts_opt,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* MXFP8 quantisation of bf16 rows, the activation format of the scaled-MFMA
+   expert path (expert_act_mxfp8; the MX format of "Kimi K3 ... Open Frontier
+   Intelligence", section "MXFP4 Quantization-Aware Training", with 8-bit E4M3
+   elements): x [rows, K] bf16 with row stride ld elements, K % 32 == 0 ->
+   codes [rows, K] E4M3 bytes and scales [rows, K/32] e8m0 bytes, per block of
+   32: X = floor(log2 amax) - 8 clamped to [-127, 127] (amax = 0: -127), byte
+   X + 127; code = E4M3 nearest to v / 2^X (ties to even), saturating at
+   +-448, sign bit when v < 0. Device pointers owned by the caller;
+   asynchronous on stream; allocates nothing. */
+int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, int64_t ld, uint8_t* codes,
+                       uint8_t* scales, void* stream);
 
 /* Quantile Balancing: the per-expert selection bias from quantiles of the
    router scores ("Kimi K3の896エキスパートを「896人の専門家」と呼ぶと何がズレるか",

@@ -193,6 +193,72 @@ def permute(idx: np.ndarray, E: int):
 # fp64 forward
 # --------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# MXFP8 (OCP MX, E4M3 elements) activations for the scaled-MFMA expert path
+# ("Kimi K3 ... Open Frontier Intelligence", section "MXFP4 Quantization-Aware
+# Training": 4-bit MX weights; the matrix cores that take MX weights also take
+# the activations in an MX format, here 8-bit E4M3 with one power-of-two scale
+# per 32 elements along K)
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP FP8 E4M3 code (bias 7; exponent field 0 = subnormal;
+    0x7F / 0xFF are NaN)."""
+    s, e, m = code >> 7, (code >> 3) & 15, code & 7
+    if e == 15 and m == 7:
+        return float("nan")
+    v = (m / 8.0) * 2.0 ** -6 if e == 0 else (1 + m / 8.0) * 2.0 ** (e - 7)
+    return -v if s else v
+
+
+def _exp2_floor(a: np.ndarray) -> np.ndarray:
+    """floor(log2 |a|) of nonzero finite values (numpy frexp: a = f 2^e, 0.5 <= |f| < 1)."""
+    return np.frexp(a)[1].astype(np.int64) - 1
+
+
+def mx8_quantize(a: np.ndarray):
+    """Rows of K values (K % 32 == 0) -> (E4M3 codes uint8 [rows, K], e8m0 scale
+    bytes uint8 [rows, K/32]). Per 32-element block: X = floor(log2 amax) - 8
+    (8 = the largest E4M3 exponent), clamped to [-127, 127], amax = 0 gives
+    X = -127; byte = X + 127. Element: y = v / 2^X (exact), rounded to nearest
+    even on the E4M3 grid, saturating at +-448; sign bit set when v < 0."""
+    a = np.asarray(a, dtype=np.float64)
+    rows, K = a.shape
+    blk = a.reshape(rows, K // 32, 32)
+    amax = np.abs(blk).max(axis=2)
+    X = np.full(amax.shape, -127, np.int64)
+    nz = amax > 0
+    X[nz] = np.clip(_exp2_floor(amax[nz]) - 8, -127, 127)
+    y = np.abs(blk) * np.ldexp(1.0, -X)[..., None]
+    code = np.zeros(y.shape, np.int64)
+    sub = y < 2.0 ** -6
+    # subnormal range: multiples of 2^-9 (q = 8 is the first normal, code 0x08)
+    code[sub] = np.rint(y[sub] * 2.0 ** 9).astype(np.int64)
+    nrm = ~sub
+    e = _exp2_floor(np.where(nrm, y, 1.0))
+    m = np.rint((y * np.ldexp(1.0, -e) - 1.0) * 8.0).astype(np.int64)
+    carry = m == 8
+    e = np.where(carry, e + 1, e)
+    m = np.where(carry, 0, m)
+    code_n = ((e + 7) << 3) | m
+    code_n = np.where((y >= E4M3_MAX) | (code_n > 0x7E), 0x7E, code_n)
+    code[nrm] = code_n[nrm]
+    code = code | np.where(blk < 0, 0x80, 0)
+    return code.reshape(rows, K).astype(np.uint8), (X + 127).astype(np.uint8)
+
+
+def mx8_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """E4M3 codes [rows, K] with e8m0 bytes [rows, K/32] -> float64 values."""
+    table = np.array([e4m3_value(c) for c in range(256)], np.float64)
+    rows, K = codes.shape
+    v = table[codes.astype(np.int64)].reshape(rows, K // 32, 32)
+    v = v * np.ldexp(1.0, scales.astype(np.int64) - 127)[..., None]
+    return v.reshape(rows, K)
+
+
 def qb_target(T: int, E: int, k: int) -> int:
     """Target tokens per expert: round(T k / E) (ties up), clamped to [1, T]."""
     c = (T * k + E // 2) // E
@@ -320,7 +386,10 @@ def forward(cfg, w, tokens=None, routing=None, keep=False):
     # z = W_down x, stored
     z = store(linear(X, widen(w.raw("W_ld"))), storage)
 
-    # routed experts, expert by expert: o[t, j] = W_o[e] act(W_g[e] z_t, W_v[e] z_t)
+    # routed experts, expert by expert: o[t, j] = W_o[e] act(W_g[e] z_t, W_v[e] z_t);
+    # with MXFP8 expert inputs, z rows and h rows are quantised first (the same
+    # codes the scaled-MFMA path multiplies)
+    mx_act = getattr(cfg, "expert_act", "act") == "mxfp8"
     o = np.zeros((n_tok, cfg.k, cfg.d_lat), dtype=np.float64)
     for e in np.unique(idx):
         rows_t, rows_j = np.nonzero(idx == e)
@@ -329,7 +398,11 @@ def forward(cfg, w, tokens=None, routing=None, keep=False):
         Wv = widen(w.raw("W_v", e * cfg.F, cfg.F))
         Wo = widen(w.raw("W_o", e * cfg.d_lat, cfg.d_lat))
         Z = z[rows_t]
+        if mx_act:
+            Z = mx8_dequantize(*mx8_quantize(Z))
         H = glu(linear(Z, Wg), linear(Z, Wv), cfg.c, storage)
+        if mx_act:
+            H = mx8_dequantize(*mx8_quantize(H))
         o[rows_t, rows_j] = store(linear(H, Wo), storage)
 
     # u = sum_j p_j o_j (slot order), n = RMSNorm(u)

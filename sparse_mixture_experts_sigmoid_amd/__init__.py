@@ -28,7 +28,7 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
 EXPORTS = ["moe_workspace_bytes", "moe_check_desc", "moe_route", "moe_permute", "moe_latent_down",
            "moe_expert_ffn", "moe_combine", "moe_output", "moe_layer_forward",
            "moe_status_string", "moe_last_error", "moe_trace_enable", "moe_trace_read",
-           "moe_trace_stage_name", "moe_qb_bias"]
+           "moe_trace_stage_name", "moe_qb_bias", "moe_quantize_mxfp8"]
 MOE_TRACE_STAGES = 10
 
 
@@ -44,7 +44,8 @@ class MoeDesc(ctypes.Structure):
                 ("n_shared", ctypes.c_int32), ("d_ff_shared", ctypes.c_int32),
                 ("situ_c", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("act_dtype", ctypes.c_int32), ("expert_w_dtype", ctypes.c_int32),
-                ("latent_w_dtype", ctypes.c_int32), ("dense_w_dtype", ctypes.c_int32)]
+                ("latent_w_dtype", ctypes.c_int32), ("dense_w_dtype", ctypes.c_int32),
+                ("expert_act_mxfp8", ctypes.c_int32)]
 
 
 class MoeW(ctypes.Structure):
@@ -82,6 +83,7 @@ def lib():
         "moe_trace_read": ([ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(ctypes.c_int)], i32),
         "moe_trace_stage_name": ([i32], ctypes.c_char_p),
         "moe_qb_bias": ([D, vp, vp, vp, vp], i32),
+        "moe_quantize_mxfp8": ([vp, ctypes.c_int64, i32, ctypes.c_int64, vp, vp, vp], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -101,7 +103,8 @@ def make_desc(cfg, T=None) -> MoeDesc:
                    n_experts=cfg.E, top_k=cfg.k, d_ff=cfg.F, n_shared=cfg.S, d_ff_shared=cfg.Fs,
                    situ_c=cfg.c, rms_eps=cfg.eps, act_dtype=DTYPES[cfg.act],
                    expert_w_dtype=DTYPES[cfg.expert_w], latent_w_dtype=DTYPES[cfg.latent_w],
-                   dense_w_dtype=DTYPES[cfg.dense_w])
+                   dense_w_dtype=DTYPES[cfg.dense_w],
+                   expert_act_mxfp8=1 if getattr(cfg, "expert_act", "act") == "mxfp8" else 0)
 
 
 def _ptr(t):
@@ -213,6 +216,13 @@ def moe_qb_bias(desc, scores, bias_out, quantile_out, stream=None):
     """Quantile Balancing bias from router scores [T, E] (fp32 device tensors)."""
     _check(lib().moe_qb_bias(ctypes.byref(desc), _ptr(scores), _ptr(bias_out), _ptr(quantile_out),
                              _stream(stream)))
+
+
+def moe_quantize_mxfp8(x, codes, scales, stream=None):
+    """MXFP8 codes [rows, K] uint8 and e8m0 scales [rows, K/32] of bf16 rows x [rows, K]."""
+    rows, K = x.shape
+    _check(lib().moe_quantize_mxfp8(_ptr(x), rows, K, x.stride(0), _ptr(codes), _ptr(scales),
+                                    _stream(stream)))
 
 
 def moe_trace_enable(max_calls: int):

@@ -11,7 +11,7 @@ OUT = os.path.join(HERE, "libmoe.so")
 BUILD = os.path.join(os.path.dirname(HERE), "_build", "moe")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["abi.hip", "router.hip", "permute.hip", "gemm.hip", "gemm_f32.hip", "combine.hip",
-           "qb.hip"]
+           "qb.hip", "mx8.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",
          "-Wall", "-Wno-unused-function",
          # packed fp32 vector ops stay off in every kernel

@@ -78,6 +78,12 @@ int check_desc(const moe_desc_t* d) {
   if (d->d_model % 32 || d->d_latent % 32 || d->d_ff % 32 ||
       (d->n_shared > 0 && d->d_ff_shared % 32))
     return fail(MOE_ERR_UNSUPPORTED, "d_model, d_latent, d_ff, d_ff_shared must be multiples of 32");
+  if (d->expert_act_mxfp8 != 0 && d->expert_act_mxfp8 != 1)
+    return fail(MOE_ERR_INVALID_ARG, "expert_act_mxfp8 must be 0 or 1");
+  if (d->expert_act_mxfp8 &&
+      (d->act_dtype != MOE_BF16 || d->expert_w_dtype != MOE_MXFP4 || d->d_latent % 128 || d->d_ff % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "MXFP8 expert activations need bf16 activations, MXFP4 expert "
+                "weights and d_latent, d_ff multiples of 128");
   if (d->n_experts > kMaxExperts)
     return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", kMaxExperts);
   if (d->n_shared + 1 > moe::kMaxSegments)
@@ -104,6 +110,7 @@ struct Plan {
 
 struct LayerWs {
   size_t s, key, norms, idx, gate, counts, offsets, perm, inv, blk, z, tile_off, tile_info, H, O, n, Hs, P;
+  size_t zq, zqs, hq, hqs;   // MXFP8 z and h (codes, scales) of the scaled-MFMA expert path
 };
 
 int max_tiles(const moe_desc_t* d) {
@@ -123,6 +130,13 @@ void plan_expert(const moe_desc_t* d, Plan& p, LayerWs& w) {
   w.tile_off = p.take((size_t)(d->n_experts + 1) * 4);
   w.tile_info = p.take((size_t)max_tiles(d) * 16);
   w.H = p.take((size_t)d->T * d->top_k * d->d_ff * elem_bytes(d->act_dtype));
+  if (d->expert_act_mxfp8) {
+    const size_t rows = (size_t)d->T * d->top_k;
+    w.zq = p.take((size_t)d->T * d->d_latent);
+    w.zqs = p.take((size_t)d->T * d->d_latent / 32);
+    w.hq = p.take(rows * d->d_ff);
+    w.hqs = p.take(rows * d->d_ff / 32);
+  }
 }
 // fp32 split-K partials of the dense GEMMs that run with few tokens
 moe::SplitK latent_split(const moe_desc_t* d) {
@@ -318,10 +332,25 @@ int do_latent_down(const moe_desc_t* d, const void* x, moe_w_t w, void* z, float
   return MOE_OK;
 }
 
+// MXFP8 copies of z and h for the scaled-MFMA expert path (workspace)
+struct MxBufs {
+  uint8_t *zq = nullptr, *zqs = nullptr, *hq = nullptr, *hqs = nullptr;
+};
+MxBufs mx_bufs(const moe_desc_t* d, void* ws, const LayerWs& lw) {
+  MxBufs m;
+  if (d->expert_act_mxfp8) {
+    m.zq = (uint8_t*)at(ws, lw.zq);
+    m.zqs = (uint8_t*)at(ws, lw.zqs);
+    m.hq = (uint8_t*)at(ws, lw.hq);
+    m.hqs = (uint8_t*)at(ws, lw.hqs);
+  }
+  return m;
+}
+
 int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const int32_t* offsets,
                const moe_weights_t* w, void* o_perm, int32_t* tile_off, int32_t* tile_info, void* H,
-               hipStream_t st,
-               Marker mk = {-1}) {
+               const MxBufs& mx, hipStream_t st, Marker mk = {-1}) {
+  const bool q8 = d->expert_act_mxfp8 != 0;
   const int bm = moe::grouped_bm(d->act_dtype, (int64_t)d->T * d->top_k, d->n_experts);
   const int mt = max_tiles(d);
   const int rows_cap = d->T * d->top_k;
@@ -331,8 +360,12 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
                "tile_table");
   mk.end(4, st);
   mk.beg(5, st);
+  if (q8 && d->T > 0)
+    MOE_LAUNCH(moe::launch_quantize_mx8(z, d->T, d->d_latent, d->d_latent, mx.zq, mx.zqs, st),
+               "quantize_z");
   moe::GroupedGluArgs g{};
-  g.Z = z; g.ldz = d->d_latent; g.T = d->T; g.rows_cap = rows_cap;
+  g.Z = q8 ? (const void*)mx.zq : z; g.ldz = d->d_latent; g.T = d->T; g.rows_cap = rows_cap;
+  g.act_mx8 = q8; g.z_scale = mx.zqs;
   g.perm_src = perm; g.topk = d->top_k; g.offsets = offsets; g.tile_off = tile_off;
   g.tile_info = tile_info;
   g.max_tiles = mt;
@@ -343,8 +376,12 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
   if (d->T > 0) MOE_LAUNCH(moe::launch_grouped_glu(g, st), "expert_gate_up");
   mk.end(5, st);
   mk.beg(6, st);
+  if (q8 && d->T > 0)
+    MOE_LAUNCH(moe::launch_quantize_mx8(H, rows_cap, d->d_ff, d->d_ff, mx.hq, mx.hqs, st),
+               "quantize_h");
   moe::GroupedDownArgs dn{};
-  dn.H = H; dn.ldh = d->d_ff; dn.rows_cap = rows_cap;
+  dn.H = q8 ? (const void*)mx.hq : H; dn.ldh = d->d_ff; dn.rows_cap = rows_cap;
+  dn.act_mx8 = q8; dn.h_scale = mx.hqs;
   dn.offsets = offsets; dn.tile_off = tile_off; dn.tile_info = tile_info; dn.max_tiles = mt;
   dn.Wo = wop(w->exp_down, d->expert_w_dtype);
   dn.E = d->n_experts; dn.N = d->d_latent; dn.K = d->d_ff;
@@ -604,8 +641,8 @@ int moe_expert_ffn(const moe_desc_t* d, const void* z, const int32_t* perm_src,
   LayerWs lw{};
   plan_expert(d, p, lw);
   return do_experts(d, z, perm_src, offsets, w, o_perm, (int32_t*)at(ws, lw.tile_off),
-                    (int32_t*)at(ws, lw.tile_info),
-                    at(ws, lw.H), (hipStream_t)stream);
+                    (int32_t*)at(ws, lw.tile_info), at(ws, lw.H), mx_bufs(d, ws, lw),
+                    (hipStream_t)stream);
 }
 
 int moe_combine(const moe_desc_t* d, const void* o_perm, const int32_t* inv_pos,
@@ -641,6 +678,21 @@ int moe_output(const moe_desc_t* d, const void* x, const void* n, const moe_weig
   LayerWs lw{};
   plan_output(d, p, lw);
   return do_output(d, x, n, w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), (hipStream_t)stream);
+}
+
+int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, int64_t ld, uint8_t* codes,
+                       uint8_t* scales, void* stream) {
+  g_last_error.clear();
+  if (rows < 0 || K <= 0 || K % 32 || ld < K)
+    return fail(MOE_ERR_INVALID_ARG, "rows >= 0, K > 0 with K %% 32 == 0 and ld >= K required");
+  if (rows == 0) return MOE_OK;
+  if (ld % 8) return fail(MOE_ERR_UNSUPPORTED, "ld must be a multiple of 8 (16-byte rows)");
+  MOE_CHECK(need_ptr(x, "x"));
+  MOE_CHECK(need_ptr(codes, "codes"));
+  if (scales == nullptr) return fail(MOE_ERR_INVALID_ARG, "scales is NULL");
+  MOE_LAUNCH(moe::launch_quantize_mx8(x, rows, K, ld, codes, scales, (hipStream_t)stream),
+             "quantize_mxfp8");
+  return MOE_OK;
 }
 
 int moe_qb_bias(const moe_desc_t* d, const float* scores, float* bias_out, float* quantile_out,
@@ -711,7 +763,7 @@ int moe_layer_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x
   mk.end(2, st);
   MOE_LAUNCH((int)hipStreamWaitEvent(st, sd->join, 0), "join");
   MOE_CHECK(do_experts(d, at(ws, lw.z), perm, offsets, w, at(ws, lw.O), (int32_t*)at(ws, lw.tile_off),
-                       (int32_t*)at(ws, lw.tile_info), at(ws, lw.H), st, mk));
+                       (int32_t*)at(ws, lw.tile_info), at(ws, lw.H), mx_bufs(d, ws, lw), st, mk));
   mk.beg(7, st);
   MOE_CHECK(do_combine(d, at(ws, lw.O), inv, gate, w->rms_gain, at(ws, lw.n), nullptr, st));
   mk.end(7, st);

@@ -1011,6 +1011,288 @@ __global__ void zero_f32(float* p, int64_t n) {
     p[i] = 0.0f;
 }
 
+// ---------------------------------------------------------------------------
+// Scaled-MFMA expert GEMMs: MXFP8 activations x MXFP4 weights
+// ---------------------------------------------------------------------------
+//
+// v_mfma_scale_f32_32x32x64_f8f6f4 with A = E4M3 activation rows and B = E2M1
+// weight rows, each with one e8m0 scale per 32 elements along K. Operand
+// layout (lane l, h = l / 32; checked on the GPU against a host product for
+// random codes and scales): A lane l holds row l % 32, bytes 0-15 at
+// k = 16h .. 16h+15 and bytes 16-31 at k = 32 + 16h .. 32 + 16h + 15 of the
+// instruction's 64; B lane l holds row l % 32, elements k = 32h .. 32h + 31
+// (16 bytes, low nibble first); byte 0 of each lane's scale register is the
+// scale of its row's k-block h. The accumulator layout is that of
+// v_mfma_f32_32x32x16_bf16, so the bf16 engine's epilogues apply.
+//
+// Block 128 x 256 (8 waves of 64 x 64, as the bf16 grouped GEMMs), K staged
+// 128 elements at a time through a 3-stage LDS ring; per stage: A 128 rows x
+// 128 bytes, B 256 rows x 64 bytes (both swizzled as the bf16 layouts of the
+// same row lengths), and per wave two 256-byte scale areas (its 16 A rows'
+// and 32 B rows' four scale bytes of the stage). Wave w loads A rows
+// 16w .. 16w+15 (2 DMA), B rows 32w .. 32w+31 (2 DMA), their scales (2 DMA).
+namespace mx8 {
+constexpr int kBK = 128;                       // elements per stage
+constexpr int kArow = kBK, kBrow = kBK / 2;    // bytes per row per stage
+constexpr int kA = 128 * kArow, kB = 256 * kBrow, kS = 8 * 256;
+constexpr int kStage = kA + kB + 2 * kS;       // bytes: A | B | A scales | B scales
+constexpr int kNS = 3;
+constexpr int kLoads = 6;                      // DMA per wave per stage
+using L = Cfg<2, 4, 2, 2, 64, 3>;              // accumulator / epilogue layout (128 x 256)
+static_assert(L::BM == 128 && L::BN == 256 && L::NT == 512, "layout");
+
+__device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }   // 128-byte rows
+__device__ __forceinline__ int swz_b(int r) { return (r >> 2) & 3; }   // 64-byte rows
+
+// Per-lane sources of one wave's stage loads: row byte offsets of the data
+// loads (kOOB: none) and of the scale loads.
+struct Src {
+  rsrc_t ra, rb, rsa, rsb;      // A codes, B packed, A scales, B scales
+  uint32_t aoff[2], boff[2];    // data row offsets of this lane's rows in load q
+  uint32_t asoff, bsoff;        // scale row offsets (lanes 0-15 / 0-31), or kOOB
+};
+
+// Stage kt into buf (LDS byte buffer). A chunk c (16 bytes) of tile row r sits
+// in slot c ^ swz_a(r); B chunk c in slot c ^ swz_b(r).
+__device__ __forceinline__ void stage_issue(uint8_t* buf, const Src& s, int kt, int K) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row0 = 16 * w + 8 * q;          // A: 8 rows of 8 chunks per load
+    const int c = (lane & 7) ^ swz_a(row0 + (lane >> 3));
+    const int k = kt * kBK + 16 * c;          // fp8: 16 elements per chunk
+    const uint32_t o = s.aoff[q];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.ra, (lds_ptr_t)(buf + row0 * kArow), 16,
+                                             (k < K && o != kOOB) ? o + (uint32_t)k : kOOB, 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row0 = 32 * w + 16 * q;         // B: 16 rows of 4 chunks per load
+    const int c = (lane & 3) ^ swz_b(row0 + (lane >> 2));
+    const int k = kt * kBK + 32 * c;          // fp4: 32 elements per chunk
+    const uint32_t o = s.boff[q];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rb, (lds_ptr_t)(buf + kA + row0 * kBrow), 16,
+                                             (k < K && o != kOOB) ? o + (uint32_t)(k / 2) : kOOB,
+                                             0, 0, 0);
+  }
+  // four scale bytes (k-blocks 4kt .. 4kt+3) per row; K % 128 == 0
+  const bool kin = kt * kBK < K;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rsa, (lds_ptr_t)(buf + kA + kB + 256 * w), 4,
+                                           (kin && s.asoff != kOOB) ? s.asoff + 4u * (uint32_t)kt : kOOB,
+                                           0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rsb, (lds_ptr_t)(buf + kA + kB + kS + 256 * w), 4,
+                                           (kin && s.bsoff != kOOB) ? s.bsoff + 4u * (uint32_t)kt : kOOB,
+                                           0, 0, 0);
+}
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+struct Frags {
+  v8i a[2][2];          // [k-step][A fragment]
+  v8i b[2][2];          // [k-step][B fragment] (first 16 bytes used)
+  uint32_t sa[2], sb[2];  // scale dwords (blocks 4kt .. 4kt+3) of this lane's rows
+};
+
+template <int NV>
+__device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& f) {
+  if constexpr (NV > 0) {
+    const int lane = threadIdx.x & 63, wm = wave_m<L>(), wn = wave_n<L>();
+    const int lr = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int r = wm * 64 + i * 32 + lr;                 // A tile row
+      const uint8_t* row = buf + r * kArow;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint4 lo = *(const uint4*)(row + 16 * ((4 * s + h) ^ swz_a(r)));
+        const uint4 hi = *(const uint4*)(row + 16 * ((4 * s + 2 + h) ^ swz_a(r)));
+        f.a[s][i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+      f.sa[i] = *(const uint32_t*)(buf + kA + kB + 256 * (r >> 4) + 4 * (r & 15));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = wn * 64 + j * 32 + lr;                 // B tile row
+      const uint8_t* row = buf + kA + n * kBrow;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint4 v = *(const uint4*)(row + 16 * ((2 * s + h) ^ swz_b(n)));
+        f.b[s][j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+      }
+      f.sb[j] = *(const uint32_t*)(buf + kA + kB + kS + 256 * (n >> 5) + 4 * (n & 31));
+    }
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void mma(const Frags& f, Acc<L>& acc) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        // byte 0 of the scale operand: this lane's row, k-block 4kt + 2s + h
+        acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            f.a[s][i], f.b[s][j], acc.c[i][j], 0, 4, 0, (int)(f.sa[i] >> (8 * (2 * s + h))), 0,
+            (int)(f.sb[j] >> (8 * (2 * s + h))));
+}
+
+template <int NV>
+__device__ __forceinline__ void ring_step(const uint8_t* R, uint8_t* W, const Src& s, int kt, int K,
+                                          Acc<L>& acc) {
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads * (kNS - 2)));
+  wg_barrier();
+  Frags f;
+  read_frags<NV>(R, f);
+  stage_issue(W, s, kt + kNS - 1, K);
+  mma<NV>(f, acc);
+}
+
+template <int NV>
+__device__ __forceinline__ void mainloop(uint8_t* s0, uint8_t* s1, uint8_t* s2, const Src& s, int K,
+                                         Acc<L>& acc) {
+  const int nk = (int)ceil_div(K, kBK);
+  stage_issue(s0, s, 0, K);
+  stage_issue(s1, s, 1, K);
+  for (int kt = 0; kt < nk; kt += 3) {
+    ring_step<NV>(s0, s2, s, kt, K, acc);
+    ring_step<NV>(s1, s0, s, kt + 1, K, acc);
+    ring_step<NV>(s2, s1, s, kt + 2, K, acc);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  wg_barrier();
+}
+
+__device__ __forceinline__ void mainloop_rows(uint8_t* s0, uint8_t* s1, uint8_t* s2, const Src& s, int K,
+                                              int valid_rows, Acc<L>& acc) {
+  const int first = wave_m<L>() * 64;
+  const int nv = __builtin_amdgcn_readfirstlane(max(0, min(2, (valid_rows - first + 31) / 32)));
+  if (nv >= 2) mainloop<2>(s0, s1, s2, s, K, acc);
+  else if (nv == 1) mainloop<1>(s0, s1, s2, s, K, acc);
+  else mainloop<0>(s0, s1, s2, s, K, acc);
+}
+
+#define MOE_MX8_RING                                          \
+  __shared__ __align__(16) uint8_t mx0[mx8::kStage];          \
+  __shared__ __align__(16) uint8_t mx1[mx8::kStage];          \
+  __shared__ __align__(16) uint8_t mx2[mx8::kStage]
+
+// B sources of a GLU tile: tile rows 64c .. 64c+31 are the gate rows of outputs
+// f0 + 32c .. + 31, rows 64c+32 .. 64c+63 their up rows; wave w's 32 rows lie
+// in one half (gate for even w, up for odd w).
+__device__ __forceinline__ void b_src_glu(Src& s, const WOperand& g, const WOperand& v, int64_t row_base,
+                                          int K, int f0, int F) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int nf = max(0, min(F - f0, 128));
+  const bool up = (w & 1) != 0;
+  const WOperand& src = up ? v : g;
+  s.rb = make_rsrc((const uint8_t*)src.data + (row_base + f0) * (K / 2), (int64_t)nf * (K / 2));
+  s.rsb = make_rsrc(src.scale + (row_base + f0) * (K / 32), (int64_t)nf * (K / 32));
+  const int fbase = (w >> 1) * 32;                       // output of this wave's first row
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int fl = fbase + 16 * q + (lane >> 2);
+    s.boff[q] = fl < nf ? (uint32_t)(fl * (K / 2)) : kOOB;
+  }
+  const int fs = fbase + lane;
+  s.bsoff = (lane < 32 && fs < nf) ? (uint32_t)(fs * (K / 32)) : kOOB;
+}
+
+__device__ __forceinline__ void b_src_plain(Src& s, const WOperand& wo, int64_t row_base, int K, int n0,
+                                            int N) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int nrows = max(0, min(N - n0, 256));
+  s.rb = make_rsrc((const uint8_t*)wo.data + (row_base + n0) * (K / 2), (int64_t)nrows * (K / 2));
+  s.rsb = make_rsrc(wo.scale + (row_base + n0) * (K / 32), (int64_t)nrows * (K / 32));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 32 * w + 16 * q + (lane >> 2);
+    s.boff[q] = r < nrows ? (uint32_t)(r * (K / 2)) : kOOB;
+  }
+  const int rs = 32 * w + lane;
+  s.bsoff = (lane < 32 && rs < nrows) ? (uint32_t)(rs * (K / 32)) : kOOB;
+}
+}  // namespace mx8
+
+// H[r] = act(zq[perm_src[r] / k] W_g[e]^T, ... W_v[e]^T) for the rows of expert e,
+// zq in MXFP8 (codes Z, scales z_scale), W_g / W_v in MXFP4.
+__global__ __launch_bounds__(512) void grouped_glu_mx8_kernel(GroupedGluArgs a) {
+  using C = mx8::L;
+  MOE_MX8_RING;
+  const int ntn = (int)ceil_div(a.F, C::BN / 2);
+  int64_t L;
+  if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, L)) return;
+  int e, nt, row_lo, row_hi;
+  grouped_item<C::BM>(a.tile_info, ntn, a.rows_cap, L, e, nt, row_lo, row_hi);
+  const int f0 = nt * (C::BN / 2);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  mx8::Src s;
+  s.ra = make_rsrc(a.Z, (int64_t)a.T * a.ldz);
+  s.rsa = make_rsrc(a.z_scale, (int64_t)a.T * (a.K / 32));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int row = row_lo + 16 * w + 8 * q + (lane >> 3);
+    uint32_t off = kOOB;
+    if (row >= 0 && row < row_hi) {
+      const int t = a.perm_src[row] / a.topk;
+      if (a.perm_src[row] >= 0 && t < a.T) off = (uint32_t)((int64_t)t * a.ldz);
+    }
+    s.aoff[q] = off;
+  }
+  {
+    const int row = row_lo + 16 * w + lane;
+    uint32_t off = kOOB;
+    if (lane < 16 && row >= 0 && row < row_hi) {
+      const int t = a.perm_src[row] / a.topk;
+      if (a.perm_src[row] >= 0 && t < a.T) off = (uint32_t)(t * (a.K / 32));
+    }
+    s.asoff = off;
+  }
+  mx8::b_src_glu(s, a.Wg, a.Wv, (int64_t)e * a.F, a.K, f0, a.F);
+  Acc<C> acc;
+  acc_zero(acc);
+  mx8::mainloop_rows(mx0, mx1, mx2, s, a.K, row_hi - row_lo, acc);
+  store_glu(acc, (bf16_t*)a.H, a.F, f0, a.F, a.c, [=](int tr) -> int64_t {
+    const int r = row_lo + tr;
+    return (r >= 0 && r < row_hi) ? (int64_t)r : -1;
+  });
+}
+
+// O[r] = hq[r] W_o[e]^T for the rows of expert e, hq in MXFP8 (codes H, scales
+// h_scale), W_o in MXFP4.
+__global__ __launch_bounds__(512) void grouped_down_mx8_kernel(GroupedDownArgs a) {
+  using C = mx8::L;
+  MOE_MX8_RING;
+  const int ntn = (int)ceil_div(a.N, C::BN);
+  int64_t L;
+  if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, L)) return;
+  int e, nt, row_lo, row_hi;
+  grouped_item<C::BM>(a.tile_info, ntn, a.rows_cap, L, e, nt, row_lo, row_hi);
+  const int n0 = nt * C::BN;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lo = max(row_lo, 0), nrows = max(0, row_hi - lo);
+  mx8::Src s;
+  s.ra = make_rsrc((const uint8_t*)a.H + (int64_t)lo * a.ldh, (int64_t)nrows * a.ldh);
+  s.rsa = make_rsrc(a.h_scale + (int64_t)lo * (a.K / 32), (int64_t)nrows * (a.K / 32));
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int r = 16 * w + 8 * q + (lane >> 3);
+    s.aoff[q] = r < nrows ? (uint32_t)((int64_t)r * a.ldh) : kOOB;
+  }
+  const int rs = 16 * w + lane;
+  s.asoff = (lane < 16 && rs < nrows) ? (uint32_t)(rs * (a.K / 32)) : kOOB;
+  mx8::b_src_plain(s, a.Wo, (int64_t)e * a.N, a.K, n0, a.N);
+  Acc<C> acc;
+  acc_zero(acc);
+  mx8::mainloop_rows(mx0, mx1, mx2, s, a.K, row_hi - row_lo, acc);
+  store_tile(acc, (bf16_t*)a.O, a.N, row_lo, n0, row_hi, a.N);
+}
+
 }  // namespace
 
 // Below 256 single-pass tiles the chip is not full: take 128 x 128 tiles and
@@ -1079,6 +1361,12 @@ int launch_glu(const GluArgs& a, hipStream_t stream) {
 int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream) {
   if (a.act_dtype == DT_F32) return launch_grouped_glu_f32(a, stream);
   if (a.max_tiles == 0) return 0;
+  if (a.act_mx8) {
+    if (a.bm != mx8::L::BM || a.Wg.dtype != DT_MXFP4 || a.K % mx8::kBK) return -1;
+    dim3 grid((unsigned)xcd_grid(ceil_div(a.F, mx8::L::BN / 2) * a.max_tiles));
+    hipLaunchKernelGGL(grouped_glu_mx8_kernel, grid, dim3(mx8::L::NT), 0, stream, a);
+    return (int)hipGetLastError();
+  }
   if (a.bm != GroupCfg::BM) return -1;
   using C = GroupCfg;
   dim3 grid((unsigned)xcd_grid(ceil_div(a.F, C::BN / 2) * a.max_tiles));
@@ -1090,6 +1378,12 @@ int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream) {
 int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream) {
   if (a.act_dtype == DT_F32) return launch_grouped_down_f32(a, stream);
   if (a.max_tiles == 0) return 0;
+  if (a.act_mx8) {
+    if (a.bm != mx8::L::BM || a.Wo.dtype != DT_MXFP4 || a.K % mx8::kBK) return -1;
+    dim3 grid((unsigned)xcd_grid(ceil_div(a.N, mx8::L::BN) * a.max_tiles));
+    hipLaunchKernelGGL(grouped_down_mx8_kernel, grid, dim3(mx8::L::NT), 0, stream, a);
+    return (int)hipGetLastError();
+  }
   if (a.bm != GroupCfg::BM) return -1;
   using C = GroupCfg;
   dim3 grid((unsigned)xcd_grid(ceil_div(a.N, C::BN) * a.max_tiles));

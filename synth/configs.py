@@ -37,6 +37,7 @@ class LayerConfig:
     expert_w: str = "bf16"     # routed expert weights: "f32" | "bf16" | "mxfp4"
     latent_w: str = "bf16"     # W_down / W_up of the latent maps
     dense_w: str = "bf16"      # router and shared experts
+    expert_act: str = "act"    # routed experts' GEMM inputs: "act" (act dtype) | "mxfp8"
     bias: tuple = ("uniform", 0.05)   # ("uniform", halfwidth) | ("zipf", s, scale)
     c: float = 8.0             # SiTU-GLU cap
     eps: float = 1e-6          # RMSNorm epsilon
@@ -67,6 +68,10 @@ CONFIGS = [
     LayerConfig("k3_skew", T=8192, seed=3, bias=("zipf", 1.1, 0.5), **K3),
     LayerConfig("k3_prefill_mxfp4", T=16384, seed=4, expert_w="mxfp4", latent_w="mxfp4",
                 bias=("uniform", 0.05), **K3),
+    # the MXFP4 prefill layer with its routed experts on the scaled MFMA
+    # (z and h quantised to MXFP8); same inputs as k3_prefill_mxfp4
+    LayerConfig("k3_prefill_mx8", T=16384, seed=4, expert_w="mxfp4", latent_w="mxfp4",
+                expert_act="mxfp8", bias=("uniform", 0.05), **K3),
 ]
 
 BY_NAME = {c.name: c for c in CONFIGS}

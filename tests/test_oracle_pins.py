@@ -464,3 +464,78 @@ def test_qb_hand_example():
     # with the bias, each expert's top-2 scores are the ones at or above its boundary
     key = s + b
     assert ((key >= tau).sum(axis=0) == 2).all()
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 (E4M3) activation quantiser of the scaled-MFMA expert path
+# ---------------------------------------------------------------------------
+
+def test_e4m3_value_table():
+    # OCP E4M3: bias 7, 3 mantissa bits, subnormal step 2^-9, max 448 (0x7E)
+    assert oracle.e4m3_value(0x38) == 1.0
+    assert oracle.e4m3_value(0x7E) == 448.0
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6
+    assert oracle.e4m3_value(0x44) == 3.0
+    assert oracle.e4m3_value(0xC0) == -2.0
+    assert np.isnan(oracle.e4m3_value(0x7F))
+    vals = [oracle.e4m3_value(c) for c in range(0x7F)]
+    assert all(b > a for a, b in zip(vals, vals[1:]))      # codes 0..0x7E increase
+
+
+def test_mx8_grid_values_round_trip():
+    """Every finite E4M3 value, placed in a block whose amax fixes the scale
+    2^X, comes back exactly."""
+    grid = np.array([oracle.e4m3_value(c) for c in range(0x7F)] +
+                    [oracle.e4m3_value(c) for c in range(0x80, 0xFF)])
+    for X in (-3, 0, 5):
+        v = np.zeros((1, 32 * 8))
+        v[0, :len(grid)] = grid * 2.0 ** X
+        v[0, 31] = 448.0 * 2.0 ** X          # amax of block 0 -> X
+        for b in range(1, 8):
+            v[0, 32 * b + 31] = 448.0 * 2.0 ** X
+        codes, scales = oracle.mx8_quantize(v)
+        assert (scales == X + 127).all()
+        assert np.array_equal(oracle.mx8_dequantize(codes, scales), v)
+
+
+def test_mx8_scale_rule_and_bounds():
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((40, 128)) * np.exp(rng.uniform(-6, 6, (40, 1)))
+    codes, scales = oracle.mx8_quantize(v)
+    blk = np.abs(v).reshape(40, 4, 32).max(axis=2)
+    # X = floor(log2 amax) - 8, by the textbook route (math.frexp per block)
+    import math
+    want = np.array([[math.frexp(a)[1] - 1 - 8 + 127 for a in row] for row in blk])
+    assert np.array_equal(scales.astype(int), want)
+    d = oracle.mx8_dequantize(codes, scales)
+    X = np.repeat(scales.astype(np.int64) - 127, 32, axis=1)
+    # half a step: 2^-4 relative in the normal range, 2^(X-10) absolute below it;
+    # above 448 * 2^X (amax lies in [256, 512) * 2^X) the element saturates
+    err = np.abs(d - v)
+    cap = 448.0 * 2.0 ** X
+    bound = np.maximum(np.abs(v) * 2.0 ** -4, 2.0 ** (X - 10))
+    bound = np.where(np.abs(v) > cap, np.abs(v) - cap, bound)
+    assert (err <= bound * (1 + 1e-12)).all()
+    assert (np.abs(d) <= cap).all()
+    assert ((v < 0) == (codes >= 0x80)).all()
+
+
+def test_mx8_ties_saturation_and_zero():
+    one = np.zeros((1, 32))
+    one[0, 0] = 256.0                        # amax 2^8 -> X = 0
+    one[0, 1] = 1.0 + 1.0 / 16               # midway 1 and 1.125 -> even (1.0)
+    one[0, 2] = 1.0 + 3.0 / 16               # midway 1.125 and 1.25 -> even (1.25)
+    one[0, 3] = 2.0 ** -10                   # midway 0 and 2^-9 -> even (0)
+    one[0, 4] = 3 * 2.0 ** -10               # midway 2^-9 and 2^-8 -> even (2^-8)
+    one[0, 5] = -(2.0 ** -12)                # tiny negative -> -0
+    codes, scales = oracle.mx8_quantize(one)
+    assert scales[0, 0] == 127
+    assert codes[0, 1] == 0x38 and codes[0, 2] == 0x3A
+    assert codes[0, 3] == 0x00 and codes[0, 4] == 0x02 and codes[0, 5] == 0x80
+    sat = np.zeros((1, 32))
+    sat[0, 0] = 511.0                        # amax in [256, 512): X = 0, 511 > 448
+    codes, scales = oracle.mx8_quantize(sat)
+    assert scales[0, 0] == 127 and codes[0, 0] == 0x7E
+    codes, scales = oracle.mx8_quantize(np.zeros((2, 64)))
+    assert (codes == 0).all() and (scales == 0).all()
