@@ -1025,21 +1025,28 @@ __global__ void zero_f32(float* p, int64_t n) {
 // scale of its row's k-block h. The accumulator layout is that of
 // v_mfma_f32_32x32x16_bf16, so the bf16 engine's epilogues apply.
 //
-// Block 128 x 256 (8 waves of 64 x 64, as the bf16 grouped GEMMs), K staged
-// 128 elements at a time through a 3-stage LDS ring; per stage: A 128 rows x
-// 128 bytes, B 256 rows x 64 bytes (both swizzled as the bf16 layouts of the
-// same row lengths), and per wave two 256-byte scale areas (its 16 A rows'
-// and 32 B rows' four scale bytes of the stage). Wave w loads A rows
-// 16w .. 16w+15 (2 DMA), B rows 32w .. 32w+31 (2 DMA), their scales (2 DMA).
+// Block 128 x kBN (8 waves in a 2 x 4 grid, each 64 x kBN/4), K staged 128
+// elements at a time through a 3-stage LDS ring; per stage: A 128 rows x 128
+// bytes, B kBN rows x 64 bytes (both swizzled as the bf16 layouts of the same
+// row lengths), and per wave two 256-byte scale areas (the four scale bytes of
+// the stage of its 16 A rows and its kBRW B rows). Wave w loads A rows
+// 16w .. 16w+15 (2 DMA), B rows kBRW w .. kBRW w + kBRW - 1 (kBRW / 16 DMA)
+// and their scales (2 DMA).
 namespace mx8 {
+#ifndef MOE_MX8_BN
+#define MOE_MX8_BN 512
+#endif
+constexpr int kBN = MOE_MX8_BN;                // B rows (weights) per block: 256 or 512
+constexpr int kBRW = kBN / 8;                  // B rows per wave's loads
+constexpr int kBQ = kBRW / 16;                 // B DMA per wave per stage
 constexpr int kBK = 128;                       // elements per stage
 constexpr int kArow = kBK, kBrow = kBK / 2;    // bytes per row per stage
-constexpr int kA = 128 * kArow, kB = 256 * kBrow, kS = 8 * 256;
+constexpr int kA = 128 * kArow, kB = kBN * kBrow, kS = 8 * 256;
 constexpr int kStage = kA + kB + 2 * kS;       // bytes: A | B | A scales | B scales
 constexpr int kNS = 3;
-constexpr int kLoads = 6;                      // DMA per wave per stage
-using L = Cfg<2, 4, 2, 2, 64, 3>;              // accumulator / epilogue layout (128 x 256)
-static_assert(L::BM == 128 && L::BN == 256 && L::NT == 512, "layout");
+constexpr int kLoads = 2 + kBQ + 2;            // DMA per wave per stage
+using L = Cfg<2, 4, 2, kBN / 128, 64, 3>;      // accumulator / epilogue layout (128 x kBN)
+static_assert(L::BM == 128 && L::BN == kBN && L::NT == 512 && kBRW <= 64, "layout");
 
 __device__ __forceinline__ int swz_a(int r) { return (r >> 1) & 7; }   // 128-byte rows
 __device__ __forceinline__ int swz_b(int r) { return (r >> 2) & 3; }   // 64-byte rows
@@ -1048,8 +1055,8 @@ __device__ __forceinline__ int swz_b(int r) { return (r >> 2) & 3; }   // 64-byt
 // loads (kOOB: none) and of the scale loads.
 struct Src {
   rsrc_t ra, rb, rsa, rsb;      // A codes, B packed, A scales, B scales
-  uint32_t aoff[2], boff[2];    // data row offsets of this lane's rows in load q
-  uint32_t asoff, bsoff;        // scale row offsets (lanes 0-15 / 0-31), or kOOB
+  uint32_t aoff[2], boff[kBQ];  // data row offsets of this lane's rows in load q
+  uint32_t asoff, bsoff;        // scale row offsets (lanes 0-15 / 0 .. kBRW-1), or kOOB
 };
 
 // Stage kt into buf (LDS byte buffer). A chunk c (16 bytes) of tile row r sits
@@ -1067,8 +1074,8 @@ __device__ __forceinline__ void stage_issue(uint8_t* buf, const Src& s, int kt, 
                                              (k < K && o != kOOB) ? o + (uint32_t)k : kOOB, 0, 0, 0);
   }
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row0 = 32 * w + 16 * q;         // B: 16 rows of 4 chunks per load
+  for (int q = 0; q < kBQ; ++q) {
+    const int row0 = kBRW * w + 16 * q;       // B: 16 rows of 4 chunks per load
     const int c = (lane & 3) ^ swz_b(row0 + (lane >> 2));
     const int k = kt * kBK + 32 * c;          // fp4: 32 elements per chunk
     const uint32_t o = s.boff[q];
@@ -1089,9 +1096,9 @@ __device__ __forceinline__ void stage_issue(uint8_t* buf, const Src& s, int kt, 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 struct Frags {
-  v8i a[2][2];          // [k-step][A fragment]
-  v8i b[2][2];          // [k-step][B fragment] (first 16 bytes used)
-  uint32_t sa[2], sb[2];  // scale dwords (blocks 4kt .. 4kt+3) of this lane's rows
+  v8i a[2][2];            // [k-step][A fragment]
+  v8i b[2][L::WN];        // [k-step][B fragment] (first 16 bytes used)
+  uint32_t sa[2], sb[L::WN];  // scale dwords (blocks 4kt .. 4kt+3) of this lane's rows
 };
 
 template <int NV>
@@ -1112,15 +1119,15 @@ __device__ __forceinline__ void read_frags(const uint8_t* buf, Frags& f) {
       f.sa[i] = *(const uint32_t*)(buf + kA + kB + 256 * (r >> 4) + 4 * (r & 15));
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = wn * 64 + j * 32 + lr;                 // B tile row
+    for (int j = 0; j < L::WN; ++j) {
+      const int n = wn * (kBN / 4) + j * 32 + lr;          // B tile row
       const uint8_t* row = buf + kA + n * kBrow;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const uint4 v = *(const uint4*)(row + 16 * ((2 * s + h) ^ swz_b(n)));
         f.b[s][j] = v8i{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
       }
-      f.sb[j] = *(const uint32_t*)(buf + kA + kB + kS + 256 * (n >> 5) + 4 * (n & 31));
+      f.sb[j] = *(const uint32_t*)(buf + kA + kB + kS + 256 * (n / kBRW) + 4 * (n % kBRW));
     }
   }
 }
@@ -1133,7 +1140,7 @@ __device__ __forceinline__ void mma(const Frags& f, Acc<L>& acc) {
 #pragma unroll
     for (int i = 0; i < NV; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < L::WN; ++j)
         // byte 0 of the scale operand: this lane's row, k-block 4kt + 2s + h
         acc.c[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             f.a[s][i], f.b[s][j], acc.c[i][j], 0, 4, 0, (int)(f.sa[i] >> (8 * (2 * s + h))), 0,
@@ -1180,42 +1187,44 @@ __device__ __forceinline__ void mainloop_rows(uint8_t* s0, uint8_t* s1, uint8_t*
   __shared__ __align__(16) uint8_t mx1[mx8::kStage];          \
   __shared__ __align__(16) uint8_t mx2[mx8::kStage]
 
-// B sources of a GLU tile: tile rows 64c .. 64c+31 are the gate rows of outputs
-// f0 + 32c .. + 31, rows 64c+32 .. 64c+63 their up rows; wave w's 32 rows lie
-// in one half (gate for even w, up for odd w).
+// B sources of a GLU tile (H = kBRW = the outputs of one consumer column):
+// tile rows 2Hc .. 2Hc+H-1 are the gate rows of outputs f0 + Hc .. + H-1, rows
+// 2Hc+H .. 2Hc+2H-1 their up rows; wave w's kBRW rows lie in one half (gate
+// for even w, up for odd w).
 __device__ __forceinline__ void b_src_glu(Src& s, const WOperand& g, const WOperand& v, int64_t row_base,
                                           int K, int f0, int F) {
+  static_assert(kBN / (2 * 4) == kBRW, "a wave's B rows are one half of a consumer column");
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int nf = max(0, min(F - f0, 128));
+  const int nf = max(0, min(F - f0, kBN / 2));
   const bool up = (w & 1) != 0;
   const WOperand& src = up ? v : g;
   s.rb = make_rsrc((const uint8_t*)src.data + (row_base + f0) * (K / 2), (int64_t)nf * (K / 2));
   s.rsb = make_rsrc(src.scale + (row_base + f0) * (K / 32), (int64_t)nf * (K / 32));
-  const int fbase = (w >> 1) * 32;                       // output of this wave's first row
+  const int fbase = (w >> 1) * kBRW;                     // output of this wave's first row
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+  for (int q = 0; q < kBQ; ++q) {
     const int fl = fbase + 16 * q + (lane >> 2);
     s.boff[q] = fl < nf ? (uint32_t)(fl * (K / 2)) : kOOB;
   }
   const int fs = fbase + lane;
-  s.bsoff = (lane < 32 && fs < nf) ? (uint32_t)(fs * (K / 32)) : kOOB;
+  s.bsoff = (lane < kBRW && fs < nf) ? (uint32_t)(fs * (K / 32)) : kOOB;
 }
 
 __device__ __forceinline__ void b_src_plain(Src& s, const WOperand& wo, int64_t row_base, int K, int n0,
                                             int N) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  const int nrows = max(0, min(N - n0, 256));
+  const int nrows = max(0, min(N - n0, kBN));
   s.rb = make_rsrc((const uint8_t*)wo.data + (row_base + n0) * (K / 2), (int64_t)nrows * (K / 2));
   s.rsb = make_rsrc(wo.scale + (row_base + n0) * (K / 32), (int64_t)nrows * (K / 32));
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = 32 * w + 16 * q + (lane >> 2);
+  for (int q = 0; q < kBQ; ++q) {
+    const int r = kBRW * w + 16 * q + (lane >> 2);
     s.boff[q] = r < nrows ? (uint32_t)(r * (K / 2)) : kOOB;
   }
-  const int rs = 32 * w + lane;
-  s.bsoff = (lane < 32 && rs < nrows) ? (uint32_t)(rs * (K / 32)) : kOOB;
+  const int rs = kBRW * w + lane;
+  s.bsoff = (lane < kBRW && rs < nrows) ? (uint32_t)(rs * (K / 32)) : kOOB;
 }
 }  // namespace mx8
 

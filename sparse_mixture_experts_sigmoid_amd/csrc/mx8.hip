@@ -13,6 +13,10 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef MOE_MX8_HWCVT
+#define MOE_MX8_HWCVT 1
+#endif
+
 namespace moe {
 namespace {
 
@@ -29,47 +33,81 @@ __device__ __forceinline__ uint32_t e4m3_mag(float y) {
   return (y >= 448.0f || code > 0x7Eu) ? 0x7Eu : code;
 }
 
-// One thread per 8 consecutive elements (a 16-byte bf16 load); the 4 threads
-// of a 32-element block are adjacent lanes and share amax through shuffles.
+// A thread converts runs of 8 consecutive elements (a 16-byte bf16 load); the 4
+// threads of a 32-element block are adjacent lanes and share amax through
+// shuffles.
+constexpr int kU = 8;
+
+__device__ __forceinline__ void quantize_run(const uint4 v, bool live, int64_t row, int c8, int K,
+                                             uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  // X = floor(log2 amax) - 8; a zero or subnormal amax has exponent field 0 -> -127
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  const int X = ef == 0 ? -127 : max(-127, min(127, ef - 127 - 8));
+#if MOE_MX8_HWCVT
+  // gfx950's v_cvt_pk_fp8_f32 rounds to the nearest OCP E4M3 value (ties to
+  // even, subnormals kept) and keeps the sign; clamping to +-448 first gives the
+  // saturation. The input gets + 0.0f, which turns -0.0 into +0.0 (no sign bit
+  // for v = 0) and leaves every other value as it is, so a negative v whose
+  // scaled value underflows to -0.0 still gets the sign bit
+  float y[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = fminf(fmaxf(__builtin_ldexpf(x[i] + 0.0f, -X), -448.0f), 448.0f);
+  uint32_t lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)lo, true);
+  uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
+  if (live) {
+#else
+  uint32_t q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float y = __builtin_ldexpf(fabsf(x[i]), -X);
+    q[i] = e4m3_mag(y) | (x[i] < 0.0f ? 0x80u : 0u);
+  }
+  if (live) {
+    const uint32_t lo = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+    const uint32_t hi = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+#endif
+    *(uint2*)(codes + row * K + (int64_t)c8 * 8) = make_uint2(lo, hi);
+    if ((c8 & 3) == 0) scales[row * (K / 32) + c8 / 4] = (uint8_t)(X + 127);
+  }
+}
+
+// One wave per row at a time: lane l takes the 8-element runs l, l + 64, ...
+// of the row, all kU of a pass loaded before any is converted. No division on
+// the index path; a wave's lanes past the row's end work on zeros and store
+// nothing (a 4-lane group is wholly live or wholly idle, as K % 32 == 0).
 __global__ __launch_bounds__(256) void quantize_mx8_kernel(const bf16_t* __restrict__ in, int64_t rows,
                                                            int K, int64_t ld, uint8_t* __restrict__ codes,
                                                            uint8_t* __restrict__ scales) {
   const int per_row = K / 8;
-  const int64_t n = rows * per_row;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g - (threadIdx.x & 63) < n;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    // every lane of the wave runs the shuffles (a wave is 8 whole blocks: 64 % 4 == 0,
-    // per_row % 4 == 0); lanes past the end work on zeros and store nothing
-    const bool live = g < n;
-    const int64_t row = live ? g / per_row : 0;
-    const int c8 = live ? (int)(g % per_row) : 0;
-    uint4 v = live ? *(const uint4*)(in + row * ld + (int64_t)c8 * 8) : make_uint4(0, 0, 0, 0);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float x[8];
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
+  for (int64_t row = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); row < rows; row += waves) {
+    const bf16_t* src = in + row * ld;
+    for (int c0 = 0; c0 < per_row; c0 += 64 * kU) {
+      uint4 v[kU];
+      bool live[kU];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(w[i] << 16);
-      x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-    }
-    float amax = 0.0f;
+      for (int u = 0; u < kU; ++u) {
+        const int c8 = c0 + 64 * u + lane;
+        live[u] = c8 < per_row;
+        v[u] = live[u] ? *(const uint4*)(src + (int64_t)c8 * 8) : make_uint4(0, 0, 0, 0);
+      }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    // X = floor(log2 amax) - 8; a zero or subnormal amax has exponent field 0 -> -127
-    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
-    const int X = ef == 0 ? -127 : max(-127, min(127, ef - 127 - 8));
-    uint32_t q[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float y = __builtin_ldexpf(fabsf(x[i]), -X);
-      q[i] = e4m3_mag(y) | (x[i] < 0.0f ? 0x80u : 0u);
-    }
-    if (live) {
-      const uint32_t lo = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-      const uint32_t hi = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-      *(uint2*)(codes + row * K + (int64_t)c8 * 8) = make_uint2(lo, hi);
-      if ((c8 & 3) == 0) scales[row * (K / 32) + c8 / 4] = (uint8_t)(X + 127);
+      for (int u = 0; u < kU; ++u) quantize_run(v[u], live[u], row, c0 + 64 * u + lane, K, codes, scales);
     }
   }
 }
@@ -80,8 +118,7 @@ int launch_quantize_mx8(const void* in, int64_t rows, int K, int64_t ld, uint8_t
                         uint8_t* scales, hipStream_t stream) {
   if (rows == 0) return 0;
   if (K % 32) return -1;
-  const int64_t n = rows * (K / 8);
-  const int64_t blocks = ceil_div(n, 256) < 8192 ? ceil_div(n, 256) : 8192;
+  const int64_t blocks = ceil_div(rows, 4) < 8192 ? ceil_div(rows, 4) : 8192;
   hipLaunchKernelGGL(quantize_mx8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      (const bf16_t*)in, rows, K, ld, codes, scales);
   return (int)hipGetLastError();

@@ -39,6 +39,45 @@ def test_quantize_mxfp8_bit_exact(rows, K, spread, device):
     assert np.array_equal(codes.cpu().numpy(), c_ref), "element codes differ"
 
 
+def _exhaustive_blocks(amax_bits):
+    """Blocks of 32 bf16 values: element 0 is the block maximum (bit pattern
+    amax_bits), the other 31 run through every bf16 value of smaller magnitude,
+    both signs and both zeros, so every rounding case of one scale is met."""
+    amax = np.array([amax_bits << 16], np.uint32).view(np.float32)[0]
+    allv = (np.arange(1 << 16, dtype=np.uint32) << 16).view(np.float32)
+    cand = allv[np.isfinite(allv) & (np.abs(allv) < amax)]
+    n = -(-cand.size // 31)
+    body = np.zeros(n * 31, np.float32)
+    body[:cand.size] = cand
+    blk = np.concatenate([np.full((n, 1), amax, np.float32), body.reshape(n, 31)], axis=1)
+    return blk.reshape(-1)
+
+
+@pytest.mark.parametrize("amax_bits", [0x3FE0, 0x3F80, 0x0C00, 0x0300, 0x7F7F],
+                         ids=["1.75", "1.0", "2^-103", "2^-121", "bf16max"])
+def test_quantize_mxfp8_every_bf16_value(amax_bits, device):
+    """Every bf16 value below the block maximum, at five block scales: a plain
+    one, a power of two, a tiny one, one so tiny that X is clamped at -127 and
+    bf16 subnormals get nonzero codes, and the bf16 maximum."""
+    say(f"mxfp8 quantise: every bf16 value under amax bits {amax_bits:#06x}")
+    flat = _exhaustive_blocks(amax_bits)
+    K = 32 * 64
+    flat = np.concatenate([flat, np.zeros(-flat.size % K, np.float32)])
+    x = torch.from_numpy(flat.reshape(-1, K)).to(torch.bfloat16)
+    rows = x.shape[0]
+    codes = torch.full((rows, K), 0x5A, dtype=torch.uint8, device=device)
+    scales = torch.full((rows, K // 32), 0x5A, dtype=torch.uint8, device=device)
+    moe.moe_quantize_mxfp8(x.to(device), codes, scales)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.mx8_quantize(x.float().numpy().astype(np.float64))
+    assert np.array_equal(scales.cpu().numpy(), s_ref), "scale bytes differ"
+    got = codes.cpu().numpy()
+    bad = np.argwhere(got != c_ref)
+    assert bad.size == 0, (f"{len(bad)} codes differ, first at {tuple(bad[0])}: "
+                           f"v={x[tuple(bad[0])].item()!r} got {got[tuple(bad[0])]:#04x} "
+                           f"want {c_ref[tuple(bad[0])]:#04x}")
+
+
 def test_quantize_mxfp8_strided_rows(device):
     x, _ = _bf16_rows(20, 256, seed=9, spread=4)
     big = torch.zeros((20, 320), dtype=torch.bfloat16)
