@@ -192,6 +192,22 @@ def test_layer_small_full_parity(cfg, device):
     check_y(cfg, to64(y), y_ref)
 
 
+@pytest.mark.parametrize("cfg", [SMALL_BF16, SMALL_MX,
+                                 LayerConfig("small_mx8", T=0, d=128, d_lat=128, E=10, k=3, F=256, S=1,
+                                             Fs=96, seed=41, expert_w="mxfp4", latent_w="mxfp4",
+                                             expert_act="mxfp8")],
+                         ids=lambda c: c.name)
+def test_layer_empty_batch(cfg, device):
+    """T = 0: the layer returns MOE_OK without touching token buffers (NULL here,
+    as torch gives empty tensors no storage) and reports every expert empty."""
+    cfg = cfg.replace(T=0)
+    say(f"layer {cfg.name} with T = 0")
+    inp = synth.device_inputs(cfg, device)
+    y, idx, gate, counts = run_layer(cfg, inp, device)
+    assert y.shape == (0, cfg.d) and idx.shape == (0, cfg.k)
+    assert counts.cpu().numpy().tolist() == [0] * cfg.E
+
+
 def test_staged_entry_points_equal_layer(device):
     cfg = MID_BF16
     inp = synth.device_inputs(cfg, device)
