@@ -237,13 +237,19 @@ __device__ __forceinline__ void wave_sync() {
 //     each expert's fixed-order key, and L_k, the k-th largest key_lo.
 //  2. The candidates {e : key_hi >= L_k} (compacted in LDS), their fixed-order
 //     logits 64 at a time, one per lane: the W rows of the 64 candidates pass
-//     through LDS in chunks of kChunk k (coalesced loads of the next chunk run
+//     through LDS in chunks of KC k (coalesced loads of the next chunk run
 //     while the lanes walk the current one); x goes to LDS widened to fp32.
+//     KC = 256 for small batches (one wave per CU: fewer, larger chunks in
+//     flight hide the memory latency), 64 otherwise.
 //  3. The top-k of the exact keys (key descending, ties to the lower index)
 //     and the gates s_j / sum_slots s, the sum in slot order.
-template <int NPER>
+template <int NPER, int KC>
 __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coef) {
-  constexpr int kChunk = 64;                 // k per staged chunk
+  constexpr int kChunk = KC;                 // k per staged chunk
+  constexpr int kPPR = kChunk / 8;           // 16-byte pieces per W row per chunk
+  constexpr int kRPL = 64 / kPPR;            // W rows per load instruction
+  constexpr int kNJ = 64 / kRPL;             // load instructions per lane per chunk
+  static_assert(kPPR <= 64 && 64 % kPPR == 0, "chunk");
   constexpr int kRowBytes = kChunk * 2 + 16; // LDS row stride (16 B pad: conflict-free reads)
   __shared__ int32_t cand_e[NPER * 64];
   __shared__ __align__(16) uint8_t wst[64 * kRowBytes];
@@ -311,29 +317,29 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coe
   for (int i = 0; i < NPER; ++i) { code[i] = 0ull; sc[i] = 0.0f; }
   const int npass = (int)ceil_div(ncand, 64);
   for (int r = 0; r < npass; ++r) {
-    // rows this lane loads: (lane >> 3) + 8 j, 16-byte piece lane & 7
-    uint32_t roff[8];
+    // rows this lane loads: lane / kPPR + kRPL j, 16-byte piece lane % kPPR
+    uint32_t roff[kNJ];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int p = 64 * r + (lane >> 3) + 8 * j;
-      roff[j] = p < ncand ? (uint32_t)cand_e[p] * (uint32_t)a.d * 2u + (uint32_t)(lane & 7) * 16u
+    for (int j = 0; j < kNJ; ++j) {
+      const int p = 64 * r + lane / kPPR + kRPL * j;
+      roff[j] = p < ncand ? (uint32_t)cand_e[p] * (uint32_t)a.d * 2u + (uint32_t)(lane % kPPR) * 16u
                           : kOOB;
     }
-    const uint32_t xoff = lane < 8 ? (uint32_t)lane * 16u : kOOB;
-    uint4 pw[8], px;
+    const uint32_t xoff = lane < kPPR ? (uint32_t)lane * 16u : kOOB;
+    uint4 pw[kNJ], px;
     auto load_chunk = [&](int c) {
       const uint32_t k0b = 2u * (uint32_t)(c * kChunk);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pw[j] = bload16(wres, roff[j] != kOOB ? roff[j] + k0b : kOOB);
+      for (int j = 0; j < kNJ; ++j) pw[j] = bload16(wres, roff[j] != kOOB ? roff[j] + k0b : kOOB);
       px = bload16(xres, xoff != kOOB ? xoff + k0b : kOOB);
     };
     load_chunk(0);
     float acc = 0.0f;
     for (int c = 0; c < nchunks; ++c) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        *(uint4*)(wst + ((lane >> 3) + 8 * j) * kRowBytes + (lane & 7) * 16) = pw[j];
-      if (lane < 8) {
+      for (int j = 0; j < kNJ; ++j)
+        *(uint4*)(wst + (lane / kPPR + kRPL * j) * kRowBytes + (lane % kPPR) * 16) = pw[j];
+      if (lane < kPPR) {
         const uint32_t xv[4] = {px.x, px.y, px.z, px.w};
         float4 lo4, hi4;
         lo4.x = __uint_as_float(xv[0] << 16); lo4.y = __uint_as_float(xv[0] & 0xFFFF0000u);
@@ -468,8 +474,16 @@ int launch_router_select(const SelectArgs& a, hipStream_t stream) {
   const double du = (double)a.d * 0x1p-24;
   const float beta_coef = (float)(6.0 * du / (1.0 - du));
   const int nper = (int)ceil_div(a.E, 64);
-#define MOE_SEL(N) \
-  hipLaunchKernelGGL(select_kernel<N>, dim3((unsigned)a.T), dim3(64), 0, stream, a, beta_coef)
+  // one wave per token: with fewer tokens than about 8 waves per CU the chunk
+  // loads are the wave's only cover for the memory latency, so make them big
+  const bool big = a.T < 2048 && a.d % 256 == 0;
+#define MOE_SEL(N)                                                                                     \
+  do {                                                                                                 \
+    if (big) hipLaunchKernelGGL((select_kernel<N, 256>), dim3((unsigned)a.T), dim3(64), 0, stream, a, \
+                                beta_coef);                                                           \
+    else hipLaunchKernelGGL((select_kernel<N, 64>), dim3((unsigned)a.T), dim3(64), 0, stream, a,      \
+                            beta_coef);                                                               \
+  } while (0)
   if (nper <= 1) MOE_SEL(1);
   else if (nper <= 2) MOE_SEL(2);
   else if (nper <= 4) MOE_SEL(4);
