@@ -239,11 +239,14 @@ __device__ __forceinline__ void wave_sync() {
 //     logits 64 at a time, one per lane: the W rows of the 64 candidates pass
 //     through LDS in chunks of KC k (coalesced loads of the next chunk run
 //     while the lanes walk the current one); x goes to LDS widened to fp32.
-//     KC = 256 for small batches (one wave per CU: fewer, larger chunks in
-//     flight hide the memory latency), 64 otherwise.
 //  3. The top-k of the exact keys (key descending, ties to the lower index)
 //     and the gates s_j / sum_slots s, the sum in slot order.
-template <int NPER, int KC>
+// DIRECT (few tokens, one wave per CU, d % 256 == 0): step 2 keeps x in LDS
+// as fp32 (dynamic shared memory, d floats) and each lane streams its own
+// candidate's W row into registers, four 64-k chunks ahead; the FMA chain is
+// the same. With no LDS staging of W there is no per-chunk wave sync, and the
+// x reads are broadcasts.
+template <int NPER, int KC, bool DIRECT = false>
 __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coef) {
   constexpr int kChunk = KC;                 // k per staged chunk
   constexpr int kPPR = kChunk / 8;           // 16-byte pieces per W row per chunk
@@ -263,17 +266,27 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coe
   // 1. interval keys; L_k
   uint64_t lo_code[NPER];
   float key_hi[NPER];
+  // all loads first (index clamped into range, results of e >= E unused), so
+  // their latencies overlap instead of adding up slot by slot
+  float lv[NPER], wv[NPER], bv[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const int ec = min(lane + 64 * i, a.E - 1);
+    lv[i] = Lr[ec];
+    wv[i] = a.wn[ec];
+    bv[i] = a.bias[ec];
+  }
 #pragma unroll
   for (int i = 0; i < NPER; ++i) {
     const int e = lane + 64 * i;
     lo_code[i] = 0ull;
     key_hi[i] = -INFINITY;
     if (e < a.E) {
-      const float l = Lr[e];
-      const float beta = beta_coef * xn * a.wn[e] + 1e-30f;
+      const float l = lv[i];
+      const float beta = beta_coef * xn * wv[i] + 1e-30f;
       const float s_lo = sigmoid_fixed(l - beta) * (1.0f - 0x1p-20f);
       const float s_hi = sigmoid_fixed(l + beta) * (1.0f + 0x1p-20f);
-      const float b = a.bias[e];
+      const float b = bv[i];
       lo_code[i] = ((uint64_t)key_code(__fadd_rn(s_lo, b)) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)e);
       key_hi[i] = __fadd_rn(s_hi, b);
     }
@@ -316,14 +329,79 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coe
 #pragma unroll
   for (int i = 0; i < NPER; ++i) { code[i] = 0ull; sc[i] = 0.0f; }
   const int npass = (int)ceil_div(ncand, 64);
-  for (int r = 0; r < npass; ++r) {
+  if constexpr (DIRECT) {
+    extern __shared__ __align__(16) float xs_dyn[];
+    for (int i = lane; i < a.d / 8; i += 64) {
+      const uint4 v = bload16(xres, (uint32_t)i * 16u);
+      const uint32_t xv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        xs_dyn[8 * i + 2 * m] = __uint_as_float(xv[m] << 16);
+        xs_dyn[8 * i + 2 * m + 1] = __uint_as_float(xv[m] & 0xFFFF0000u);
+      }
+    }
+    wave_sync();
+    const int nch = a.d / 64;                // a multiple of 4 (d % 256 == 0)
+    for (int r = 0; r < npass; ++r) {
+      const int p = 64 * r + lane;
+      const int ce = cand_e[p];              // in range: p < 64 NPER
+      const uint32_t base = p < ncand ? (uint32_t)ce * (uint32_t)a.d * 2u : kOOB;
+      uint4 q0[8], q1[8], q2[8], q3[8];
+      auto load = [&](uint4 (&q)[8], int c) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          q[j] = bload16(wres, (base != kOOB && c < nch) ? base + 128u * (uint32_t)c + 16u * (uint32_t)j : kOOB);
+      };
+      float acc = 0.0f;
+      auto chain = [&](uint4 (&q)[8], int c) {
+        float4 xv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) xv[j] = *(const float4*)(xs_dyn + 64 * c + 4 * j);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float4 x0 = xv[2 * j], x1 = xv[2 * j + 1];
+          const uint4 wv = q[j];
+          acc = __builtin_fmaf(x0.x, __uint_as_float(wv.x << 16), acc);
+          acc = __builtin_fmaf(x0.y, __uint_as_float(wv.x & 0xFFFF0000u), acc);
+          acc = __builtin_fmaf(x0.z, __uint_as_float(wv.y << 16), acc);
+          acc = __builtin_fmaf(x0.w, __uint_as_float(wv.y & 0xFFFF0000u), acc);
+          acc = __builtin_fmaf(x1.x, __uint_as_float(wv.z << 16), acc);
+          acc = __builtin_fmaf(x1.y, __uint_as_float(wv.z & 0xFFFF0000u), acc);
+          acc = __builtin_fmaf(x1.z, __uint_as_float(wv.w << 16), acc);
+          acc = __builtin_fmaf(x1.w, __uint_as_float(wv.w & 0xFFFF0000u), acc);
+        }
+        load(q, c + 4);
+      };
+      load(q0, 0);
+      load(q1, 1);
+      load(q2, 2);
+      load(q3, 3);
+      for (int c = 0; c < nch; c += 4) {
+        chain(q0, c);
+        chain(q1, c + 1);
+        chain(q2, c + 2);
+        chain(q3, c + 3);
+      }
+      if (p < ncand) {
+        const float sv = sigmoid_fixed(acc);
+        const uint64_t cd = ((uint64_t)key_code(__fadd_rn(sv, a.bias[ce])) << 32) |
+                            (uint64_t)(0xFFFFFFFFu - (uint32_t)ce);
+#pragma unroll
+        for (int i = 0; i < NPER; ++i)
+          if (i == r) { code[i] = cd; sc[i] = sv; }
+      }
+    }
+  }
+  for (int r = 0; r < (DIRECT ? 0 : npass); ++r) {
     // rows this lane loads: lane / kPPR + kRPL j, 16-byte piece lane % kPPR
     uint32_t roff[kNJ];
+    int ce[kNJ];
+#pragma unroll
+    for (int j = 0; j < kNJ; ++j) ce[j] = cand_e[64 * r + lane / kPPR + kRPL * j];   // in range: p < 64 NPER
 #pragma unroll
     for (int j = 0; j < kNJ; ++j) {
       const int p = 64 * r + lane / kPPR + kRPL * j;
-      roff[j] = p < ncand ? (uint32_t)cand_e[p] * (uint32_t)a.d * 2u + (uint32_t)(lane % kPPR) * 16u
-                          : kOOB;
+      roff[j] = p < ncand ? (uint32_t)ce[j] * (uint32_t)a.d * 2u + (uint32_t)(lane % kPPR) * 16u : kOOB;
     }
     const uint32_t xoff = lane < kPPR ? (uint32_t)lane * 16u : kOOB;
     uint4 pw[kNJ], px;
@@ -474,15 +552,17 @@ int launch_router_select(const SelectArgs& a, hipStream_t stream) {
   const double du = (double)a.d * 0x1p-24;
   const float beta_coef = (float)(6.0 * du / (1.0 - du));
   const int nper = (int)ceil_div(a.E, 64);
-  // one wave per token: with fewer tokens than about 8 waves per CU the chunk
-  // loads are the wave's only cover for the memory latency, so make them big
-  const bool big = a.T < 2048 && a.d % 256 == 0;
-#define MOE_SEL(N)                                                                                     \
-  do {                                                                                                 \
-    if (big) hipLaunchKernelGGL((select_kernel<N, 256>), dim3((unsigned)a.T), dim3(64), 0, stream, a, \
-                                beta_coef);                                                           \
-    else hipLaunchKernelGGL((select_kernel<N, 64>), dim3((unsigned)a.T), dim3(64), 0, stream, a,      \
-                            beta_coef);                                                               \
+  // one wave per token: with fewer tokens than about 8 waves per CU the wave
+  // has nothing to hide its latencies behind, so its candidates' W rows go
+  // straight to registers several chunks ahead (x in dynamic LDS)
+  const bool direct = a.T < 2048 && a.d % 256 == 0 && (size_t)a.d * 4 <= 96 * 1024;
+  const size_t xs_bytes = direct ? (size_t)a.d * 4 : 0;
+#define MOE_SEL(N)                                                                                    \
+  do {                                                                                                \
+    if (direct) hipLaunchKernelGGL((select_kernel<N, 64, true>), dim3((unsigned)a.T), dim3(64),        \
+                                   xs_bytes, stream, a, beta_coef);                                   \
+    else hipLaunchKernelGGL((select_kernel<N, 64>), dim3((unsigned)a.T), dim3(64), 0, stream, a,     \
+                            beta_coef);                                                              \
   } while (0)
   if (nper <= 1) MOE_SEL(1);
   else if (nper <= 2) MOE_SEL(2);
