@@ -133,8 +133,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the layer's hot path is "
-                                   "measured on a single MI355X; use --gpus 1"}))
+        print(json.dumps({"error": "one GPU only: the layer's hot path is measured on a single "
+                                   "MI355X (the expert-parallel layout across GPUs is a design, not "
+                                   "code); use --gpus 1"}))
         return 2
 
     if args.copy_probe > 0:
