@@ -24,7 +24,7 @@ What it computes, step by step (pages cited by title and section):
   "Kimi K3 ... Open Frontier Intelligence" (ai-tech-express.jp), section
       "MXFP4 Quantization-Aware Training": MXFP4 weights, decoded exactly.
 
-Readings where the pages are silent (each also listed in the design doc):
+Readings where the pages are silent:
   * bias is added to the sigmoid score s (not the logit); key = fp32(s + b).
   * ties among keys go to the lower expert index; idx[t] lists the chosen
     experts by key descending (same rule).
