@@ -49,6 +49,10 @@
  * with router/shared weights BF16 and latent / expert weights BF16 or MXFP4.
  * Other combinations return MOE_ERR_UNSUPPORTED. d, d_lat, F and Fs must be
  * multiples of 32; 1 <= k <= E <= 4096; T >= 0 (T = 0 is an empty batch).
+ * Size limits of one call (MOE_ERR_UNSUPPORTED beyond them): T * k <= 2^30,
+ * T * k / 128 + E <= 65535, and with bf16 activations z (T * d_lat * 2 bytes)
+ * under 2 GiB, since the expert kernels gather its rows with 32-bit offsets;
+ * split larger batches into several calls.
  */
 #ifndef MOE_H_
 #define MOE_H_

@@ -92,6 +92,10 @@ int check_desc(const moe_desc_t* d) {
   if (rows > (int64_t)1 << 30) return fail(MOE_ERR_UNSUPPORTED, "T * top_k too large");
   if (rows / 128 + d->n_experts > 65535 || (int64_t)d->T / 128 + 1 > 65535)
     return fail(MOE_ERR_UNSUPPORTED, "batch too large for one launch");
+  // the routed experts gather their z rows through one buffer resource with
+  // 32-bit offsets: the whole z must stay under 2 GiB
+  if (d->act_dtype == MOE_BF16 && (int64_t)d->T * d->d_latent * 2 >= ((int64_t)1 << 31))
+    return fail(MOE_ERR_UNSUPPORTED, "T * d_latent * 2 bytes of z must stay under 2 GiB (T = %d)", d->T);
   return MOE_OK;
 }
 

@@ -70,6 +70,7 @@ def _desc(**kw):
     (dict(expert_w_dtype=moe.MOE_F32), moe.MOE_ERR_UNSUPPORTED),
     (dict(n_experts=5000, top_k=16), moe.MOE_ERR_UNSUPPORTED),
     (dict(n_shared=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=300_000), moe.MOE_ERR_UNSUPPORTED),                # z over 2 GiB (32-bit gather offsets)
 ])
 def test_invalid_descriptors(kw, status):
     d = _desc(**kw)
