@@ -44,6 +44,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix
 MFMA_FP8_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix (the scaled MXFP8 x MXFP4 expert path)
+VALU_FP32_PEAK_TFLOPS = 157.3   # MI355X fp32 vector (the all-fp32 layer runs its GEMMs on the VALU)
 METRIC = "tokens/s per K3-shape LatentMoE layer; % MFMA peak (prefill), % HBM BW (decode)"
 
 
@@ -200,8 +201,9 @@ def main():
         algo = rows * 2 * 2 * cfg.d_lat * cfg.F
         achieved = algo / t_gu / 1e12
         mx8 = cfg.expert_act == "mxfp8"
-        peak = MFMA_FP8_PEAK_TFLOPS if mx8 else MFMA_BF16_PEAK_TFLOPS
-        roof = {"bound": "mfma",
+        f32 = cfg.act == "f32"
+        peak = MFMA_FP8_PEAK_TFLOPS if mx8 else VALU_FP32_PEAK_TFLOPS if f32 else MFMA_BF16_PEAK_TFLOPS
+        roof = {"bound": "alu" if f32 else "mfma",
                 "kernel": ("expert_gate_up (MXFP8 quantise of z + scaled-MFMA grouped GEMM + SiTU-GLU)"
                            if mx8 else "expert_gate_up (grouped GEMM + SiTU-GLU)"),
                 "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
