@@ -189,7 +189,7 @@ def main():
     wbytes = {"bf16": 2.0, "f32": 4.0, "mxfp4": 0.5 + 1.0 / 32}[cfg.expert_w]
     abytes = 4 if cfg.act == "f32" else 2
     t_gu = stages["expert_gate_up"] * 1e-3
-    decode = cfg.name == "k3_decode"
+    decode = cfg.name.startswith("k3_decode")
     if decode:
         algo = touched * 2 * cfg.F * cfg.d_lat * wbytes + rows * (cfg.d_lat + cfg.F) * abytes
         achieved = algo / t_gu / 1e9

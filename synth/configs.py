@@ -72,6 +72,13 @@ CONFIGS = [
     # (z and h quantised to MXFP8); same inputs as k3_prefill_mxfp4
     LayerConfig("k3_prefill_mx8", T=16384, seed=4, expert_w="mxfp4", latent_w="mxfp4",
                 expert_act="mxfp8", bias=("uniform", 0.05), **K3),
+    # the decode batch with the deployment weight format: MXFP4 expert and
+    # latent weights, decoded to bf16 in the GEMM (..._mxfp4) or fed to the
+    # scaled MFMA with MXFP8 expert inputs (..._mx8); same inputs as k3_decode
+    LayerConfig("k3_decode_mxfp4", T=256, seed=1, expert_w="mxfp4", latent_w="mxfp4",
+                bias=("uniform", 0.05), **K3),
+    LayerConfig("k3_decode_mx8", T=256, seed=1, expert_w="mxfp4", latent_w="mxfp4",
+                expert_act="mxfp8", bias=("uniform", 0.05), **K3),
 ]
 
 BY_NAME = {c.name: c for c in CONFIGS}

@@ -18,7 +18,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("name,n_sample", [("k3_skew", 10), ("k3_prefill", 8),
-                                           ("k3_prefill_mxfp4", 8), ("k3_prefill_mx8", 8)])
+                                           ("k3_prefill_mxfp4", 8), ("k3_prefill_mx8", 8),
+                                           ("k3_decode_mxfp4", 12), ("k3_decode_mx8", 12)])
 def test_k3_full_size(name, n_sample, device):
     cfg = synth.config(name)
     say(f"{name}: generating inputs on the GPU")
