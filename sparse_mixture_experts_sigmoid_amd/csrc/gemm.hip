@@ -1056,7 +1056,8 @@ __device__ __forceinline__ int swz_b(int r) { return (r >> 2) & 3; }   // 64-byt
 struct Src {
   rsrc_t ra, rb, rsa, rsb;      // A codes, B packed, A scales, B scales
   uint32_t aoff[2], boff[kBQ];  // data row offsets of this lane's rows in load q
-  uint32_t asoff, bsoff;        // scale row offsets (lanes 0-15 / 0 .. kBRW-1), or kOOB
+  uint32_t asoff, bsoff;        // scale offsets of stage 0 (lanes 0-15 / 0 .. kBRW-1), or kOOB
+  uint32_t bsstep;              // B scale bytes between stages: 4 (rows) or 256 (stage-tiled)
 };
 
 // Stage kt into buf (LDS byte buffer). A chunk c (16 bytes) of tile row r sits
@@ -1089,7 +1090,7 @@ __device__ __forceinline__ void stage_issue(uint8_t* buf, const Src& s, int kt, 
                                            (kin && s.asoff != kOOB) ? s.asoff + 4u * (uint32_t)kt : kOOB,
                                            0, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rsb, (lds_ptr_t)(buf + kA + kB + kS + 256 * w), 4,
-                                           (kin && s.bsoff != kOOB) ? s.bsoff + 4u * (uint32_t)kt : kOOB,
+                                           (kin && s.bsoff != kOOB) ? s.bsoff + s.bsstep * (uint32_t)kt : kOOB,
                                            0, 0, 0);
 }
 
@@ -1187,12 +1188,24 @@ __device__ __forceinline__ void mainloop_rows(uint8_t* s0, uint8_t* s1, uint8_t*
   __shared__ __align__(16) uint8_t mx1[mx8::kStage];          \
   __shared__ __align__(16) uint8_t mx2[mx8::kStage]
 
+// B scale offset of wave-row `first + lane` at stage 0 and the step between
+// stages. Row-major scales [R, K/32]: the row's own K/32 bytes, 4 per stage.
+// Stage-tiled scales [R/64][K/128][64][4]: 64-row tiles, each stage's 4 bytes
+// of the tile's 64 rows contiguous (256 bytes), so one wave load of its 64 rows
+// reads two whole cache lines instead of 4 bytes from each of 64 rows. `first`
+// is 64-aligned in absolute rows (the callers require d_ff, d_latent % 128).
+__device__ __forceinline__ void b_scale_src(Src& s, bool tiled, int first, int lane, int K, bool live) {
+  s.bsstep = tiled ? 256u : 4u;
+  s.bsoff = !live ? kOOB
+                  : tiled ? (uint32_t)(first * (K / 32) + 4 * lane) : (uint32_t)((first + lane) * (K / 32));
+}
+
 // B sources of a GLU tile (H = kBRW = the outputs of one consumer column):
 // tile rows 2Hc .. 2Hc+H-1 are the gate rows of outputs f0 + Hc .. + H-1, rows
 // 2Hc+H .. 2Hc+2H-1 their up rows; wave w's kBRW rows lie in one half (gate
 // for even w, up for odd w).
 __device__ __forceinline__ void b_src_glu(Src& s, const WOperand& g, const WOperand& v, int64_t row_base,
-                                          int K, int f0, int F) {
+                                          int K, int f0, int F, bool tiled) {
   static_assert(kBN / (2 * 4) == kBRW, "a wave's B rows are one half of a consumer column");
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -1207,12 +1220,11 @@ __device__ __forceinline__ void b_src_glu(Src& s, const WOperand& g, const WOper
     const int fl = fbase + 16 * q + (lane >> 2);
     s.boff[q] = fl < nf ? (uint32_t)(fl * (K / 2)) : kOOB;
   }
-  const int fs = fbase + lane;
-  s.bsoff = (lane < kBRW && fs < nf) ? (uint32_t)(fs * (K / 32)) : kOOB;
+  b_scale_src(s, tiled, fbase, lane, K, lane < kBRW && fbase + lane < nf);
 }
 
 __device__ __forceinline__ void b_src_plain(Src& s, const WOperand& wo, int64_t row_base, int K, int n0,
-                                            int N) {
+                                            int N, bool tiled) {
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int nrows = max(0, min(N - n0, kBN));
@@ -1223,8 +1235,7 @@ __device__ __forceinline__ void b_src_plain(Src& s, const WOperand& wo, int64_t 
     const int r = kBRW * w + 16 * q + (lane >> 2);
     s.boff[q] = r < nrows ? (uint32_t)(r * (K / 2)) : kOOB;
   }
-  const int rs = kBRW * w + lane;
-  s.bsoff = (lane < kBRW && rs < nrows) ? (uint32_t)(rs * (K / 32)) : kOOB;
+  b_scale_src(s, tiled, kBRW * w, lane, K, lane < kBRW && kBRW * w + lane < nrows);
 }
 }  // namespace mx8
 
@@ -1262,7 +1273,7 @@ __global__ __launch_bounds__(512) void grouped_glu_mx8_kernel(GroupedGluArgs a) 
     }
     s.asoff = off;
   }
-  mx8::b_src_glu(s, a.Wg, a.Wv, (int64_t)e * a.F, a.K, f0, a.F);
+  mx8::b_src_glu(s, a.Wg, a.Wv, (int64_t)e * a.F, a.K, f0, a.F, a.w_scale_tiled != 0);
   Acc<C> acc;
   acc_zero(acc);
   mx8::mainloop_rows(mx0, mx1, mx2, s, a.K, row_hi - row_lo, acc);
@@ -1295,7 +1306,7 @@ __global__ __launch_bounds__(512) void grouped_down_mx8_kernel(GroupedDownArgs a
   }
   const int rs = 16 * w + lane;
   s.asoff = (lane < 16 && rs < nrows) ? (uint32_t)(rs * (a.K / 32)) : kOOB;
-  mx8::b_src_plain(s, a.Wo, (int64_t)e * a.N, a.K, n0, a.N);
+  mx8::b_src_plain(s, a.Wo, (int64_t)e * a.N, a.K, n0, a.N, a.w_scale_tiled != 0);
   Acc<C> acc;
   acc_zero(acc);
   mx8::mainloop_rows(mx0, mx1, mx2, s, a.K, row_hi - row_lo, acc);
@@ -1372,6 +1383,7 @@ int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream) {
   if (a.max_tiles == 0) return 0;
   if (a.act_mx8) {
     if (a.bm != mx8::L::BM || a.Wg.dtype != DT_MXFP4 || a.K % mx8::kBK) return -1;
+    if (a.w_scale_tiled && (a.F % 64 || mx8::kBRW != 64)) return -1;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.F, mx8::L::BN / 2) * a.max_tiles));
     hipLaunchKernelGGL(grouped_glu_mx8_kernel, grid, dim3(mx8::L::NT), 0, stream, a);
     return (int)hipGetLastError();
@@ -1389,6 +1401,7 @@ int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream) {
   if (a.max_tiles == 0) return 0;
   if (a.act_mx8) {
     if (a.bm != mx8::L::BM || a.Wo.dtype != DT_MXFP4 || a.K % mx8::kBK) return -1;
+    if (a.w_scale_tiled && (a.N % 64 || mx8::kBRW != 64)) return -1;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.N, mx8::L::BN) * a.max_tiles));
     hipLaunchKernelGGL(grouped_down_mx8_kernel, grid, dim3(mx8::L::NT), 0, stream, a);
     return (int)hipGetLastError();

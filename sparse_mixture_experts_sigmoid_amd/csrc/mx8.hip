@@ -112,7 +112,35 @@ __global__ __launch_bounds__(256) void quantize_mx8_kernel(const bf16_t* __restr
   }
 }
 
+// One thread per output dword: the 4 scale bytes (one 128-element stage) of
+// one row, read as a dword from the row-major array (K/32 % 4 == 0 keeps it
+// aligned) and written where the tiled layout puts them, so that consecutive
+// threads write consecutive dwords.
+__global__ __launch_bounds__(256) void tile_scales_kernel(const uint32_t* __restrict__ in,
+                                                          uint32_t* __restrict__ out, int64_t rows,
+                                                          int nk) {
+  const int64_t n = rows * nk;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t tile = i / (64 * (int64_t)nk);
+    const int rem = (int)(i - tile * 64 * nk);
+    const int kt = rem >> 6, rl = rem & 63;
+    out[i] = in[(tile * 64 + rl) * nk + kt];
+  }
+}
+
 }  // namespace
+
+int launch_tile_scales(const uint8_t* in, uint8_t* out, int64_t rows, int K, hipStream_t stream) {
+  if (rows % 64 || K % 128 || ((uintptr_t)in | (uintptr_t)out) % 4) return -1;
+  if (rows == 0) return 0;
+  const int nk = K / 128;
+  const int64_t n = rows * nk;
+  const int64_t blocks = ceil_div(n, 256) < 16384 ? ceil_div(n, 256) : 16384;
+  hipLaunchKernelGGL(tile_scales_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     (const uint32_t*)in, (uint32_t*)out, rows, nk);
+  return (int)hipGetLastError();
+}
 
 int launch_quantize_mx8(const void* in, int64_t rows, int K, int64_t ld, uint8_t* codes,
                         uint8_t* scales, hipStream_t stream) {

@@ -49,7 +49,7 @@ def run_layer(cfg, inp, dev="cuda:0"):
     gate = torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev)
     counts = torch.empty((cfg.E,), dtype=torch.int32, device=dev)
     ws = moe.workspace(desc, moe.MOE_OP_LAYER, dev)
-    moe.moe_layer_forward(desc, inp, inp["x"], y, idx, gate, counts, ws)
+    moe.moe_layer_forward(desc, moe.prepare_weights(cfg, inp), inp["x"], y, idx, gate, counts, ws)
     torch.cuda.synchronize()
     return y, idx, gate, counts
 

@@ -71,6 +71,8 @@ def _desc(**kw):
     (dict(n_experts=5000, top_k=16), moe.MOE_ERR_UNSUPPORTED),
     (dict(n_shared=8), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=300_000), moe.MOE_ERR_UNSUPPORTED),                # z over 2 GiB (32-bit gather offsets)
+    (dict(expert_w_scale_tiled=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(expert_w_scale_tiled=1), moe.MOE_ERR_UNSUPPORTED),   # tiled scales without MXFP8 inputs
 ])
 def test_invalid_descriptors(kw, status):
     d = _desc(**kw)
@@ -149,6 +151,34 @@ def test_mxfp4_weights_need_scales():
     w = _weights(W_g=(FAKE, None))
     assert _call_layer(d, w) == moe.MOE_ERR_INVALID_ARG
     assert b"scales" in moe.lib().moe_last_error()
+
+
+def test_mxfp4_scales_must_be_4_byte_aligned():
+    d = moe.make_desc(synth.config("k3_decode_mx8"))
+    mx = {k: (FAKE, FAKE) for k in ("W_ld", "W_lu", "W_g", "W_v")}
+    w = _weights(W_o=(FAKE, FAKE + 2), **mx)
+    assert _call_layer(d, w) == moe.MOE_ERR_INVALID_ARG
+    assert b"aligned" in moe.lib().moe_last_error()
+
+
+def test_tiled_scale_configs_are_valid():
+    for name in ("k3_decode_mx8", "k3_prefill_mx8"):
+        d = moe.make_desc(synth.config(name))
+        assert d.expert_w_scale_tiled == 1 and d.expert_act_mxfp8 == 1
+        assert moe.moe_check_desc(d) == moe.MOE_OK
+
+
+@pytest.mark.parametrize("rows,K,src,dst,status", [
+    (64, 100, FAKE, FAKE + (1 << 20), moe.MOE_ERR_INVALID_ARG),      # K % 128
+    (96, 128, FAKE, FAKE + (1 << 20), moe.MOE_ERR_INVALID_ARG),      # rows % 64
+    (-64, 128, FAKE, FAKE + (1 << 20), moe.MOE_ERR_INVALID_ARG),
+    (64, 128, None, FAKE + (1 << 20), moe.MOE_ERR_INVALID_ARG),
+    (64, 128, FAKE, FAKE + 2, moe.MOE_ERR_INVALID_ARG),               # misaligned
+    (64, 128, FAKE, FAKE + 128, moe.MOE_ERR_INVALID_ARG),             # overlaps (256 bytes)
+    (0, 128, None, None, moe.MOE_OK),                                  # nothing to do
+])
+def test_tile_scales_validates_before_any_launch(rows, K, src, dst, status):
+    assert moe.lib().moe_mxfp4_tile_scales(src, dst, rows, K, None) == status
 
 
 def test_staged_entry_points_validate():

@@ -112,3 +112,33 @@ def test_layer_mx8_full_parity(cfg, device):
     rms = float(np.sqrt((y_ref ** 2).mean()))
     say(f"  {cfg.name}: MXFP8-input vs bf16-input oracle: max|dy| = "
         f"{np.abs(y_ref - y_bf16).max() / rms:.3e} x RMS")
+
+
+@pytest.mark.parametrize("rows,K", [(64, 128), (192, 3584), (1920, 384), (0, 128)])
+def test_tile_scales_is_the_documented_permutation(rows, K, device):
+    """moe_mxfp4_tile_scales moves byte (r, b) of [rows, K/32] to
+    ((r/64)(K/128) + b/4) 256 + (r%64) 4 + b%4, bit for bit (numpy reshape of
+    the same order as the expected value)."""
+    rng = np.random.default_rng(rows + K)
+    s = rng.integers(0, 256, (rows, K // 32), dtype=np.uint8)
+    src = torch.from_numpy(s).to(device)
+    out = torch.full_like(src, 0xAB)
+    moe.moe_mxfp4_tile_scales(src, out)
+    torch.cuda.synchronize()
+    want = s.reshape(rows // 64, 64, K // 128, 4).transpose(0, 2, 1, 3).reshape(rows, K // 32)
+    assert np.array_equal(out.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("cfg", [MX8_SMALL, MX8_MID], ids=lambda c: c.name)
+def test_layer_mx8_tiled_scales(cfg, device):
+    """Stage-tiled expert scales change only where the kernels read the scale
+    bytes: the layer output equals, bit for bit, the row-major run's, and both
+    meet the oracle."""
+    inp = synth.device_inputs(cfg, device)
+    y_rows, idx, gate, _ = run_layer(cfg, inp, device)
+    cfg_t = cfg.replace(name=cfg.name + "_tiled", expert_scales="tiled")
+    y_t, idx_t, gate_t, _ = run_layer(cfg_t, inp, device)
+    assert torch.equal(idx, idx_t) and torch.equal(gate, gate_t)
+    assert torch.equal(y_rows, y_t)
+    y_ref = oracle.forward(cfg, synth.HostWeights(cfg))
+    check_y(cfg_t, to64(y_t), y_ref)
