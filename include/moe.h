@@ -40,10 +40,13 @@
  *   MXFP4 weight [R, K]: data = packed bytes [R, K/2] (element 2i in the low
  *   nibble of byte i, 16-byte aligned like every tensor), scale = e8m0 bytes
  *   [R, K/32] (4-byte aligned).
- *   Stage-tiled MXFP4 scales (routed experts on the MXFP8 path only, see
- *   expert_w_scale_tiled): the same bytes in [R/64][K/128][64][4] order, i.e.
- *   the scale of row r, 32-element block b sits at byte
- *   ((r/64) (K/128) + b/4) 256 + (r%64) 4 + b%4 (moe_mxfp4_tile_scales).
+ *   Tiled MXFP4 weight (routed experts on the MXFP8 path only, see
+ *   expert_w_tiled; made by moe_mxfp4_tile; R % 64 == 0, K % 128 == 0): the
+ *   same bytes reordered. Packed: byte j (0..63) of row r's 128-element stage
+ *   kt (row-major byte 64 kt + j of the row) at ((r/2) (K/128) + kt) 128 +
+ *   (r%2) 64 + j, i.e. [R/2][K/128][2][64]: a stage of a row pair is one
+ *   128-byte line. Scales: the scale of row r, 32-element block b at
+ *   ((r/64) (K/128) + b/4) 256 + (r%64) 4 + b%4, i.e. [R/64][K/128][64][4].
  *   topk_idx [T, k] int32, topk_gate [T, k] fp32 (slot order = key descending,
  *   ties to the lower expert index).
  *   Permutation: rows of expert e are offsets[e] .. offsets[e+1]-1 (offsets has
@@ -108,12 +111,13 @@ typedef struct {
      d_latent, d_ff multiples of 128. Changes the numerics (the oracle quantises
      the same way). */
   int32_t expert_act_mxfp8;
-  /* 0: W_g, W_v, W_o scales row-major [R, K/32]. 1: stage-tiled (the layout
-     above, made once per weight set by moe_mxfp4_tile_scales); needs
-     expert_act_mxfp8 = 1. The scaled-MFMA expert kernels read each 128-element
-     K stage's scales for 64 weight rows as 256 contiguous bytes instead of 4
-     bytes from each of 64 rows 112+ bytes apart. Same results either way. */
-  int32_t expert_w_scale_tiled;
+  /* 0: W_g, W_v, W_o row-major. 1: in the tiled MXFP4 layout above (made once
+     per weight set by moe_mxfp4_tile); needs expert_act_mxfp8 = 1. The
+     scaled-MFMA expert kernels then read each 128-element K stage as whole
+     128-byte lines of row pairs and the stage's scales of 64 weight rows as
+     256 contiguous bytes, instead of half lines and 4 bytes from each of 64
+     rows. Same results either way. */
+  int32_t expert_w_tiled;
 } moe_desc_t;
 
 /* A weight tensor: data (dtype of its class) and, for MXFP4 only, scales. */
@@ -224,16 +228,19 @@ int moe_layer_forward(const moe_desc_t* desc, const moe_weights_t* w, const void
 int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, int64_t ld, uint8_t* codes,
                        uint8_t* scales, void* stream);
 
-/* Stage-tiled copy of the e8m0 scales of an MXFP4 weight ("Kimi K3 ... Open
-   Frontier Intelligence", section "MXFP4 Quantization-Aware Training": one
-   scale per 32 elements along K): scale [rows, K/32] row-major in, out in the
-   stage-tiled order given under Layouts. A pure permutation of bytes, made
-   once when a weight set is loaded (W_g, W_v as rows = E * F, K = d_latent;
-   W_o as rows = E * d_latent, K = d_ff), not per batch. rows % 64 == 0 and
-   K % 128 == 0 (else MOE_ERR_INVALID_ARG); both pointers device memory owned
-   by the caller, 4-byte aligned, not overlapping; asynchronous on stream;
-   allocates nothing. rows == 0 does nothing. */
-int moe_mxfp4_tile_scales(const uint8_t* scale, uint8_t* out, int64_t rows, int32_t K, void* stream);
+/* Tiled copy of an MXFP4 weight ("Kimi K3 ... Open Frontier Intelligence",
+   section "MXFP4 Quantization-Aware Training": e2m1 elements with one e8m0
+   scale per 32 along K) for the scaled-MFMA expert path: data [rows, K/2] and
+   scale [rows, K/32] row-major in, data_out and scale_out in the tiled order
+   given under Layouts. A pure permutation of bytes, made once when a weight
+   set is loaded (W_g, W_v as rows = E * F, K = d_latent; W_o as rows =
+   E * d_latent, K = d_ff), not per batch. rows % 64 == 0 and K % 128 == 0;
+   data pointers 16-byte and scale pointers 4-byte aligned; no output may
+   overlap an input or the other output (else MOE_ERR_INVALID_ARG). Device
+   memory owned by the caller; asynchronous on stream; allocates nothing.
+   rows == 0 does nothing. */
+int moe_mxfp4_tile(const uint8_t* data, const uint8_t* scale, uint8_t* data_out, uint8_t* scale_out,
+                   int64_t rows, int32_t K, void* stream);
 
 /* Quantile Balancing: the per-expert selection bias from quantiles of the
    router scores ("Kimi K3の896エキスパートを「896人の専門家」と呼ぶと何がズレるか",

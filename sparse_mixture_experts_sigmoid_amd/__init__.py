@@ -28,7 +28,7 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
 EXPORTS = ["moe_workspace_bytes", "moe_check_desc", "moe_route", "moe_permute", "moe_latent_down",
            "moe_expert_ffn", "moe_combine", "moe_output", "moe_layer_forward",
            "moe_status_string", "moe_last_error", "moe_trace_enable", "moe_trace_read",
-           "moe_trace_stage_name", "moe_qb_bias", "moe_quantize_mxfp8", "moe_mxfp4_tile_scales"]
+           "moe_trace_stage_name", "moe_qb_bias", "moe_quantize_mxfp8", "moe_mxfp4_tile"]
 MOE_TRACE_STAGES = 10
 
 
@@ -45,7 +45,7 @@ class MoeDesc(ctypes.Structure):
                 ("situ_c", ctypes.c_float), ("rms_eps", ctypes.c_float),
                 ("act_dtype", ctypes.c_int32), ("expert_w_dtype", ctypes.c_int32),
                 ("latent_w_dtype", ctypes.c_int32), ("dense_w_dtype", ctypes.c_int32),
-                ("expert_act_mxfp8", ctypes.c_int32), ("expert_w_scale_tiled", ctypes.c_int32)]
+                ("expert_act_mxfp8", ctypes.c_int32), ("expert_w_tiled", ctypes.c_int32)]
 
 
 class MoeW(ctypes.Structure):
@@ -84,7 +84,7 @@ def lib():
         "moe_trace_stage_name": ([i32], ctypes.c_char_p),
         "moe_qb_bias": ([D, vp, vp, vp, vp], i32),
         "moe_quantize_mxfp8": ([vp, ctypes.c_int64, i32, ctypes.c_int64, vp, vp, vp], i32),
-        "moe_mxfp4_tile_scales": ([vp, vp, ctypes.c_int64, i32, vp], i32),
+        "moe_mxfp4_tile": ([vp, vp, vp, vp, ctypes.c_int64, i32, vp], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -106,7 +106,7 @@ def make_desc(cfg, T=None) -> MoeDesc:
                    expert_w_dtype=DTYPES[cfg.expert_w], latent_w_dtype=DTYPES[cfg.latent_w],
                    dense_w_dtype=DTYPES[cfg.dense_w],
                    expert_act_mxfp8=1 if getattr(cfg, "expert_act", "act") == "mxfp8" else 0,
-                   expert_w_scale_tiled=1 if getattr(cfg, "expert_scales", "rows") == "tiled" else 0)
+                   expert_w_tiled=1 if getattr(cfg, "expert_layout", "rows") == "tiled" else 0)
 
 
 def _ptr(t):
@@ -227,26 +227,28 @@ def moe_quantize_mxfp8(x, codes, scales, stream=None):
                                     _stream(stream)))
 
 
-def moe_mxfp4_tile_scales(scale, out, stream=None):
-    """Stage-tiled copy (out) of row-major MXFP4 scales [rows, K/32] (uint8 device tensors)."""
+def moe_mxfp4_tile(data, scale, data_out, scale_out, stream=None):
+    """Tiled copy (data_out, scale_out) of a row-major MXFP4 weight: packed
+    [rows, K/2] and scales [rows, K/32], uint8 device tensors."""
     rows, kb = scale.shape
-    _check(lib().moe_mxfp4_tile_scales(_ptr(scale), _ptr(out), rows, kb * 32, _stream(stream)))
+    _check(lib().moe_mxfp4_tile(_ptr(data), _ptr(scale), _ptr(data_out), _ptr(scale_out), rows,
+                                kb * 32, _stream(stream)))
 
 
 def prepare_weights(cfg, weights: dict, stream=None) -> dict:
     """The weight dict the layer reads for `cfg`: the same tensors, except that a
-    config with expert_scales == 'tiled' gets stage-tiled copies of the W_g, W_v
-    and W_o scales (made once here, on the device, not per batch)."""
-    if getattr(cfg, "expert_scales", "rows") != "tiled":
+    config with expert_layout == 'tiled' gets tiled copies of W_g, W_v and W_o
+    (made once here, on the device, not per batch)."""
+    if getattr(cfg, "expert_layout", "rows") != "tiled":
         return weights
     import torch
     out = dict(weights)
     for name in ("W_g", "W_v", "W_o"):
         packed, scale = weights[name]
-        flat = scale.reshape(-1, scale.shape[-1])
-        tiled = torch.empty_like(flat)
-        moe_mxfp4_tile_scales(flat, tiled, stream)
-        out[name] = (packed, tiled.view(scale.shape))
+        p2, s2 = packed.reshape(-1, packed.shape[-1]), scale.reshape(-1, scale.shape[-1])
+        tp, ts = torch.empty_like(p2), torch.empty_like(s2)
+        moe_mxfp4_tile(p2, s2, tp, ts, stream)
+        out[name] = (tp.view(packed.shape), ts.view(scale.shape))
     return out
 
 

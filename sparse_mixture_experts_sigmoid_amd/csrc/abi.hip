@@ -84,10 +84,10 @@ int check_desc(const moe_desc_t* d) {
       (d->act_dtype != MOE_BF16 || d->expert_w_dtype != MOE_MXFP4 || d->d_latent % 128 || d->d_ff % 128))
     return fail(MOE_ERR_UNSUPPORTED, "MXFP8 expert activations need bf16 activations, MXFP4 expert "
                 "weights and d_latent, d_ff multiples of 128");
-  if (d->expert_w_scale_tiled != 0 && d->expert_w_scale_tiled != 1)
-    return fail(MOE_ERR_INVALID_ARG, "expert_w_scale_tiled must be 0 or 1");
-  if (d->expert_w_scale_tiled && !d->expert_act_mxfp8)
-    return fail(MOE_ERR_UNSUPPORTED, "stage-tiled expert scales are read only by the MXFP8 expert path "
+  if (d->expert_w_tiled != 0 && d->expert_w_tiled != 1)
+    return fail(MOE_ERR_INVALID_ARG, "expert_w_tiled must be 0 or 1");
+  if (d->expert_w_tiled && !d->expert_act_mxfp8)
+    return fail(MOE_ERR_UNSUPPORTED, "tiled expert weights are read only by the MXFP8 expert path "
                 "(expert_act_mxfp8 = 1)");
   if (d->n_experts > kMaxExperts)
     return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", kMaxExperts);
@@ -376,7 +376,7 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
                "quantize_z");
   moe::GroupedGluArgs g{};
   g.Z = q8 ? (const void*)mx.zq : z; g.ldz = d->d_latent; g.T = d->T; g.rows_cap = rows_cap;
-  g.act_mx8 = q8; g.z_scale = mx.zqs; g.w_scale_tiled = d->expert_w_scale_tiled;
+  g.act_mx8 = q8; g.z_scale = mx.zqs; g.w_tiled = d->expert_w_tiled;
   g.perm_src = perm; g.topk = d->top_k; g.offsets = offsets; g.tile_off = tile_off;
   g.tile_info = tile_info;
   g.max_tiles = mt;
@@ -392,7 +392,7 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
                "quantize_h");
   moe::GroupedDownArgs dn{};
   dn.H = q8 ? (const void*)mx.hq : H; dn.ldh = d->d_ff; dn.rows_cap = rows_cap;
-  dn.act_mx8 = q8; dn.h_scale = mx.hqs; dn.w_scale_tiled = d->expert_w_scale_tiled;
+  dn.act_mx8 = q8; dn.h_scale = mx.hqs; dn.w_tiled = d->expert_w_tiled;
   dn.offsets = offsets; dn.tile_off = tile_off; dn.tile_info = tile_info; dn.max_tiles = mt;
   dn.Wo = wop(w->exp_down, d->expert_w_dtype);
   dn.E = d->n_experts; dn.N = d->d_latent; dn.K = d->d_ff;
@@ -706,17 +706,32 @@ int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, int64_t ld, uint8
   return MOE_OK;
 }
 
-int moe_mxfp4_tile_scales(const uint8_t* scale, uint8_t* out, int64_t rows, int32_t K, void* stream) {
+namespace {
+// do the byte ranges [a, a + na) and [b, b + nb) share a byte?
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
+}
+}
+
+int moe_mxfp4_tile(const uint8_t* data, const uint8_t* scale, uint8_t* data_out, uint8_t* scale_out,
+                   int64_t rows, int32_t K, void* stream) {
   g_last_error.clear();
   if (rows < 0 || K <= 0 || K % 128 || rows % 64)
     return fail(MOE_ERR_INVALID_ARG, "rows >= 0 with rows %% 64 == 0 and K > 0 with K %% 128 == 0 required");
   if (rows == 0) return MOE_OK;
-  if (scale == nullptr || out == nullptr) return fail(MOE_ERR_INVALID_ARG, "scale or out is NULL");
-  if (((uintptr_t)scale | (uintptr_t)out) % 4)
-    return fail(MOE_ERR_INVALID_ARG, "scale and out must be 4-byte aligned");
-  const uintptr_t a = (uintptr_t)scale, b = (uintptr_t)out, n = (uintptr_t)(rows * (K / 32));
-  if (a < b + n && b < a + n) return fail(MOE_ERR_INVALID_ARG, "scale and out overlap");
-  MOE_LAUNCH(moe::launch_tile_scales(scale, out, rows, K, (hipStream_t)stream), "mxfp4_tile_scales");
+  MOE_CHECK(need_ptr(data, "data"));
+  MOE_CHECK(need_ptr(data_out, "data_out"));
+  if (scale == nullptr || scale_out == nullptr) return fail(MOE_ERR_INVALID_ARG, "scale or scale_out is NULL");
+  if (((uintptr_t)scale | (uintptr_t)scale_out) % 4)
+    return fail(MOE_ERR_INVALID_ARG, "scale and scale_out must be 4-byte aligned");
+  const int64_t nd = rows * (K / 2), ns = rows * (K / 32);
+  if (overlap(data_out, nd, data, nd) || overlap(data_out, nd, scale, ns) ||
+      overlap(scale_out, ns, data, nd) || overlap(scale_out, ns, scale, ns) ||
+      overlap(data_out, nd, scale_out, ns))
+    return fail(MOE_ERR_INVALID_ARG, "an output overlaps an input or the other output");
+  MOE_LAUNCH(moe::launch_tile_mxfp4(data, scale, data_out, scale_out, rows, K, (hipStream_t)stream),
+             "mxfp4_tile");
   return MOE_OK;
 }
 

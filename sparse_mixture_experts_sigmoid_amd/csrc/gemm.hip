@@ -1057,11 +1057,13 @@ struct Src {
   rsrc_t ra, rb, rsa, rsb;      // A codes, B packed, A scales, B scales
   uint32_t aoff[2], boff[kBQ];  // data row offsets of this lane's rows in load q
   uint32_t asoff, bsoff;        // scale offsets of stage 0 (lanes 0-15 / 0 .. kBRW-1), or kOOB
-  uint32_t bsstep;              // B scale bytes between stages: 4 (rows) or 256 (stage-tiled)
+  uint32_t bdstep, bsstep;      // B data / scale bytes between stages: 64 / 4 (row-major) or
+                                // 128 / 256 (tiled layout)
 };
 
 // Stage kt into buf (LDS byte buffer). A chunk c (16 bytes) of tile row r sits
-// in slot c ^ swz_a(r); B chunk c in slot c ^ swz_b(r).
+// in slot c ^ swz_a(r); B chunk c in slot c ^ swz_b(r). B chunk c of a row's
+// stage kt is at its offset boff + bdstep kt + 16 c in either layout.
 __device__ __forceinline__ void stage_issue(uint8_t* buf, const Src& s, int kt, int K) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1081,7 +1083,8 @@ __device__ __forceinline__ void stage_issue(uint8_t* buf, const Src& s, int kt, 
     const int k = kt * kBK + 32 * c;          // fp4: 32 elements per chunk
     const uint32_t o = s.boff[q];
     __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rb, (lds_ptr_t)(buf + kA + row0 * kBrow), 16,
-                                             (k < K && o != kOOB) ? o + (uint32_t)(k / 2) : kOOB,
+                                             (k < K && o != kOOB) ? o + s.bdstep * (uint32_t)kt + 16u * (uint32_t)c
+                                                                  : kOOB,
                                              0, 0, 0);
   }
   // four scale bytes (k-blocks 4kt .. 4kt+3) per row; K % 128 == 0
@@ -1188,13 +1191,20 @@ __device__ __forceinline__ void mainloop_rows(uint8_t* s0, uint8_t* s1, uint8_t*
   __shared__ __align__(16) uint8_t mx1[mx8::kStage];          \
   __shared__ __align__(16) uint8_t mx2[mx8::kStage]
 
-// B scale offset of wave-row `first + lane` at stage 0 and the step between
-// stages. Row-major scales [R, K/32]: the row's own K/32 bytes, 4 per stage.
-// Stage-tiled scales [R/64][K/128][64][4]: 64-row tiles, each stage's 4 bytes
-// of the tile's 64 rows contiguous (256 bytes), so one wave load of its 64 rows
-// reads two whole cache lines instead of 4 bytes from each of 64 rows. `first`
-// is 64-aligned in absolute rows (the callers require d_ff, d_latent % 128).
+// B offsets at stage 0 and the steps between stages. Row-major: packed row r
+// at r K/2 (64 bytes a stage), scales at r K/32 (4 bytes a stage). Tiled
+// layout: the packed bytes of rows 2p and 2p+1 interleaved per stage
+// ([R/2][K/128][2][64]), so that a stage of a row pair is one 128-byte cache
+// line; the scales stage-tiled ([R/64][K/128][64][4]), so that a stage's
+// scales of 64 rows are 256 contiguous bytes instead of 4 bytes from each of
+// 64 rows. Row r of the data load is relative to an even row; `first` (the
+// wave's first scale row) is 64-aligned in absolute rows (the callers require
+// d_ff, d_latent % 128).
+__device__ __forceinline__ uint32_t b_data_off(bool tiled, int r, int K) {
+  return tiled ? (uint32_t)((r >> 1) * K + (r & 1) * 64) : (uint32_t)(r * (K / 2));
+}
 __device__ __forceinline__ void b_scale_src(Src& s, bool tiled, int first, int lane, int K, bool live) {
+  s.bdstep = tiled ? 128u : 64u;
   s.bsstep = tiled ? 256u : 4u;
   s.bsoff = !live ? kOOB
                   : tiled ? (uint32_t)(first * (K / 32) + 4 * lane) : (uint32_t)((first + lane) * (K / 32));
@@ -1218,7 +1228,7 @@ __device__ __forceinline__ void b_src_glu(Src& s, const WOperand& g, const WOper
 #pragma unroll
   for (int q = 0; q < kBQ; ++q) {
     const int fl = fbase + 16 * q + (lane >> 2);
-    s.boff[q] = fl < nf ? (uint32_t)(fl * (K / 2)) : kOOB;
+    s.boff[q] = fl < nf ? b_data_off(tiled, fl, K) : kOOB;
   }
   b_scale_src(s, tiled, fbase, lane, K, lane < kBRW && fbase + lane < nf);
 }
@@ -1233,7 +1243,7 @@ __device__ __forceinline__ void b_src_plain(Src& s, const WOperand& wo, int64_t 
 #pragma unroll
   for (int q = 0; q < kBQ; ++q) {
     const int r = kBRW * w + 16 * q + (lane >> 2);
-    s.boff[q] = r < nrows ? (uint32_t)(r * (K / 2)) : kOOB;
+    s.boff[q] = r < nrows ? b_data_off(tiled, r, K) : kOOB;
   }
   b_scale_src(s, tiled, kBRW * w, lane, K, lane < kBRW && kBRW * w + lane < nrows);
 }
@@ -1273,7 +1283,7 @@ __global__ __launch_bounds__(512) void grouped_glu_mx8_kernel(GroupedGluArgs a) 
     }
     s.asoff = off;
   }
-  mx8::b_src_glu(s, a.Wg, a.Wv, (int64_t)e * a.F, a.K, f0, a.F, a.w_scale_tiled != 0);
+  mx8::b_src_glu(s, a.Wg, a.Wv, (int64_t)e * a.F, a.K, f0, a.F, a.w_tiled != 0);
   Acc<C> acc;
   acc_zero(acc);
   mx8::mainloop_rows(mx0, mx1, mx2, s, a.K, row_hi - row_lo, acc);
@@ -1306,7 +1316,7 @@ __global__ __launch_bounds__(512) void grouped_down_mx8_kernel(GroupedDownArgs a
   }
   const int rs = 16 * w + lane;
   s.asoff = (lane < 16 && rs < nrows) ? (uint32_t)(rs * (a.K / 32)) : kOOB;
-  mx8::b_src_plain(s, a.Wo, (int64_t)e * a.N, a.K, n0, a.N, a.w_scale_tiled != 0);
+  mx8::b_src_plain(s, a.Wo, (int64_t)e * a.N, a.K, n0, a.N, a.w_tiled != 0);
   Acc<C> acc;
   acc_zero(acc);
   mx8::mainloop_rows(mx0, mx1, mx2, s, a.K, row_hi - row_lo, acc);
@@ -1383,7 +1393,7 @@ int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream) {
   if (a.max_tiles == 0) return 0;
   if (a.act_mx8) {
     if (a.bm != mx8::L::BM || a.Wg.dtype != DT_MXFP4 || a.K % mx8::kBK) return -1;
-    if (a.w_scale_tiled && (a.F % 64 || mx8::kBRW != 64)) return -1;
+    if (a.w_tiled && (a.F % 64 || mx8::kBRW != 64)) return -1;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.F, mx8::L::BN / 2) * a.max_tiles));
     hipLaunchKernelGGL(grouped_glu_mx8_kernel, grid, dim3(mx8::L::NT), 0, stream, a);
     return (int)hipGetLastError();
@@ -1401,7 +1411,7 @@ int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream) {
   if (a.max_tiles == 0) return 0;
   if (a.act_mx8) {
     if (a.bm != mx8::L::BM || a.Wo.dtype != DT_MXFP4 || a.K % mx8::kBK) return -1;
-    if (a.w_scale_tiled && (a.N % 64 || mx8::kBRW != 64)) return -1;
+    if (a.w_tiled && (a.N % 64 || mx8::kBRW != 64)) return -1;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.N, mx8::L::BN) * a.max_tiles));
     hipLaunchKernelGGL(grouped_down_mx8_kernel, grid, dim3(mx8::L::NT), 0, stream, a);
     return (int)hipGetLastError();

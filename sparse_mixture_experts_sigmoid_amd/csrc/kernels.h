@@ -134,8 +134,8 @@ struct GroupedGluArgs {
   int act_mx8;                       // Z holds MXFP8 codes ([T, K] bytes, row stride ldz
                                      // bytes) with scales z_scale [T, K/32]: scaled MFMA
   const uint8_t* z_scale;
-  int w_scale_tiled;                 // act_mx8 only: Wg / Wv scales stage-tiled
-                                     // [R/64][K/128][64][4] (launch_tile_scales)
+  int w_tiled;                       // act_mx8 only: Wg / Wv in the tiled layout
+                                     // (launch_tile_mxfp4)
 };
 int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream);
 // Tile rows of the grouped expert kernels: 1 (fp32 path), 32 (few rows per
@@ -158,16 +158,20 @@ struct GroupedDownArgs {
   int act_mx8;                       // H holds MXFP8 codes ([rows, K] bytes, row stride
                                      // ldh bytes) with scales h_scale [rows, K/32]
   const uint8_t* h_scale;
-  int w_scale_tiled;                 // act_mx8 only: Wo scales stage-tiled
+  int w_tiled;                       // act_mx8 only: Wo in the tiled layout
 };
 // MXFP8 (E4M3 + e8m0 per 32) rows of a bf16 matrix [rows, K] (row stride ld
 // elements; K % 32 == 0): codes [rows, K], scales [rows, K/32] (OCP MX rule:
 // X = floor(log2 amax) - 8, elements rounded to nearest even, saturating).
 int launch_quantize_mx8(const void* in, int64_t rows, int K, int64_t ld, uint8_t* codes,
                         uint8_t* scales, hipStream_t stream);
-// Stage-tiled copy of row-major MXFP4 scales [rows, K/32] (rows % 64 == 0,
-// K % 128 == 0): byte (r, b) goes to ((r/64)(K/128) + b/4) 256 + (r%64) 4 + b%4.
-int launch_tile_scales(const uint8_t* in, uint8_t* out, int64_t rows, int K, hipStream_t stream);
+// Tiled copy of a row-major MXFP4 weight [rows, K] (rows % 64 == 0, K % 128
+// == 0) for the scaled-MFMA kernels: packed byte j (0..63) of row r's stage kt
+// (bytes 64kt .. 64kt+63 of the row) goes to ((r/2)(K/128) + kt) 128 +
+// (r%2) 64 + j; scale byte (r, b) goes to ((r/64)(K/128) + b/4) 256 + (r%64) 4
+// + b%4.
+int launch_tile_mxfp4(const uint8_t* data, const uint8_t* scale, uint8_t* data_out, uint8_t* scale_out,
+                      int64_t rows, int K, hipStream_t stream);
 int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream);
 
 // y[M, N] = sum over segments s of A_s[M, K_s] B_s[N, K_s]^T (fp32 accumulate).

@@ -129,16 +129,34 @@ __global__ __launch_bounds__(256) void tile_scales_kernel(const uint32_t* __rest
   }
 }
 
+// One thread per output 16-byte chunk of the packed bytes: chunk c (0..3) of
+// row 2p + h's stage kt, with h = which row of the pair.
+__global__ __launch_bounds__(256) void pair_rows_kernel(const uint4* __restrict__ in, uint4* __restrict__ out,
+                                                        int64_t rows, int nk) {
+  const int64_t n = rows * nk * 4;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t pair = i / (8 * (int64_t)nk);
+    const int rem = (int)(i - pair * 8 * nk);
+    const int kt = rem >> 3, h = (rem >> 2) & 1, c = rem & 3;
+    out[i] = in[(2 * pair + h) * (4 * (int64_t)nk) + 4 * kt + c];
+  }
+}
+
 }  // namespace
 
-int launch_tile_scales(const uint8_t* in, uint8_t* out, int64_t rows, int K, hipStream_t stream) {
-  if (rows % 64 || K % 128 || ((uintptr_t)in | (uintptr_t)out) % 4) return -1;
+int launch_tile_mxfp4(const uint8_t* data, const uint8_t* scale, uint8_t* data_out, uint8_t* scale_out,
+                      int64_t rows, int K, hipStream_t stream) {
+  if (rows % 64 || K % 128 || ((uintptr_t)scale | (uintptr_t)scale_out) % 4 ||
+      ((uintptr_t)data | (uintptr_t)data_out) % 16)
+    return -1;
   if (rows == 0) return 0;
   const int nk = K / 128;
-  const int64_t n = rows * nk;
-  const int64_t blocks = ceil_div(n, 256) < 16384 ? ceil_div(n, 256) : 16384;
-  hipLaunchKernelGGL(tile_scales_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const uint32_t*)in, (uint32_t*)out, rows, nk);
+  const int64_t nd = rows * nk * 4, ns = rows * nk;
+  hipLaunchKernelGGL(pair_rows_kernel, dim3((unsigned)(ceil_div(nd, 256) < 16384 ? ceil_div(nd, 256) : 16384)),
+                     dim3(256), 0, stream, (const uint4*)data, (uint4*)data_out, rows, nk);
+  hipLaunchKernelGGL(tile_scales_kernel, dim3((unsigned)(ceil_div(ns, 256) < 16384 ? ceil_div(ns, 256) : 16384)),
+                     dim3(256), 0, stream, (const uint32_t*)scale, (uint32_t*)scale_out, rows, nk);
   return (int)hipGetLastError();
 }
 

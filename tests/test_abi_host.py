@@ -71,8 +71,8 @@ def _desc(**kw):
     (dict(n_experts=5000, top_k=16), moe.MOE_ERR_UNSUPPORTED),
     (dict(n_shared=8), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=300_000), moe.MOE_ERR_UNSUPPORTED),                # z over 2 GiB (32-bit gather offsets)
-    (dict(expert_w_scale_tiled=2), moe.MOE_ERR_INVALID_ARG),
-    (dict(expert_w_scale_tiled=1), moe.MOE_ERR_UNSUPPORTED),   # tiled scales without MXFP8 inputs
+    (dict(expert_w_tiled=2), moe.MOE_ERR_INVALID_ARG),
+    (dict(expert_w_tiled=1), moe.MOE_ERR_UNSUPPORTED),         # tiled weights without MXFP8 inputs
 ])
 def test_invalid_descriptors(kw, status):
     d = _desc(**kw)
@@ -164,21 +164,30 @@ def test_mxfp4_scales_must_be_4_byte_aligned():
 def test_tiled_scale_configs_are_valid():
     for name in ("k3_decode_mx8", "k3_prefill_mx8"):
         d = moe.make_desc(synth.config(name))
-        assert d.expert_w_scale_tiled == 1 and d.expert_act_mxfp8 == 1
+        assert d.expert_w_tiled == 1 and d.expert_act_mxfp8 == 1
         assert moe.moe_check_desc(d) == moe.MOE_OK
 
 
-@pytest.mark.parametrize("rows,K,src,dst,status", [
-    (64, 100, FAKE, FAKE + (1 << 20), moe.MOE_ERR_INVALID_ARG),      # K % 128
-    (96, 128, FAKE, FAKE + (1 << 20), moe.MOE_ERR_INVALID_ARG),      # rows % 64
-    (-64, 128, FAKE, FAKE + (1 << 20), moe.MOE_ERR_INVALID_ARG),
-    (64, 128, None, FAKE + (1 << 20), moe.MOE_ERR_INVALID_ARG),
-    (64, 128, FAKE, FAKE + 2, moe.MOE_ERR_INVALID_ARG),               # misaligned
-    (64, 128, FAKE, FAKE + 128, moe.MOE_ERR_INVALID_ARG),             # overlaps (256 bytes)
-    (0, 128, None, None, moe.MOE_OK),                                  # nothing to do
+B1 = FAKE + (1 << 20)               # a second, disjoint buffer
+B2 = FAKE + (2 << 20)
+B3 = FAKE + (3 << 20)
+
+
+@pytest.mark.parametrize("rows,K,ptrs,status", [
+    (64, 100, (FAKE, B1, B2, B3), moe.MOE_ERR_INVALID_ARG),      # K % 128
+    (96, 128, (FAKE, B1, B2, B3), moe.MOE_ERR_INVALID_ARG),      # rows % 64
+    (-64, 128, (FAKE, B1, B2, B3), moe.MOE_ERR_INVALID_ARG),
+    (64, 128, (None, B1, B2, B3), moe.MOE_ERR_INVALID_ARG),
+    (64, 128, (FAKE, B1, B2, None), moe.MOE_ERR_INVALID_ARG),
+    (64, 128, (MIS, B1, B2, B3), moe.MOE_ERR_INVALID_ARG),       # data not 16-byte aligned
+    (64, 128, (FAKE, B1 + 2, B2, B3), moe.MOE_ERR_INVALID_ARG),  # scale not 4-byte aligned
+    (64, 128, (FAKE, B1, FAKE + 2048, B3), moe.MOE_ERR_INVALID_ARG),  # data_out overlaps data (4 KB)
+    (64, 128, (FAKE, B1, B2, B1 + 128), moe.MOE_ERR_INVALID_ARG),     # scale_out overlaps scale (256 B)
+    (64, 128, (FAKE, B1, B2, B2 + 4000), moe.MOE_ERR_INVALID_ARG),    # the two outputs overlap
+    (0, 128, (None, None, None, None), moe.MOE_OK),                    # nothing to do
 ])
-def test_tile_scales_validates_before_any_launch(rows, K, src, dst, status):
-    assert moe.lib().moe_mxfp4_tile_scales(src, dst, rows, K, None) == status
+def test_tile_validates_before_any_launch(rows, K, ptrs, status):
+    assert moe.lib().moe_mxfp4_tile(*ptrs, rows, K, None) == status
 
 
 def test_staged_entry_points_validate():

@@ -115,28 +115,32 @@ def test_layer_mx8_full_parity(cfg, device):
 
 
 @pytest.mark.parametrize("rows,K", [(64, 128), (192, 3584), (1920, 384), (0, 128)])
-def test_tile_scales_is_the_documented_permutation(rows, K, device):
-    """moe_mxfp4_tile_scales moves byte (r, b) of [rows, K/32] to
-    ((r/64)(K/128) + b/4) 256 + (r%64) 4 + b%4, bit for bit (numpy reshape of
-    the same order as the expected value)."""
+def test_tile_is_the_documented_permutation(rows, K, device):
+    """moe_mxfp4_tile reorders the bytes of an MXFP4 weight as documented,
+    bit for bit (numpy reshapes of the same order give the expected values):
+    packed byte j of row r's stage kt to ((r/2)(K/128) + kt) 128 + (r%2) 64 + j,
+    scale byte (r, b) to ((r/64)(K/128) + b/4) 256 + (r%64) 4 + b%4."""
     rng = np.random.default_rng(rows + K)
+    d = rng.integers(0, 256, (rows, K // 2), dtype=np.uint8)
     s = rng.integers(0, 256, (rows, K // 32), dtype=np.uint8)
-    src = torch.from_numpy(s).to(device)
-    out = torch.full_like(src, 0xAB)
-    moe.moe_mxfp4_tile_scales(src, out)
+    dsrc, ssrc = torch.from_numpy(d).to(device), torch.from_numpy(s).to(device)
+    dout, sout = torch.full_like(dsrc, 0xAB), torch.full_like(ssrc, 0xAB)
+    moe.moe_mxfp4_tile(dsrc, ssrc, dout, sout)
     torch.cuda.synchronize()
-    want = s.reshape(rows // 64, 64, K // 128, 4).transpose(0, 2, 1, 3).reshape(rows, K // 32)
-    assert np.array_equal(out.cpu().numpy(), want)
+    want_d = d.reshape(rows // 2, 2, K // 128, 64).transpose(0, 2, 1, 3).reshape(rows, K // 2)
+    want_s = s.reshape(rows // 64, 64, K // 128, 4).transpose(0, 2, 1, 3).reshape(rows, K // 32)
+    assert np.array_equal(dout.cpu().numpy(), want_d)
+    assert np.array_equal(sout.cpu().numpy(), want_s)
 
 
 @pytest.mark.parametrize("cfg", [MX8_SMALL, MX8_MID], ids=lambda c: c.name)
-def test_layer_mx8_tiled_scales(cfg, device):
-    """Stage-tiled expert scales change only where the kernels read the scale
-    bytes: the layer output equals, bit for bit, the row-major run's, and both
-    meet the oracle."""
+def test_layer_mx8_tiled_weights(cfg, device):
+    """Tiled expert weights change only where the kernels read the weight and
+    scale bytes: the layer output equals, bit for bit, the row-major run's, and
+    both meet the oracle."""
     inp = synth.device_inputs(cfg, device)
     y_rows, idx, gate, _ = run_layer(cfg, inp, device)
-    cfg_t = cfg.replace(name=cfg.name + "_tiled", expert_scales="tiled")
+    cfg_t = cfg.replace(name=cfg.name + "_tiled", expert_layout="tiled")
     y_t, idx_t, gate_t, _ = run_layer(cfg_t, inp, device)
     assert torch.equal(idx, idx_t) and torch.equal(gate, gate_t)
     assert torch.equal(y_rows, y_t)

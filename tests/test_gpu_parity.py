@@ -198,7 +198,7 @@ def test_layer_small_full_parity(cfg, device):
                                              expert_act="mxfp8"),
                                  LayerConfig("small_mx8_tiled", T=0, d=128, d_lat=128, E=10, k=3, F=256,
                                              S=1, Fs=96, seed=41, expert_w="mxfp4", latent_w="mxfp4",
-                                             expert_act="mxfp8", expert_scales="tiled")],
+                                             expert_act="mxfp8", expert_layout="tiled")],
                          ids=lambda c: c.name)
 def test_layer_empty_batch(cfg, device):
     """T = 0: the layer returns MOE_OK without touching token buffers (NULL here,

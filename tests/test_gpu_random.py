@@ -1,8 +1,8 @@
 """GPU parity on seeded random layer shapes: 24 small layers whose sizes,
 expert counts, top-k, shared-expert counts, bias laws and weight formats are
 drawn from a fixed seed (bf16, MXFP4 weights, and MXFP4 weights with MXFP8
-expert inputs in turn, the latter with row-major and stage-tiled expert
-scales alternately). Every token is checked: routing bit-exact, gates
+expert inputs in turn, the latter with row-major and tiled expert weights
+alternately). Every token is checked: routing bit-exact, gates
 within 1e-6 relative, y within the tolerance of its format."""
 import numpy as np
 import pytest
@@ -38,7 +38,7 @@ def draw(i: int) -> LayerConfig:
     if kind == "mx8":
         kw["expert_act"] = "mxfp8"
         if (i // 3) % 2:
-            kw["expert_scales"] = "tiled"
+            kw["expert_layout"] = "tiled"
     return LayerConfig(f"rnd{i}_{kind}", T=T, d=d, d_lat=d_lat, E=E, k=k, F=F, S=S, Fs=Fs,
                        seed=500 + i, bias=bias, **kw)
 
