@@ -15,8 +15,9 @@ also be timed.
 roofline: the dominant kernel's algorithmic rate from HIP events recorded by
 the library around every stage of the timed calls (moe_trace_*), on the stream
 the kernels run on. Decode: the expert gate/up grouped GEMM is HBM-bound; its
-algorithmic bytes per launch = (touched experts) x 2*F*d_lat*2 B (W_g and W_v)
-+ (T*k routed rows) x (d_lat + F)*2 B (gathered z rows in, h rows out).
+algorithmic bytes per launch = (touched experts) x 2*F*d_lat*w B (W_g and W_v;
+w = 2 for bf16, 17/32 for MXFP4 with its scales) + (T*k routed rows) x
+(z row in + h row out: d_lat*2 + F*2 B, or d_lat*33/32 + F*2 B with MXFP8 z).
 Prefill: the same kernel is MFMA-bound; flops per launch = T*k*2*2*d_lat*F.
 
 roofline.traffic: HBM bytes per launch of that kernel from rocprofv3 PMC
@@ -192,22 +193,26 @@ def main():
     abytes = 4 if cfg.act == "f32" else 2
     t_gu = stages["expert_gate_up"] * 1e-3
     decode = cfg.name.startswith("k3_decode")
+    mx8 = cfg.expert_act == "mxfp8"
+    gu_name = ("expert_gate_up (MXFP8 quantise of z + scaled-MFMA grouped GEMM + SiTU-GLU)" if mx8
+               else "expert_gate_up (grouped GEMM + SiTU-GLU)")
     if decode:
-        algo = touched * 2 * cfg.F * cfg.d_lat * wbytes + rows * (cfg.d_lat + cfg.F) * abytes
+        # weights of the touched experts + per routed row its z row in (bf16, or
+        # MXFP8 codes and scales) and its bf16 h row out
+        zrow = cfg.d_lat * (1 + 1 / 32) if mx8 else cfg.d_lat * abytes
+        algo = touched * 2 * cfg.F * cfg.d_lat * wbytes + rows * (zrow + cfg.F * abytes)
         achieved = algo / t_gu / 1e9
-        roof = {"bound": "hbm", "kernel": "expert_gate_up (grouped GEMM + SiTU-GLU)",
+        roof = {"bound": "hbm", "kernel": gu_name,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name),
                 "algorithmic_bytes_per_launch": int(algo), "avg_launch_ms": round(t_gu * 1e3, 4)}
     else:
         algo = rows * 2 * 2 * cfg.d_lat * cfg.F
         achieved = algo / t_gu / 1e12
-        mx8 = cfg.expert_act == "mxfp8"
         f32 = cfg.act == "f32"
         peak = MFMA_FP8_PEAK_TFLOPS if mx8 else VALU_FP32_PEAK_TFLOPS if f32 else MFMA_BF16_PEAK_TFLOPS
         roof = {"bound": "alu" if f32 else "mfma",
-                "kernel": ("expert_gate_up (MXFP8 quantise of z + scaled-MFMA grouped GEMM + SiTU-GLU)"
-                           if mx8 else "expert_gate_up (grouped GEMM + SiTU-GLU)"),
+                "kernel": gu_name,
                 "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4),
                 "traffic": measured_traffic(cfg.name),
