@@ -138,8 +138,9 @@ struct GroupedGluArgs {
                                      // (launch_tile_mxfp4)
 };
 int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream);
-// Tile rows of the grouped expert kernels: 1 (fp32 path), 32 (few rows per
-// expert: the weight-streaming kernel) or 128 (the LDS-tiled MFMA kernel).
+// Tile rows of the grouped expert kernels: 1 (fp32 path) or 128 (the LDS-tiled
+// MFMA kernels, at every batch size: at decode the weight stream runs at the
+// same rate with 32- or 64-row tiles, so one tiling serves both).
 int grouped_bm(int act_dtype, int64_t rows, int E);
 
 // down: O[r] = H[r] Wo[e]^T, Wo [E, N, K].

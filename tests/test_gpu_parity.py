@@ -251,8 +251,7 @@ def test_staged_entry_points_equal_layer(device):
 def test_mxfp4_path_equals_bf16_path_on_decoded_weights(cfg, device):
     """MXFP4 decoding is exact: the MXFP4 layer must equal, bit for bit, the bf16
     layer run on the decoded weights (same kernels, same accumulation order).
-    The small layer takes the weight-streaming expert kernels, the mid one the
-    LDS-tiled ones."""
+    The small layer has one row tile per expert, the mid one several, ragged."""
     inp = synth.device_inputs(cfg, device)
     y_mx, _, _, _ = run_layer(cfg, inp, device)
     dec = dict(inp)
