@@ -40,8 +40,8 @@
  *   MXFP4 weight [R, K]: data = packed bytes [R, K/2] (element 2i in the low
  *   nibble of byte i, 16-byte aligned like every tensor), scale = e8m0 bytes
  *   [R, K/32] (4-byte aligned).
- *   Tiled MXFP4 weight (routed experts only, see expert_w_tiled; made by
- *   moe_mxfp4_tile; R % 64 == 0, K % 128 == 0): the
+ *   Tiled MXFP4 weight (routed experts on the MXFP8 path only, see
+ *   expert_w_tiled; made by moe_mxfp4_tile; R % 64 == 0, K % 128 == 0): the
  *   same bytes reordered. Packed: byte j (0..63) of row r's 128-element stage
  *   kt (row-major byte 64 kt + j of the row) at ((r/2) (K/128) + kt) 128 +
  *   (r%2) 64 + j, i.e. [R/2][K/128][2][64]: a stage of a row pair is one
@@ -112,11 +112,11 @@ typedef struct {
      the same way). */
   int32_t expert_act_mxfp8;
   /* 0: W_g, W_v, W_o row-major. 1: in the tiled MXFP4 layout above (made once
-     per weight set by moe_mxfp4_tile); needs expert_w_dtype MOE_MXFP4 and
-     d_latent, d_ff multiples of 128. The expert kernels (both the bf16 MFMA on
-     decoded weights and the scaled MFMA) then read a K stage of a row pair
-     from one cache line and the scales of 64 rows from contiguous bytes,
-     instead of pieces of separate rows. Same results either way. */
+     per weight set by moe_mxfp4_tile); needs expert_act_mxfp8 = 1. The
+     scaled-MFMA expert kernels then read each 128-element K stage as whole
+     128-byte lines of row pairs and the stage's scales of 64 weight rows as
+     256 contiguous bytes, instead of half lines and 4 bytes from each of 64
+     rows. Same results either way. */
   int32_t expert_w_tiled;
 } moe_desc_t;
 
@@ -230,7 +230,7 @@ int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, int64_t ld, uint8
 
 /* Tiled copy of an MXFP4 weight ("Kimi K3 ... Open Frontier Intelligence",
    section "MXFP4 Quantization-Aware Training": e2m1 elements with one e8m0
-   scale per 32 along K) for the routed-expert kernels: data [rows, K/2] and
+   scale per 32 along K) for the scaled-MFMA expert path: data [rows, K/2] and
    scale [rows, K/32] row-major in, data_out and scale_out in the tiled order
    given under Layouts. A pure permutation of bytes, made once when a weight
    set is loaded (W_g, W_v as rows = E * F, K = d_latent; W_o as rows =

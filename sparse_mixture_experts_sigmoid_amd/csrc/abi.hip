@@ -86,9 +86,9 @@ int check_desc(const moe_desc_t* d) {
                 "weights and d_latent, d_ff multiples of 128");
   if (d->expert_w_tiled != 0 && d->expert_w_tiled != 1)
     return fail(MOE_ERR_INVALID_ARG, "expert_w_tiled must be 0 or 1");
-  if (d->expert_w_tiled && (d->expert_w_dtype != MOE_MXFP4 || d->d_latent % 128 || d->d_ff % 128))
-    return fail(MOE_ERR_UNSUPPORTED, "tiled expert weights need MXFP4 expert weights and d_latent, d_ff "
-                "multiples of 128");
+  if (d->expert_w_tiled && !d->expert_act_mxfp8)
+    return fail(MOE_ERR_UNSUPPORTED, "tiled expert weights are read only by the MXFP8 expert path "
+                "(expert_act_mxfp8 = 1)");
   if (d->n_experts > kMaxExperts)
     return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", kMaxExperts);
   if (d->n_shared + 1 > moe::kMaxSegments)

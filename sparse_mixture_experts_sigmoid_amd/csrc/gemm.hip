@@ -125,28 +125,14 @@ __device__ __forceinline__ void dma_rows(const Rows<N>& rs, bf16_t* tile, int k0
 }
 
 // MXFP4 rows: unit j of thread t is tile row t / UR + (NT / UR) j and 32-element
-// block t % UR of the stage. Row-major weights: packed row r at r K/2, scales at
-// r K/32. Tiled weights (the routed experts' load-time layout: row pairs
-// interleaved per 128 elements, [R/2][K/128][2][64]; scales [R/64][K/128][64][4]):
-// row r's part of the offsets is (r/2) K + (r%2) 64 and (r/64)(K/128) 256 +
-// (r%64) 4, the k part (k/128) 128 + (k%128)/2 and (k/128) 256 + (k/32)%4. A
-// wave's units (64/UR rows, one stage) then read half lines of row pairs and
-// one line of scales instead of pieces of 64/UR separate rows.
+// block t % UR of the stage.
 template <int N>
 struct MxRows {
   rsrc_t rp[2], rs[2];   // packed bytes, e8m0 scales (gate / up for the GLU tile)
   int sel[N];            // resource of unit j (wave-uniform)
   uint32_t poff[N];      // packed-row byte offset, or kOOB
   uint32_t soff[N];      // scale-row byte offset
-  bool tiled;            // tiled layout (wave-uniform)
 };
-
-__device__ __forceinline__ uint32_t mx_row_doff(bool tiled, int r, int K) {
-  return tiled ? (uint32_t)((r >> 1) * K + (r & 1) * 64) : (uint32_t)(r * (K / 2));
-}
-__device__ __forceinline__ uint32_t mx_row_soff(bool tiled, int r, int K) {
-  return tiled ? (uint32_t)((r >> 6) * (K / 128) * 256 + (r & 63) * 4) : (uint32_t)(r * (K / 32));
-}
 
 struct MxStage {
   uint4 q;      // 32 e2m1 codes
@@ -161,15 +147,13 @@ __device__ __forceinline__ void load_mx(const MxRows<C::MXU>& m, int k0, int K,
                                         MxStage (&st)[C::MXU]) {
   const int k = k0 + (threadIdx.x % C::UR) * 32;
   const bool kin = k < K;
-  const uint32_t kd = m.tiled ? (uint32_t)((k >> 7) * 128 + ((k & 127) >> 1)) : (uint32_t)(k >> 1);
-  const uint32_t ks = m.tiled ? (uint32_t)((k >> 7) * 256 + ((k >> 5) & 3)) : (uint32_t)(k >> 5);
 #pragma unroll
   for (int j = 0; j < C::MXU; ++j) {
     const bool ok = kin && m.poff[j] != kOOB;
     const rsrc_t rp = m.sel[j] ? m.rp[1] : m.rp[0];
     const rsrc_t rsc = m.sel[j] ? m.rs[1] : m.rs[0];
-    st[j].q = bload16(rp, ok ? m.poff[j] + kd : kOOB);
-    st[j].s = __builtin_amdgcn_raw_buffer_load_b8(rsc, ok ? m.soff[j] + ks : kOOB, 0, 0);
+    st[j].q = bload16(rp, ok ? m.poff[j] + (uint32_t)(k / 2) : kOOB);
+    st[j].s = __builtin_amdgcn_raw_buffer_load_b8(rsc, ok ? m.soff[j] + (uint32_t)(k / 32) : kOOB, 0, 0);
   }
 }
 
@@ -494,9 +478,8 @@ __device__ __forceinline__ Rows<C::BR> b_rows_plain(const void* W, int K, int n0
 
 template <class C>
 __device__ __forceinline__ MxRows<C::MXU> b_mx_plain(const WOperand& w, int64_t row_base, int K, int n0,
-                                                     int N, bool tiled = false) {
+                                                     int N) {
   MxRows<C::MXU> m;
-  m.tiled = tiled;
   const int nrows = max(0, min(N - n0, C::BN));
   const int64_t r0 = row_base + n0;
   m.rp[0] = m.rp[1] = make_rsrc((const uint8_t*)w.data + r0 * (K / 2), (int64_t)nrows * (K / 2));
@@ -505,8 +488,8 @@ __device__ __forceinline__ MxRows<C::MXU> b_mx_plain(const WOperand& w, int64_t 
   for (int j = 0; j < C::MXU; ++j) {
     const int row = mx_row<C>(j);
     m.sel[j] = 0;
-    m.poff[j] = row < nrows ? mx_row_doff(tiled, row, K) : kOOB;
-    m.soff[j] = row < nrows ? mx_row_soff(tiled, row, K) : kOOB;
+    m.poff[j] = row < nrows ? (uint32_t)(row * (K / 2)) : kOOB;
+    m.soff[j] = row < nrows ? (uint32_t)(row * (K / 32)) : kOOB;
   }
   return m;
 }
@@ -542,13 +525,11 @@ __device__ __forceinline__ Rows<C::BR> b_rows_glu(const WOperand& g, const WOper
 
 template <class C>
 __device__ __forceinline__ MxRows<C::MXU> b_mx_glu(const WOperand& g, const WOperand& v,
-                                                   int64_t row_base, int K, int f0, int F,
-                                                   bool tiled = false) {
+                                                   int64_t row_base, int K, int f0, int F) {
   constexpr int H = C::BN / (2 * C::WGN);
   // a wave's units cover 64 / UR consecutive tile rows: all gate or all up
   static_assert(H % (64 / C::UR) == 0, "gate/up split must be wave-uniform");
   MxRows<C::MXU> m;
-  m.tiled = tiled;
   const int nf = max(0, min(F - f0, C::BN / 2));
   m.rp[0] = make_rsrc((const uint8_t*)g.data + (row_base + f0) * (K / 2), (int64_t)nf * (K / 2));
   m.rs[0] = make_rsrc(g.scale + (row_base + f0) * (K / 32), (int64_t)nf * (K / 32));
@@ -559,8 +540,8 @@ __device__ __forceinline__ MxRows<C::MXU> b_mx_glu(const WOperand& g, const WOpe
     const int tr = mx_row<C>(j);                            // tile row
     m.sel[j] = __builtin_amdgcn_readfirstlane((tr % (2 * H)) >= H ? 1 : 0);
     const int fl = (tr / (2 * H)) * H + (tr % H);
-    m.poff[j] = fl < nf ? mx_row_doff(tiled, fl, K) : kOOB;
-    m.soff[j] = fl < nf ? mx_row_soff(tiled, fl, K) : kOOB;
+    m.poff[j] = fl < nf ? (uint32_t)(fl * (K / 2)) : kOOB;
+    m.soff[j] = fl < nf ? (uint32_t)(fl * (K / 32)) : kOOB;
   }
   return m;
 }
@@ -746,7 +727,7 @@ __global__ __launch_bounds__(GroupCfg::NT) void grouped_glu_kernel(GroupedGluArg
   acc_zero(acc);
   Rows<C::BR> br{};
   MxRows<C::MXU> bm{};
-  if constexpr (B_MX) bm = b_mx_glu<C>(a.Wg, a.Wv, wrow, a.K, f0, a.F, a.w_tiled != 0);
+  if constexpr (B_MX) bm = b_mx_glu<C>(a.Wg, a.Wv, wrow, a.K, f0, a.F);
   else br = b_rows_glu<C>(a.Wg, a.Wv, wrow, a.K, f0, a.F);
   mainloop_rows<C, B_MX>(MOE_RING, ar, br, bm, a.K, row_hi - row_lo, acc);
   store_glu(acc, (bf16_t*)a.H, a.F, f0, a.F, a.c, [=](int tr) -> int64_t {
@@ -771,7 +752,7 @@ __global__ __launch_bounds__(GroupCfg::NT) void grouped_down_kernel(GroupedDownA
   acc_zero(acc);
   Rows<C::BR> br{};
   MxRows<C::MXU> bm{};
-  if constexpr (B_MX) bm = b_mx_plain<C>(a.Wo, wrow, a.K, n0, a.N, a.w_tiled != 0);
+  if constexpr (B_MX) bm = b_mx_plain<C>(a.Wo, wrow, a.K, n0, a.N);
   else br = b_rows_plain<C>((const bf16_t*)a.Wo.data + wrow * a.K, a.K, n0, a.N);
   mainloop_rows<C, B_MX>(MOE_RING, ar, br, bm, a.K, row_hi - row_lo, acc);
   store_tile(acc, (bf16_t*)a.O, a.N, row_lo, n0, row_hi, a.N);
@@ -1418,7 +1399,6 @@ int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream) {
     return (int)hipGetLastError();
   }
   if (a.bm != GroupCfg::BM) return -1;
-  if (a.w_tiled && (a.Wg.dtype != DT_MXFP4 || a.K % 128 || a.F % 64)) return -1;
   using C = GroupCfg;
   dim3 grid((unsigned)xcd_grid(ceil_div(a.F, C::BN / 2) * a.max_tiles));
   if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(grouped_glu_kernel<true>, grid, dim3(C::NT), 0, stream, a);
@@ -1437,7 +1417,6 @@ int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream) {
     return (int)hipGetLastError();
   }
   if (a.bm != GroupCfg::BM) return -1;
-  if (a.w_tiled && (a.Wo.dtype != DT_MXFP4 || a.K % 128 || a.N % 64)) return -1;
   using C = GroupCfg;
   dim3 grid((unsigned)xcd_grid(ceil_div(a.N, C::BN) * a.max_tiles));
   if (a.Wo.dtype == DT_MXFP4) hipLaunchKernelGGL(grouped_down_kernel<true>, grid, dim3(C::NT), 0, stream, a);

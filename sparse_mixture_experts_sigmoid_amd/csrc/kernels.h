@@ -134,7 +134,7 @@ struct GroupedGluArgs {
   int act_mx8;                       // Z holds MXFP8 codes ([T, K] bytes, row stride ldz
                                      // bytes) with scales z_scale [T, K/32]: scaled MFMA
   const uint8_t* z_scale;
-  int w_tiled;                       // MXFP4 Wg / Wv in the tiled layout
+  int w_tiled;                       // act_mx8 only: Wg / Wv in the tiled layout
                                      // (launch_tile_mxfp4)
 };
 int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream);
@@ -159,7 +159,7 @@ struct GroupedDownArgs {
   int act_mx8;                       // H holds MXFP8 codes ([rows, K] bytes, row stride
                                      // ldh bytes) with scales h_scale [rows, K/32]
   const uint8_t* h_scale;
-  int w_tiled;                       // MXFP4 Wo in the tiled layout
+  int w_tiled;                       // act_mx8 only: Wo in the tiled layout
 };
 // MXFP8 (E4M3 + e8m0 per 32) rows of a bf16 matrix [rows, K] (row stride ld
 // elements; K % 32 == 0): codes [rows, K], scales [rows, K/32] (OCP MX rule:
@@ -167,7 +167,7 @@ struct GroupedDownArgs {
 int launch_quantize_mx8(const void* in, int64_t rows, int K, int64_t ld, uint8_t* codes,
                         uint8_t* scales, hipStream_t stream);
 // Tiled copy of a row-major MXFP4 weight [rows, K] (rows % 64 == 0, K % 128
-// == 0) for the routed-expert kernels: packed byte j (0..63) of row r's stage kt
+// == 0) for the scaled-MFMA kernels: packed byte j (0..63) of row r's stage kt
 // (bytes 64kt .. 64kt+63 of the row) goes to ((r/2)(K/128) + kt) 128 +
 // (r%2) 64 + j; scale byte (r, b) goes to ((r/64)(K/128) + b/4) 256 + (r%64) 4
 // + b%4.

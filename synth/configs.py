@@ -38,7 +38,7 @@ class LayerConfig:
     latent_w: str = "bf16"     # W_down / W_up of the latent maps
     dense_w: str = "bf16"      # router and shared experts
     expert_act: str = "act"    # routed experts' GEMM inputs: "act" (act dtype) | "mxfp8"
-    expert_layout: str = "rows"  # MXFP4 expert weight layout: "rows" | "tiled" (d_lat, F % 128 == 0)
+    expert_layout: str = "rows"  # MXFP4 expert weight layout: "rows" | "tiled" (mxfp8 inputs only)
     bias: tuple = ("uniform", 0.05)   # ("uniform", halfwidth) | ("zipf", s, scale)
     c: float = 8.0             # SiTU-GLU cap
     eps: float = 1e-6          # RMSNorm epsilon

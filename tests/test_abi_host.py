@@ -72,9 +72,9 @@ def _desc(**kw):
     (dict(n_shared=8), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=300_000), moe.MOE_ERR_UNSUPPORTED),                # z over 2 GiB (32-bit gather offsets)
     (dict(expert_w_tiled=2), moe.MOE_ERR_INVALID_ARG),
-    (dict(expert_w_tiled=1), moe.MOE_ERR_UNSUPPORTED),         # tiled bf16 expert weights
-    (dict(expert_w_tiled=1, expert_w_dtype=moe.MOE_MXFP4, d_ff=3104),
-     moe.MOE_ERR_UNSUPPORTED),                                  # d_ff not a multiple of 128
+    (dict(expert_w_tiled=1), moe.MOE_ERR_UNSUPPORTED),         # tiled weights without MXFP8 inputs
+    (dict(expert_w_tiled=1, expert_w_dtype=moe.MOE_MXFP4, latent_w_dtype=moe.MOE_MXFP4),
+     moe.MOE_ERR_UNSUPPORTED),                                  # MXFP4, but bf16 expert inputs
 ])
 def test_invalid_descriptors(kw, status):
     d = _desc(**kw)
@@ -164,10 +164,9 @@ def test_mxfp4_scales_must_be_4_byte_aligned():
 
 
 def test_tiled_configs_are_valid():
-    for name in ("k3_decode_mx8", "k3_prefill_mx8", "k3_decode_mxfp4", "k3_prefill_mxfp4"):
-        cfg = synth.config(name).replace(expert_layout="tiled")
-        d = moe.make_desc(cfg)
-        assert d.expert_w_tiled == 1
+    for name in ("k3_decode_mx8", "k3_prefill_mx8"):
+        d = moe.make_desc(synth.config(name))
+        assert d.expert_w_tiled == 1 and d.expert_act_mxfp8 == 1
         assert moe.moe_check_desc(d) == moe.MOE_OK
 
 

@@ -264,30 +264,6 @@ def test_mxfp4_path_equals_bf16_path_on_decoded_weights(cfg, device):
     assert torch.equal(y_mx, y_b)
 
 
-# the exact MXFP4 path (bf16 MFMA on decoded weights) with tiled expert weights:
-# d_latent and d_ff multiples of 128; the mid one ragged in M and in the down N
-TILED_MX = [LayerConfig("small_mxfp4_128", T=70, d=96, d_lat=128, E=10, k=3, F=256, S=2, Fs=96, seed=15,
-                        expert_w="mxfp4", latent_w="mxfp4", bias=("uniform", 0.05)),
-            LayerConfig("mid_mxfp4_128", T=700, d=320, d_lat=384, E=6, k=2, F=384, S=1, Fs=160, seed=16,
-                        expert_w="mxfp4", latent_w="mxfp4", bias=("uniform", 0.05))]
-
-
-@pytest.mark.parametrize("cfg", TILED_MX, ids=lambda c: c.name)
-def test_mxfp4_tiled_weights_equal_row_major(cfg, device):
-    """Tiled expert weights change only where the exact MXFP4 kernels read the
-    packed and scale bytes: the layer output equals, bit for bit, the row-major
-    run's, and both meet the oracle."""
-    inp = synth.device_inputs(cfg, device)
-    y_rows, idx, gate, _ = run_layer(cfg, inp, device)
-    cfg_t = cfg.replace(name=cfg.name + "_tiled", expert_layout="tiled")
-    y_t, idx_t, gate_t, _ = run_layer(cfg_t, inp, device)
-    assert torch.equal(idx, idx_t) and torch.equal(gate, gate_t)
-    assert torch.equal(y_rows, y_t)
-    y_ref, inter = oracle.forward(cfg, synth.HostWeights(cfg), keep=True)
-    assert np.array_equal(idx.cpu().numpy(), inter["idx"])
-    check_y(cfg_t, to64(y_t), y_ref)
-
-
 def test_k3_decode_parity_and_determinism(device):
     cfg = synth.config("k3_decode")
     say("k3_decode: generating inputs on the GPU")
