@@ -138,7 +138,8 @@ void plan_permute(const moe_desc_t* d, Plan& p, LayerWs& w) {
 void plan_expert(const moe_desc_t* d, Plan& p, LayerWs& w) {
   w.tile_off = p.take((size_t)(d->n_experts + 1) * 4);
   w.tile_info = p.take((size_t)max_tiles(d) * 16);
-  w.H = p.take((size_t)d->T * d->top_k * d->d_ff * elem_bytes(d->act_dtype));
+  // bf16 h [T k, F]; the scaled-MFMA path writes h only in MXFP8 (hq, hqs)
+  w.H = p.take(d->expert_act_mxfp8 ? 0 : (size_t)d->T * d->top_k * d->d_ff * elem_bytes(d->act_dtype));
   if (d->expert_act_mxfp8) {
     const size_t rows = (size_t)d->T * d->top_k;
     w.zq = p.take((size_t)d->T * d->d_latent);
@@ -377,6 +378,8 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
   moe::GroupedGluArgs g{};
   g.Z = q8 ? (const void*)mx.zq : z; g.ldz = d->d_latent; g.T = d->T; g.rows_cap = rows_cap;
   g.act_mx8 = q8; g.z_scale = mx.zqs; g.w_tiled = d->expert_w_tiled;
+  // the scaled-MFMA path writes h straight in MXFP8 (the down GEMM's input)
+  g.hq = q8 ? mx.hq : nullptr; g.hqs = q8 ? mx.hqs : nullptr;
   g.perm_src = perm; g.topk = d->top_k; g.offsets = offsets; g.tile_off = tile_off;
   g.tile_info = tile_info;
   g.max_tiles = mt;
@@ -387,9 +390,6 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
   if (d->T > 0) MOE_LAUNCH(moe::launch_grouped_glu(g, st), "expert_gate_up");
   mk.end(5, st);
   mk.beg(6, st);
-  if (q8 && d->T > 0)
-    MOE_LAUNCH(moe::launch_quantize_mx8(H, rows_cap, d->d_ff, d->d_ff, mx.hq, mx.hqs, st),
-               "quantize_h");
   moe::GroupedDownArgs dn{};
   dn.H = q8 ? (const void*)mx.hq : H; dn.ldh = d->d_ff; dn.rows_cap = rows_cap;
   dn.act_mx8 = q8; dn.h_scale = mx.hqs; dn.w_tiled = d->expert_w_tiled;

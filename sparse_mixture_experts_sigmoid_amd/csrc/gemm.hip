@@ -1249,8 +1249,80 @@ __device__ __forceinline__ void b_src_plain(Src& s, const WOperand& wo, int64_t 
 }
 }  // namespace mx8
 
+namespace mx8 {
+// GLU epilogue that writes h already in MXFP8 (codes [rows, F], e8m0 scales
+// [rows, F/32]), the down GEMM's input, instead of bf16 h for a separate
+// quantisation pass: the same numbers as rounding h to bf16 and quantising
+// that row by row, step for step as the standalone quantiser does. The tile's
+// bf16 h (128 rows x 256 outputs) first goes to the LDS ring, free after the
+// main loop (rows 0-63 in lo, 64-127 in hi, 512 bytes a row); each thread then
+// quantises whole 32-output blocks of one row from 64 contiguous bytes and
+// stores their 32 codes as two 16-byte writes.
+template <class RowMap>
+__device__ __forceinline__ void store_glu_q8(const Acc<L>& acc, uint8_t* lo, uint8_t* hi, uint8_t* hq,
+                                             uint8_t* hqs, int f0, int F, float c, RowMap out_row) {
+  static_assert(L::BM == 128 && L::BN / 2 == 256 && kStage >= 64 * 512, "tile of h in the ring");
+  const int lane = threadIdx.x & 63, wn = wave_n<L>();
+  const float inv_c = 1.0f / c;
+#pragma unroll
+  for (int j = 0; j < L::WN / 2; ++j) {
+    const int fl = wn * glu_half_rows<L>() + j * 32 + (lane & 31);   // output within the tile
+#pragma unroll
+    for (int i = 0; i < L::WM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tr = acc_row<L>(i, r);
+        if (out_row(tr) < 0) continue;   // padding rows: never read back
+        bf16_t* row = (bf16_t*)((tr < 64 ? lo : hi) + (tr & 63) * 512);
+        row[fl] = f32_to_bf16(situ_glu(acc.c[i][j][r], acc.c[i][j + L::WN / 2][r], c, inv_c));
+      }
+  }
+  wg_barrier();
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = (int)threadIdx.x + L::NT * u;   // 128 rows x 8 blocks = 2 per thread
+    const int tr = q >> 3, b = q & 7;
+    const int f = f0 + 32 * b;
+    const int64_t orow = out_row(tr);
+    if (orow < 0 || f >= F) continue;
+    const uint4* src = (const uint4*)((tr < 64 ? lo : hi) + (tr & 63) * 512 + 64 * b);
+    uint32_t w[16];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint4 x = src[v];
+      w[4 * v] = x.x; w[4 * v + 1] = x.y; w[4 * v + 2] = x.z; w[4 * v + 3] = x.w;
+    }
+    float x[32];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      x[2 * e] = __uint_as_float(w[e] << 16);
+      x[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) amax = fmaxf(amax, fabsf(x[e]));
+    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+    const int X = ef == 0 ? -127 : max(-127, min(127, ef - 127 - 8));
+    uint32_t code[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float y[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) y[t] = fminf(fmaxf(__builtin_ldexpf(x[4 * e + t] + 0.0f, -X), -448.0f), 448.0f);
+      uint32_t p = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+      code[e] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)p, true);
+    }
+    uint4* dst = (uint4*)(hq + orow * F + f);
+    dst[0] = make_uint4(code[0], code[1], code[2], code[3]);
+    dst[1] = make_uint4(code[4], code[5], code[6], code[7]);
+    hqs[orow * (F / 32) + f / 32] = (uint8_t)(X + 127);
+  }
+}
+}  // namespace mx8
+
 // H[r] = act(zq[perm_src[r] / k] W_g[e]^T, ... W_v[e]^T) for the rows of expert e,
-// zq in MXFP8 (codes Z, scales z_scale), W_g / W_v in MXFP4.
+// zq in MXFP8 (codes Z, scales z_scale), W_g / W_v in MXFP4. With a.hq set the
+// rows go out in MXFP8 (hq, hqs) instead of bf16 H.
 __global__ __launch_bounds__(512) void grouped_glu_mx8_kernel(GroupedGluArgs a) {
   using C = mx8::L;
   MOE_MX8_RING;
@@ -1287,10 +1359,12 @@ __global__ __launch_bounds__(512) void grouped_glu_mx8_kernel(GroupedGluArgs a) 
   Acc<C> acc;
   acc_zero(acc);
   mx8::mainloop_rows(mx0, mx1, mx2, s, a.K, row_hi - row_lo, acc);
-  store_glu(acc, (bf16_t*)a.H, a.F, f0, a.F, a.c, [=](int tr) -> int64_t {
+  const auto rowmap = [=](int tr) -> int64_t {
     const int r = row_lo + tr;
     return (r >= 0 && r < row_hi) ? (int64_t)r : -1;
-  });
+  };
+  if (a.hq != nullptr) mx8::store_glu_q8(acc, mx0, mx1, a.hq, a.hqs, f0, a.F, a.c, rowmap);
+  else store_glu(acc, (bf16_t*)a.H, a.F, f0, a.F, a.c, rowmap);
 }
 
 // O[r] = hq[r] W_o[e]^T for the rows of expert e, hq in MXFP8 (codes H, scales

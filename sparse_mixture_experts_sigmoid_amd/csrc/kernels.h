@@ -136,6 +136,8 @@ struct GroupedGluArgs {
   const uint8_t* z_scale;
   int w_tiled;                       // act_mx8 only: Wg / Wv in the tiled layout
                                      // (launch_tile_mxfp4)
+  uint8_t* hq;                       // act_mx8 only, optional: write h as MXFP8 codes
+  uint8_t* hqs;                      // [rows, F] and scales [rows, F/32] instead of H
 };
 int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream);
 // Tile rows of the grouped expert kernels: 1 (fp32 path) or 128 (the LDS-tiled
