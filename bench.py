@@ -17,7 +17,7 @@ the library around every stage of the timed calls (moe_trace_*), on the stream
 the kernels run on. Decode: the expert gate/up grouped GEMM is HBM-bound; its
 algorithmic bytes per launch = (touched experts) x 2*F*d_lat*w B (W_g and W_v;
 w = 2 for bf16, 17/32 for MXFP4 with its scales) + (T*k routed rows) x
-(z row in + h row out: d_lat*2 + F*2 B, or d_lat*33/32 + F*2 B with MXFP8 z).
+(z row in + h row out: d_lat*2 + F*2 B, or (d_lat + F)*33/32 B in MXFP8).
 Prefill: the same kernel is MFMA-bound; flops per launch = T*k*2*2*d_lat*F.
 
 roofline.traffic: HBM bytes per launch of that kernel from rocprofv3 PMC
@@ -197,10 +197,11 @@ def main():
     gu_name = ("expert_gate_up (MXFP8 quantise of z + scaled-MFMA grouped GEMM + SiTU-GLU)" if mx8
                else "expert_gate_up (grouped GEMM + SiTU-GLU)")
     if decode:
-        # weights of the touched experts + per routed row its z row in (bf16, or
-        # MXFP8 codes and scales) and its bf16 h row out
+        # weights of the touched experts + per routed row its z row in and its h
+        # row out (bf16, or MXFP8 codes and scales on the scaled-MFMA path)
         zrow = cfg.d_lat * (1 + 1 / 32) if mx8 else cfg.d_lat * abytes
-        algo = touched * 2 * cfg.F * cfg.d_lat * wbytes + rows * (zrow + cfg.F * abytes)
+        hrow = cfg.F * (1 + 1 / 32) if mx8 else cfg.F * abytes
+        algo = touched * 2 * cfg.F * cfg.d_lat * wbytes + rows * (zrow + hrow)
         achieved = algo / t_gu / 1e9
         roof = {"bound": "hbm", "kernel": gu_name,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
