@@ -102,6 +102,19 @@ def test_workspace_sizes():
     assert moe.moe_workspace_bytes(dd, moe.MOE_OP_OUTPUT) >= hs + 2 * dec.T * dec.d * 4
 
 
+def test_mxfp8_workspace_holds_no_bf16_h():
+    """With MXFP8 expert inputs the gate/up writes h only as MXFP8 codes and
+    scales: the expert workspace is the bf16 path's minus the bf16 h rows plus
+    the MXFP8 z and h copies."""
+    mx8 = synth.config("k3_prefill_mx8")
+    bf = mx8.replace(expert_act="act", expert_layout="rows")
+    w8 = moe.moe_workspace_bytes(moe.make_desc(mx8), moe.MOE_OP_EXPERT_FFN)
+    wb = moe.moe_workspace_bytes(moe.make_desc(bf), moe.MOE_OP_EXPERT_FFN)
+    rows, F, dl = mx8.T * mx8.k, mx8.F, mx8.d_lat
+    mx_copies = mx8.T * dl * 33 // 32 + rows * F * 33 // 32
+    assert abs((w8 - wb) - (mx_copies - rows * F * 2)) <= 4 * 256   # 256-byte sub-buffer rounding
+
+
 FAKE = 0x7f0000001000          # a 16-byte-aligned address that is never dereferenced
 MIS = FAKE + 4                 # misaligned
 
