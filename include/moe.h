@@ -16,6 +16,10 @@
  *     "MXFP4 Quantization-Aware Training": MXFP4 weights (OCP MX v1.0 e2m1
  *     elements, one e8m0 scale per 32 elements along K).
  *
+ * Library state: none in device memory. On the host: the per-device side
+ * stream of moe_layer_forward (two events with it), the trace events of
+ * moe_trace_enable, and the thread-local error text of moe_last_error.
+ *
  * Calling convention (all entry points):
  *   - Every pointer argument is a DEVICE pointer (hipMalloc'd or equivalent)
  *     unless stated; descriptors and weight structs are HOST memory read
@@ -85,7 +89,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype_t;
 /* Which entry point a workspace is sized for. */
 typedef enum {
   MOE_OP_ROUTE = 0, MOE_OP_PERMUTE = 1, MOE_OP_LATENT_DOWN = 2, MOE_OP_EXPERT_FFN = 3,
-  MOE_OP_COMBINE = 4, MOE_OP_OUTPUT = 5, MOE_OP_LAYER = 6
+  MOE_OP_COMBINE = 4, MOE_OP_OUTPUT = 5, MOE_OP_LAYER = 6, MOE_OP_EXPERT_GATE_UP = 7
 } moe_op_t;
 
 typedef struct {
@@ -189,6 +193,25 @@ int moe_expert_ffn(const moe_desc_t* desc, const void* z, const int32_t* perm_sr
                    const int32_t* offsets, const moe_weights_t* w, void* o_perm,
                    void* ws, size_t ws_bytes, void* stream);
 
+/* First half of moe_expert_ffn (the gated up-projection of E_i in the u
+   equation, with the SiTU-GLU activation of "Kimi K3 テクニカルレポート",
+   section "幅のスケーリング: Stable LatentMoE"): for every row r of expert e with
+   token t = perm_src[r] / k, h[r] = act(W_g[e] z_t, W_v[e] z_t). Reads exp_gate
+   and exp_up of `w`. Output, exactly one of:
+     h_out [T*k, F] in the act dtype (permuted rows), or
+     hq_out [T*k, F] E4M3 codes and hqs_out [T*k, F/32] e8m0 scale bytes: h
+       rounded to bf16 and quantised to MXFP8 by the rule of
+       moe_quantize_mxfp8, the form in which moe_expert_ffn passes h to the
+       down projection on the scaled-MFMA path (expert_act_mxfp8 = 1 only).
+   With expert_act_mxfp8 = 1, z is quantised to MXFP8 first, as in
+   moe_expert_ffn. Anything else (both or neither output, hq without hqs, hq
+   without expert_act_mxfp8) is MOE_ERR_INVALID_ARG. ws: at least
+   moe_workspace_bytes(desc, MOE_OP_EXPERT_GATE_UP) bytes (tile table and the
+   MXFP8 copy of z). Rows past offsets[E] are not written. */
+int moe_expert_gate_up(const moe_desc_t* desc, const void* z, const int32_t* perm_src,
+                       const int32_t* offsets, const moe_weights_t* w, void* h_out,
+                       uint8_t* hq_out, uint8_t* hqs_out, void* ws, size_t ws_bytes, void* stream);
+
 /* Weighted combine and RMSNorm (u equation, then RMSNorm of the y equation):
    u_t = sum_j topk_gate[t][j] * o_perm[inv_pos[t*k + j]] (fp32, j ascending);
    n_t = u_t / sqrt(mean(u_t^2) + eps) * gain, stored in the act dtype.
@@ -208,10 +231,16 @@ int moe_output(const moe_desc_t* desc, const void* x, const void* n, const moe_w
    y [T, d] act dtype. Optional outputs (NULL to skip): topk_idx [T, k],
    topk_gate [T, k], counts [E]. The latent down-projection and the shared
    experts' gate/up do not depend on the routing: they run on a second stream
-   that the library keeps per device (created on the first call, default
-   priority), forked from `stream` with an event at the start of the call and
-   joined back into it before the routed experts, so the call remains ordered
-   on `stream` like any other work there (and can be captured into a graph). */
+   that the library keeps per device, forked from `stream` with an event at
+   the start of the call and joined back into it before the routed experts,
+   so the call remains ordered on `stream` like any other work there.
+   Library state behind this call (host side, the only state the library
+   keeps besides the thread-local error text and the trace events of
+   moe_trace_enable): per device, one non-blocking stream of default priority
+   and two events, created by the first call on that device and kept until
+   the process ends; a per-device mutex serialises the fork / join of
+   concurrent callers. Capture of this call into a HIP graph is not tested
+   and not promised. */
 int moe_layer_forward(const moe_desc_t* desc, const moe_weights_t* w, const void* x, void* y,
                       int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* counts_opt,
                       void* ws, size_t ws_bytes, void* stream);

@@ -375,7 +375,11 @@ def forward(cfg, w, tokens=None, routing=None, keep=False):
     cfg: dims (d, d_lat, E, k, F, S, Fs), c, eps, act dtype.
     w:   weight source with .raw(name, row0, rows), .bias(), .gain().
     routing: optional dict with 'idx' and 'p' rows for these tokens (else routed here).
-    keep: also return intermediates (z, n, and the routing)."""
+    keep: also return intermediates: z (stored), z_in [n, d_lat] and h [n, k, F]
+          (the routed experts' gate/up input and down input of every (token,
+          slot), after the MXFP8 quantisation when the expert inputs are
+          MXFP8), o [n, k, d_lat], u, n (stored), hs [n, S, Fs] (the shared
+          experts' stored activations) and the routing."""
     storage = _storage(cfg.act)
     X = _x_rows(cfg, w, tokens).astype(np.float64)
     n_tok = X.shape[0]
@@ -391,6 +395,9 @@ def forward(cfg, w, tokens=None, routing=None, keep=False):
     # codes the scaled-MFMA path multiplies)
     mx_act = getattr(cfg, "expert_act", "act") == "mxfp8"
     o = np.zeros((n_tok, cfg.k, cfg.d_lat), dtype=np.float64)
+    if keep:
+        z_in = np.zeros((n_tok, cfg.d_lat), dtype=np.float64)
+        h_all = np.zeros((n_tok, cfg.k, cfg.F), dtype=np.float64)
     for e in np.unique(idx):
         rows_t, rows_j = np.nonzero(idx == e)
         e = int(e)
@@ -404,6 +411,9 @@ def forward(cfg, w, tokens=None, routing=None, keep=False):
         if mx_act:
             H = mx8_dequantize(*mx8_quantize(H))
         o[rows_t, rows_j] = store(linear(H, Wo), storage)
+        if keep:
+            z_in[rows_t] = Z
+            h_all[rows_t, rows_j] = H
 
     # u = sum_j p_j o_j (slot order), n = RMSNorm(u)
     u = np.zeros((n_tok, cfg.d_lat), dtype=np.float64)
@@ -413,12 +423,16 @@ def forward(cfg, w, tokens=None, routing=None, keep=False):
 
     # y = W_up n + sum_s shared_s(x)
     y = linear(n, widen(w.raw("W_lu")))
+    hs_all = np.zeros((n_tok, cfg.S, cfg.Fs), dtype=np.float64) if keep else None
     for s_ in range(cfg.S):
         Wgs = widen(w.raw("W_gs", s_ * cfg.Fs, cfg.Fs))
         Wvs = widen(w.raw("W_vs", s_ * cfg.Fs, cfg.Fs))
         Wos = widen(w.raw("W_os", s_ * cfg.d, cfg.d))
         Hs = glu(linear(X, Wgs), linear(X, Wvs), cfg.c, storage)
         y = y + linear(Hs, Wos)
+        if keep:
+            hs_all[:, s_] = Hs
     if keep:
-        return y, {"z": z, "u": u, "n": n, "o": o, "idx": idx, "p": p}
+        return y, {"z": z, "z_in": z_in, "h": h_all, "u": u, "n": n, "o": o, "hs": hs_all,
+                   "idx": idx, "p": p}
     return y

@@ -21,12 +21,12 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_MXFP4 = 0, 1, 2
 (MOE_OP_ROUTE, MOE_OP_PERMUTE, MOE_OP_LATENT_DOWN, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE,
- MOE_OP_OUTPUT, MOE_OP_LAYER) = range(7)
+ MOE_OP_OUTPUT, MOE_OP_LAYER, MOE_OP_EXPERT_GATE_UP) = range(8)
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
 
 EXPORTS = ["moe_workspace_bytes", "moe_check_desc", "moe_route", "moe_permute", "moe_latent_down",
-           "moe_expert_ffn", "moe_combine", "moe_output", "moe_layer_forward",
+           "moe_expert_ffn", "moe_expert_gate_up", "moe_combine", "moe_output", "moe_layer_forward",
            "moe_status_string", "moe_last_error", "moe_trace_enable", "moe_trace_read",
            "moe_trace_stage_name", "moe_qb_bias", "moe_quantize_mxfp8", "moe_mxfp4_tile"]
 MOE_TRACE_STAGES = 10
@@ -74,6 +74,7 @@ def lib():
         "moe_permute": ([D, vp, vp, vp, vp, vp, vp, sz, vp], i32),
         "moe_latent_down": ([D, vp, W, vp, vp, sz, vp], i32),
         "moe_expert_ffn": ([D, vp, vp, vp, WS, vp, vp, sz, vp], i32),
+        "moe_expert_gate_up": ([D, vp, vp, vp, WS, vp, vp, vp, vp, sz, vp], i32),
         "moe_combine": ([D, vp, vp, vp, vp, vp, vp, vp], i32),
         "moe_output": ([D, vp, vp, WS, vp, vp, sz, vp], i32),
         "moe_layer_forward": ([D, WS, vp, vp, vp, vp, vp, vp, sz, vp], i32),
@@ -191,6 +192,17 @@ def moe_expert_ffn(desc, z, perm_src, offsets, weights: dict, o_perm, ws=None, s
     w = make_weights(weights)
     _check(lib().moe_expert_ffn(ctypes.byref(desc), _ptr(z), _ptr(perm_src), _ptr(offsets),
                                 ctypes.byref(w), _ptr(o_perm), p, n, _stream(stream)))
+
+
+def moe_expert_gate_up(desc, z, perm_src, offsets, weights: dict, h=None, hq=None, hqs=None,
+                       ws=None, stream=None):
+    """h [T*k, F] in the act dtype, or (expert_act_mxfp8 only) hq [T*k, F] and
+    hqs [T*k, F/32] uint8: give one of the two."""
+    p, n = _ws(ws)
+    w = make_weights(weights)
+    _check(lib().moe_expert_gate_up(ctypes.byref(desc), _ptr(z), _ptr(perm_src), _ptr(offsets),
+                                    ctypes.byref(w), _ptr(h), _ptr(hq), _ptr(hqs), p, n,
+                                    _stream(stream)))
 
 
 def moe_combine(desc, o_perm, inv_pos, topk_gate, rms_gain, n_out, u_out=None, stream=None):

@@ -27,11 +27,19 @@ def _compile(src: str) -> str:
     return obj
 
 
+# ceiling probes for the benchmark (not part of the layer): libmoe_probe.so
+PROBE_SOURCES = ["probe.hip"]
+PROBE_OUT = os.path.join(HERE, "libmoe_probe.so")
+
+
 def build(jobs: int = 8) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", OUT, *objs],
+        objs = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    n = len(SOURCES)
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", OUT, *objs[:n]],
+                   check=True)
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", PROBE_OUT, *objs[n:]],
                    check=True)
     return OUT
 

@@ -123,7 +123,7 @@ struct LayerWs {
 };
 
 int max_tiles(const moe_desc_t* d) {
-  const int bm = moe::grouped_bm(d->act_dtype, (int64_t)d->T * d->top_k, d->n_experts);
+  const int bm = moe::grouped_bm(d->act_dtype, d->expert_w_dtype, d->expert_act_mxfp8, (int64_t)d->T * d->top_k, d->n_experts);
   return (int)(((int64_t)d->T * d->top_k + bm - 1) / bm + d->n_experts);
 }
 
@@ -135,15 +135,21 @@ void plan_route(const moe_desc_t* d, Plan& p, LayerWs& w) {
 void plan_permute(const moe_desc_t* d, Plan& p, LayerWs& w) {
   w.blk = p.take((size_t)moe::permute_blocks(d->T) * d->n_experts * 4);
 }
-void plan_expert(const moe_desc_t* d, Plan& p, LayerWs& w) {
+// tile table and, on the scaled-MFMA path, the MXFP8 copy of z
+void plan_gate_up(const moe_desc_t* d, Plan& p, LayerWs& w) {
   w.tile_off = p.take((size_t)(d->n_experts + 1) * 4);
   w.tile_info = p.take((size_t)max_tiles(d) * 16);
+  if (d->expert_act_mxfp8) {
+    w.zq = p.take((size_t)d->T * d->d_latent);
+    w.zqs = p.take((size_t)d->T * d->d_latent / 32);
+  }
+}
+void plan_expert(const moe_desc_t* d, Plan& p, LayerWs& w) {
+  plan_gate_up(d, p, w);
   // bf16 h [T k, F]; the scaled-MFMA path writes h only in MXFP8 (hq, hqs)
   w.H = p.take(d->expert_act_mxfp8 ? 0 : (size_t)d->T * d->top_k * d->d_ff * elem_bytes(d->act_dtype));
   if (d->expert_act_mxfp8) {
     const size_t rows = (size_t)d->T * d->top_k;
-    w.zq = p.take((size_t)d->T * d->d_latent);
-    w.zqs = p.take((size_t)d->T * d->d_latent / 32);
     w.hq = p.take(rows * d->d_ff);
     w.hqs = p.take(rows * d->d_ff / 32);
   }
@@ -201,6 +207,7 @@ size_t ws_bytes_for(const moe_desc_t* d, int op) {
     case MOE_OP_PERMUTE: plan_permute(d, p, w); break;
     case MOE_OP_LATENT_DOWN: plan_latent(d, p, w); break;
     case MOE_OP_EXPERT_FFN: plan_expert(d, p, w); break;
+    case MOE_OP_EXPERT_GATE_UP: plan_gate_up(d, p, w); break;
     case MOE_OP_COMBINE: break;
     case MOE_OP_OUTPUT: plan_output(d, p, w); break;
     case MOE_OP_LAYER: p = plan_layer(d, w); break;
@@ -359,13 +366,14 @@ MxBufs mx_bufs(const moe_desc_t* d, void* ws, const LayerWs& lw) {
   return m;
 }
 
-int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const int32_t* offsets,
-               const moe_weights_t* w, void* o_perm, int32_t* tile_off, int32_t* tile_info, void* H,
+// Tile table, then h = act(W_g z, W_v z) for every permuted row: into H (act
+// dtype) when H is set, else (scaled-MFMA path only) straight into MXFP8 codes
+// hq and scales hqs, the down GEMM's input.
+int do_gate_up(const moe_desc_t* d, const void* z, const int32_t* perm, const int32_t* offsets,
+               const moe_weights_t* w, int32_t* tile_off, int32_t* tile_info, void* H,
                const MxBufs& mx, hipStream_t st, Marker mk = {-1}) {
   const bool q8 = d->expert_act_mxfp8 != 0;
-  const int bm = moe::grouped_bm(d->act_dtype, (int64_t)d->T * d->top_k, d->n_experts);
-  const int mt = max_tiles(d);
-  const int rows_cap = d->T * d->top_k;
+  const int bm = moe::grouped_bm(d->act_dtype, d->expert_w_dtype, d->expert_act_mxfp8, (int64_t)d->T * d->top_k, d->n_experts);
   mk.beg(4, st);
   if (d->T > 0)
     MOE_LAUNCH(moe::launch_tile_table(offsets, d->n_experts, bm, tile_off, tile_info, st),
@@ -376,19 +384,30 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
     MOE_LAUNCH(moe::launch_quantize_mx8(z, d->T, d->d_latent, d->d_latent, mx.zq, mx.zqs, st),
                "quantize_z");
   moe::GroupedGluArgs g{};
-  g.Z = q8 ? (const void*)mx.zq : z; g.ldz = d->d_latent; g.T = d->T; g.rows_cap = rows_cap;
+  g.Z = q8 ? (const void*)mx.zq : z; g.ldz = d->d_latent; g.T = d->T; g.rows_cap = d->T * d->top_k;
   g.act_mx8 = q8; g.z_scale = mx.zqs; g.w_tiled = d->expert_w_tiled;
-  // the scaled-MFMA path writes h straight in MXFP8 (the down GEMM's input)
-  g.hq = q8 ? mx.hq : nullptr; g.hqs = q8 ? mx.hqs : nullptr;
+  g.hq = H == nullptr ? mx.hq : nullptr; g.hqs = H == nullptr ? mx.hqs : nullptr;
   g.perm_src = perm; g.topk = d->top_k; g.offsets = offsets; g.tile_off = tile_off;
   g.tile_info = tile_info;
-  g.max_tiles = mt;
+  g.max_tiles = max_tiles(d);
   g.Wg = wop(w->exp_gate, d->expert_w_dtype);
   g.Wv = wop(w->exp_up, d->expert_w_dtype);
   g.E = d->n_experts; g.F = d->d_ff; g.K = d->d_latent;
   g.H = H; g.c = d->situ_c; g.act_dtype = d->act_dtype; g.bm = bm;
   if (d->T > 0) MOE_LAUNCH(moe::launch_grouped_glu(g, st), "expert_gate_up");
   mk.end(5, st);
+  return MOE_OK;
+}
+
+int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const int32_t* offsets,
+               const moe_weights_t* w, void* o_perm, int32_t* tile_off, int32_t* tile_info, void* H,
+               const MxBufs& mx, hipStream_t st, Marker mk = {-1}) {
+  const bool q8 = d->expert_act_mxfp8 != 0;
+  const int bm = moe::grouped_bm(d->act_dtype, d->expert_w_dtype, d->expert_act_mxfp8, (int64_t)d->T * d->top_k, d->n_experts);
+  const int mt = max_tiles(d);
+  const int rows_cap = d->T * d->top_k;
+  // the scaled-MFMA path writes h straight in MXFP8 (the down GEMM's input)
+  MOE_CHECK(do_gate_up(d, z, perm, offsets, w, tile_off, tile_info, q8 ? nullptr : H, mx, st, mk));
   mk.beg(6, st);
   moe::GroupedDownArgs dn{};
   dn.H = q8 ? (const void*)mx.hq : H; dn.ldh = d->d_ff; dn.rows_cap = rows_cap;
@@ -501,6 +520,74 @@ int side_stream(SideStream** out) {
     sd.s = s;
   }
   *out = &sd;
+  return MOE_OK;
+}
+
+int check_layer_args(const moe_desc_t* d, const moe_weights_t* w, const void* x, const void* y,
+                     const int32_t* topk_idx_opt, const float* topk_gate_opt, const int32_t* counts_opt) {
+  MOE_CHECK(check_desc(d));
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  MOE_CHECK(need_ptr_t(d, x, "x"));
+  MOE_CHECK(need_ptr_t(d, y, "y"));
+  MOE_CHECK(need_w(w->router, d->dense_w_dtype, "router"));
+  MOE_CHECK(need_ptr(w->router_bias, "router_bias"));
+  MOE_CHECK(need_w(w->lat_down, d->latent_w_dtype, "lat_down"));
+  MOE_CHECK(need_w(w->lat_up, d->latent_w_dtype, "lat_up"));
+  MOE_CHECK(opt_ptr(w->rms_gain, "rms_gain"));
+  MOE_CHECK(need_w(w->exp_gate, d->expert_w_dtype, "exp_gate"));
+  MOE_CHECK(need_w(w->exp_up, d->expert_w_dtype, "exp_up"));
+  MOE_CHECK(need_w(w->exp_down, d->expert_w_dtype, "exp_down"));
+  if (d->n_shared > 0) {
+    MOE_CHECK(need_w(w->sh_gate, d->dense_w_dtype, "sh_gate"));
+    MOE_CHECK(need_w(w->sh_up, d->dense_w_dtype, "sh_up"));
+    MOE_CHECK(need_w(w->sh_down, d->dense_w_dtype, "sh_down"));
+  }
+  MOE_CHECK(opt_ptr(topk_idx_opt, "topk_idx"));
+  MOE_CHECK(opt_ptr(topk_gate_opt, "topk_gate"));
+  MOE_CHECK(opt_ptr(counts_opt, "counts"));
+  return MOE_OK;
+}
+
+// The layer on workspace ws. With a side stream sd (held locked by the caller)
+// the routing-independent GEMMs (latent down, shared gate/up) run on it,
+// forked from and joined back into st; without one everything runs on st in
+// order.
+int run_layer(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y, int32_t* topk_idx_opt,
+              float* topk_gate_opt, int32_t* counts_opt, void* ws, hipStream_t st, SideStream* sd,
+              Marker mk) {
+  LayerWs lw{};
+  plan_layer(d, lw);
+  int32_t* idx = topk_idx_opt ? topk_idx_opt : (int32_t*)at(ws, lw.idx);
+  float* gate = topk_gate_opt ? topk_gate_opt : (float*)at(ws, lw.gate);
+  int32_t* counts = counts_opt ? counts_opt : (int32_t*)at(ws, lw.counts);
+  int32_t* offsets = (int32_t*)at(ws, lw.offsets);
+  int32_t* perm = (int32_t*)at(ws, lw.perm);
+  int32_t* inv = (int32_t*)at(ws, lw.inv);
+  hipStream_t side = st;
+  if (sd != nullptr) {
+    MOE_LAUNCH((int)hipEventRecord(sd->fork, st), "fork");
+    MOE_LAUNCH((int)hipStreamWaitEvent(sd->s, sd->fork, 0), "fork");
+    side = sd->s;
+  }
+  // the routing-independent GEMMs (z and the shared experts' H)
+  mk.beg(3, side);
+  MOE_CHECK(do_latent_down(d, x, w->lat_down, at(ws, lw.z), (float*)at(ws, lw.P), side));
+  mk.end(3, side);
+  MOE_CHECK(do_shared_glu(d, x, w, at(ws, lw.Hs), (float*)at(ws, lw.P), side, mk));
+  if (sd != nullptr) MOE_LAUNCH((int)hipEventRecord(sd->join, sd->s), "join");
+  // routing and permutation, then (after the join) the experts
+  MOE_CHECK(do_route(d, x, w->router, w->router_bias, idx, gate, (float*)at(ws, lw.s),
+                     (float*)at(ws, lw.key), (float*)at(ws, lw.norms), false, st, mk));
+  mk.beg(2, st);
+  MOE_CHECK(do_permute(d, idx, counts, offsets, perm, inv, (int32_t*)at(ws, lw.blk), st));
+  mk.end(2, st);
+  if (sd != nullptr) MOE_LAUNCH((int)hipStreamWaitEvent(st, sd->join, 0), "join");
+  MOE_CHECK(do_experts(d, at(ws, lw.z), perm, offsets, w, at(ws, lw.O), (int32_t*)at(ws, lw.tile_off),
+                       (int32_t*)at(ws, lw.tile_info), at(ws, lw.H), mx_bufs(d, ws, lw), st, mk));
+  mk.beg(7, st);
+  MOE_CHECK(do_combine(d, at(ws, lw.O), inv, gate, w->rms_gain, at(ws, lw.n), nullptr, st));
+  mk.end(7, st);
+  MOE_CHECK(do_output_gemm(d, at(ws, lw.n), w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), st, mk));
   return MOE_OK;
 }
 
@@ -656,6 +743,43 @@ int moe_expert_ffn(const moe_desc_t* d, const void* z, const int32_t* perm_src,
                     (hipStream_t)stream);
 }
 
+int moe_expert_gate_up(const moe_desc_t* d, const void* z, const int32_t* perm_src,
+                       const int32_t* offsets, const moe_weights_t* w, void* h_out, uint8_t* hq_out,
+                       uint8_t* hqs_out, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  MOE_CHECK(check_desc(d));
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  MOE_CHECK(need_ptr_t(d, z, "z"));
+  MOE_CHECK(need_ptr_t(d, perm_src, "perm_src"));
+  MOE_CHECK(need_ptr(offsets, "offsets"));
+  MOE_CHECK(need_w(w->exp_gate, d->expert_w_dtype, "exp_gate"));
+  MOE_CHECK(need_w(w->exp_up, d->expert_w_dtype, "exp_up"));
+  const bool q8_out = hq_out != nullptr || hqs_out != nullptr;
+  if (q8_out && !d->expert_act_mxfp8)
+    return fail(MOE_ERR_INVALID_ARG, "hq_out / hqs_out need expert_act_mxfp8 = 1");
+  if (q8_out == (h_out != nullptr) && d->T > 0)
+    return fail(MOE_ERR_INVALID_ARG, "give either h_out or both hq_out and hqs_out");
+  if (q8_out) {
+    MOE_CHECK(need_ptr_t(d, hq_out, "hq_out"));
+    if (hqs_out == nullptr && d->T > 0) return fail(MOE_ERR_INVALID_ARG, "hqs_out is NULL");
+  } else {
+    MOE_CHECK(need_ptr_t(d, h_out, "h_out"));
+  }
+  MOE_CHECK(check_ws(d, MOE_OP_EXPERT_GATE_UP, ws, ws_bytes));
+  Plan p;
+  LayerWs lw{};
+  plan_gate_up(d, p, lw);
+  MxBufs mx;
+  if (d->expert_act_mxfp8) {
+    mx.zq = (uint8_t*)at(ws, lw.zq);
+    mx.zqs = (uint8_t*)at(ws, lw.zqs);
+    mx.hq = hq_out;
+    mx.hqs = hqs_out;
+  }
+  return do_gate_up(d, z, perm_src, offsets, w, (int32_t*)at(ws, lw.tile_off),
+                    (int32_t*)at(ws, lw.tile_info), h_out, mx, (hipStream_t)stream);
+}
+
 int moe_combine(const moe_desc_t* d, const void* o_perm, const int32_t* inv_pos,
                 const float* topk_gate, const float* rms_gain, void* n_out, float* u_out_opt,
                 void* stream) {
@@ -753,62 +877,13 @@ int moe_layer_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x
                       int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* counts_opt, void* ws,
                       size_t ws_bytes, void* stream) {
   g_last_error.clear();
-  MOE_CHECK(check_desc(d));
-  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
-  MOE_CHECK(need_ptr_t(d, x, "x"));
-  MOE_CHECK(need_ptr_t(d, y, "y"));
-  MOE_CHECK(need_w(w->router, d->dense_w_dtype, "router"));
-  MOE_CHECK(need_ptr(w->router_bias, "router_bias"));
-  MOE_CHECK(need_w(w->lat_down, d->latent_w_dtype, "lat_down"));
-  MOE_CHECK(need_w(w->lat_up, d->latent_w_dtype, "lat_up"));
-  MOE_CHECK(opt_ptr(w->rms_gain, "rms_gain"));
-  MOE_CHECK(need_w(w->exp_gate, d->expert_w_dtype, "exp_gate"));
-  MOE_CHECK(need_w(w->exp_up, d->expert_w_dtype, "exp_up"));
-  MOE_CHECK(need_w(w->exp_down, d->expert_w_dtype, "exp_down"));
-  if (d->n_shared > 0) {
-    MOE_CHECK(need_w(w->sh_gate, d->dense_w_dtype, "sh_gate"));
-    MOE_CHECK(need_w(w->sh_up, d->dense_w_dtype, "sh_up"));
-    MOE_CHECK(need_w(w->sh_down, d->dense_w_dtype, "sh_down"));
-  }
-  MOE_CHECK(opt_ptr(topk_idx_opt, "topk_idx"));
-  MOE_CHECK(opt_ptr(topk_gate_opt, "topk_gate"));
-  MOE_CHECK(opt_ptr(counts_opt, "counts"));
+  MOE_CHECK(check_layer_args(d, w, x, y, topk_idx_opt, topk_gate_opt, counts_opt));
   MOE_CHECK(check_ws(d, MOE_OP_LAYER, ws, ws_bytes));
-  LayerWs lw{};
-  plan_layer(d, lw);
-  hipStream_t st = (hipStream_t)stream;
-  int32_t* idx = topk_idx_opt ? topk_idx_opt : (int32_t*)at(ws, lw.idx);
-  float* gate = topk_gate_opt ? topk_gate_opt : (float*)at(ws, lw.gate);
-  int32_t* counts = counts_opt ? counts_opt : (int32_t*)at(ws, lw.counts);
-  int32_t* offsets = (int32_t*)at(ws, lw.offsets);
-  int32_t* perm = (int32_t*)at(ws, lw.perm);
-  int32_t* inv = (int32_t*)at(ws, lw.inv);
   SideStream* sd = nullptr;
   MOE_CHECK(side_stream(&sd));
   std::lock_guard<std::mutex> lk(sd->mu);
-  const Marker mk{trace_begin()};
-  // side stream: the routing-independent GEMMs (z and the shared experts' H)
-  MOE_LAUNCH((int)hipEventRecord(sd->fork, st), "fork");
-  MOE_LAUNCH((int)hipStreamWaitEvent(sd->s, sd->fork, 0), "fork");
-  mk.beg(3, sd->s);
-  MOE_CHECK(do_latent_down(d, x, w->lat_down, at(ws, lw.z), (float*)at(ws, lw.P), sd->s));
-  mk.end(3, sd->s);
-  MOE_CHECK(do_shared_glu(d, x, w, at(ws, lw.Hs), (float*)at(ws, lw.P), sd->s, mk));
-  MOE_LAUNCH((int)hipEventRecord(sd->join, sd->s), "join");
-  // caller's stream: routing and permutation, then (after the join) the experts
-  MOE_CHECK(do_route(d, x, w->router, w->router_bias, idx, gate, (float*)at(ws, lw.s),
-                     (float*)at(ws, lw.key), (float*)at(ws, lw.norms), false, st, mk));
-  mk.beg(2, st);
-  MOE_CHECK(do_permute(d, idx, counts, offsets, perm, inv, (int32_t*)at(ws, lw.blk), st));
-  mk.end(2, st);
-  MOE_LAUNCH((int)hipStreamWaitEvent(st, sd->join, 0), "join");
-  MOE_CHECK(do_experts(d, at(ws, lw.z), perm, offsets, w, at(ws, lw.O), (int32_t*)at(ws, lw.tile_off),
-                       (int32_t*)at(ws, lw.tile_info), at(ws, lw.H), mx_bufs(d, ws, lw), st, mk));
-  mk.beg(7, st);
-  MOE_CHECK(do_combine(d, at(ws, lw.O), inv, gate, w->rms_gain, at(ws, lw.n), nullptr, st));
-  mk.end(7, st);
-  MOE_CHECK(do_output_gemm(d, at(ws, lw.n), w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), st, mk));
-  return MOE_OK;
+  return run_layer(d, w, x, y, topk_idx_opt, topk_gate_opt, counts_opt, ws, (hipStream_t)stream, sd,
+                   Marker{trace_begin()});
 }
 
 }  // extern "C"

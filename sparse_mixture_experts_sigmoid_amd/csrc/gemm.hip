@@ -57,12 +57,20 @@ struct Cfg {
   static constexpr int MXU = BN * UR / NT;     // MXFP4 (row, block) units per thread per stage
   static constexpr int STAGE = (BM + BN) * BK;   // bf16 elements per LDS stage
   static_assert(BK == 32 || BK == 64, "BK");
-  static_assert(AR >= 1 && BR >= 1 && MXU >= 1, "tile too small for the DMA pattern");
-  static_assert(AR * NW * RPI == BM && BR * NW * RPI == BN && MXU * NT == BN * UR, "DMA cover");
+  static_assert(AR >= 1 && BR >= 1, "tile too small for the DMA pattern");
+  static_assert(AR * NW * RPI == BM && BR * NW * RPI == BN, "DMA cover");
   static_assert(NS >= 2 && NS <= 5, "ring depth");
+  // MXFP4 B (decoded through registers): whole (row, block) units per thread
+  static constexpr bool MX_OK = MXU >= 1 && MXU * NT == BN * UR;
 };
 using DenseCfg = Cfg<2, 2, 4, 2, 64, 3>;   // 256 x 128, 4 waves, 3 stages of 48 KB
 using GroupCfg = Cfg<2, 4, 2, 2, 64, 3>;   // 128 x 256, 8 waves, 3 stages of 48 KB
+// Grouped expert GEMMs on bf16 weights with many rows per expert: 256 x 256,
+// 8 waves of 128 x 64, the pipelined main loop.
+#ifndef MOE_BIG_CFG
+#define MOE_BIG_CFG Cfg<2, 4, 4, 2, 64, 2>
+#endif
+using GroupBigCfg = MOE_BIG_CFG;
 using SplitCfg = Cfg<2, 2, 2, 2, 64, 3>;   // 128 x 128 (small batches, split K)
 
 // ---------------------------------------------------------------------------
@@ -145,6 +153,7 @@ __device__ __forceinline__ int mx_row(int j) { return threadIdx.x / C::UR + (C::
 template <class C>
 __device__ __forceinline__ void load_mx(const MxRows<C::MXU>& m, int k0, int K,
                                         MxStage (&st)[C::MXU]) {
+  static_assert(C::MX_OK, "MXFP4 B needs whole (row, block) units per thread");
   const int k = k0 + (threadIdx.x % C::UR) * 32;
   const bool kin = k < K;
 #pragma unroll
@@ -434,6 +443,184 @@ __device__ __forceinline__ void mainloop_rows(bf16_t* s0, bf16_t* s1, bf16_t* s2
     else if constexpr (C::WM > 2) {
       if (nv == 2) mainloop<C, B_MX, 2>(s0, s1, s2, s3, s4, ar, br, bm, K, acc);
       else if constexpr (C::WM > 3) mainloop<C, B_MX, 3>(s0, s1, s2, s3, s4, ar, br, bm, K, acc);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the pipelined main loop (grouped expert GEMMs)
+// ---------------------------------------------------------------------------
+//
+// Large wave tiles (WM x WN = 4 x 2 fragments, 128 x 64 per wave) cut the LDS
+// bytes read per MFMA to 3/4 of the 64 x 64 tiles' (6 fragment reads per 8
+// MFMAs), and 256 x 256 block tiles cut the L2-to-LDS bytes per flop to 2/3
+// of the 128 x 256 tiles'. Fragment reads run one k-step (16 k) ahead of the
+// MFMAs in two register sets, so a wave's matrix work never waits for its
+// own LDS reads; the one workgroup barrier of a K-tile sits before that
+// tile's last k-step, where every wave has its last fragments of the tile in
+// registers: after it the stage just consumed takes the DMA of the K-tile NS
+// ahead, and the first fragments of the next tile are read while the last
+// k-step's MFMAs run.
+
+template <class C>
+struct KFrag {
+  bf16x8 a[C::WM], b[C::WN];
+};
+
+// Fragments of k-step ks (16 k) of a stage: A fragments 0 .. NV-1 of this wave
+// (the others hold padding rows only) and every B fragment.
+template <class C, int NV>
+__device__ __forceinline__ void read_kstep(const bf16_t* S, int ks, KFrag<C>& f) {
+  if constexpr (NV > 0) {
+    const int lane = threadIdx.x & 63, wm = wave_m<C>(), wn = wave_n<C>();
+    const int lr = lane & 31, lh = lane >> 5;
+    const bf16_t* Aw = S + (wm * (C::BM / C::WGM) + lr) * C::BK;
+    const bf16_t* Bw = S + C::BM * C::BK + (wn * (C::BN / C::WGN) + lr) * C::BK;
+    const int slot = 8 * ((2 * ks + lh) ^ swz<C>(lr));
+#pragma unroll
+    for (int i = 0; i < NV; ++i) f.a[i] = *(const bf16x8*)(Aw + i * 32 * C::BK + slot);
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j) f.b[j] = *(const bf16x8*)(Bw + j * 32 * C::BK + slot);
+  }
+}
+
+template <class C, int NV>
+__device__ __forceinline__ void mma_kstep(const KFrag<C>& f, Acc<C>& acc) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int j = 0; j < C::WN; ++j)
+      acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc.c[i][j], 0, 0, 0);
+}
+
+// s_waitcnt: LDS/scalar counter 0 and the vector-memory counter limited to n.
+constexpr int waitcnt_lgkm0_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (7 << 4); }
+
+// k-steps KSI .. KS-2 of a K-tile in stage R: each issues the fragment reads of
+// the next k-step (into the other register set) between its MFMAs. Even
+// k-steps compute from f0, odd ones from f1 (compile-time choice: a runtime
+// pick between the two sets would put them in scratch memory).
+template <class C, int NV, int KSI>
+__device__ __forceinline__ void pipe_ksteps(const bf16_t* R, Acc<C>& acc, KFrag<C>& f0, KFrag<C>& f1) {
+  constexpr int KS = C::BK / 16;
+  if constexpr (KSI + 1 < KS) {
+    constexpr int kReads = NV > 0 ? NV + C::WN : 0;    // fragment reads per k-step
+    constexpr int kMfma = NV * C::WN;                  // MFMAs per k-step
+    if constexpr (KSI % 2 == 0) {
+      read_kstep<C, NV>(R, KSI + 1, f1);
+      mma_kstep<C, NV>(f0, acc);
+    } else {
+      read_kstep<C, NV>(R, KSI + 1, f0);
+      mma_kstep<C, NV>(f1, acc);
+    }
+    if constexpr (kMfma > 0) {
+      // one read after each of the first kReads MFMAs
+#pragma unroll
+      for (int q = 0; q < (kReads < kMfma ? kReads : kMfma); ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if constexpr (kReads > kMfma) __builtin_amdgcn_sched_group_barrier(0x100, kReads - kMfma, 0);
+      if constexpr (kMfma > kReads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kReads, 0);
+    }
+    pipe_ksteps<C, NV, KSI + 1>(R, acc, f0, f1);
+  }
+}
+
+// One K-tile kt: its stage R has landed and every wave passed the barrier
+// that says so; f0 holds its k-step 0. Nx is the stage of tile kt + 1.
+template <class C, int NV>
+__device__ __forceinline__ void pipe_step(bf16_t* R, const bf16_t* Nx, const Rows<C::AR>& ar,
+                                          const Rows<C::BR>& br, int kt, int K, Acc<C>& acc,
+                                          KFrag<C>& f0, KFrag<C>& f1) {
+  static_assert((C::BK / 16) % 2 == 0, "k-steps alternate between the two fragment sets");
+  constexpr int kLoads = C::AR + C::BR;                // DMA per thread per stage
+  static_assert(kLoads * (C::NS - 1) < 64, "vmcnt range");
+  constexpr int kReads = NV > 0 ? NV + C::WN : 0;
+  constexpr int kMfma = NV * C::WN;
+  pipe_ksteps<C, NV, 0>(R, acc, f0, f1);
+  // last k-step: its fragments (f1) are read; tile kt + 1 must land, and every
+  // wave must be done with R before R takes tile kt + NS
+  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0_vm(kLoads * (C::NS - 2)));
+  wg_barrier();
+  dma_rows<C>(ar, R, (kt + C::NS) * C::BK, K);
+  dma_rows<C>(br, R + C::BM * C::BK, (kt + C::NS) * C::BK, K);
+  read_kstep<C, NV>(Nx, 0, f0);
+  mma_kstep<C, NV>(f1, acc);
+  if constexpr (kMfma > 0) {
+    constexpr int kPer = kMfma / kLoads > 0 ? kMfma / kLoads : 1;   // MFMAs between two DMA
+#pragma unroll
+    for (int q = 0; q < kLoads; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kPer, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+    if constexpr (kMfma > kPer * kLoads) __builtin_amdgcn_sched_group_barrier(0x008, kMfma - kPer * kLoads, 0);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void stage_dma(bf16_t* S, const Rows<C::AR>& ar, const Rows<C::BR>& br, int kt,
+                                          int K) {
+  dma_rows<C>(ar, S, kt * C::BK, K);
+  dma_rows<C>(br, S + C::BM * C::BK, kt * C::BK, K);
+}
+
+// acc += A_tile B_tile^T over k in [0, K), bf16 A and B by DMA through the
+// NS-stage ring (all NS stages filled up front; K-tiles past K read zeros).
+template <class C, int NV>
+__device__ __forceinline__ void mainloop_pipe(bf16_t* s0, bf16_t* s1, bf16_t* s2, bf16_t* s3, bf16_t*,
+                                              const Rows<C::AR>& ar, const Rows<C::BR>& br, int K,
+                                              Acc<C>& acc) {
+  static_assert(C::NS >= 2 && C::NS <= 4, "pipelined ring depth");
+  const int nk = (int)ceil_div(K, C::BK);
+  stage_dma<C>(s0, ar, br, 0, K);
+  stage_dma<C>(s1, ar, br, 1, K);
+  if constexpr (C::NS > 2) stage_dma<C>(s2, ar, br, 2, K);
+  if constexpr (C::NS > 3) stage_dma<C>(s3, ar, br, 3, K);
+  constexpr int kLoads = C::AR + C::BR;
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads * (C::NS - 1)));
+  wg_barrier();
+  KFrag<C> f0, f1;
+  read_kstep<C, NV>(s0, 0, f0);
+  for (int kt = 0; kt < nk; kt += C::NS) {
+    // whole rounds of NS K-tiles (tiles past K are zeros): a loop with one
+    // exit keeps one copy of the accumulators
+    if constexpr (C::NS == 2) {
+      pipe_step<C, NV>(s0, s1, ar, br, kt, K, acc, f0, f1);
+      pipe_step<C, NV>(s1, s0, ar, br, kt + 1, K, acc, f0, f1);
+    } else if constexpr (C::NS == 3) {
+      pipe_step<C, NV>(s0, s1, ar, br, kt, K, acc, f0, f1);
+      pipe_step<C, NV>(s1, s2, ar, br, kt + 1, K, acc, f0, f1);
+      pipe_step<C, NV>(s2, s0, ar, br, kt + 2, K, acc, f0, f1);
+    } else {
+      pipe_step<C, NV>(s0, s1, ar, br, kt, K, acc, f0, f1);
+      pipe_step<C, NV>(s1, s2, ar, br, kt + 1, K, acc, f0, f1);
+      pipe_step<C, NV>(s2, s3, ar, br, kt + 2, K, acc, f0, f1);
+      pipe_step<C, NV>(s3, s0, ar, br, kt + 3, K, acc, f0, f1);
+    }
+  }
+  // drain the trailing (zero) loads before the LDS is reused or the block ends
+  __builtin_amdgcn_s_waitcnt(0);
+  wg_barrier();
+}
+
+// mainloop_pipe for a tile whose rows at or past `valid_rows` are padding.
+template <class C>
+__device__ __forceinline__ void mainloop_pipe_rows(bf16_t* s0, bf16_t* s1, bf16_t* s2, bf16_t* s3,
+                                                   bf16_t* s4, const Rows<C::AR>& ar,
+                                                   const Rows<C::BR>& br, int K, int valid_rows,
+                                                   Acc<C>& acc) {
+  static_assert(C::WM <= 4, "fragment dispatch");
+  const int first = wave_m<C>() * (C::BM / C::WGM);
+  const int nv = __builtin_amdgcn_readfirstlane(max(0, min(C::WM, (valid_rows - first + 31) / 32)));
+  if (nv >= C::WM) mainloop_pipe<C, C::WM>(s0, s1, s2, s3, s4, ar, br, K, acc);
+  else if (nv == 0) mainloop_pipe<C, 0>(s0, s1, s2, s3, s4, ar, br, K, acc);
+  else if constexpr (C::WM > 1) {
+    if (nv == 1) mainloop_pipe<C, 1>(s0, s1, s2, s3, s4, ar, br, K, acc);
+    else if constexpr (C::WM > 2) {
+      if (nv == 2) mainloop_pipe<C, 2>(s0, s1, s2, s3, s4, ar, br, K, acc);
+      else if constexpr (C::WM > 3) mainloop_pipe<C, 3>(s0, s1, s2, s3, s4, ar, br, K, acc);
     }
   }
 }
@@ -734,6 +921,57 @@ __global__ __launch_bounds__(GroupCfg::NT) void grouped_glu_kernel(GroupedGluArg
     const int r = row_lo + tr;
     return (r >= 0 && r < row_hi) ? (int64_t)r : -1;
   });
+}
+
+// grouped_glu_kernel<false> on GroupBigCfg tiles with the pipelined main loop
+__global__ __launch_bounds__(GroupBigCfg::NT) void grouped_glu_big_kernel(GroupedGluArgs a) {
+  using C = GroupBigCfg;
+  MOE_LDS_RING(C);
+  const int ntn = (int)ceil_div(a.F, C::BN / 2);
+  int64_t L;
+  if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, L)) return;
+  int e, nt, row_lo, row_hi;
+  grouped_item<C::BM>(a.tile_info, ntn, a.rows_cap, L, e, nt, row_lo, row_hi);
+  const int f0 = nt * (C::BN / 2);
+  Rows<C::AR> ar;
+  ar.r[0] = ar.r[1] = make_rsrc(a.Z, (int64_t)a.T * a.ldz * 2);
+#pragma unroll
+  for (int q = 0; q < C::AR; ++q) {
+    ar.sel[q] = 0;
+    const int row = row_lo + dma_row<C, C::AR>(q);
+    uint32_t off = kOOB;
+    if (row >= 0 && row < row_hi) {
+      const int src = a.perm_src[row];
+      const int t = src / a.topk;
+      if (src >= 0 && t < a.T) off = (uint32_t)((int64_t)t * a.ldz * 2);
+    }
+    ar.off[q] = off;
+  }
+  const Rows<C::BR> br = b_rows_glu<C>(a.Wg, a.Wv, (int64_t)e * a.F, a.K, f0, a.F);
+  Acc<C> acc;
+  acc_zero(acc);
+  mainloop_pipe_rows<C>(MOE_RING, ar, br, a.K, row_hi - row_lo, acc);
+  store_glu(acc, (bf16_t*)a.H, a.F, f0, a.F, a.c, [=](int tr) -> int64_t {
+    const int r = row_lo + tr;
+    return (r >= 0 && r < row_hi) ? (int64_t)r : -1;
+  });
+}
+
+__global__ __launch_bounds__(GroupBigCfg::NT) void grouped_down_big_kernel(GroupedDownArgs a) {
+  using C = GroupBigCfg;
+  MOE_LDS_RING(C);
+  const int ntn = (int)ceil_div(a.N, C::BN);
+  int64_t L;
+  if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, L)) return;
+  int e, nt, row_lo, row_hi;
+  grouped_item<C::BM>(a.tile_info, ntn, a.rows_cap, L, e, nt, row_lo, row_hi);
+  const int n0 = nt * C::BN;
+  const Rows<C::AR> ar = a_rows_dense<C, C::AR>(a.H, a.ldh, max(row_lo, 0), max(row_hi, 0));
+  const Rows<C::BR> br = b_rows_plain<C>((const bf16_t*)a.Wo.data + (int64_t)e * a.N * a.K, a.K, n0, a.N);
+  Acc<C> acc;
+  acc_zero(acc);
+  mainloop_pipe_rows<C>(MOE_RING, ar, br, a.K, row_hi - row_lo, acc);
+  store_tile(acc, (bf16_t*)a.O, a.N, row_lo, n0, row_hi, a.N);
 }
 
 template <bool B_MX>
@@ -1420,7 +1658,21 @@ int multiseg_slices(int act_dtype, int M, int N, int nseg) {
   return nseg;
 }
 
-int grouped_bm(int act_dtype, int64_t, int) { return act_dtype == DT_F32 ? 1 : GroupCfg::BM; }
+// Row tiles of the grouped expert GEMMs: 1 on the fp32 path; 128 on the
+// scaled-MFMA path and with MXFP4 weights; with bf16 weights, 256 (the
+// pipelined big tiles) once the experts average at least kBigRows rows, else
+// 128 (at decode sizes the weight stream sets the pace and the smaller tiles
+// waste no DMA on padding rows).
+#ifndef MOE_BIG_ROWS
+#define MOE_BIG_ROWS 64
+#endif
+constexpr int kBigRows = MOE_BIG_ROWS;
+int grouped_bm(int act_dtype, int expert_w_dtype, int act_mx8, int64_t rows, int E) {
+  if (act_dtype == DT_F32) return 1;
+  if (act_mx8) return mx8::L::BM;
+  if (expert_w_dtype == DT_BF16 && rows >= (int64_t)kBigRows * E) return GroupBigCfg::BM;
+  return GroupCfg::BM;
+}
 
 int launch_dense(const DenseArgs& a, hipStream_t stream) {
   if (a.act_dtype == DT_F32) return launch_dense_f32(a, stream);
@@ -1468,8 +1720,17 @@ int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream) {
   if (a.act_mx8) {
     if (a.bm != mx8::L::BM || a.Wg.dtype != DT_MXFP4 || a.K % mx8::kBK) return -1;
     if (a.w_tiled && (a.F % 64 || mx8::kBRW != 64)) return -1;
+    // h goes either to bf16 H or, as MXFP8, to hq and hqs: never to neither
+    if (a.hq != nullptr ? a.hqs == nullptr : a.H == nullptr) return -1;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.F, mx8::L::BN / 2) * a.max_tiles));
     hipLaunchKernelGGL(grouped_glu_mx8_kernel, grid, dim3(mx8::L::NT), 0, stream, a);
+    return (int)hipGetLastError();
+  }
+  if (a.H == nullptr) return -1;
+  if (a.bm == GroupBigCfg::BM && a.bm != GroupCfg::BM) {
+    if (a.Wg.dtype != DT_BF16) return -1;
+    dim3 grid((unsigned)xcd_grid(ceil_div(a.F, GroupBigCfg::BN / 2) * a.max_tiles));
+    hipLaunchKernelGGL(grouped_glu_big_kernel, grid, dim3(GroupBigCfg::NT), 0, stream, a);
     return (int)hipGetLastError();
   }
   if (a.bm != GroupCfg::BM) return -1;
@@ -1488,6 +1749,12 @@ int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream) {
     if (a.w_tiled && (a.N % 64 || mx8::kBRW != 64)) return -1;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.N, mx8::L::BN) * a.max_tiles));
     hipLaunchKernelGGL(grouped_down_mx8_kernel, grid, dim3(mx8::L::NT), 0, stream, a);
+    return (int)hipGetLastError();
+  }
+  if (a.bm == GroupBigCfg::BM && a.bm != GroupCfg::BM) {
+    if (a.Wo.dtype != DT_BF16) return -1;
+    dim3 grid((unsigned)xcd_grid(ceil_div(a.N, GroupBigCfg::BN) * a.max_tiles));
+    hipLaunchKernelGGL(grouped_down_big_kernel, grid, dim3(GroupBigCfg::NT), 0, stream, a);
     return (int)hipGetLastError();
   }
   if (a.bm != GroupCfg::BM) return -1;

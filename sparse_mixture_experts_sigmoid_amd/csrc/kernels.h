@@ -136,14 +136,15 @@ struct GroupedGluArgs {
   const uint8_t* z_scale;
   int w_tiled;                       // act_mx8 only: Wg / Wv in the tiled layout
                                      // (launch_tile_mxfp4)
-  uint8_t* hq;                       // act_mx8 only, optional: write h as MXFP8 codes
-  uint8_t* hqs;                      // [rows, F] and scales [rows, F/32] instead of H
+  uint8_t* hq;                       // act_mx8 only: with hq (and hqs) set, h goes out as
+  uint8_t* hqs;                      // MXFP8 codes [rows, F] and scales [rows, F/32];
+                                     // else to bf16 H (one of the two must be given)
 };
 int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream);
-// Tile rows of the grouped expert kernels: 1 (fp32 path) or 128 (the LDS-tiled
-// MFMA kernels, at every batch size: at decode the weight stream runs at the
-// same rate with 32- or 64-row tiles, so one tiling serves both).
-int grouped_bm(int act_dtype, int64_t rows, int E);
+// Tile rows of the grouped expert kernels for `rows` routed rows over E
+// experts: 1 (fp32 path), 128 or 256 (the LDS-tiled MFMA kernels; the launchers
+// take the kernel that matches).
+int grouped_bm(int act_dtype, int expert_w_dtype, int act_mx8, int64_t rows, int E);
 
 // down: O[r] = H[r] Wo[e]^T, Wo [E, N, K].
 struct GroupedDownArgs {

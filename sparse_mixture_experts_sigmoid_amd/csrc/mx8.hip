@@ -5,33 +5,16 @@
 // exponent; clamped to [-127, 127], amax = 0 gives -127), stored as the e8m0
 // byte X + 127; element code = the E4M3 value nearest to v / 2^X (ties to
 // even), saturating at +-448, sign bit set when v < 0. Every step is exact
-// except the one rounding (v / 2^X is a power-of-two scaling of a bf16 value;
-// the mantissa rounding is rintf in the default round-to-nearest-even mode).
+// except the one rounding (v / 2^X is a power-of-two scaling of a bf16 value),
+// which gfx950's v_cvt_pk_fp8_f32 performs.
 // MXFP4 weights ("Kimi K3 ... Open Frontier Intelligence", section "MXFP4
 // Quantization-Aware Training") meet these activations in the gfx950 scaled
 // MFMA, which takes both operands in MX formats.
 #include "common.h"
 #include "kernels.h"
 
-#ifndef MOE_MX8_HWCVT
-#define MOE_MX8_HWCVT 1
-#endif
-
 namespace moe {
 namespace {
-
-// floor(log2 |y|) of a normal fp32 value from its exponent field
-__device__ __forceinline__ int exp_field(float y) { return (int)((__float_as_uint(y) >> 23) & 0xFFu) - 127; }
-
-// E4M3 code of y = |v| / 2^X (0 <= y < 512)
-__device__ __forceinline__ uint32_t e4m3_mag(float y) {
-  if (y < 0x1p-6f) return (uint32_t)__builtin_rintf(y * 512.0f);   // subnormal steps of 2^-9 (8 -> 0x08)
-  int e = exp_field(y);
-  uint32_t m = (uint32_t)__builtin_rintf((__builtin_ldexpf(y, -e) - 1.0f) * 8.0f);
-  if (m == 8u) { m = 0u; ++e; }
-  const uint32_t code = ((uint32_t)(e + 7) << 3) | m;
-  return (y >= 448.0f || code > 0x7Eu) ? 0x7Eu : code;
-}
 
 // A thread converts runs of 8 consecutive elements (a 16-byte bf16 load); the 4
 // threads of a 32-element block are adjacent lanes and share amax through
@@ -55,7 +38,6 @@ __device__ __forceinline__ void quantize_run(const uint4 v, bool live, int64_t r
   // X = floor(log2 amax) - 8; a zero or subnormal amax has exponent field 0 -> -127
   const int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
   const int X = ef == 0 ? -127 : max(-127, min(127, ef - 127 - 8));
-#if MOE_MX8_HWCVT
   // gfx950's v_cvt_pk_fp8_f32 rounds to the nearest OCP E4M3 value (ties to
   // even, subnormals kept) and keeps the sign; clamping to +-448 first gives the
   // saturation. The input gets + 0.0f, which turns -0.0 into +0.0 (no sign bit
@@ -69,17 +51,6 @@ __device__ __forceinline__ void quantize_run(const uint4 v, bool live, int64_t r
   uint32_t hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
   hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], (int)hi, true);
   if (live) {
-#else
-  uint32_t q[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float y = __builtin_ldexpf(fabsf(x[i]), -X);
-    q[i] = e4m3_mag(y) | (x[i] < 0.0f ? 0x80u : 0u);
-  }
-  if (live) {
-    const uint32_t lo = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-    const uint32_t hi = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-#endif
     *(uint2*)(codes + row * K + (int64_t)c8 * 8) = make_uint2(lo, hi);
     if ((c8 & 3) == 0) scales[row * (K / 32) + c8 / 4] = (uint8_t)(X + 127);
   }

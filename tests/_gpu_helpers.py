@@ -84,3 +84,88 @@ def sample_tokens(cfg, idx: np.ndarray, n: int, seed: int = 0) -> np.ndarray:
             break
         picks.add(int(t))
     return np.array(sorted(picks), dtype=np.int64)
+
+
+def staged_front(cfg, inp, dev="cuda:0"):
+    """Routing, permutation and z of a layer through the staged entry points:
+    (desc, idx, gate, offsets, perm_src, inv_pos, z)."""
+    desc = moe.make_desc(cfg)
+    T, k, E = cfg.T, cfg.k, cfg.E
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    moe.moe_route(desc, inp["x"], inp["W_r"], inp["b"], idx, gate, None,
+                  moe.workspace(desc, moe.MOE_OP_ROUTE, dev))
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    moe.moe_permute(desc, idx, counts, offsets, perm, inv, moe.workspace(desc, moe.MOE_OP_PERMUTE, dev))
+    z = torch.empty((T, cfg.d_lat), dtype=act_torch(cfg), device=dev)
+    moe.moe_latent_down(desc, inp["x"], inp["W_ld"], z, moe.workspace(desc, moe.MOE_OP_LATENT_DOWN, dev))
+    return desc, idx, gate, offsets, perm, inv, z
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |v| (normal range; 2^-133 below it)."""
+    e = np.frexp(np.abs(np.asarray(v, np.float64)))[1]
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def check_mx8_layer(cfg, y_gpu, y_ref, z_gpu, z_ref, what=""):
+    """End-to-end check of a layer whose experts take MXFP8 z (rows = tokens).
+
+    The MXFP8 code of a z element is an integer decided by floating point: a
+    z computed with fp32 accumulation (GPU) and one with fp64 (oracle) may
+    differ by one bf16 step, and where that step crosses an E4M3 rounding
+    midpoint the two codes differ by one E4M3 step. Both codes are correct
+    quantisations of an admissible z. So: every z element must be within one
+    bf16 step (plus 2^-12 RMS(z) near zero) of the oracle's; tokens whose z quantises identically on both
+    sides must meet the tolerance; tokens with a code flip are counted (at most
+    2 % of them) and only guarded against gross error (0.25 x RMS); their
+    values on the oracle's own z are checked exactly by check on the staged path
+    (experts, combine, output on the oracle's z)."""
+    # one bf16 step of the value, plus 2^-12 of RMS(z) for elements near zero
+    # (where the fp32-vs-fp64 difference of a 7168-term sum spans many steps
+    # of a tiny value)
+    dz = np.abs(z_gpu - z_ref)
+    zr = float(np.sqrt((z_ref ** 2).mean()))
+    bound = bf16_ulp(z_ref) + 2.0 ** -12 * zr
+    assert (dz <= bound).all(), (f"{cfg.name}{what}: z differs by {float((dz / bound).max()):.2f} x "
+                                 f"(one bf16 step + 2^-12 RMS(z))")
+    cg, sg = oracle.mx8_quantize(z_gpu)
+    co, so = oracle.mx8_quantize(z_ref)
+    flip = ((cg != co).any(1)) | ((sg != so).any(1))
+    rms = float(np.sqrt((y_ref ** 2).mean()))
+    err = np.abs(y_gpu - y_ref).max(1) / rms
+    tol = tol_of(cfg)
+    agree_max = float(err[~flip].max()) if (~flip).any() else 0.0
+    flip_max = float(err[flip].max()) if flip.any() else 0.0
+    say(f"  {cfg.name}{what}: {int(flip.sum())} of {len(err)} tokens with an MXFP8 z code flip "
+        f"(max|dy| {flip_max:.3e} x RMS); the others max|dy| = {agree_max:.3e} x RMS (tol {tol:g})")
+    assert agree_max <= tol, f"{cfg.name}{what}: max|dy|/RMS = {agree_max:.3e} > {tol}"
+    assert flip.mean() <= 0.02, f"{cfg.name}{what}: {int(flip.sum())} tokens with z code flips"
+    assert flip_max <= 0.25, f"{cfg.name}{what}: a flipped token is off by {flip_max:.3e} x RMS"
+
+
+def staged_on_z(cfg, inp, x, z, dev="cuda:0"):
+    """y of the tokens x [n, d] through the staged entry points, with the
+    latent z [n, d_lat] given (instead of computed by moe_latent_down)."""
+    c = cfg.replace(T=x.shape[0])
+    desc = moe.make_desc(c)
+    T, k, E = c.T, c.k, c.E
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gate = torch.empty((T, k), dtype=torch.float32, device=dev)
+    moe.moe_route(desc, x, inp["W_r"], inp["b"], idx, gate, None, moe.workspace(desc, moe.MOE_OP_ROUTE, dev))
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    moe.moe_permute(desc, idx, counts, offsets, perm, inv, moe.workspace(desc, moe.MOE_OP_PERMUTE, dev))
+    o = torch.empty((T * k, c.d_lat), dtype=act_torch(c), device=dev)
+    moe.moe_expert_ffn(desc, z, perm, offsets, inp, o, moe.workspace(desc, moe.MOE_OP_EXPERT_FFN, dev))
+    n = torch.empty((T, c.d_lat), dtype=act_torch(c), device=dev)
+    moe.moe_combine(desc, o, inv, gate, inp["gain"], n)
+    y = torch.empty((T, c.d), dtype=act_torch(c), device=dev)
+    moe.moe_output(desc, x, n, inp, y, moe.workspace(desc, moe.MOE_OP_OUTPUT, dev))
+    torch.cuda.synchronize()
+    return y, idx

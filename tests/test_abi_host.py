@@ -15,8 +15,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+PROBE_HEADER = os.path.join(ROOT, "include", "moe_probe.h")
+PROBE_LIB = os.path.join(ROOT, "sparse_mixture_experts_sigmoid_amd", "libmoe_probe.so")
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
@@ -28,6 +32,28 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(L, n), n
     assert set(moe.EXPORTS) == set(names)
+
+
+def test_probe_library_exports_and_validates():
+    """libmoe_probe.so (the benchmark's ceiling probes) exports what
+    include/moe_probe.h declares and rejects bad arguments before a launch."""
+    names = declared_functions(PROBE_HEADER)
+    assert names == ["moe_probe_hbm_read", "moe_probe_mfma", "moe_probe_mfma_flops"]
+    L = ctypes.CDLL(PROBE_LIB)
+    for n in names:
+        assert hasattr(L, n), n
+    L.moe_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    L.moe_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    L.moe_probe_mfma_flops.restype = ctypes.c_double
+    L.moe_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    assert L.moe_probe_mfma(2, 1, 1, FAKE, None) == -1
+    assert L.moe_probe_mfma(0, 0, 1, FAKE, None) == -1
+    assert L.moe_probe_mfma(0, 1, 1, None, None) == -1
+    assert L.moe_probe_hbm_read(FAKE, 24, 1, FAKE, None) == -1
+    assert L.moe_probe_hbm_read(MIS, 32, 1, FAKE, None) == -1
+    assert L.moe_probe_mfma_flops(0, 1, 1) == 4 * 4 * 2 * 32 * 32 * 16
+    assert L.moe_probe_mfma_flops(1, 2, 3) == 2 * 3 * 4 * 4 * 2 * 32 * 32 * 64
 
 
 def test_status_strings():
@@ -255,3 +281,29 @@ def test_qb_bias_validates_before_any_launch():
     d0 = moe.make_desc(synth.config("k3_prefill").replace(T=0))
     assert L.moe_qb_bias(ctypes.byref(d0), FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert b"T > 0" in L.moe_last_error()
+
+
+def test_expert_gate_up_validates_its_outputs():
+    """moe_expert_gate_up takes exactly one output: bf16 h, or MXFP8 hq with hqs
+    (the latter only on the scaled-MFMA path); every other mix is rejected on
+    the host, before any launch."""
+    L = moe.lib()
+    big = 1 << 40
+    d = moe.make_desc(synth.config("k3_decode"))
+    mw = moe.make_weights(_weights())
+    gu = lambda dd, h, hq, hqs, ws=FAKE, n=big: L.moe_expert_gate_up(
+        ctypes.byref(dd), FAKE, FAKE, FAKE, ctypes.byref(mw), h, hq, hqs, ws, n, None)
+    assert gu(d, None, None, None) == moe.MOE_ERR_INVALID_ARG            # no output
+    assert gu(d, FAKE, FAKE, FAKE) == moe.MOE_ERR_INVALID_ARG            # hq without MXFP8
+    assert gu(d, MIS, None, None) == moe.MOE_ERR_INVALID_ARG             # misaligned h
+    assert gu(d, FAKE, None, None, ws=FAKE, n=8) == moe.MOE_ERR_WORKSPACE
+    d8 = moe.make_desc(synth.config("k3_decode_mx8"))
+    mw = moe.make_weights(_weights(W_g=(FAKE, FAKE), W_v=(FAKE, FAKE), W_o=(FAKE, FAKE)))
+    assert gu(d8, FAKE, FAKE, FAKE) == moe.MOE_ERR_INVALID_ARG           # both outputs
+    assert gu(d8, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG           # hq without hqs
+    assert gu(d8, None, None, None) == moe.MOE_ERR_INVALID_ARG
+    need = moe.moe_workspace_bytes(d8, moe.MOE_OP_EXPERT_GATE_UP)
+    cfg8 = synth.config("k3_decode_mx8")
+    assert need >= cfg8.T * cfg8.d_lat                                  # the MXFP8 copy of z
+    assert need < moe.moe_workspace_bytes(d8, moe.MOE_OP_EXPERT_FFN)
+    assert gu(d8, None, FAKE, FAKE, ws=FAKE, n=need - 1) == moe.MOE_ERR_WORKSPACE

@@ -1,8 +1,9 @@
 """GPU parity at the K3 layer size for the prefill, skewed-routing and MXFP4
 prefill workloads, in the launch configuration bench.py times
 (moe_layer_forward, full batch). Routing (indices, gates, counts, and the
-permutation of the GPU's own routing) is compared for every token; outputs on
-a seeded token sample that includes the hottest and the coldest expert
+permutation of the GPU's own routing) is compared for every token; outputs for
+every token of the decode batches and for a seeded sample of 1024 tokens of the
+larger batches that includes tokens of the hottest and the coldest expert
 (tokens are independent in the forward pass, so each sampled row is exact)."""
 import numpy as np
 import pytest
@@ -12,14 +13,15 @@ import oracle
 import synth
 import sparse_mixture_experts_sigmoid_amd as moe
 
-from _gpu_helpers import say, to64, run_layer, check_y, sample_tokens
+from _gpu_helpers import (say, to64, run_layer, check_y, sample_tokens, check_mx8_layer,
+                          staged_on_z)
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name,n_sample", [("k3_skew", 10), ("k3_prefill", 8),
-                                           ("k3_prefill_mxfp4", 8), ("k3_prefill_mx8", 8),
-                                           ("k3_decode_mxfp4", 12), ("k3_decode_mx8", 12)])
+@pytest.mark.parametrize("name,n_sample", [("k3_skew", 1024), ("k3_prefill", 1024),
+                                           ("k3_prefill_mxfp4", 1024), ("k3_prefill_mx8", 1024),
+                                           ("k3_decode_mxfp4", 256), ("k3_decode_mx8", 256)])
 def test_k3_full_size(name, n_sample, device):
     cfg = synth.config(name)
     say(f"{name}: generating inputs on the GPU")
@@ -52,6 +54,21 @@ def test_k3_full_size(name, n_sample, device):
 
     toks = sample_tokens(cfg, idx_np, n_sample)
     say(f"{name}: oracle forward on {len(toks)} tokens")
-    y_ref = oracle.forward(cfg, w, tokens=toks,
-                           routing={"idx": ref["idx"][toks], "p": ref["p"][toks]})
-    check_y(cfg, to64(y)[toks], y_ref, " (sampled tokens)")
+    y_ref, inter = oracle.forward(cfg, w, tokens=toks,
+                                  routing={"idx": ref["idx"][toks], "p": ref["p"][toks]}, keep=True)
+    if cfg.expert_act != "mxfp8":
+        check_y(cfg, to64(y)[toks], y_ref, " (sampled tokens)")
+        return
+    # MXFP8 expert inputs: the layer's own z (within one bf16 step of the
+    # oracle's) decides the z codes; then the staged path on the oracle's z
+    inp = moe.prepare_weights(cfg, inp)
+    z = torch.empty((T, cfg.d_lat), dtype=torch.bfloat16, device=device)
+    moe.moe_latent_down(desc, inp["x"], inp["W_ld"], z, moe.workspace(desc, moe.MOE_OP_LATENT_DOWN, device))
+    torch.cuda.synchronize()
+    check_mx8_layer(cfg, to64(y)[toks], y_ref, to64(z)[toks], inter["z"], " (sampled tokens, layer)")
+    tk = torch.from_numpy(toks).to(device)
+    z_ref = torch.from_numpy(inter["z"].astype(np.float32)).to(torch.bfloat16).to(device)
+    assert np.array_equal(z_ref.float().cpu().numpy().astype(np.float64), inter["z"])
+    y_st, idx_st = staged_on_z(cfg, inp, inp["x"][tk].contiguous(), z_ref, device)
+    assert np.array_equal(idx_st.cpu().numpy(), ref["idx"][toks])
+    check_y(cfg, to64(y_st), y_ref, " (sampled tokens, staged on the oracle's z)")

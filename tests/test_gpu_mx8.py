@@ -11,7 +11,7 @@ import synth
 import sparse_mixture_experts_sigmoid_amd as moe
 from synth.configs import LayerConfig
 
-from _gpu_helpers import say, to64, run_layer, check_y
+from _gpu_helpers import say, to64, run_layer, check_y, staged_front
 
 pytestmark = pytest.mark.gpu
 
@@ -107,11 +107,15 @@ def test_layer_mx8_full_parity(cfg, device):
     assert np.array_equal(idx.cpu().numpy(), inter["idx"])
     assert np.array_equal(gate.cpu().numpy(), inter["p"])
     check_y(cfg, to64(y), y_ref)
-    # the scaled path is a different computation: it must not equal the bf16-input path
+    # the scaled path is a different computation: the GPU output must be much
+    # closer to the quantising oracle than to the bf16-input one
     y_bf16 = oracle.forward(cfg.replace(expert_act="act"), synth.HostWeights(cfg))
     rms = float(np.sqrt((y_ref ** 2).mean()))
+    e_q = float(np.abs(to64(y) - y_ref).max())
+    e_b = float(np.abs(to64(y) - y_bf16).max())
     say(f"  {cfg.name}: MXFP8-input vs bf16-input oracle: max|dy| = "
-        f"{np.abs(y_ref - y_bf16).max() / rms:.3e} x RMS")
+        f"{np.abs(y_ref - y_bf16).max() / rms:.3e} x RMS; GPU vs them {e_q / rms:.3e}, {e_b / rms:.3e}")
+    assert e_b > 3 * e_q, "the GPU output does not follow the MXFP8 quantisation"
 
 
 @pytest.mark.parametrize("rows,K", [(64, 128), (192, 3584), (1920, 384), (0, 128)])
@@ -146,3 +150,28 @@ def test_layer_mx8_tiled_weights(cfg, device):
     assert torch.equal(y_rows, y_t)
     y_ref = oracle.forward(cfg, synth.HostWeights(cfg))
     check_y(cfg_t, to64(y_t), y_ref)
+
+
+@pytest.mark.parametrize("name", ["mx8_small", "mx8_mid", "k3_decode_mx8"])
+def test_fused_h_quantisation_equals_quantiser(name, device):
+    """The gate/up epilogue that writes h straight in MXFP8 gives, bit for bit,
+    the codes and scales of the standalone quantiser (moe_quantize_mxfp8)
+    applied to the bf16 h that the same kernel writes without the fusion."""
+    cfg = {MX8_SMALL.name: MX8_SMALL, MX8_MID.name: MX8_MID}.get(name) or synth.config(name)
+    say(f"fused MXFP8 h: {name}")
+    inp = moe.prepare_weights(cfg, synth.device_inputs(cfg, device))
+    desc, idx, gate, offsets, perm, inv, z = staged_front(cfg, inp, device)
+    rows = cfg.T * cfg.k
+    ws = moe.workspace(desc, moe.MOE_OP_EXPERT_GATE_UP, device)
+    h = torch.empty((rows, cfg.F), dtype=torch.bfloat16, device=device)
+    moe.moe_expert_gate_up(desc, z, perm, offsets, inp, h=h, ws=ws)
+    hq = torch.full((rows, cfg.F), 0x5A, dtype=torch.uint8, device=device)
+    hqs = torch.full((rows, cfg.F // 32), 0x5A, dtype=torch.uint8, device=device)
+    moe.moe_expert_gate_up(desc, z, perm, offsets, inp, hq=hq, hqs=hqs, ws=ws)
+    q_ref = torch.empty_like(hq)
+    s_ref = torch.empty_like(hqs)
+    moe.moe_quantize_mxfp8(h, q_ref, s_ref)
+    torch.cuda.synchronize()
+    assert torch.equal(hqs, s_ref), "scale bytes differ"
+    bad = int((hq != q_ref).sum())
+    assert bad == 0, f"{bad} of {hq.numel()} codes differ"

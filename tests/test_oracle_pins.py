@@ -539,3 +539,104 @@ def test_mx8_ties_saturation_and_zero():
     assert scales[0, 0] == 127 and codes[0, 0] == 0x7E
     codes, scales = oracle.mx8_quantize(np.zeros((2, 64)))
     assert (codes == 0).all() and (scales == 0).all()
+
+
+# --------------------------------------------------------------------------
+# storage points: which intermediates the oracle rounds, and to what
+# --------------------------------------------------------------------------
+
+def _bf16_representable(v):
+    """Exactly a bf16 value: an fp32 value whose low 16 mantissa bits are zero."""
+    v = np.asarray(v, np.float64)
+    f = v.astype(np.float32)
+    return (f.astype(np.float64) == v) & ((f.view(np.uint32) & 0xFFFF) == 0)
+
+
+def _f32_representable(v):
+    v = np.asarray(v, np.float64)
+    return v.astype(np.float32).astype(np.float64) == v
+
+
+def _bf16_half_ulp(v):
+    """Half the spacing of bf16 values at |v| (normal range)."""
+    e = np.frexp(np.abs(np.asarray(v, np.float64)))[1]     # |v| in [2^(e-1), 2^e)
+    return np.ldexp(1.0, e - 1 - 8)
+
+
+def _routed_rows(inter, cfg):
+    """(token, slot) pairs in use (every slot of every token)."""
+    return inter["o"].reshape(-1, cfg.d_lat), inter["h"].reshape(-1, cfg.F)
+
+
+PIN_BF16 = LayerConfig("pin_bf16", T=24, d=64, d_lat=64, E=6, k=2, F=32, S=2, Fs=32, seed=5,
+                       bias=("uniform", 0.05))
+PIN_MX8 = LayerConfig("pin_mx8", T=24, d=64, d_lat=128, E=5, k=2, F=128, S=1, Fs=32, seed=6,
+                      expert_w="mxfp4", latent_w="mxfp4", expert_act="mxfp8", bias=("uniform", 0.05))
+
+
+def test_storage_points_bf16():
+    """bf16 activations: z, h, o, n and the shared experts' h are stored in bf16
+    (each one exactly a bf16 value, none of them all zero), z and n by rounding
+    to nearest (within half a bf16 step of the unrounded fp64 value, computed
+    here with numpy's matmul); y is not rounded."""
+    cfg = PIN_BF16
+    w = synth.HostWeights(cfg)
+    y, inter = oracle.forward(cfg, w, keep=True)
+    o, h = _routed_rows(inter, cfg)
+    for name, v in (("z", inter["z"]), ("h", h), ("o", o), ("n", inter["n"]), ("hs", inter["hs"])):
+        assert np.abs(v).max() > 0, name
+        assert _bf16_representable(v).all(), f"{name} is not stored in bf16"
+    assert np.array_equal(inter["z_in"], inter["z"]), "bf16 experts take z as stored"
+    x = oracle.widen(w.raw("x")).astype(np.float64)
+    z_exact = x @ oracle.widen(w.raw("W_ld")).astype(np.float64).T
+    assert (np.abs(inter["z"] - z_exact) <= _bf16_half_ulp(z_exact) * (1 + 1e-9)).all()
+    u = inter["u"]
+    n_exact = u / np.sqrt((u ** 2).mean(1, keepdims=True) + cfg.eps)
+    assert (np.abs(inter["n"] - n_exact) <= _bf16_half_ulp(n_exact) * (1 + 1e-9)).all()
+    assert not _bf16_representable(y).all(), "y is returned unrounded"
+
+
+def test_storage_points_fp32():
+    """fp32 activations: the same intermediates are fp32 values, and most of
+    them are not on the bf16 grid (nothing is rounded to bf16)."""
+    cfg = synth.config("tiny_f32")
+    y, inter = oracle.forward(cfg, synth.HostWeights(cfg), keep=True)
+    o, h = _routed_rows(inter, cfg)
+    for name, v in (("z", inter["z"]), ("h", h), ("o", o), ("n", inter["n"]), ("hs", inter["hs"])):
+        assert _f32_representable(v).all(), f"{name} is not stored in fp32"
+        nz = v[v != 0]
+        assert (~_bf16_representable(nz)).mean() > 0.9, f"{name} looks rounded to bf16"
+
+
+def test_storage_points_mxfp8_expert_inputs():
+    """MXFP8 expert inputs: the z rows and h rows the experts multiply are MXFP8
+    values (quantising them again changes nothing), they differ from the bf16
+    values they came from (the quantisation took place), and o, n and the
+    shared h stay bf16."""
+    cfg = PIN_MX8
+    y, inter = oracle.forward(cfg, synth.HostWeights(cfg), keep=True)
+    o, h = _routed_rows(inter, cfg)
+    for name, v in (("z_in", inter["z_in"]), ("h", h)):
+        assert np.abs(v).max() > 0, name
+        again = oracle.mx8_dequantize(*oracle.mx8_quantize(v))
+        assert np.array_equal(again, v), f"{name} is not an MXFP8 value"
+    assert _bf16_representable(inter["z"]).all()
+    assert not np.array_equal(inter["z_in"], inter["z"]), "z was not quantised"
+    # bf16 h of the same rows, recomputed from the quantised z (numpy matmul);
+    # the kept h must be its MXFP8 image, not the bf16 value itself
+    w = synth.HostWeights(cfg)
+    idx = inter["idx"]
+    t, j = 3, 1
+    e = int(idx[t, j])
+    Wg = oracle.widen(w.raw("W_g", e * cfg.F, cfg.F)).astype(np.float64)
+    Wv = oracle.widen(w.raw("W_v", e * cfg.F, cfg.F)).astype(np.float64)
+    zt = inter["z_in"][t]
+    g, v = Wg @ zt, Wv @ zt
+    hb = np.array([oracle.lib().orc_round_bf16(c * math.tanh(gg / (1 + math.exp(-gg)) / c) *
+                                               c * math.tanh(vv / c))
+                   for gg, vv, c in zip(g, v, [cfg.c] * len(g))])
+    hq = oracle.mx8_dequantize(*oracle.mx8_quantize(hb[None, :]))[0]
+    assert np.array_equal(inter["h"][t, j], hq)
+    assert not np.array_equal(hq, hb)
+    for name, v in (("o", o), ("n", inter["n"]), ("hs", inter["hs"])):
+        assert _bf16_representable(v).all(), f"{name} is not stored in bf16"
