@@ -16,8 +16,10 @@
  *     "MXFP4 Quantization-Aware Training": MXFP4 weights (OCP MX v1.0 e2m1
  *     elements, one e8m0 scale per 32 elements along K).
  *
- * Library state: none in device memory. On the host: the per-device side
- * stream of moe_layer_forward (two events with it), the trace events of
+ * Library state: in device memory only the fixed scratch array of
+ * moe_layer_forward_noalloc (one copy per GPU the library runs on). On the
+ * host: the per-device side stream of moe_layer_forward (two events with it),
+ * the device address of that scratch per GPU, the trace events of
  * moe_trace_enable, and the thread-local error text of moe_last_error.
  *
  * Calling convention (all entry points):
@@ -244,6 +246,24 @@ int moe_output(const moe_desc_t* desc, const void* x, const void* n, const moe_w
 int moe_layer_forward(const moe_desc_t* desc, const moe_weights_t* w, const void* x, void* y,
                       int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* counts_opt,
                       void* ws, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+   capture, tight serving loops, harnesses that forbid allocation): the same
+   layer as moe_layer_forward, with the same arguments except the workspace.
+   Its scratch is a fixed array of moe_noalloc_scratch_bytes() bytes (128 MiB)
+   inside the library's code object: one copy on every GPU the library runs
+   on, held until the process ends. The call allocates nothing and runs every
+   stage in order on `stream` (no second stream, no events, no tracing).
+   A batch whose workspace (moe_workspace_bytes(desc, MOE_OP_LAYER)) exceeds
+   the array is rejected on the host with MOE_ERR_UNSUPPORTED (at the K3 shape
+   that is above about 360 tokens). All calls on one GPU share its array:
+   calls that overlap on one GPU (different streams, or host threads) race and
+   must be serialised by the caller. Nothing in the array needs clearing
+   between calls (every kernel writes what the same call later reads). */
+int moe_layer_forward_noalloc(const moe_desc_t* desc, const moe_weights_t* w, const void* x,
+                              void* y, int32_t* topk_idx_opt, float* topk_gate_opt,
+                              int32_t* counts_opt, void* stream);
+size_t moe_noalloc_scratch_bytes(void);
 
 /* MXFP8 quantisation of bf16 rows, the activation format of the scaled-MFMA
    expert path (expert_act_mxfp8; the MX format of "Kimi K3 ... Open Frontier

@@ -27,6 +27,7 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
 
 EXPORTS = ["moe_workspace_bytes", "moe_check_desc", "moe_route", "moe_permute", "moe_latent_down",
            "moe_expert_ffn", "moe_expert_gate_up", "moe_combine", "moe_output", "moe_layer_forward",
+           "moe_layer_forward_noalloc", "moe_noalloc_scratch_bytes",
            "moe_status_string", "moe_last_error", "moe_trace_enable", "moe_trace_read",
            "moe_trace_stage_name", "moe_qb_bias", "moe_quantize_mxfp8", "moe_mxfp4_tile"]
 MOE_TRACE_STAGES = 10
@@ -78,6 +79,8 @@ def lib():
         "moe_combine": ([D, vp, vp, vp, vp, vp, vp, vp], i32),
         "moe_output": ([D, vp, vp, WS, vp, vp, sz, vp], i32),
         "moe_layer_forward": ([D, WS, vp, vp, vp, vp, vp, vp, sz, vp], i32),
+        "moe_layer_forward_noalloc": ([D, WS, vp, vp, vp, vp, vp, vp], i32),
+        "moe_noalloc_scratch_bytes": ([], sz),
         "moe_status_string": ([i32], ctypes.c_char_p),
         "moe_last_error": ([], ctypes.c_char_p),
         "moe_trace_enable": ([i32], i32),
@@ -224,6 +227,19 @@ def moe_layer_forward(desc, weights: dict, x, y, topk_idx=None, topk_gate=None, 
     _check(lib().moe_layer_forward(ctypes.byref(desc), ctypes.byref(w), _ptr(x), _ptr(y),
                                    _ptr(topk_idx), _ptr(topk_gate), _ptr(counts), p, n,
                                    _stream(stream)))
+
+
+def moe_layer_forward_noalloc(desc, weights: dict, x, y, topk_idx=None, topk_gate=None,
+                              counts=None, stream=None):
+    """moe_layer_forward on the library's fixed scratch (no workspace argument)."""
+    w = make_weights(weights)
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(desc), ctypes.byref(w), _ptr(x), _ptr(y),
+                                           _ptr(topk_idx), _ptr(topk_gate), _ptr(counts),
+                                           _stream(stream)))
+
+
+def moe_noalloc_scratch_bytes() -> int:
+    return int(lib().moe_noalloc_scratch_bytes())
 
 
 def moe_qb_bias(desc, scores, bias_out, quantile_out, stream=None):

@@ -591,6 +591,38 @@ int run_layer(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* 
   return MOE_OK;
 }
 
+// Scratch of moe_layer_forward_noalloc, for callers that cannot allocate
+// device memory: a fixed array in the code object, one copy on every GPU the
+// library runs on, held until the process ends. In host code `scratch` names
+// a host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, once per device (with that device current), and only
+// that address is ever passed to a kernel. Calls on one GPU share its copy
+// (the last call's contents stay); no kernel reads scratch that the same call
+// has not written first, so nothing needs clearing between calls. Calls that
+// overlap on one GPU race on it.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail((int)e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail((int)e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------------
@@ -884,6 +916,25 @@ int moe_layer_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x
   std::lock_guard<std::mutex> lk(sd->mu);
   return run_layer(d, w, x, y, topk_idx_opt, topk_gate_opt, counts_opt, ws, (hipStream_t)stream, sd,
                    Marker{trace_begin()});
+}
+
+size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int moe_layer_forward_noalloc(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
+                              int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* counts_opt,
+                              void* stream) {
+  g_last_error.clear();
+  MOE_CHECK(check_layer_args(d, w, x, y, topk_idx_opt, topk_gate_opt, counts_opt));
+  const size_t need = ws_bytes_for(d, MOE_OP_LAYER);
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "moe_layer_forward_noalloc: this batch needs %zu bytes of scratch, more than the "
+                "library's fixed %zu (use moe_layer_forward with a workspace, or fewer tokens)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  MOE_CHECK(scratch_ptr(&ws));
+  return run_layer(d, w, x, y, topk_idx_opt, topk_gate_opt, counts_opt, ws, (hipStream_t)stream,
+                   nullptr, Marker{-1});
 }
 
 }  // extern "C"
