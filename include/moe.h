@@ -53,6 +53,24 @@
  *   (r%2) 64 + j, i.e. [R/2][K/128][2][64]: a stage of a row pair is one
  *   128-byte line. Scales: the scale of row r, 32-element block b at
  *   ((r/64) (K/128) + b/4) 256 + (r%64) 4 + b%4, i.e. [R/64][K/128][64][4].
+ *   Fragment-tiled bf16 weight (routed experts, see expert_w_tiled; made by
+ *   moe_bf16_tile; R % 32 == 0): K padded with zeros to Kp, the next multiple
+ *   of 64; for each group g of 32 rows and each k-step s of 16 elements, the
+ *   1 KB at byte (g (Kp/16) + s) 1024 holds 64 pieces of 8 elements, piece l
+ *   = row 32 g + l % 32, k = 16 s + 8 (l / 32) .. +7 (the order in which the
+ *   bf16 matrix instruction takes its B operand). W_g, W_v as R = E F rows of
+ *   K = d_latent, W_o as R = E d_latent rows of K = d_ff; moe_bf16_tiled_bytes
+ *   gives the size (R Kp 2 bytes).
+ *   Fragment-tiled MXFP4 weight (routed experts on the bf16-activation path,
+ *   see expert_w_tiled; made by moe_mxfp4_frag_tile; R % 32 == 0, K % 32 ==
+ *   0): K padded with zeros to Kp, the next multiple of 128. Packed codes: for
+ *   each group g of 32 rows and each 64-element tile t, the 1 KB at byte
+ *   (g (Kp/64) + t) 1024 holds 64 pieces of 16 bytes; piece l (row 32 g +
+ *   l % 32) holds in its bytes 4s .. 4s+3 the 8 codes of k = 64 t + 16 s +
+ *   8 (l / 32) .. +7 (s = 0..3, low nibble first). Scales: for each group g
+ *   and 128-element pair p, the 128 bytes at (g (Kp/128) + p) 128 hold, for
+ *   each of the 32 rows, the 4 scale bytes of its 32-element blocks 4p .. 4p+3.
+ *   moe_mxfp4_frag_tiled_bytes gives both sizes (R Kp/2 and R Kp/32 bytes).
  *   topk_idx [T, k] int32, topk_gate [T, k] fp32 (slot order = key descending,
  *   ties to the lower expert index).
  *   Permutation: rows of expert e are offsets[e] .. offsets[e+1]-1 (offsets has
@@ -117,12 +135,20 @@ typedef struct {
      d_latent, d_ff multiples of 128. Changes the numerics (the oracle quantises
      the same way). */
   int32_t expert_act_mxfp8;
-  /* 0: W_g, W_v, W_o row-major. 1: in the tiled MXFP4 layout above (made once
-     per weight set by moe_mxfp4_tile); needs expert_act_mxfp8 = 1. The
-     scaled-MFMA expert kernels then read each 128-element K stage as whole
-     128-byte lines of row pairs and the stage's scales of 64 weight rows as
-     256 contiguous bytes, instead of half lines and 4 bytes from each of 64
-     rows. Same results either way. */
+  /* 0: W_g, W_v, W_o row-major. 1: tiled, made once per weight set at load
+     time (needs act_dtype MOE_BF16):
+     - MXFP4 weights with expert_act_mxfp8 = 1: the tiled MXFP4 layout above
+       (moe_mxfp4_tile); the scaled-MFMA expert kernels then read each
+       128-element K stage as whole 128-byte lines of row pairs and the
+       stage's scales of 64 weight rows as 256 contiguous bytes;
+     - MXFP4 weights with expert_act_mxfp8 = 0: the fragment-tiled MXFP4
+       layout above (moe_mxfp4_frag_tile); the expert kernels load each
+       64-element K tile of a weight fragment as one 1 KB line straight into
+       registers and decode it there;
+     - bf16 weights: the fragment-tiled bf16 layout above (moe_bf16_tile); the
+       expert kernels load each weight fragment straight into registers as
+       one 1 KB line, without staging it in LDS.
+     Same results as the row-major weights in every case. */
   int32_t expert_w_tiled;
 } moe_desc_t;
 
@@ -290,6 +316,34 @@ int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, int64_t ld, uint8
    rows == 0 does nothing. */
 int moe_mxfp4_tile(const uint8_t* data, const uint8_t* scale, uint8_t* data_out, uint8_t* scale_out,
                    int64_t rows, int32_t K, void* stream);
+
+/* Fragment-tiled copy of an MXFP4 expert weight (layout under Layouts) for
+   the expert kernels that decode the weights in registers (bf16 activations,
+   expert_act_mxfp8 = 0; "Kimi K3 ... Open Frontier Intelligence", section
+   "MXFP4 Quantization-Aware Training"): data [rows, K/2] and scale [rows, K/32]
+   row-major in; data_out and scale_out of the sizes moe_mxfp4_frag_tiled_bytes
+   gives. A reordering of the same codes and scales (K padded with code 0 and
+   scale byte 0), made once when a weight set is loaded. rows % 32 == 0,
+   K % 32 == 0; data pointers 16-byte and scale_out 4-byte aligned; no output
+   may overlap an input or the other output (else MOE_ERR_INVALID_ARG). Device
+   memory owned by the caller; asynchronous on stream; allocates nothing. */
+int moe_mxfp4_frag_tile(const uint8_t* data, const uint8_t* scale, uint8_t* data_out, uint8_t* scale_out,
+                        int64_t rows, int32_t K, void* stream);
+/* Sizes of that copy (host only): *data_bytes = rows Kp / 2, *scale_bytes =
+   rows Kp / 32 with Kp = K rounded up to a multiple of 128. */
+int moe_mxfp4_frag_tiled_bytes(int64_t rows, int32_t K, int64_t* data_bytes, int64_t* scale_bytes);
+
+/* Fragment-tiled copy of a bf16 expert weight (layout under Layouts) for the
+   bf16 expert kernels that keep the weights in registers: data [rows, K]
+   row-major in, data_out of moe_bf16_tiled_bytes(rows, K) bytes out (K padded
+   with zeros to a multiple of 64). A reordering of the same values, made once
+   when a weight set is loaded, not per batch. rows % 32 == 0, K % 8 == 0,
+   both pointers 16-byte aligned, data_out not overlapping data (else
+   MOE_ERR_INVALID_ARG). Device memory owned by the caller; asynchronous on
+   stream; allocates nothing. rows == 0 does nothing. */
+int moe_bf16_tile(const void* data, void* data_out, int64_t rows, int32_t K, void* stream);
+/* Bytes of that copy: rows * Kp * 2 (0 for invalid rows / K). Host only. */
+int64_t moe_bf16_tiled_bytes(int64_t rows, int32_t K);
 
 /* Quantile Balancing: the per-expert selection bias from quantiles of the
    router scores ("Kimi K3の896エキスパートを「896人の専門家」と呼ぶと何がズレるか",

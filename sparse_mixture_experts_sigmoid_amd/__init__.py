@@ -29,7 +29,8 @@ EXPORTS = ["moe_workspace_bytes", "moe_check_desc", "moe_route", "moe_permute", 
            "moe_expert_ffn", "moe_expert_gate_up", "moe_combine", "moe_output", "moe_layer_forward",
            "moe_layer_forward_noalloc", "moe_noalloc_scratch_bytes",
            "moe_status_string", "moe_last_error", "moe_trace_enable", "moe_trace_read",
-           "moe_trace_stage_name", "moe_qb_bias", "moe_quantize_mxfp8", "moe_mxfp4_tile"]
+           "moe_trace_stage_name", "moe_qb_bias", "moe_quantize_mxfp8", "moe_mxfp4_tile", "moe_bf16_tile",
+           "moe_bf16_tiled_bytes", "moe_mxfp4_frag_tile", "moe_mxfp4_frag_tiled_bytes"]
 MOE_TRACE_STAGES = 10
 
 
@@ -89,6 +90,11 @@ def lib():
         "moe_qb_bias": ([D, vp, vp, vp, vp], i32),
         "moe_quantize_mxfp8": ([vp, ctypes.c_int64, i32, ctypes.c_int64, vp, vp, vp], i32),
         "moe_mxfp4_tile": ([vp, vp, vp, vp, ctypes.c_int64, i32, vp], i32),
+        "moe_bf16_tile": ([vp, vp, ctypes.c_int64, i32, vp], i32),
+        "moe_bf16_tiled_bytes": ([ctypes.c_int64, i32], ctypes.c_int64),
+        "moe_mxfp4_frag_tile": ([vp, vp, vp, vp, ctypes.c_int64, i32, vp], i32),
+        "moe_mxfp4_frag_tiled_bytes": ([ctypes.c_int64, i32, ctypes.POINTER(ctypes.c_int64),
+                                        ctypes.POINTER(ctypes.c_int64)], i32),
     }
     for name, (args, res) in sigs.items():
         fn = getattr(L, name)
@@ -263,14 +269,60 @@ def moe_mxfp4_tile(data, scale, data_out, scale_out, stream=None):
                                 kb * 32, _stream(stream)))
 
 
+def moe_bf16_tile(data, data_out, stream=None):
+    """Fragment-tiled copy of a bf16 weight [rows, K] into data_out (a device
+    byte tensor of moe_bf16_tiled_bytes(rows, K) bytes)."""
+    rows, K = data.shape
+    _check(lib().moe_bf16_tile(_ptr(data), _ptr(data_out), rows, K, _stream(stream)))
+
+
+def moe_bf16_tiled_bytes(rows: int, K: int) -> int:
+    return int(lib().moe_bf16_tiled_bytes(rows, K))
+
+
+def moe_mxfp4_frag_tiled_bytes(rows: int, K: int) -> tuple[int, int]:
+    """(packed bytes, scale bytes) of the fragment-tiled copy of an MXFP4 weight."""
+    d, s = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib().moe_mxfp4_frag_tiled_bytes(rows, K, ctypes.byref(d), ctypes.byref(s)))
+    return int(d.value), int(s.value)
+
+
+def moe_mxfp4_frag_tile(data, scale, data_out, scale_out, stream=None):
+    """Fragment-tiled copy (data_out, scale_out) of a row-major MXFP4 weight:
+    packed [rows, K/2] and scales [rows, K/32], uint8 device tensors."""
+    rows, kb = scale.shape
+    _check(lib().moe_mxfp4_frag_tile(_ptr(data), _ptr(scale), _ptr(data_out), _ptr(scale_out), rows,
+                                     kb * 32, _stream(stream)))
+
+
 def prepare_weights(cfg, weights: dict, stream=None) -> dict:
     """The weight dict the layer reads for `cfg`: the same tensors, except that a
     config with expert_layout == 'tiled' gets tiled copies of W_g, W_v and W_o
-    (made once here, on the device, not per batch)."""
+    (made once here, on the device, not per batch): the MXFP4 tiled layout for
+    MXFP4 expert weights, the fragment-tiled layout for bf16 ones."""
     if getattr(cfg, "expert_layout", "rows") != "tiled":
         return weights
     import torch
     out = dict(weights)
+    if getattr(cfg, "expert_w", "bf16") == "bf16":
+        for name in ("W_g", "W_v", "W_o"):
+            w = weights[name]
+            w2 = w.reshape(-1, w.shape[-1])
+            t = torch.empty(moe_bf16_tiled_bytes(w2.shape[0], w2.shape[1]), dtype=torch.uint8,
+                            device=w.device)
+            moe_bf16_tile(w2, t, stream)
+            out[name] = t
+        return out
+    if getattr(cfg, "expert_act", "act") != "mxfp8":
+        for name in ("W_g", "W_v", "W_o"):
+            packed, scale = weights[name]
+            p2, s2 = packed.reshape(-1, packed.shape[-1]), scale.reshape(-1, scale.shape[-1])
+            nd, ns = moe_mxfp4_frag_tiled_bytes(p2.shape[0], s2.shape[1] * 32)
+            tp = torch.empty(nd, dtype=torch.uint8, device=packed.device)
+            ts = torch.empty(ns, dtype=torch.uint8, device=packed.device)
+            moe_mxfp4_frag_tile(p2, s2, tp, ts, stream)
+            out[name] = (tp, ts)
+        return out
     for name in ("W_g", "W_v", "W_o"):
         packed, scale = weights[name]
         p2, s2 = packed.reshape(-1, packed.shape[-1]), scale.reshape(-1, scale.shape[-1])

@@ -86,9 +86,8 @@ int check_desc(const moe_desc_t* d) {
                 "weights and d_latent, d_ff multiples of 128");
   if (d->expert_w_tiled != 0 && d->expert_w_tiled != 1)
     return fail(MOE_ERR_INVALID_ARG, "expert_w_tiled must be 0 or 1");
-  if (d->expert_w_tiled && !d->expert_act_mxfp8)
-    return fail(MOE_ERR_UNSUPPORTED, "tiled expert weights are read only by the MXFP8 expert path "
-                "(expert_act_mxfp8 = 1)");
+  if (d->expert_w_tiled && d->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_UNSUPPORTED, "tiled expert weights need bf16 activations");
   if (d->n_experts > kMaxExperts)
     return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", kMaxExperts);
   if (d->n_shared + 1 > moe::kMaxSegments)
@@ -123,7 +122,7 @@ struct LayerWs {
 };
 
 int max_tiles(const moe_desc_t* d) {
-  const int bm = moe::grouped_bm(d->act_dtype, d->expert_w_dtype, d->expert_act_mxfp8, (int64_t)d->T * d->top_k, d->n_experts);
+  const int bm = moe::grouped_bm(d->act_dtype, d->expert_w_dtype, d->expert_act_mxfp8, d->expert_w_tiled, (int64_t)d->T * d->top_k, d->n_experts);
   return (int)(((int64_t)d->T * d->top_k + bm - 1) / bm + d->n_experts);
 }
 
@@ -373,7 +372,7 @@ int do_gate_up(const moe_desc_t* d, const void* z, const int32_t* perm, const in
                const moe_weights_t* w, int32_t* tile_off, int32_t* tile_info, void* H,
                const MxBufs& mx, hipStream_t st, Marker mk = {-1}) {
   const bool q8 = d->expert_act_mxfp8 != 0;
-  const int bm = moe::grouped_bm(d->act_dtype, d->expert_w_dtype, d->expert_act_mxfp8, (int64_t)d->T * d->top_k, d->n_experts);
+  const int bm = moe::grouped_bm(d->act_dtype, d->expert_w_dtype, d->expert_act_mxfp8, d->expert_w_tiled, (int64_t)d->T * d->top_k, d->n_experts);
   mk.beg(4, st);
   if (d->T > 0)
     MOE_LAUNCH(moe::launch_tile_table(offsets, d->n_experts, bm, tile_off, tile_info, st),
@@ -403,7 +402,7 @@ int do_experts(const moe_desc_t* d, const void* z, const int32_t* perm, const in
                const moe_weights_t* w, void* o_perm, int32_t* tile_off, int32_t* tile_info, void* H,
                const MxBufs& mx, hipStream_t st, Marker mk = {-1}) {
   const bool q8 = d->expert_act_mxfp8 != 0;
-  const int bm = moe::grouped_bm(d->act_dtype, d->expert_w_dtype, d->expert_act_mxfp8, (int64_t)d->T * d->top_k, d->n_experts);
+  const int bm = moe::grouped_bm(d->act_dtype, d->expert_w_dtype, d->expert_act_mxfp8, d->expert_w_tiled, (int64_t)d->T * d->top_k, d->n_experts);
   const int mt = max_tiles(d);
   const int rows_cap = d->T * d->top_k;
   // the scaled-MFMA path writes h straight in MXFP8 (the down GEMM's input)
@@ -888,6 +887,54 @@ int moe_mxfp4_tile(const uint8_t* data, const uint8_t* scale, uint8_t* data_out,
     return fail(MOE_ERR_INVALID_ARG, "an output overlaps an input or the other output");
   MOE_LAUNCH(moe::launch_tile_mxfp4(data, scale, data_out, scale_out, rows, K, (hipStream_t)stream),
              "mxfp4_tile");
+  return MOE_OK;
+}
+
+int moe_mxfp4_frag_tiled_bytes(int64_t rows, int32_t K, int64_t* data_bytes, int64_t* scale_bytes) {
+  g_last_error.clear();
+  if (rows < 0 || K <= 0 || rows % 32 || K % 32)
+    return fail(MOE_ERR_INVALID_ARG, "rows >= 0 with rows %% 32 == 0 and K > 0 with K %% 32 == 0 required");
+  if (!data_bytes || !scale_bytes) return fail(MOE_ERR_INVALID_ARG, "data_bytes or scale_bytes is NULL");
+  moe::tiled_mxfp4_frag_bytes(rows, K, data_bytes, scale_bytes);
+  return MOE_OK;
+}
+
+int moe_mxfp4_frag_tile(const uint8_t* data, const uint8_t* scale, uint8_t* data_out, uint8_t* scale_out,
+                        int64_t rows, int32_t K, void* stream) {
+  g_last_error.clear();
+  if (rows < 0 || K <= 0 || rows % 32 || K % 32)
+    return fail(MOE_ERR_INVALID_ARG, "rows >= 0 with rows %% 32 == 0 and K > 0 with K %% 32 == 0 required");
+  if (rows == 0) return MOE_OK;
+  MOE_CHECK(need_ptr(data, "data"));
+  MOE_CHECK(need_ptr(data_out, "data_out"));
+  if (scale == nullptr || scale_out == nullptr) return fail(MOE_ERR_INVALID_ARG, "scale or scale_out is NULL");
+  if (((uintptr_t)scale_out) % 4) return fail(MOE_ERR_INVALID_ARG, "scale_out must be 4-byte aligned");
+  int64_t nd = 0, ns = 0;
+  moe::tiled_mxfp4_frag_bytes(rows, K, &nd, &ns);
+  const int64_t id = rows * (K / 2), is = rows * (K / 32);
+  if (overlap(data_out, nd, data, id) || overlap(data_out, nd, scale, is) || overlap(scale_out, ns, data, id) ||
+      overlap(scale_out, ns, scale, is) || overlap(data_out, nd, scale_out, ns))
+    return fail(MOE_ERR_INVALID_ARG, "an output overlaps an input or the other output");
+  MOE_LAUNCH(moe::launch_tile_mxfp4_frag(data, scale, data_out, scale_out, rows, K, (hipStream_t)stream),
+             "mxfp4_frag_tile");
+  return MOE_OK;
+}
+
+int64_t moe_bf16_tiled_bytes(int64_t rows, int32_t K) {
+  if (rows < 0 || K <= 0 || rows % 32 || K % 8) return 0;
+  return moe::tiled_bf16_bytes(rows, K);
+}
+
+int moe_bf16_tile(const void* data, void* data_out, int64_t rows, int32_t K, void* stream) {
+  g_last_error.clear();
+  if (rows < 0 || K <= 0 || rows % 32 || K % 8)
+    return fail(MOE_ERR_INVALID_ARG, "rows >= 0 with rows %% 32 == 0 and K > 0 with K %% 8 == 0 required");
+  if (rows == 0) return MOE_OK;
+  MOE_CHECK(need_ptr(data, "data"));
+  MOE_CHECK(need_ptr(data_out, "data_out"));
+  if (overlap(data_out, moe::tiled_bf16_bytes(rows, K), data, rows * (int64_t)K * 2))
+    return fail(MOE_ERR_INVALID_ARG, "data_out overlaps data");
+  MOE_LAUNCH(moe::launch_tile_bf16(data, data_out, rows, K, (hipStream_t)stream), "bf16_tile");
   return MOE_OK;
 }
 

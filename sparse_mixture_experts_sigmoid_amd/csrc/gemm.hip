@@ -1635,7 +1635,587 @@ __global__ __launch_bounds__(512) void grouped_down_mx8_kernel(GroupedDownArgs a
   store_tile(acc, (bf16_t*)a.O, a.N, row_lo, n0, row_hi, a.N);
 }
 
+// ---------------------------------------------------------------------------
+// Grouped expert GEMMs with the weights in registers (bf16, fragment-tiled)
+// ---------------------------------------------------------------------------
+//
+// The expert weights are re-laid once at load time (moe_bf16_tile) in the
+// order the MFMA takes them: for each group of 32 weight rows and each k-step
+// of 16, the 32 x 16 block as 64 lanes x 16 bytes, lane l holding row l % 32,
+// k = 8 (l / 32) .. +7 (the B operand of v_mfma_f32_32x32x16_bf16); K padded to
+// a multiple of 64 with zeros. One B fragment is then one fully used 1 KB load
+// straight into registers: the weights never pass through LDS. Only the
+// gathered z (or h) rows do, through a 4-stage ring of 64-k tiles (16 KB
+// each), shared by the block's 4 waves.
+//
+// Block 128 rows x 512 weight rows, 4 waves of 128 x 128 (4 x 4 fragments,
+// one wave per SIMD): per 16-k step a wave reads 4 A fragments from LDS and
+// takes 4 B fragments from registers for 16 MFMAs. The B fragments of k-step
+// q + 7 are loaded while k-step q computes, into a ring of 8 register slots.
+namespace bt {
+constexpr int BM = 128, BN = 512, NW = 4, BK = 64, KS = BK / 16;
+constexpr int NSA = 4;                     // A stages
+constexpr int LEAD = 7, SLOTS = 8;         // B k-steps loaded ahead; register slots
+constexpr int AR = BM / (NW * 8);          // A DMA per wave per stage (8 rows of 128 B each)
+using L = Cfg<1, 4, 4, 4, 64, 2>;          // accumulator / epilogue layout (128 x 512)
+static_assert(L::BM == BM && L::BN == BN && L::NT == 256 && L::AR == AR, "layout");
+
+struct BSrc {
+  rsrc_t r[2];                 // weight resources (gate, up for a GLU tile; one for plain)
+  uint32_t off[4];             // byte offset of fragment j's first k-step tile + 16 lane, or kOOB
+};
+
+// 4 B fragments (one k-step) into slot registers: fragment j of k-step q is
+// the 1 KB at off[j] + 1024 q.
+__device__ __forceinline__ void load_b(const BSrc& b, int q, bf16x8 (&dst)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t o = b.off[j];
+    dst[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                            b.r[j >= 2 ? 1 : 0], o + 1024u * (uint32_t)q, 0, 0));
+  }
+}
+
+// A fragments of k-step ks of an A stage (BM x BK, the swizzled 128-byte rows
+// of the DMA engine): NV fragments of 32 rows.
+template <int NV>
+__device__ __forceinline__ void read_a(const bf16_t* S, int ks, bf16x8 (&fa)[4]) {
+  if constexpr (NV > 0) {
+    const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
+    const bf16_t* Aw = S + lr * BK;
+    const int slot = 8 * ((2 * ks + lh) ^ swz<L>(lr));
+#pragma unroll
+    for (int i = 0; i < NV; ++i) fa[i] = *(const bf16x8*)(Aw + i * 32 * BK + slot);
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void mma_q(const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], Acc<L>& acc) {
+#pragma unroll
+  for (int i = 0; i < NV; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
+}
+
+__device__ __forceinline__ void dma_a(const Rows<AR>& ar, bf16_t* S, int kt, int K) {
+  dma_rows<L, AR>(ar, S, kt * BK, K);
+}
+
+// B register slots: slot s holds the 4 fragments of the k-steps q = s (mod SLOTS).
+struct BRing {
+  bf16x8 b[SLOTS][4];
+};
+
+// One k-step Q (0 .. 15) of a round of NSA K-tiles (round base k-step q0):
+// load B of k-step q0 + Q + LEAD, then (ks < 3) read the next A fragments of
+// this tile or (ks == 3) wait for the next tile's stage, barrier, refill this
+// stage with tile kt + NSA and read the next tile's first A fragments; then
+// this k-step's MFMAs.
+template <int NV, int Q>
+__device__ __forceinline__ void bt_kstep(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const BSrc& bs,
+                                         int q0, int K, BRing& br, bf16x8 (&fa0)[4], bf16x8 (&fa1)[4],
+                                         Acc<L>& acc) {
+  constexpr int T = Q / KS, ks = Q % KS;
+  constexpr int slot = Q % SLOTS, lslot = (Q + LEAD) % SLOTS;
+  if constexpr (ks + 1 < KS) {
+    load_b(bs, q0 + Q + LEAD, br.b[lslot]);
+    if constexpr (ks & 1) read_a<NV>(st[T], ks + 1, fa0);
+    else read_a<NV>(st[T], ks + 1, fa1);
+  } else {
+    load_b(bs, q0 + Q + LEAD, br.b[lslot]);
+    // the next tile's A stage must have landed (own DMA, then every wave's),
+    // and every wave must be done reading this stage before it is refilled.
+    // 24 = the vector-memory ops issued after the next tile's DMA in the
+    // first round (A of tiles 2, 3 and the B loads of 4 k-steps); later
+    // rounds issue more, so this waits a little longer than needed there.
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0_vm(24));
+    wg_barrier();
+    dma_a(ar, st[T], (q0 / KS) + T + NSA, K);
+    static_assert(KS % 2 == 0, "k-step 0 of a tile reads into fa0");
+    read_a<NV>(st[(T + 1) % NSA], 0, fa0);
+  }
+  if constexpr (ks & 1) mma_q<NV>(fa1, br.b[slot], acc);
+  else mma_q<NV>(fa0, br.b[slot], acc);
+  // one wave per SIMD: the next k-step's A reads and the loads go between the
+  // MFMAs, so that their latency overlaps matrix work. Per A fragment i:
+  // MFMA, read, MFMA, load, 2 MFMAs (loads: B before the tile's barrier, the
+  // refill DMA of the A stage after it).
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (ks + 1 < KS || i < AR) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+  }
+}
+
+template <int NV, int Q>
+__device__ __forceinline__ void bt_round(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const BSrc& bs, int q0,
+                                         int K, BRing& br, bf16x8 (&fa0)[4], bf16x8 (&fa1)[4], Acc<L>& acc) {
+  if constexpr (Q < NSA * KS) {
+    bt_kstep<NV, Q>(st, ar, bs, q0, K, br, fa0, fa1, acc);
+    bt_round<NV, Q + 1>(st, ar, bs, q0, K, br, fa0, fa1, acc);
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void bt_mainloop(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const BSrc& bs,
+                                            int K, Acc<L>& acc) {
+  static_assert((NSA * KS) % SLOTS == 0 && SLOTS == LEAD + 1, "slot ring");
+  const int nq = (int)ceil_div(K, BK) * KS;       // k-steps, whole K-tiles
+  BRing br;
+  // B of k-steps 0 .. LEAD-1, then A of tiles 0 .. NSA-1
+  if constexpr (LEAD > 0) load_b(bs, 0, br.b[0]);
+  if constexpr (LEAD > 1) load_b(bs, 1, br.b[1]);
+  if constexpr (LEAD > 2) load_b(bs, 2, br.b[2]);
+  if constexpr (LEAD > 3) load_b(bs, 3, br.b[3]);
+  if constexpr (LEAD > 4) load_b(bs, 4, br.b[4]);
+  if constexpr (LEAD > 5) load_b(bs, 5, br.b[5]);
+  if constexpr (LEAD > 6) load_b(bs, 6, br.b[6]);
+  static_assert(LEAD <= 7, "prologue");
+#pragma unroll
+  for (int t = 0; t < NSA; ++t) dma_a(ar, st[t], t, K);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(AR * (NSA - 1)));
+  wg_barrier();
+  bf16x8 fa0[4], fa1[4];
+  read_a<NV>(st[0], 0, fa0);
+  // whole rounds of NSA K-tiles (tiles past K are zeros on both operands)
+  for (int q0 = 0; q0 < nq; q0 += NSA * KS) bt_round<NV, 0>(st, ar, bs, q0, K, br, fa0, fa1, acc);
+  __builtin_amdgcn_s_waitcnt(0);
+  wg_barrier();
+}
+
+template <int UNUSED = 0>
+__device__ __forceinline__ void bt_mainloop_rows(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const BSrc& bs,
+                                                 int K, int valid_rows, Acc<L>& acc) {
+  const int nv = __builtin_amdgcn_readfirstlane(max(0, min(4, (valid_rows + 31) / 32)));
+  if (nv >= 4) bt_mainloop<4>(st, ar, bs, K, acc);
+  else if (nv == 3) bt_mainloop<3>(st, ar, bs, K, acc);
+  else if (nv == 2) bt_mainloop<2>(st, ar, bs, K, acc);
+  else if (nv == 1) bt_mainloop<1>(st, ar, bs, K, acc);
+  else bt_mainloop<0>(st, ar, bs, K, acc);
+}
+
+// Byte offset, in the tiled layout of a weight with K padded to Kp (a
+// multiple of 64), of this lane's 16 bytes of k-step 0 of the 32-row group
+// holding row r (r % 32 == 0).
+__device__ __forceinline__ uint32_t tiled_off(int r, int Kp) {
+  return (uint32_t)(r / 32) * (uint32_t)(Kp / 16) * 1024u + 16u * (uint32_t)(threadIdx.x & 63);
+}
+
+// MXFP4 weights in the fragment order (moe_mxfp4_frag_tile), decoded in
+// registers. Packed codes: per group g of 32 rows and 64-k tile t, 1 KB of 64
+// lanes x 16 bytes; lane l (row 32 g + l % 32) holds in dword s the 8 codes of
+// k-step s (k = 64 t + 16 s + 8 (l / 32) .. +7, low nibble first). Scales: per
+// group g and 128-k pair p, 32 rows x 4 bytes (the e8m0 scales of the 32-element
+// k-blocks 4 p .. 4 p + 3). K is padded to a multiple of 128 with code 0 and
+// scale byte 0 (zeros). A k-step's 8 codes decode to the bf16 B fragment with
+// four v_cvt_scalef32_pk_bf16_fp4 (exact: a power-of-two scaling of a 2-bit
+// significand), the same values the row-major MXFP4 path stages in LDS.
+struct MxSrc {
+  rsrc_t rp[2], rs[2];           // packed codes, scales (gate, up; or one weight twice)
+  uint32_t poff[4], soff[4];     // fragment j: byte offset of tile / pair 0 for this lane, or kOOB
+};
+constexpr int TSLOTS = 4, LEADT = 3;   // packed tiles in registers; tiles loaded ahead
+
+struct MxRing {
+  uint4 p[TSLOTS][4];            // packed codes of a tile, per fragment
+  uint32_t sc[2][4];             // scale dwords of a tile pair, per fragment
+};
+
+__device__ __forceinline__ void load_mx_tile(const MxSrc& m, int t, uint4 (&dst)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dst[j] = bload16(m.rp[j >= 2 ? 1 : 0], m.poff[j] + 1024u * (uint32_t)t);
+}
+__device__ __forceinline__ void load_mx_scales(const MxSrc& m, int pr, uint32_t (&dst)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    dst[j] = __builtin_amdgcn_raw_buffer_load_b32(m.rs[j >= 2 ? 1 : 0], m.soff[j] + 128u * (uint32_t)pr, 0, 0);
+}
+
+// bf16 B fragments of one k-step from 8 e2m1 codes (a dword) and their e8m0 scale byte.
+__device__ __forceinline__ bf16x8 decode_frag(uint32_t codes, uint32_t sbyte) {
+  const float scale = sbyte == 0u ? 0x1p-127f : __uint_as_float(sbyte << 23);
+  const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+  const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+  const uint32_t w2 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+  const uint32_t w3 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
+  return __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
+}
+
+// Decoded fragments of k-step ks of the tile in packed slot PS (scale slot SS,
+// tile parity TP).
+template <int PS, int SS, int TP, int KSI>
+__device__ __forceinline__ void decode_kstep(const MxRing& r, bf16x8 (&fb)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint4 q = r.p[PS][j];
+    const uint32_t codes = KSI == 0 ? q.x : KSI == 1 ? q.y : KSI == 2 ? q.z : q.w;
+    const uint32_t sbyte = (r.sc[SS][j] >> (8 * (2 * TP + KSI / 2))) & 0xFFu;
+    fb[j] = decode_frag(codes, sbyte);
+  }
+}
+
+// One k-step Q (0 .. 15) of a round of NSA K-tiles on MXFP4 B: as bt_kstep, with
+// the packed codes of tile kt + LEADT (and, at even tiles, the scales of the
+// pair after the current one) loaded at each tile's first k-step, and the
+// next k-step's B fragments decoded while this one's MFMAs run.
+template <int NV, int Q>
+__device__ __forceinline__ void btmx_kstep(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const MxSrc& ms,
+                                           int q0, int K, MxRing& mr, bf16x8 (&fa0)[4], bf16x8 (&fa1)[4],
+                                           bf16x8 (&fb0)[4], bf16x8 (&fb1)[4], Acc<L>& acc) {
+  constexpr int T = Q / KS, ks = Q % KS;
+  const int t0 = q0 / KS;                              // first tile of the round (a multiple of 4)
+  constexpr int QN = Q + 1, TN = (QN / KS) % NSA, KN = QN % KS;   // the next k-step
+  int nvmem = 0;
+  if constexpr (ks == 0) {
+    load_mx_tile(ms, t0 + T + LEADT, mr.p[(T + LEADT) % TSLOTS]);
+    nvmem += 4;
+    if constexpr (T % 2 == 0) {
+      load_mx_scales(ms, (t0 + T) / 2 + 1, mr.sc[(T / 2 + 1) % 2]);
+      nvmem += 4;
+    }
+  }
+  (void)nvmem;
+  // next k-step's B fragments (the next tile's first when ks == 3)
+  if constexpr (ks & 1) decode_kstep<TN % TSLOTS, (TN / 2) % 2, TN % 2, KN>(mr, fb0);
+  else decode_kstep<TN % TSLOTS, (TN / 2) % 2, TN % 2, KN>(mr, fb1);
+  if constexpr (ks + 1 < KS) {
+    if constexpr (ks & 1) read_a<NV>(st[T], ks + 1, fa0);
+    else read_a<NV>(st[T], ks + 1, fa1);
+  } else {
+    // as in bt_kstep; 16 = the vector-memory ops issued after the next tile's
+    // DMA in the first round (A of tiles 2, 3, then tile 3's codes and the
+    // second pair's scales)
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0_vm(16));
+    wg_barrier();
+    dma_a(ar, st[T], t0 + T + NSA, K);
+    read_a<NV>(st[(T + 1) % NSA], 0, fa0);
+  }
+  if constexpr (ks & 1) mma_q<NV>(fa1, fb1, acc);
+  else mma_q<NV>(fa0, fb0, acc);
+  if constexpr (NV > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, NV, 0);
+      if (i < NV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+    }
+  }
+}
+
+template <int NV, int Q>
+__device__ __forceinline__ void btmx_round(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const MxSrc& ms,
+                                           int q0, int K, MxRing& mr, bf16x8 (&fa0)[4], bf16x8 (&fa1)[4],
+                                           bf16x8 (&fb0)[4], bf16x8 (&fb1)[4], Acc<L>& acc) {
+  if constexpr (Q < NSA * KS) {
+    btmx_kstep<NV, Q>(st, ar, ms, q0, K, mr, fa0, fa1, fb0, fb1, acc);
+    btmx_round<NV, Q + 1>(st, ar, ms, q0, K, mr, fa0, fa1, fb0, fb1, acc);
+  }
+}
+
+template <int NV>
+__device__ __forceinline__ void btmx_mainloop(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const MxSrc& ms,
+                                              int K, Acc<L>& acc) {
+  static_assert(NSA % TSLOTS == 0 && LEADT < TSLOTS && NSA % 2 == 0, "slot rings");
+  const int nq = (int)ceil_div(K, BK) * KS;
+  MxRing mr;
+  load_mx_tile(ms, 0, mr.p[0]);
+  load_mx_tile(ms, 1, mr.p[1]);
+  load_mx_tile(ms, 2, mr.p[2]);
+  static_assert(LEADT == 3, "prologue");
+  load_mx_scales(ms, 0, mr.sc[0]);
+#pragma unroll
+  for (int t = 0; t < NSA; ++t) dma_a(ar, st[t], t, K);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(AR * (NSA - 1)));
+  wg_barrier();
+  bf16x8 fa0[4], fa1[4], fb0[4], fb1[4];
+  read_a<NV>(st[0], 0, fa0);
+  decode_kstep<0, 0, 0, 0>(mr, fb0);
+  for (int q0 = 0; q0 < nq; q0 += NSA * KS) btmx_round<NV, 0>(st, ar, ms, q0, K, mr, fa0, fa1, fb0, fb1, acc);
+  __builtin_amdgcn_s_waitcnt(0);
+  wg_barrier();
+}
+
+template <int UNUSED = 0>
+__device__ __forceinline__ void btmx_mainloop_rows(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const MxSrc& ms,
+                                                   int K, int valid_rows, Acc<L>& acc) {
+  const int nv = __builtin_amdgcn_readfirstlane(max(0, min(4, (valid_rows + 31) / 32)));
+  if (nv >= 4) btmx_mainloop<4>(st, ar, ms, K, acc);
+  else if (nv == 3) btmx_mainloop<3>(st, ar, ms, K, acc);
+  else if (nv == 2) btmx_mainloop<2>(st, ar, ms, K, acc);
+  else if (nv == 1) btmx_mainloop<1>(st, ar, ms, K, acc);
+  else btmx_mainloop<0>(st, ar, ms, K, acc);
+}
+
+// Byte offsets, in the fragment-tiled MXFP4 layout of a weight with K padded
+// to Kp (a multiple of 128), of this lane's packed 16 bytes of tile 0 and its
+// scale dword of pair 0, for the 32-row group holding row r (r % 32 == 0).
+__device__ __forceinline__ uint32_t mx_tiled_poff(int r, int Kp) {
+  return (uint32_t)(r / 32) * (uint32_t)(Kp / 64) * 1024u + 16u * (uint32_t)(threadIdx.x & 63);
+}
+__device__ __forceinline__ uint32_t mx_tiled_soff(int r, int Kp) {
+  return (uint32_t)(r / 32) * (uint32_t)(Kp / 128) * 128u + 4u * (uint32_t)(threadIdx.x & 31);
+}
+
+#define MOE_BT_RING                                             \
+  __shared__ __align__(16) bf16_t la0[BM * BK];                  \
+  __shared__ __align__(16) bf16_t la1[BM * BK];                  \
+  __shared__ __align__(16) bf16_t la2[BM * BK];                  \
+  __shared__ __align__(16) bf16_t la3[BM * BK];                  \
+  bf16_t* const st[NSA] = {la0, la1, la2, la3}
+static_assert(NSA == 4, "ring arrays");
+}  // namespace bt
+
+// grouped_glu on tiled bf16 weights: H[r] = act(z W_g[e]^T, z W_v[e]^T) for the
+// rows of expert e, 256 outputs per block (wave w: outputs f0 + 64 w + 0..63,
+// fragments 0-1 gate, 2-3 up).
+__global__ __launch_bounds__(bt::NW * 64) void grouped_glu_bt_kernel(GroupedGluArgs a) {
+  using namespace bt;
+  using C = L;
+  MOE_BT_RING;
+  const int ntn = (int)ceil_div(a.F, BN / 2);
+  int64_t Li;
+  if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, Li)) return;
+  int e, nt, row_lo, row_hi;
+  grouped_item<BM>(a.tile_info, ntn, a.rows_cap, Li, e, nt, row_lo, row_hi);
+  const int f0 = nt * (BN / 2);
+  Rows<AR> ar;
+  ar.r[0] = ar.r[1] = make_rsrc(a.Z, (int64_t)a.T * a.ldz * 2);
+#pragma unroll
+  for (int q = 0; q < AR; ++q) {
+    ar.sel[q] = 0;
+    const int row = row_lo + dma_row<C, AR>(q);
+    uint32_t off = kOOB;
+    if (row >= 0 && row < row_hi) {
+      const int src = a.perm_src[row];
+      const int t = src / a.topk;
+      if (src >= 0 && t < a.T) off = (uint32_t)((int64_t)t * a.ldz * 2);
+    }
+    ar.off[q] = off;
+  }
+  const int Kp = (int)ceil_div(a.K, BK) * BK;
+  const int64_t ebytes = (int64_t)a.F * Kp * 2;                 // one expert's tiled weight
+  BSrc bs;
+  bs.r[0] = make_rsrc((const uint8_t*)a.Wg.data + e * ebytes, ebytes);
+  bs.r[1] = make_rsrc((const uint8_t*)a.Wv.data + e * ebytes, ebytes);
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int f = f0 + 64 * w + 32 * (j & 1);
+    bs.off[j] = f < a.F ? bt::tiled_off(f, Kp) : kOOB;
+  }
+  Acc<C> acc;
+  acc_zero(acc);
+  bt_mainloop_rows(st, ar, bs, a.K, row_hi - row_lo, acc);
+  store_glu(acc, (bf16_t*)a.H, a.F, f0, a.F, a.c, [=](int tr) -> int64_t {
+    const int r = row_lo + tr;
+    return (r >= 0 && r < row_hi) ? (int64_t)r : -1;
+  });
+}
+
+// grouped_down on tiled bf16 weights: O[r] = H[r] W_o[e]^T, 512 outputs per block.
+__global__ __launch_bounds__(bt::NW * 64) void grouped_down_bt_kernel(GroupedDownArgs a) {
+  using namespace bt;
+  using C = L;
+  MOE_BT_RING;
+  const int ntn = (int)ceil_div(a.N, BN);
+  int64_t Li;
+  if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, Li)) return;
+  int e, nt, row_lo, row_hi;
+  grouped_item<BM>(a.tile_info, ntn, a.rows_cap, Li, e, nt, row_lo, row_hi);
+  const int n0 = nt * BN;
+  const Rows<AR> ar = a_rows_dense<C, AR>(a.H, a.ldh, max(row_lo, 0), max(row_hi, 0));
+  const int Kp = (int)ceil_div(a.K, BK) * BK;
+  const int64_t ebytes = (int64_t)a.N * Kp * 2;
+  BSrc bs;
+  bs.r[0] = bs.r[1] = make_rsrc((const uint8_t*)a.Wo.data + e * ebytes, ebytes);
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 128 * w + 32 * j;
+    bs.off[j] = n < a.N ? bt::tiled_off(n, Kp) : kOOB;
+  }
+  Acc<C> acc;
+  acc_zero(acc);
+  bt_mainloop_rows(st, ar, bs, a.K, row_hi - row_lo, acc);
+  store_tile(acc, (bf16_t*)a.O, a.N, row_lo, n0, row_hi, a.N);
+}
+
+// grouped_glu_bt on fragment-tiled MXFP4 weights (decoded in registers).
+__global__ __launch_bounds__(bt::NW * 64) void grouped_glu_btmx_kernel(GroupedGluArgs a) {
+  using namespace bt;
+  using C = L;
+  MOE_BT_RING;
+  const int ntn = (int)ceil_div(a.F, BN / 2);
+  int64_t Li;
+  if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, Li)) return;
+  int e, nt, row_lo, row_hi;
+  grouped_item<BM>(a.tile_info, ntn, a.rows_cap, Li, e, nt, row_lo, row_hi);
+  const int f0 = nt * (BN / 2);
+  Rows<AR> ar;
+  ar.r[0] = ar.r[1] = make_rsrc(a.Z, (int64_t)a.T * a.ldz * 2);
+#pragma unroll
+  for (int q = 0; q < AR; ++q) {
+    ar.sel[q] = 0;
+    const int row = row_lo + dma_row<C, AR>(q);
+    uint32_t off = kOOB;
+    if (row >= 0 && row < row_hi) {
+      const int src = a.perm_src[row];
+      const int t = src / a.topk;
+      if (src >= 0 && t < a.T) off = (uint32_t)((int64_t)t * a.ldz * 2);
+    }
+    ar.off[q] = off;
+  }
+  const int Kp = (int)ceil_div(a.K, 128) * 128;
+  const int64_t pbytes = (int64_t)a.F * Kp / 2, sbytes = (int64_t)a.F * Kp / 32;   // one expert
+  MxSrc ms;
+  ms.rp[0] = make_rsrc((const uint8_t*)a.Wg.data + e * pbytes, pbytes);
+  ms.rp[1] = make_rsrc((const uint8_t*)a.Wv.data + e * pbytes, pbytes);
+  ms.rs[0] = make_rsrc(a.Wg.scale + e * sbytes, sbytes);
+  ms.rs[1] = make_rsrc(a.Wv.scale + e * sbytes, sbytes);
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int f = f0 + 64 * w + 32 * (j & 1);
+    ms.poff[j] = f < a.F ? bt::mx_tiled_poff(f, Kp) : kOOB;
+    ms.soff[j] = f < a.F ? bt::mx_tiled_soff(f, Kp) : kOOB;
+  }
+  Acc<C> acc;
+  acc_zero(acc);
+  btmx_mainloop_rows(st, ar, ms, a.K, row_hi - row_lo, acc);
+  store_glu(acc, (bf16_t*)a.H, a.F, f0, a.F, a.c, [=](int tr) -> int64_t {
+    const int r = row_lo + tr;
+    return (r >= 0 && r < row_hi) ? (int64_t)r : -1;
+  });
+}
+
+__global__ __launch_bounds__(bt::NW * 64) void grouped_down_btmx_kernel(GroupedDownArgs a) {
+  using namespace bt;
+  using C = L;
+  MOE_BT_RING;
+  const int ntn = (int)ceil_div(a.N, BN);
+  int64_t Li;
+  if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, Li)) return;
+  int e, nt, row_lo, row_hi;
+  grouped_item<BM>(a.tile_info, ntn, a.rows_cap, Li, e, nt, row_lo, row_hi);
+  const int n0 = nt * BN;
+  const Rows<AR> ar = a_rows_dense<C, AR>(a.H, a.ldh, max(row_lo, 0), max(row_hi, 0));
+  const int Kp = (int)ceil_div(a.K, 128) * 128;
+  const int64_t pbytes = (int64_t)a.N * Kp / 2, sbytes = (int64_t)a.N * Kp / 32;
+  MxSrc ms;
+  ms.rp[0] = ms.rp[1] = make_rsrc((const uint8_t*)a.Wo.data + e * pbytes, pbytes);
+  ms.rs[0] = ms.rs[1] = make_rsrc(a.Wo.scale + e * sbytes, sbytes);
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = n0 + 128 * w + 32 * j;
+    ms.poff[j] = n < a.N ? bt::mx_tiled_poff(n, Kp) : kOOB;
+    ms.soff[j] = n < a.N ? bt::mx_tiled_soff(n, Kp) : kOOB;
+  }
+  Acc<C> acc;
+  acc_zero(acc);
+  btmx_mainloop_rows(st, ar, ms, a.K, row_hi - row_lo, acc);
+  store_tile(acc, (bf16_t*)a.O, a.N, row_lo, n0, row_hi, a.N);
+}
+
+// Fragment-tiled copy of a row-major MXFP4 weight (packed [rows, K/2], scales
+// [rows, K/32]; rows % 32 == 0, K % 32 == 0), K padded to Kp = ceil(K / 128)
+// 128: one thread per output dword of the packed codes (lane l's dword s of
+// tile t of group g: the 4 bytes of row 32 g + l % 32 holding k = 64 t + 16 s +
+// 8 (l / 32) .. +7), and one per output scale dword (4 scales of a row).
+__global__ __launch_bounds__(256) void tile_mxfp4_frag_kernel(const uint8_t* __restrict__ packed,
+                                                              const uint8_t* __restrict__ scale,
+                                                              uint32_t* __restrict__ pout,
+                                                              uint32_t* __restrict__ sout, int64_t rows,
+                                                              int K, int Kp) {
+  const int64_t np = rows / 32 * (Kp / 64) * 256;       // dwords of packed codes
+  const int64_t ns = rows * (Kp / 128);                 // scale dwords
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < np + ns;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    if (i < np) {
+      const int sdw = (int)(i & 3), lane = (int)((i >> 2) & 63);
+      const int64_t tile = i >> 8;
+      const int t = (int)(tile % (Kp / 64));
+      const int64_t g = tile / (Kp / 64);
+      const int64_t r = g * 32 + (lane & 31);
+      const int k = 64 * t + 16 * sdw + 8 * (lane >> 5);     // 8 codes = 4 bytes from k / 2
+      uint32_t v = 0;
+      if (k < K) v = *(const uint32_t*)(packed + r * (K / 2) + k / 2);   // K % 32: all 8 in or out
+      pout[i] = v;
+    } else {
+      const int64_t j = i - np;                          // (g, pair, row-in-group) order
+      const int rl = (int)(j & 31);
+      const int64_t gp = j >> 5;
+      const int pr = (int)(gp % (Kp / 128));
+      const int64_t g = gp / (Kp / 128);
+      const int64_t r = g * 32 + rl;
+      uint32_t v = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int kb = 4 * pr + b;                       // 32-element block
+        if (kb < K / 32) v |= (uint32_t)scale[r * (K / 32) + kb] << (8 * b);
+      }
+      sout[j] = v;
+    }
+  }
+}
+
+// Fragment-tiled copy of a bf16 weight [rows, K] (rows % 32 == 0): one thread
+// per 16-byte piece of the output; K padded to Kp = ceil(K / 64) 64 with zeros.
+__global__ __launch_bounds__(256) void tile_bf16_kernel(const bf16_t* __restrict__ in, uint4* __restrict__ out,
+                                                        int64_t rows, int K, int Kp) {
+  const int64_t n = rows / 32 * (Kp / 16) * 64;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(i & 63);
+    const int64_t tile = i >> 6;
+    const int s = (int)(tile % (Kp / 16));
+    const int64_t g = tile / (Kp / 16);
+    const int64_t r = g * 32 + (lane & 31);
+    const int k = 16 * s + 8 * (lane >> 5);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (k < K) v = *(const uint4*)(in + r * K + k);      // K % 8 == 0: a piece is all in or all out
+    out[i] = v;
+  }
+}
+
 }  // namespace
+
+int launch_tile_bf16(const void* in, void* out, int64_t rows, int K, hipStream_t stream) {
+  if (rows % 32 || K % 8 || ((uintptr_t)in | (uintptr_t)out) % 16) return -1;
+  if (rows == 0) return 0;
+  const int Kp = (int)ceil_div(K, bt::BK) * bt::BK;
+  const int64_t n = rows / 32 * (Kp / 16) * 64;
+  hipLaunchKernelGGL(tile_bf16_kernel, dim3((unsigned)(ceil_div(n, 256) < 16384 ? ceil_div(n, 256) : 16384)),
+                     dim3(256), 0, stream, (const bf16_t*)in, (uint4*)out, rows, K, Kp);
+  return (int)hipGetLastError();
+}
+
+int64_t tiled_bf16_bytes(int64_t rows, int K) { return rows * (ceil_div(K, bt::BK) * bt::BK) * 2; }
+
+int launch_tile_mxfp4_frag(const uint8_t* data, const uint8_t* scale, uint8_t* data_out, uint8_t* scale_out,
+                           int64_t rows, int K, hipStream_t stream) {
+  if (rows % 32 || K % 32 || ((uintptr_t)data_out | (uintptr_t)scale_out) % 4 || (uintptr_t)data % 4)
+    return -1;
+  if (rows == 0) return 0;
+  const int Kp = (int)ceil_div(K, 128) * 128;
+  const int64_t n = rows / 32 * (Kp / 64) * 256 + rows * (Kp / 128);
+  hipLaunchKernelGGL(tile_mxfp4_frag_kernel, dim3((unsigned)(ceil_div(n, 256) < 16384 ? ceil_div(n, 256) : 16384)),
+                     dim3(256), 0, stream, data, scale, (uint32_t*)data_out, (uint32_t*)scale_out, rows, K, Kp);
+  return (int)hipGetLastError();
+}
+
+void tiled_mxfp4_frag_bytes(int64_t rows, int K, int64_t* data_bytes, int64_t* scale_bytes) {
+  const int64_t Kp = ceil_div(K, 128) * 128;
+  *data_bytes = rows * Kp / 2;
+  *scale_bytes = rows * Kp / 32;
+}
 
 // Below 256 single-pass tiles the chip is not full: take 128 x 128 tiles and
 // split K until about 256 blocks run, each over at least 6 K-tiles.
@@ -1667,9 +2247,10 @@ int multiseg_slices(int act_dtype, int M, int N, int nseg) {
 #define MOE_BIG_ROWS 64
 #endif
 constexpr int kBigRows = MOE_BIG_ROWS;
-int grouped_bm(int act_dtype, int expert_w_dtype, int act_mx8, int64_t rows, int E) {
+int grouped_bm(int act_dtype, int expert_w_dtype, int act_mx8, int w_tiled, int64_t rows, int E) {
   if (act_dtype == DT_F32) return 1;
   if (act_mx8) return mx8::L::BM;
+  if (w_tiled) return bt::BM;         // fragment-tiled bf16 or MXFP4 weights
   if (expert_w_dtype == DT_BF16 && rows >= (int64_t)kBigRows * E) return GroupBigCfg::BM;
   return GroupCfg::BM;
 }
@@ -1727,6 +2308,13 @@ int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream) {
     return (int)hipGetLastError();
   }
   if (a.H == nullptr) return -1;
+  if (a.w_tiled) {
+    if (a.bm != bt::BM) return -1;
+    dim3 grid((unsigned)xcd_grid(ceil_div(a.F, bt::BN / 2) * a.max_tiles));
+    if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(grouped_glu_btmx_kernel, grid, dim3(bt::NW * 64), 0, stream, a);
+    else hipLaunchKernelGGL(grouped_glu_bt_kernel, grid, dim3(bt::NW * 64), 0, stream, a);
+    return (int)hipGetLastError();
+  }
   if (a.bm == GroupBigCfg::BM && a.bm != GroupCfg::BM) {
     if (a.Wg.dtype != DT_BF16) return -1;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.F, GroupBigCfg::BN / 2) * a.max_tiles));
@@ -1749,6 +2337,13 @@ int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream) {
     if (a.w_tiled && (a.N % 64 || mx8::kBRW != 64)) return -1;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.N, mx8::L::BN) * a.max_tiles));
     hipLaunchKernelGGL(grouped_down_mx8_kernel, grid, dim3(mx8::L::NT), 0, stream, a);
+    return (int)hipGetLastError();
+  }
+  if (a.w_tiled) {
+    if (a.bm != bt::BM) return -1;
+    dim3 grid((unsigned)xcd_grid(ceil_div(a.N, bt::BN) * a.max_tiles));
+    if (a.Wo.dtype == DT_MXFP4) hipLaunchKernelGGL(grouped_down_btmx_kernel, grid, dim3(bt::NW * 64), 0, stream, a);
+    else hipLaunchKernelGGL(grouped_down_bt_kernel, grid, dim3(bt::NW * 64), 0, stream, a);
     return (int)hipGetLastError();
   }
   if (a.bm == GroupBigCfg::BM && a.bm != GroupCfg::BM) {

@@ -134,8 +134,8 @@ struct GroupedGluArgs {
   int act_mx8;                       // Z holds MXFP8 codes ([T, K] bytes, row stride ldz
                                      // bytes) with scales z_scale [T, K/32]: scaled MFMA
   const uint8_t* z_scale;
-  int w_tiled;                       // act_mx8 only: Wg / Wv in the tiled layout
-                                     // (launch_tile_mxfp4)
+  int w_tiled;                       // Wg / Wv tiled: MXFP4 with act_mx8 (launch_tile_mxfp4),
+                                     // or bf16 (launch_tile_bf16)
   uint8_t* hq;                       // act_mx8 only: with hq (and hqs) set, h goes out as
   uint8_t* hqs;                      // MXFP8 codes [rows, F] and scales [rows, F/32];
                                      // else to bf16 H (one of the two must be given)
@@ -144,7 +144,25 @@ int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream);
 // Tile rows of the grouped expert kernels for `rows` routed rows over E
 // experts: 1 (fp32 path), 128 or 256 (the LDS-tiled MFMA kernels; the launchers
 // take the kernel that matches).
-int grouped_bm(int act_dtype, int expert_w_dtype, int act_mx8, int64_t rows, int E);
+int grouped_bm(int act_dtype, int expert_w_dtype, int act_mx8, int w_tiled, int64_t rows, int E);
+// Fragment-tiled copy of a bf16 weight [rows, K] (rows % 32 == 0, K % 8 == 0)
+// for the grouped expert kernels that keep the weights in registers: for each
+// group g of 32 rows and k-step s of 16 (K padded with zeros to Kp, the next
+// multiple of 64), the 1 KB at (g (Kp/16) + s) 1024 holds 64 lanes x 8 bf16,
+// lane l = row 32 g + l % 32, k = 16 s + 8 (l / 32) .. +7. tiled_bf16_bytes:
+// the size of that copy.
+int launch_tile_bf16(const void* in, void* out, int64_t rows, int K, hipStream_t stream);
+int64_t tiled_bf16_bytes(int64_t rows, int K);
+// Fragment-tiled copy of a row-major MXFP4 weight (rows % 32 == 0, K % 32 ==
+// 0) for the same kernels, decoded in registers: K padded to Kp (the next
+// multiple of 128) with zeros; packed codes: per group g of 32 rows and 64-k
+// tile t, the 1 KB at (g (Kp/64) + t) 1024 holds 64 lanes x 16 bytes, lane l
+// (row 32 g + l % 32) with the 8 codes of k = 64 t + 16 s + 8 (l / 32) .. +7 in
+// its dword s; scales: per group g and 128-k pair p, the 128 bytes at
+// (g (Kp/128) + p) 128 hold 32 rows x the 4 scale bytes of k-blocks 4p .. 4p+3.
+int launch_tile_mxfp4_frag(const uint8_t* data, const uint8_t* scale, uint8_t* data_out, uint8_t* scale_out,
+                           int64_t rows, int K, hipStream_t stream);
+void tiled_mxfp4_frag_bytes(int64_t rows, int K, int64_t* data_bytes, int64_t* scale_bytes);
 
 // down: O[r] = H[r] Wo[e]^T, Wo [E, N, K].
 struct GroupedDownArgs {
@@ -162,7 +180,7 @@ struct GroupedDownArgs {
   int act_mx8;                       // H holds MXFP8 codes ([rows, K] bytes, row stride
                                      // ldh bytes) with scales h_scale [rows, K/32]
   const uint8_t* h_scale;
-  int w_tiled;                       // act_mx8 only: Wo in the tiled layout
+  int w_tiled;                       // Wo tiled (as GroupedGluArgs::w_tiled)
 };
 // MXFP8 (E4M3 + e8m0 per 32) rows of a bf16 matrix [rows, K] (row stride ld
 // elements; K % 32 == 0): codes [rows, K], scales [rows, K/32] (OCP MX rule:

@@ -38,7 +38,7 @@ class LayerConfig:
     latent_w: str = "bf16"     # W_down / W_up of the latent maps
     dense_w: str = "bf16"      # router and shared experts
     expert_act: str = "act"    # routed experts' GEMM inputs: "act" (act dtype) | "mxfp8"
-    expert_layout: str = "rows"  # MXFP4 expert weight layout: "rows" | "tiled" (mxfp8 inputs only)
+    expert_layout: str = "rows"  # expert weight layout in HBM: "rows" | "tiled" (made at load)
     bias: tuple = ("uniform", 0.05)   # ("uniform", halfwidth) | ("zipf", s, scale)
     c: float = 8.0             # SiTU-GLU cap
     eps: float = 1e-6          # RMSNorm epsilon
@@ -67,8 +67,10 @@ CONFIGS = [
     # Zipf-shaped selection bias: b_e = 0.5 * ln(rank_e ** -1.1), rank_e = e + 1,
     # shifted to zero mean (computed in fp64, stored fp32)
     LayerConfig("k3_skew", T=8192, seed=3, bias=("zipf", 1.1, 0.5), **K3),
+    # MXFP4 expert weights are re-laid once at load into the fragment order
+    # (expert_layout "tiled": loaded straight into registers, decoded there)
     LayerConfig("k3_prefill_mxfp4", T=16384, seed=4, expert_w="mxfp4", latent_w="mxfp4",
-                bias=("uniform", 0.05), **K3),
+                expert_layout="tiled", bias=("uniform", 0.05), **K3),
     # the MXFP4 prefill layer with its routed experts on the scaled MFMA
     # (z and h quantised to MXFP8, expert weights tiled once at load);
     # same inputs as k3_prefill_mxfp4
@@ -78,7 +80,7 @@ CONFIGS = [
     # latent weights, decoded to bf16 in the GEMM (..._mxfp4) or fed to the
     # scaled MFMA with MXFP8 expert inputs (..._mx8); same inputs as k3_decode
     LayerConfig("k3_decode_mxfp4", T=256, seed=1, expert_w="mxfp4", latent_w="mxfp4",
-                bias=("uniform", 0.05), **K3),
+                expert_layout="tiled", bias=("uniform", 0.05), **K3),
     LayerConfig("k3_decode_mx8", T=256, seed=1, expert_w="mxfp4", latent_w="mxfp4",
                 expert_act="mxfp8", expert_layout="tiled", bias=("uniform", 0.05), **K3),
 ]

@@ -98,9 +98,9 @@ def _desc(**kw):
     (dict(n_shared=8), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=300_000), moe.MOE_ERR_UNSUPPORTED),                # z over 2 GiB (32-bit gather offsets)
     (dict(expert_w_tiled=2), moe.MOE_ERR_INVALID_ARG),
-    (dict(expert_w_tiled=1), moe.MOE_ERR_UNSUPPORTED),         # tiled weights without MXFP8 inputs
-    (dict(expert_w_tiled=1, expert_w_dtype=moe.MOE_MXFP4, latent_w_dtype=moe.MOE_MXFP4),
-     moe.MOE_ERR_UNSUPPORTED),                                  # MXFP4, but bf16 expert inputs
+    (dict(expert_w_tiled=1, act_dtype=moe.MOE_F32, expert_w_dtype=moe.MOE_F32,
+          latent_w_dtype=moe.MOE_F32, dense_w_dtype=moe.MOE_F32),
+     moe.MOE_ERR_UNSUPPORTED),                                  # tiled weights need bf16 activations
 ])
 def test_invalid_descriptors(kw, status):
     d = _desc(**kw)
@@ -307,3 +307,35 @@ def test_expert_gate_up_validates_its_outputs():
     assert need >= cfg8.T * cfg8.d_lat                                  # the MXFP8 copy of z
     assert need < moe.moe_workspace_bytes(d8, moe.MOE_OP_EXPERT_FFN)
     assert gu(d8, None, FAKE, FAKE, ws=FAKE, n=need - 1) == moe.MOE_ERR_WORKSPACE
+
+
+def test_bf16_tile_validates_and_sizes():
+    """moe_bf16_tile: rows % 32, K % 8, alignment and overlap are checked on the
+    host; the tiled size pads K to a multiple of 64."""
+    L = moe.lib()
+    assert moe.moe_check_desc(_desc(expert_w_tiled=1)) == moe.MOE_OK   # fragment-tiled bf16 experts
+    assert moe.moe_bf16_tiled_bytes(64, 3584) == 64 * 3584 * 2
+    assert moe.moe_bf16_tiled_bytes(32, 200) == 32 * 256 * 2
+    assert moe.moe_bf16_tiled_bytes(33, 64) == 0 and moe.moe_bf16_tiled_bytes(32, 12) == 0
+    big = FAKE + (1 << 30)
+    assert L.moe_bf16_tile(FAKE, big, 48, 64, None) == moe.MOE_ERR_INVALID_ARG      # rows % 32
+    assert L.moe_bf16_tile(FAKE, big, 64, 60, None) == moe.MOE_ERR_INVALID_ARG      # K % 8
+    assert L.moe_bf16_tile(MIS, big, 64, 64, None) == moe.MOE_ERR_INVALID_ARG       # alignment
+    assert L.moe_bf16_tile(FAKE, FAKE + 4096, 64, 64, None) == moe.MOE_ERR_INVALID_ARG  # overlap
+    assert L.moe_bf16_tile(None, None, 0, 64, None) == moe.MOE_OK
+
+
+def test_mxfp4_frag_tile_validates_and_sizes():
+    L = moe.lib()
+    assert moe.moe_check_desc(_desc(expert_w_tiled=1, expert_w_dtype=moe.MOE_MXFP4,
+                                    latent_w_dtype=moe.MOE_MXFP4)) == moe.MOE_OK
+    assert moe.moe_mxfp4_frag_tiled_bytes(64, 3584) == (64 * 3584 // 2, 64 * 3584 // 32)
+    assert moe.moe_mxfp4_frag_tiled_bytes(32, 96) == (32 * 128 // 2, 32 * 128 // 32)
+    with pytest.raises(moe.MoeError):
+        moe.moe_mxfp4_frag_tiled_bytes(48, 64)
+    big = FAKE + (1 << 30)
+    assert L.moe_mxfp4_frag_tile(FAKE, FAKE + 4096, big, big + 65536, 48, 64, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mxfp4_frag_tile(FAKE, FAKE + 4096, big, big + 65536, 64, 48, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mxfp4_frag_tile(FAKE, FAKE + 4096, big, big + 2, 64, 64, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mxfp4_frag_tile(FAKE, FAKE + 4096, FAKE + 64, big, 64, 64, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_mxfp4_frag_tile(None, None, None, None, 0, 64, None) == moe.MOE_OK
