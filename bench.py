@@ -160,8 +160,8 @@ def measure_ceilings(stream):
                                  ctypes.c_void_p]
     L.moe_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     L.moe_probe_mfma_flops.restype = ctypes.c_double
-    L.moe_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
-                                     ctypes.c_void_p]
+    L.moe_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
     sh = stream.cuda_stream
 
     def timed(fn, reps=5):
@@ -185,16 +185,19 @@ def measure_ceilings(stream):
                 raise RuntimeError("moe_probe_mfma failed")
         t = timed(launch)
         res[key] = round(L.moe_probe_mfma_flops(kind, blocks, iters) / t / 1e12, 1)
+    # the best of a few launch shapes (blocks per CU x loads in flight per thread)
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
-    rblocks = 256 * 8
-    sink = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda:0")
-
-    def read():
-        if L.moe_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes, rblocks,
-                                ctypes.c_void_p(sink.data_ptr()), sh) != 0:
-            raise RuntimeError("moe_probe_hbm_read failed")
-    res["hbm_read_GBps"] = round(nbytes / timed(read) / 1e9, 1)
+    sink = torch.empty(256 * 16 * 256, dtype=torch.int32, device="cuda:0")
+    best = 0.0
+    for per_cu in (4, 8, 16):
+        for unroll in (4, 8, 16):
+            def read(per_cu=per_cu, unroll=unroll):
+                if L.moe_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes, 256 * per_cu, unroll,
+                                        ctypes.c_void_p(sink.data_ptr()), sh) != 0:
+                    raise RuntimeError("moe_probe_hbm_read failed")
+            best = max(best, nbytes / timed(read) / 1e9)
+    res["hbm_read_GBps"] = round(best, 1)
     del buf, sink, out
     torch.cuda.empty_cache()
     return res

@@ -13,7 +13,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-constexpr int kChains = 4;   // independent accumulators per wave
+constexpr int kChains = 4;   // independent accumulators per wave (waves per SIMD give the rest)
 
 // Each wave: `iters` rounds of kChains independent v_mfma_f32_32x32x16_bf16.
 // The operands come from the thread index (never constant-folded); one lane
@@ -59,21 +59,23 @@ __global__ __launch_bounds__(256) void mfma_f8f4_kernel(int iters, float* out) {
   if ((threadIdx.x & 63) == 0) out[blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64] = s;
 }
 
-// Grid-stride read of n16 16-byte chunks; each thread folds what it read into
-// one word that it writes, so every load is live.
+// Each block reads contiguous spans of U x 256 16-byte chunks (all U loads of
+// a thread issued before any is used), spans handed out grid-stride; each
+// thread folds what it read into one word that it writes, so every load is live.
+template <int U>
 __global__ __launch_bounds__(256) void hbm_read_kernel(const uint4* __restrict__ p, int64_t n16,
                                                        uint32_t* __restrict__ out) {
   uint32_t acc = 0;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 v0 = p[i], v1 = p[i + stride], v2 = p[i + 2 * stride], v3 = p[i + 3 * stride];
-    acc ^= v0.x ^ v0.y ^ v0.z ^ v0.w ^ v1.x ^ v1.y ^ v1.z ^ v1.w;
-    acc ^= v2.x ^ v2.y ^ v2.z ^ v2.w ^ v3.x ^ v3.y ^ v3.z ^ v3.w;
-  }
-  for (; i < n16; i += stride) {
-    const uint4 v = p[i];
-    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  const int64_t span = (int64_t)U * 256;
+  for (int64_t b = (int64_t)blockIdx.x * span; b < n16; b += (int64_t)gridDim.x * span) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = b + u * 256 + threadIdx.x;
+      v[u] = i < n16 ? p[i] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
@@ -96,12 +98,15 @@ double moe_probe_mfma_flops(int kind, int blocks, int iters) {
   return per * kChains * 4.0 * blocks * (double)iters;   // 4 waves per block
 }
 
-int moe_probe_hbm_read(const void* buf, int64_t bytes, int blocks, uint32_t* out, void* stream) {
+int moe_probe_hbm_read(const void* buf, int64_t bytes, int blocks, int unroll, uint32_t* out, void* stream) {
   if (buf == nullptr || out == nullptr || bytes <= 0 || bytes % 16 || blocks <= 0 ||
-      ((uintptr_t)buf & 15u))
+      ((uintptr_t)buf & 15u) || (unroll != 4 && unroll != 8 && unroll != 16))
     return -1;
-  hipLaunchKernelGGL(hbm_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
-                     (const uint4*)buf, bytes / 16, out);
+  const uint4* p = (const uint4*)buf;
+  hipStream_t s = (hipStream_t)stream;
+  if (unroll == 4) hipLaunchKernelGGL(hbm_read_kernel<4>, dim3(blocks), dim3(256), 0, s, p, bytes / 16, out);
+  else if (unroll == 8) hipLaunchKernelGGL(hbm_read_kernel<8>, dim3(blocks), dim3(256), 0, s, p, bytes / 16, out);
+  else hipLaunchKernelGGL(hbm_read_kernel<16>, dim3(blocks), dim3(256), 0, s, p, bytes / 16, out);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

@@ -45,13 +45,14 @@ def test_probe_library_exports_and_validates():
     L.moe_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     L.moe_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
     L.moe_probe_mfma_flops.restype = ctypes.c_double
-    L.moe_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
-                                     ctypes.c_void_p]
+    L.moe_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
     assert L.moe_probe_mfma(2, 1, 1, FAKE, None) == -1
     assert L.moe_probe_mfma(0, 0, 1, FAKE, None) == -1
     assert L.moe_probe_mfma(0, 1, 1, None, None) == -1
-    assert L.moe_probe_hbm_read(FAKE, 24, 1, FAKE, None) == -1
-    assert L.moe_probe_hbm_read(MIS, 32, 1, FAKE, None) == -1
+    assert L.moe_probe_hbm_read(FAKE, 24, 1, 8, FAKE, None) == -1
+    assert L.moe_probe_hbm_read(MIS, 32, 1, 8, FAKE, None) == -1
+    assert L.moe_probe_hbm_read(FAKE, 32, 1, 5, FAKE, None) == -1
     assert L.moe_probe_mfma_flops(0, 1, 1) == 4 * 4 * 2 * 32 * 32 * 16
     assert L.moe_probe_mfma_flops(1, 2, 3) == 2 * 3 * 4 * 4 * 2 * 32 * 32 * 64
 
