@@ -65,10 +65,10 @@ struct Cfg {
 };
 using DenseCfg = Cfg<2, 2, 4, 2, 64, 3>;   // 256 x 128, 4 waves, 3 stages of 48 KB
 using GroupCfg = Cfg<2, 4, 2, 2, 64, 3>;   // 128 x 256, 8 waves, 3 stages of 48 KB
-// Grouped expert GEMMs on bf16 weights with many rows per expert: 256 x 256,
-// 8 waves of 128 x 64, the pipelined main loop.
+// Grouped expert GEMMs on bf16 weights with many rows per expert: 320 x 256,
+// 8 waves of 160 x 64, the pipelined main loop (2 stages of 72 KB; 253 VGPRs).
 #ifndef MOE_BIG_CFG
-#define MOE_BIG_CFG Cfg<2, 4, 4, 2, 64, 2>
+#define MOE_BIG_CFG Cfg<2, 4, 5, 2, 64, 2>
 #endif
 using GroupBigCfg = MOE_BIG_CFG;
 using SplitCfg = Cfg<2, 2, 2, 2, 64, 3>;   // 128 x 128 (small batches, split K)
@@ -451,9 +451,9 @@ __device__ __forceinline__ void mainloop_rows(bf16_t* s0, bf16_t* s1, bf16_t* s2
 // the pipelined main loop (grouped expert GEMMs)
 // ---------------------------------------------------------------------------
 //
-// Large wave tiles (WM x WN = 4 x 2 fragments, 128 x 64 per wave) cut the LDS
-// bytes read per MFMA to 3/4 of the 64 x 64 tiles' (6 fragment reads per 8
-// MFMAs), and 256 x 256 block tiles cut the L2-to-LDS bytes per flop to 2/3
+// Large wave tiles (WM x WN = 5 x 2 fragments, 160 x 64 per wave) cut the LDS
+// bytes read per MFMA to 7/10 of the 64 x 64 tiles' (7 fragment reads per 10
+// MFMAs), and 320 x 256 block tiles cut the L2-to-LDS bytes per flop to 0.6
 // of the 128 x 256 tiles'. Fragment reads run one k-step (16 k) ahead of the
 // MFMAs in two register sets, so a wave's matrix work never waits for its
 // own LDS reads; the one workgroup barrier of a K-tile sits before that
@@ -605,24 +605,29 @@ __device__ __forceinline__ void mainloop_pipe(bf16_t* s0, bf16_t* s1, bf16_t* s2
   wg_barrier();
 }
 
+// mainloop_pipe with NV = the largest count <= nv of this wave's 32-row
+// fragments that hold valid rows (one instantiation per count).
+template <class C, int NV>
+__device__ __forceinline__ void pipe_dispatch(int nv, bf16_t* s0, bf16_t* s1, bf16_t* s2, bf16_t* s3,
+                                              bf16_t* s4, const Rows<C::AR>& ar, const Rows<C::BR>& br,
+                                              int K, Acc<C>& acc) {
+  if constexpr (NV == 0) {
+    mainloop_pipe<C, 0>(s0, s1, s2, s3, s4, ar, br, K, acc);
+  } else {
+    if (nv >= NV) mainloop_pipe<C, NV>(s0, s1, s2, s3, s4, ar, br, K, acc);
+    else pipe_dispatch<C, NV - 1>(nv, s0, s1, s2, s3, s4, ar, br, K, acc);
+  }
+}
+
 // mainloop_pipe for a tile whose rows at or past `valid_rows` are padding.
 template <class C>
 __device__ __forceinline__ void mainloop_pipe_rows(bf16_t* s0, bf16_t* s1, bf16_t* s2, bf16_t* s3,
                                                    bf16_t* s4, const Rows<C::AR>& ar,
                                                    const Rows<C::BR>& br, int K, int valid_rows,
                                                    Acc<C>& acc) {
-  static_assert(C::WM <= 4, "fragment dispatch");
   const int first = wave_m<C>() * (C::BM / C::WGM);
   const int nv = __builtin_amdgcn_readfirstlane(max(0, min(C::WM, (valid_rows - first + 31) / 32)));
-  if (nv >= C::WM) mainloop_pipe<C, C::WM>(s0, s1, s2, s3, s4, ar, br, K, acc);
-  else if (nv == 0) mainloop_pipe<C, 0>(s0, s1, s2, s3, s4, ar, br, K, acc);
-  else if constexpr (C::WM > 1) {
-    if (nv == 1) mainloop_pipe<C, 1>(s0, s1, s2, s3, s4, ar, br, K, acc);
-    else if constexpr (C::WM > 2) {
-      if (nv == 2) mainloop_pipe<C, 2>(s0, s1, s2, s3, s4, ar, br, K, acc);
-      else if constexpr (C::WM > 3) mainloop_pipe<C, 3>(s0, s1, s2, s3, s4, ar, br, K, acc);
-    }
-  }
+  pipe_dispatch<C, C::WM>(nv, s0, s1, s2, s3, s4, ar, br, K, acc);
 }
 
 // Element (i, j, r) of this lane's accumulators sits at tile row / column
@@ -2239,7 +2244,7 @@ int multiseg_slices(int act_dtype, int M, int N, int nseg) {
 }
 
 // Row tiles of the grouped expert GEMMs: 1 on the fp32 path; 128 on the
-// scaled-MFMA path and with MXFP4 weights; with bf16 weights, 256 (the
+// scaled-MFMA path and with MXFP4 weights; with bf16 weights, 320 (the
 // pipelined big tiles) once the experts average at least kBigRows rows, else
 // 128 (at decode sizes the weight stream sets the pace and the smaller tiles
 // waste no DMA on padding rows).
