@@ -179,7 +179,8 @@ def measure_ceilings(stream):
     blocks, iters = 256 * 4, 20000                    # 4 waves per SIMD on 256 CUs
     out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda:0")
     res = {}
-    for kind, key in ((0, "mfma_bf16_tflops"), (1, "mfma_fp8xfp4_tflops")):
+    for kind, key in ((0, "mfma_bf16_tflops"), (1, "mfma_fp8xfp4_tflops"), (2, "mfma_bf16_changing_data_tflops"),
+                      (3, "mfma_fp8xfp4_changing_data_tflops")):
         def launch(kind=kind):
             if L.moe_probe_mfma(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()), sh) != 0:
                 raise RuntimeError("moe_probe_mfma failed")

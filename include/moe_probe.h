@@ -18,10 +18,12 @@ extern "C" {
 
 /* Back-to-back matrix-core instructions with no memory traffic: `blocks`
    workgroups of 4 waves, each wave `iters` rounds of 4 independent
-   accumulators. kind 0: v_mfma_f32_32x32x16_bf16; kind 1:
+   accumulators. kind 0: v_mfma_f32_32x32x16_bf16 on fixed operands; kind 1:
    v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 x E2M1 operands (the scaled-MFMA
-   expert path). out: one float per wave (blocks * 4), written so the work is
-   live; its values mean nothing. */
+   expert path); kinds 2 and 3: the same two instructions on pseudo-random
+   operands that change at every instruction, as in a real GEMM (iters a
+   multiple of 4). out: one float per wave (blocks * 4), written so the work is live; its
+   values mean nothing. */
 int moe_probe_mfma(int kind, int blocks, int iters, float* out, void* stream);
 
 /* Algorithmic FLOP of one moe_probe_mfma call (host only, no HIP call). */

@@ -286,13 +286,16 @@ int trace_begin() {
 
 constexpr size_t kTraceEvents = 2 * MOE_TRACE_STAGES;   // per traced call
 
+// Stage markers of a traced call. Tracing never fails the layer: an event that
+// could not be recorded leaves that stage's time unreadable (moe_trace_read
+// then returns the HIP error).
 struct Marker {
   int slot;
   void beg(int stage, hipStream_t s) const {
-    if (slot >= 0) hipEventRecord(g_trace.ev[(size_t)slot * kTraceEvents + 2 * stage], s);
+    if (slot >= 0) (void)hipEventRecord(g_trace.ev[(size_t)slot * kTraceEvents + 2 * stage], s);
   }
   void end(int stage, hipStream_t s) const {
-    if (slot >= 0) hipEventRecord(g_trace.ev[(size_t)slot * kTraceEvents + 2 * stage + 1], s);
+    if (slot >= 0) (void)hipEventRecord(g_trace.ev[(size_t)slot * kTraceEvents + 2 * stage + 1], s);
   }
 };
 

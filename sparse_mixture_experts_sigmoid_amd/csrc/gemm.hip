@@ -760,24 +760,45 @@ __device__ __forceinline__ void store_tile(const Acc<C>& acc, bf16_t* Cm, int64_
 }
 
 // out_row(tile_row) -> output row index, or < 0 to skip
+// The output rows of one accumulator fragment (i, j): 16 values per lane.
+template <class C, int I, int J, typename RowMap>
+__device__ __forceinline__ void store_glu_frag(const Acc<C>& acc, bf16_t* H, int64_t ldh, int f, float c,
+                                               float inv_c, RowMap out_row) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t orow = out_row(acc_row<C>(I, r));
+    if (orow < 0) continue;
+    H[orow * ldh + f] = f32_to_bf16(situ_glu(acc.c[I][J][r], acc.c[I][J + C::WN / 2][r], c, inv_c));
+  }
+}
+
+// Fragments (I .. WM-1, J) by recursion, so that every accumulator index is a
+// constant however long the unrolled epilogue grows (a rolled loop would put
+// the accumulators in scratch memory).
+template <class C, int I, int J, typename RowMap>
+__device__ __forceinline__ void store_glu_rows(const Acc<C>& acc, bf16_t* H, int64_t ldh, int f, float c,
+                                               float inv_c, RowMap out_row) {
+  if constexpr (I < C::WM) {
+    store_glu_frag<C, I, J>(acc, H, ldh, f, c, inv_c, out_row);
+    store_glu_rows<C, I + 1, J>(acc, H, ldh, f, c, inv_c, out_row);
+  }
+}
+
+template <class C, int J, typename RowMap>
+__device__ __forceinline__ void store_glu_cols(const Acc<C>& acc, bf16_t* H, int64_t ldh, int f0, int F,
+                                               float c, float inv_c, RowMap out_row) {
+  if constexpr (J < C::WN / 2) {
+    const int lane = threadIdx.x & 63;
+    const int f = f0 + wave_n<C>() * glu_half_rows<C>() + J * 32 + (lane & 31);
+    if (f < F) store_glu_rows<C, 0, J>(acc, H, ldh, f, c, inv_c, out_row);
+    store_glu_cols<C, J + 1>(acc, H, ldh, f0, F, c, inv_c, out_row);
+  }
+}
+
 template <class C, typename RowMap>
 __device__ __forceinline__ void store_glu(const Acc<C>& acc, bf16_t* H, int64_t ldh, int f0, int F,
                                           float c, RowMap out_row) {
-  const int lane = threadIdx.x & 63, wn = wave_n<C>();
-  const float inv_c = 1.0f / c;
-#pragma unroll
-  for (int j = 0; j < C::WN / 2; ++j) {
-    const int f = f0 + wn * glu_half_rows<C>() + j * 32 + (lane & 31);
-    if (f >= F) continue;
-#pragma unroll
-    for (int i = 0; i < C::WM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t orow = out_row(acc_row<C>(i, r));
-        if (orow < 0) continue;
-        H[orow * ldh + f] = f32_to_bf16(situ_glu(acc.c[i][j][r], acc.c[i][j + C::WN / 2][r], c, inv_c));
-      }
-  }
+  store_glu_cols<C, 0>(acc, H, ldh, f0, F, c, 1.0f / c, out_row);
 }
 
 // XCD-aware block order. Workgroups are handed to the 8 XCDs round-robin
@@ -1653,38 +1674,60 @@ __global__ __launch_bounds__(512) void grouped_down_mx8_kernel(GroupedDownArgs a
 // gathered z (or h) rows do, through a 4-stage ring of 64-k tiles (16 KB
 // each), shared by the block's 4 waves.
 //
-// Block 128 rows x 512 weight rows, 4 waves of 128 x 128 (4 x 4 fragments,
-// one wave per SIMD): per 16-k step a wave reads 4 A fragments from LDS and
-// takes 4 B fragments from registers for 16 MFMAs. The B fragments of k-step
-// q + 7 are loaded while k-step q computes, into a ring of 8 register slots.
+// A block is 4 waves side by side in N, one per SIMD, each owning WM x WN
+// fragments of 32 x 32 (Shape). Per 16-k step a wave reads its WM A fragments
+// from LDS and takes its WN B fragments from registers for WM x WN MFMAs; the
+// B fragments of k-step q + LEAD are loaded while k-step q computes, into a
+// ring of LEAD + 1 register slots. Wide, the shape of every kernel here:
+// 128 x 512 (4 x 4 fragments per wave, B 7 k-steps ahead). A 256 x 256 shape
+// (8 x 2 fragments, B 15 k-steps ahead) ran the K3 prefill gate/up no faster
+// (15.1 ms both) and the decode batch at 7.9 against 6.3 ms.
 namespace bt {
-constexpr int BM = 128, BN = 512, NW = 4, BK = 64, KS = BK / 16;
+constexpr int NW = 4, BK = 64, KS = BK / 16;
 constexpr int NSA = 4;                     // A stages
-constexpr int LEAD = 7, SLOTS = 8;         // B k-steps loaded ahead; register slots
-constexpr int AR = BM / (NW * 8);          // A DMA per wave per stage (8 rows of 128 B each)
-using L = Cfg<1, 4, 4, 4, 64, 2>;          // accumulator / epilogue layout (128 x 512)
-static_assert(L::BM == BM && L::BN == BN && L::NT == 256 && L::AR == AR, "layout");
 
+template <int WM_, int WN_, int LEAD_>
+struct Shape {
+  static constexpr int WM = WM_, WN = WN_, LEAD = LEAD_, SLOTS = LEAD_ + 1;
+  static constexpr int BM = 32 * WM, BN = 32 * WN * NW;
+  static constexpr int AR = BM / (NW * 8);          // A DMA per wave per stage (8 rows of 128 B)
+  using L = Cfg<1, NW, WM, WN, BK, 2>;              // accumulator / epilogue layout
+  static_assert(L::BM == BM && L::BN == BN && L::NT == 256 && L::AR == AR, "layout");
+  static_assert((NSA * KS) % SLOTS == 0 && WN % 2 == 0, "slot ring; gate/up halves");
+  // vector-memory ops issued after the DMA of the A stage that the end of
+  // tile T (0 .. NSA-1 within a round) waits for: the later stages' DMAs and
+  // the B loads of the tiles since. The first round issues fewer (its DMAs
+  // all come before its B loads).
+  static constexpr int vm_after_dma(int T, bool first) {
+    return (NSA - 2) * AR + ((first && T + 1 < NSA - 1) ? T + 1 : NSA - 1) * KS * WN;
+  }
+};
+using Wide = Shape<4, 4, 7>;
+constexpr int BM = Wide::BM, BN = Wide::BN, AR = Wide::AR;
+using L = Wide::L;
+
+template <int WN>
 struct BSrc {
   rsrc_t r[2];                 // weight resources (gate, up for a GLU tile; one for plain)
-  uint32_t off[4];             // byte offset of fragment j's first k-step tile + 16 lane, or kOOB
+  uint32_t off[WN];            // byte offset of fragment j's first k-step tile + 16 lane, or kOOB
 };
 
-// 4 B fragments (one k-step) into slot registers: fragment j of k-step q is
-// the 1 KB at off[j] + 1024 q.
-__device__ __forceinline__ void load_b(const BSrc& b, int q, bf16x8 (&dst)[4]) {
+// WN B fragments (one k-step) into slot registers: fragment j of k-step q is
+// the 1 KB at off[j] + 1024 q (the second half of the fragments through r[1]).
+template <int WN>
+__device__ __forceinline__ void load_b(const BSrc<WN>& b, int q, bf16x8 (&dst)[WN]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < WN; ++j) {
     const uint32_t o = b.off[j];
     dst[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                            b.r[j >= 2 ? 1 : 0], o + 1024u * (uint32_t)q, 0, 0));
+                                            b.r[j >= WN / 2 ? 1 : 0], o + 1024u * (uint32_t)q, 0, 0));
   }
 }
 
 // A fragments of k-step ks of an A stage (BM x BK, the swizzled 128-byte rows
 // of the DMA engine): NV fragments of 32 rows.
-template <int NV>
-__device__ __forceinline__ void read_a(const bf16_t* S, int ks, bf16x8 (&fa)[4]) {
+template <int NV, int WM>
+__device__ __forceinline__ void read_a(const bf16_t* S, int ks, bf16x8 (&fa)[WM]) {
   if constexpr (NV > 0) {
     const int lane = threadIdx.x & 63, lr = lane & 31, lh = lane >> 5;
     const bf16_t* Aw = S + lr * BK;
@@ -1694,115 +1737,116 @@ __device__ __forceinline__ void read_a(const bf16_t* S, int ks, bf16x8 (&fa)[4])
   }
 }
 
-template <int NV>
-__device__ __forceinline__ void mma_q(const bf16x8 (&fa)[4], const bf16x8 (&fb)[4], Acc<L>& acc) {
+template <int NV, class C>
+__device__ __forceinline__ void mma_q(const bf16x8 (&fa)[C::WM], const bf16x8 (&fb)[C::WN], Acc<C>& acc) {
 #pragma unroll
   for (int i = 0; i < NV; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < C::WN; ++j)
       acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc.c[i][j], 0, 0, 0);
 }
 
-__device__ __forceinline__ void dma_a(const Rows<AR>& ar, bf16_t* S, int kt, int K) {
-  dma_rows<L, AR>(ar, S, kt * BK, K);
+template <class S>
+__device__ __forceinline__ void dma_a(const Rows<S::AR>& ar, bf16_t* St, int kt, int K) {
+  dma_rows<typename S::L, S::AR>(ar, St, kt * BK, K);
 }
 
-// B register slots: slot s holds the 4 fragments of the k-steps q = s (mod SLOTS).
+// B register slots: slot s holds the WN fragments of the k-steps q = s (mod SLOTS).
+template <class S>
 struct BRing {
-  bf16x8 b[SLOTS][4];
+  bf16x8 b[S::SLOTS][S::WN];
 };
 
-// One k-step Q (0 .. 15) of a round of NSA K-tiles (round base k-step q0):
-// load B of k-step q0 + Q + LEAD, then (ks < 3) read the next A fragments of
-// this tile or (ks == 3) wait for the next tile's stage, barrier, refill this
-// stage with tile kt + NSA and read the next tile's first A fragments; then
-// this k-step's MFMAs.
-template <int NV, int Q>
-__device__ __forceinline__ void bt_kstep(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const BSrc& bs,
-                                         int q0, int K, BRing& br, bf16x8 (&fa0)[4], bf16x8 (&fa1)[4],
-                                         Acc<L>& acc) {
+// One k-step Q (0 .. NSA KS - 1) of a round of NSA K-tiles (round base k-step
+// q0): load B of k-step q0 + Q + LEAD, then (ks < KS-1) read the next A
+// fragments of this tile or (ks == KS-1) wait for the next tile's stage,
+// barrier, refill this stage with tile kt + NSA and read the next tile's first
+// A fragments; then this k-step's MFMAs.
+template <class S, int NV, int Q>
+__device__ __forceinline__ void bt_kstep(bf16_t* const (&st)[NSA], const Rows<S::AR>& ar,
+                                         const BSrc<S::WN>& bs, int q0, int K, BRing<S>& br,
+                                         bf16x8 (&fa0)[S::WM], bf16x8 (&fa1)[S::WM],
+                                         Acc<typename S::L>& acc) {
   constexpr int T = Q / KS, ks = Q % KS;
-  constexpr int slot = Q % SLOTS, lslot = (Q + LEAD) % SLOTS;
+  constexpr int slot = Q % S::SLOTS, lslot = (Q + S::LEAD) % S::SLOTS;
+  load_b<S::WN>(bs, q0 + Q + S::LEAD, br.b[lslot]);
   if constexpr (ks + 1 < KS) {
-    load_b(bs, q0 + Q + LEAD, br.b[lslot]);
     if constexpr (ks & 1) read_a<NV>(st[T], ks + 1, fa0);
     else read_a<NV>(st[T], ks + 1, fa1);
   } else {
-    load_b(bs, q0 + Q + LEAD, br.b[lslot]);
     // the next tile's A stage must have landed (own DMA, then every wave's),
-    // and every wave must be done reading this stage before it is refilled.
-    // 24 = the vector-memory ops issued after the next tile's DMA in the
-    // first round (A of tiles 2, 3 and the B loads of 4 k-steps); later
-    // rounds issue more, so this waits a little longer than needed there.
-    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0_vm(24));
+    // and every wave must be done reading this stage before it is refilled;
+    // the B loads issued since that DMA stay in flight.
+    if (q0 == 0) __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0_vm(S::vm_after_dma(T, true)));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0_vm(S::vm_after_dma(T, false)));
     wg_barrier();
-    dma_a(ar, st[T], (q0 / KS) + T + NSA, K);
+    dma_a<S>(ar, st[T], (q0 / KS) + T + NSA, K);
     static_assert(KS % 2 == 0, "k-step 0 of a tile reads into fa0");
     read_a<NV>(st[(T + 1) % NSA], 0, fa0);
   }
-  if constexpr (ks & 1) mma_q<NV>(fa1, br.b[slot], acc);
-  else mma_q<NV>(fa0, br.b[slot], acc);
+  if constexpr (ks & 1) mma_q<NV, typename S::L>(fa1, br.b[slot], acc);
+  else mma_q<NV, typename S::L>(fa0, br.b[slot], acc);
   // one wave per SIMD: the next k-step's A reads and the loads go between the
   // MFMAs, so that their latency overlaps matrix work. Per A fragment i:
-  // MFMA, read, MFMA, load, 2 MFMAs (loads: B before the tile's barrier, the
-  // refill DMA of the A stage after it).
+  // MFMA, read, MFMA, one load (the B loads before the tile's barrier, the
+  // refill DMA of the A stage after it), the other MFMAs.
   if constexpr (NV > 0) {
+    constexpr int V = ks + 1 < KS ? S::WN : S::AR;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (ks + 1 < KS || i < AR) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (i < V) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if constexpr (S::WN > 2) __builtin_amdgcn_sched_group_barrier(0x008, S::WN - 2, 0);
     }
   }
 }
 
-template <int NV, int Q>
-__device__ __forceinline__ void bt_round(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const BSrc& bs, int q0,
-                                         int K, BRing& br, bf16x8 (&fa0)[4], bf16x8 (&fa1)[4], Acc<L>& acc) {
+template <class S, int NV, int Q>
+__device__ __forceinline__ void bt_round(bf16_t* const (&st)[NSA], const Rows<S::AR>& ar,
+                                         const BSrc<S::WN>& bs, int q0, int K, BRing<S>& br,
+                                         bf16x8 (&fa0)[S::WM], bf16x8 (&fa1)[S::WM],
+                                         Acc<typename S::L>& acc) {
   if constexpr (Q < NSA * KS) {
-    bt_kstep<NV, Q>(st, ar, bs, q0, K, br, fa0, fa1, acc);
-    bt_round<NV, Q + 1>(st, ar, bs, q0, K, br, fa0, fa1, acc);
+    bt_kstep<S, NV, Q>(st, ar, bs, q0, K, br, fa0, fa1, acc);
+    bt_round<S, NV, Q + 1>(st, ar, bs, q0, K, br, fa0, fa1, acc);
   }
 }
 
-template <int NV>
-__device__ __forceinline__ void bt_mainloop(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const BSrc& bs,
-                                            int K, Acc<L>& acc) {
-  static_assert((NSA * KS) % SLOTS == 0 && SLOTS == LEAD + 1, "slot ring");
+template <class S, int NV>
+__device__ __forceinline__ void bt_mainloop(bf16_t* const (&st)[NSA], const Rows<S::AR>& ar,
+                                            const BSrc<S::WN>& bs, int K, Acc<typename S::L>& acc) {
   const int nq = (int)ceil_div(K, BK) * KS;       // k-steps, whole K-tiles
-  BRing br;
+  BRing<S> br;
   // B of k-steps 0 .. LEAD-1, then A of tiles 0 .. NSA-1
-  if constexpr (LEAD > 0) load_b(bs, 0, br.b[0]);
-  if constexpr (LEAD > 1) load_b(bs, 1, br.b[1]);
-  if constexpr (LEAD > 2) load_b(bs, 2, br.b[2]);
-  if constexpr (LEAD > 3) load_b(bs, 3, br.b[3]);
-  if constexpr (LEAD > 4) load_b(bs, 4, br.b[4]);
-  if constexpr (LEAD > 5) load_b(bs, 5, br.b[5]);
-  if constexpr (LEAD > 6) load_b(bs, 6, br.b[6]);
-  static_assert(LEAD <= 7, "prologue");
 #pragma unroll
-  for (int t = 0; t < NSA; ++t) dma_a(ar, st[t], t, K);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(AR * (NSA - 1)));
+  for (int q = 0; q < S::LEAD; ++q) load_b<S::WN>(bs, q, br.b[q]);
+#pragma unroll
+  for (int t = 0; t < NSA; ++t) dma_a<S>(ar, st[t], t, K);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(S::AR * (NSA - 1)));
   wg_barrier();
-  bf16x8 fa0[4], fa1[4];
+  bf16x8 fa0[S::WM], fa1[S::WM];
   read_a<NV>(st[0], 0, fa0);
   // whole rounds of NSA K-tiles (tiles past K are zeros on both operands)
-  for (int q0 = 0; q0 < nq; q0 += NSA * KS) bt_round<NV, 0>(st, ar, bs, q0, K, br, fa0, fa1, acc);
+  for (int q0 = 0; q0 < nq; q0 += NSA * KS) bt_round<S, NV, 0>(st, ar, bs, q0, K, br, fa0, fa1, acc);
   __builtin_amdgcn_s_waitcnt(0);
   wg_barrier();
 }
 
-template <int UNUSED = 0>
-__device__ __forceinline__ void bt_mainloop_rows(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const BSrc& bs,
-                                                 int K, int valid_rows, Acc<L>& acc) {
-  const int nv = __builtin_amdgcn_readfirstlane(max(0, min(4, (valid_rows + 31) / 32)));
-  if (nv >= 4) bt_mainloop<4>(st, ar, bs, K, acc);
-  else if (nv == 3) bt_mainloop<3>(st, ar, bs, K, acc);
-  else if (nv == 2) bt_mainloop<2>(st, ar, bs, K, acc);
-  else if (nv == 1) bt_mainloop<1>(st, ar, bs, K, acc);
-  else bt_mainloop<0>(st, ar, bs, K, acc);
+// bt_mainloop with NV = the number of this block's 32-row fragments that hold
+// valid rows (one instantiation per count).
+template <class S, int NV = S::WM>
+__device__ __forceinline__ void bt_mainloop_rows(bf16_t* const (&st)[NSA], const Rows<S::AR>& ar,
+                                                 const BSrc<S::WN>& bs, int K, int valid_rows,
+                                                 Acc<typename S::L>& acc) {
+  if constexpr (NV == 0) {
+    bt_mainloop<S, 0>(st, ar, bs, K, acc);
+  } else {
+    const int nv = __builtin_amdgcn_readfirstlane(max(0, min(S::WM, (valid_rows + 31) / 32)));
+    if (nv >= NV) bt_mainloop<S, NV>(st, ar, bs, K, acc);
+    else bt_mainloop_rows<S, NV - 1>(st, ar, bs, K, valid_rows, acc);
+  }
 }
 
 // Byte offset, in the tiled layout of a weight with K padded to Kp (a
@@ -1898,7 +1942,7 @@ __device__ __forceinline__ void btmx_kstep(bf16_t* const (&st)[NSA], const Rows<
     // second pair's scales)
     __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0_vm(16));
     wg_barrier();
-    dma_a(ar, st[T], t0 + T + NSA, K);
+    dma_a<Wide>(ar, st[T], t0 + T + NSA, K);
     read_a<NV>(st[(T + 1) % NSA], 0, fa0);
   }
   if constexpr (ks & 1) mma_q<NV>(fa1, fb1, acc);
@@ -1936,7 +1980,7 @@ __device__ __forceinline__ void btmx_mainloop(bf16_t* const (&st)[NSA], const Ro
   static_assert(LEADT == 3, "prologue");
   load_mx_scales(ms, 0, mr.sc[0]);
 #pragma unroll
-  for (int t = 0; t < NSA; ++t) dma_a(ar, st[t], t, K);
+  for (int t = 0; t < NSA; ++t) dma_a<Wide>(ar, st[t], t, K);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(AR * (NSA - 1)));
   wg_barrier();
   bf16x8 fa0[4], fa1[4], fb0[4], fb1[4];
@@ -1968,34 +2012,36 @@ __device__ __forceinline__ uint32_t mx_tiled_soff(int r, int Kp) {
   return (uint32_t)(r / 32) * (uint32_t)(Kp / 128) * 128u + 4u * (uint32_t)(threadIdx.x & 31);
 }
 
-#define MOE_BT_RING                                             \
-  __shared__ __align__(16) bf16_t la0[BM * BK];                  \
-  __shared__ __align__(16) bf16_t la1[BM * BK];                  \
-  __shared__ __align__(16) bf16_t la2[BM * BK];                  \
-  __shared__ __align__(16) bf16_t la3[BM * BK];                  \
-  bf16_t* const st[NSA] = {la0, la1, la2, la3}
+// the A ring of a register-B block of ROWS rows: NSA stages of ROWS x BK bf16
+#define MOE_BT_RING(ROWS)                                       \
+  __shared__ __align__(16) bf16_t la0[(ROWS) * bt::BK];          \
+  __shared__ __align__(16) bf16_t la1[(ROWS) * bt::BK];          \
+  __shared__ __align__(16) bf16_t la2[(ROWS) * bt::BK];          \
+  __shared__ __align__(16) bf16_t la3[(ROWS) * bt::BK];          \
+  bf16_t* const st[bt::NSA] = {la0, la1, la2, la3}
 static_assert(NSA == 4, "ring arrays");
 }  // namespace bt
 
 // grouped_glu on tiled bf16 weights: H[r] = act(z W_g[e]^T, z W_v[e]^T) for the
-// rows of expert e, 256 outputs per block (wave w: outputs f0 + 64 w + 0..63,
-// fragments 0-1 gate, 2-3 up).
+// rows of expert e, BN/2 outputs per block (wave w: outputs f0 + w BN/8 + 0 ..
+// BN/8 - 1; its first WN/2 fragments gate, the others up).
 __global__ __launch_bounds__(bt::NW * 64) void grouped_glu_bt_kernel(GroupedGluArgs a) {
   using namespace bt;
-  using C = L;
-  MOE_BT_RING;
-  const int ntn = (int)ceil_div(a.F, BN / 2);
+  using S = Wide;
+  using C = S::L;
+  MOE_BT_RING(S::BM);
+  const int ntn = (int)ceil_div(a.F, S::BN / 2);
   int64_t Li;
   if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, Li)) return;
   int e, nt, row_lo, row_hi;
-  grouped_item<BM>(a.tile_info, ntn, a.rows_cap, Li, e, nt, row_lo, row_hi);
-  const int f0 = nt * (BN / 2);
-  Rows<AR> ar;
+  grouped_item<S::BM>(a.tile_info, ntn, a.rows_cap, Li, e, nt, row_lo, row_hi);
+  const int f0 = nt * (S::BN / 2);
+  Rows<S::AR> ar;
   ar.r[0] = ar.r[1] = make_rsrc(a.Z, (int64_t)a.T * a.ldz * 2);
 #pragma unroll
-  for (int q = 0; q < AR; ++q) {
+  for (int q = 0; q < S::AR; ++q) {
     ar.sel[q] = 0;
-    const int row = row_lo + dma_row<C, AR>(q);
+    const int row = row_lo + dma_row<C, S::AR>(q);
     uint32_t off = kOOB;
     if (row >= 0 && row < row_hi) {
       const int src = a.perm_src[row];
@@ -2006,49 +2052,51 @@ __global__ __launch_bounds__(bt::NW * 64) void grouped_glu_bt_kernel(GroupedGluA
   }
   const int Kp = (int)ceil_div(a.K, BK) * BK;
   const int64_t ebytes = (int64_t)a.F * Kp * 2;                 // one expert's tiled weight
-  BSrc bs;
+  BSrc<S::WN> bs;
   bs.r[0] = make_rsrc((const uint8_t*)a.Wg.data + e * ebytes, ebytes);
   bs.r[1] = make_rsrc((const uint8_t*)a.Wv.data + e * ebytes, ebytes);
   const int w = threadIdx.x >> 6;
+  constexpr int H = S::WN / 2;                                   // gate (= up) fragments per wave
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int f = f0 + 64 * w + 32 * (j & 1);
-    bs.off[j] = f < a.F ? bt::tiled_off(f, Kp) : kOOB;
+  for (int j = 0; j < S::WN; ++j) {
+    const int f = f0 + 32 * H * w + 32 * (j % H);
+    bs.off[j] = f < a.F ? tiled_off(f, Kp) : kOOB;
   }
   Acc<C> acc;
   acc_zero(acc);
-  bt_mainloop_rows(st, ar, bs, a.K, row_hi - row_lo, acc);
+  bt_mainloop_rows<S>(st, ar, bs, a.K, row_hi - row_lo, acc);
   store_glu(acc, (bf16_t*)a.H, a.F, f0, a.F, a.c, [=](int tr) -> int64_t {
     const int r = row_lo + tr;
     return (r >= 0 && r < row_hi) ? (int64_t)r : -1;
   });
 }
 
-// grouped_down on tiled bf16 weights: O[r] = H[r] W_o[e]^T, 512 outputs per block.
+// grouped_down on tiled bf16 weights: O[r] = H[r] W_o[e]^T, BN outputs per block.
 __global__ __launch_bounds__(bt::NW * 64) void grouped_down_bt_kernel(GroupedDownArgs a) {
   using namespace bt;
-  using C = L;
-  MOE_BT_RING;
-  const int ntn = (int)ceil_div(a.N, BN);
+  using S = Wide;
+  using C = S::L;
+  MOE_BT_RING(S::BM);
+  const int ntn = (int)ceil_div(a.N, S::BN);
   int64_t Li;
   if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, Li)) return;
   int e, nt, row_lo, row_hi;
-  grouped_item<BM>(a.tile_info, ntn, a.rows_cap, Li, e, nt, row_lo, row_hi);
-  const int n0 = nt * BN;
-  const Rows<AR> ar = a_rows_dense<C, AR>(a.H, a.ldh, max(row_lo, 0), max(row_hi, 0));
+  grouped_item<S::BM>(a.tile_info, ntn, a.rows_cap, Li, e, nt, row_lo, row_hi);
+  const int n0 = nt * S::BN;
+  const Rows<S::AR> ar = a_rows_dense<C, S::AR>(a.H, a.ldh, max(row_lo, 0), max(row_hi, 0));
   const int Kp = (int)ceil_div(a.K, BK) * BK;
   const int64_t ebytes = (int64_t)a.N * Kp * 2;
-  BSrc bs;
+  BSrc<S::WN> bs;
   bs.r[0] = bs.r[1] = make_rsrc((const uint8_t*)a.Wo.data + e * ebytes, ebytes);
   const int w = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int n = n0 + 128 * w + 32 * j;
-    bs.off[j] = n < a.N ? bt::tiled_off(n, Kp) : kOOB;
+  for (int j = 0; j < S::WN; ++j) {
+    const int n = n0 + (S::BN / NW) * w + 32 * j;
+    bs.off[j] = n < a.N ? tiled_off(n, Kp) : kOOB;
   }
   Acc<C> acc;
   acc_zero(acc);
-  bt_mainloop_rows(st, ar, bs, a.K, row_hi - row_lo, acc);
+  bt_mainloop_rows<S>(st, ar, bs, a.K, row_hi - row_lo, acc);
   store_tile(acc, (bf16_t*)a.O, a.N, row_lo, n0, row_hi, a.N);
 }
 
@@ -2056,7 +2104,7 @@ __global__ __launch_bounds__(bt::NW * 64) void grouped_down_bt_kernel(GroupedDow
 __global__ __launch_bounds__(bt::NW * 64) void grouped_glu_btmx_kernel(GroupedGluArgs a) {
   using namespace bt;
   using C = L;
-  MOE_BT_RING;
+  MOE_BT_RING(BM);
   const int ntn = (int)ceil_div(a.F, BN / 2);
   int64_t Li;
   if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, Li)) return;
@@ -2103,7 +2151,7 @@ __global__ __launch_bounds__(bt::NW * 64) void grouped_glu_btmx_kernel(GroupedGl
 __global__ __launch_bounds__(bt::NW * 64) void grouped_down_btmx_kernel(GroupedDownArgs a) {
   using namespace bt;
   using C = L;
-  MOE_BT_RING;
+  MOE_BT_RING(BM);
   const int ntn = (int)ceil_div(a.N, BN);
   int64_t Li;
   if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, Li)) return;

@@ -1,7 +1,7 @@
 // Ceiling probes of one MI355X, the measured denominators that bench.py
 // reports beside the published peaks: back-to-back matrix-core instructions
-// with no memory traffic (bf16 and MXFP8 x MXFP4), and a plain streaming read
-// of HBM. Not part of the layer: libmoe_probe.so is loaded by bench.py only.
+// with no memory traffic (bf16 and MXFP8 x MXFP4, each with fixed or with
+// changing operands), and a plain streaming read of HBM. Not part of the layer: libmoe_probe.so is loaded by bench.py only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,6 +30,40 @@ __global__ __launch_bounds__(256) void mfma_bf16_kernel(int iters, float* out) {
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int c = 0; c < kChains; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+  }
+  float s = 0.0f;
+  for (int c = 0; c < kChains; ++c)
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  if ((threadIdx.x & 63) == 0) out[blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64] = s;
+}
+
+// As mfma_bf16_kernel, but with operands that change at every instruction:
+// four A and four B fragments of pseudo-random bf16 values in [-2, 2) (from a
+// hash of the lane), each chain stepping through the 16 pairs, so that the
+// matrix cores switch on data like a real GEMM (their power, and with it the
+// clock, depends on it).
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+  x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+  return x;
+}
+__global__ __launch_bounds__(256) void mfma_bf16_data_kernel(int iters, float* out) {
+  bf16x8 a[4], b[4];
+  for (int u = 0; u < 4; ++u)
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ha = probe_hash(threadIdx.x * 64u + u * 8u + i + 1u);
+      const uint32_t hb = probe_hash(threadIdx.x * 64u + u * 8u + i + 0x9e3779b9u);
+      a[u][i] = (__bf16)((float)(ha & 0xFFFFu) * (4.0f / 65536.0f) - 2.0f);
+      b[u][i] = (__bf16)((float)(hb & 0xFFFFu) * (4.0f / 65536.0f) - 2.0f);
+    }
+  f32x16 acc[kChains];
+  for (int c = 0; c < kChains; ++c)
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+  for (int it = 0; it < iters; it += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < kChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(u + c) & 3], b[(u + 2 * c + (c >> 1)) & 3], acc[c], 0, 0, 0);
   }
   float s = 0.0f;
   for (int c = 0; c < kChains; ++c)
@@ -80,21 +114,58 @@ __global__ __launch_bounds__(256) void hbm_read_kernel(const uint4* __restrict__
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// As mfma_f8f4_kernel, but with pseudo-random E4M3 and E2M1 codes that change
+// at every instruction (four A and four B operand sets per lane, as above).
+// E4M3 codes 0x7f / 0xff (NaN) are mapped to 0x7e / 0xfe.
+__global__ __launch_bounds__(256) void mfma_f8f4_data_kernel(int iters, float* out) {
+  v8i a[4], b[4];
+  for (int u = 0; u < 4; ++u)
+    for (int i = 0; i < 8; ++i) {
+      uint32_t ha = probe_hash(threadIdx.x * 64u + u * 8u + i + 7u);
+      const uint32_t hb = probe_hash(threadIdx.x * 64u + u * 8u + i + 0x85ebca6bu);
+      for (int k = 0; k < 4; ++k) {        // no NaN bytes
+        const uint32_t byte = (ha >> (8 * k)) & 0xFFu;
+        if ((byte & 0x7Fu) == 0x7Fu) ha ^= 1u << (8 * k);
+      }
+      a[u][i] = (int)ha;
+      b[u][i] = i < 4 ? (int)hb : 0;
+    }
+  f32x16 acc[kChains];
+  for (int c = 0; c < kChains; ++c)
+    for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+  for (int it = 0; it < iters; it += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < kChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[(u + c) & 3], b[(u + 2 * c + (c >> 1)) & 3],
+                                                                 acc[c], 0, 4, 0, 127, 0, 127);
+  }
+  float s = 0.0f;
+  for (int c = 0; c < kChains; ++c)
+    for (int r = 0; r < 16; ++r) s += acc[c][r];
+  if ((threadIdx.x & 63) == 0) out[blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64] = s;
+}
+
 }  // namespace
 
 extern "C" {
 
 int moe_probe_mfma(int kind, int blocks, int iters, float* out, void* stream) {
-  if (blocks <= 0 || iters <= 0 || out == nullptr || (kind != 0 && kind != 1)) return -1;
+  if (blocks <= 0 || iters <= 0 || out == nullptr || kind < 0 || kind > 3 || (kind >= 2 && iters % 4)) return -1;
   if (kind == 0)
     hipLaunchKernelGGL(mfma_bf16_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
-  else
+  else if (kind == 1)
     hipLaunchKernelGGL(mfma_f8f4_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
+  else if (kind == 2)
+    hipLaunchKernelGGL(mfma_bf16_data_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
+  else
+    hipLaunchKernelGGL(mfma_f8f4_data_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 double moe_probe_mfma_flops(int kind, int blocks, int iters) {
-  const double per = kind == 0 ? 2.0 * 32 * 32 * 16 : 2.0 * 32 * 32 * 64;
+  const double per = (kind == 1 || kind == 3) ? 2.0 * 32 * 32 * 64 : 2.0 * 32 * 32 * 16;
   return per * kChains * 4.0 * blocks * (double)iters;   // 4 waves per block
 }
 

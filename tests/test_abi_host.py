@@ -47,7 +47,9 @@ def test_probe_library_exports_and_validates():
     L.moe_probe_mfma_flops.restype = ctypes.c_double
     L.moe_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_void_p]
-    assert L.moe_probe_mfma(2, 1, 1, FAKE, None) == -1
+    assert L.moe_probe_mfma(4, 1, 4, FAKE, None) == -1
+    assert L.moe_probe_mfma(3, 1, 6, FAKE, None) == -1
+    assert L.moe_probe_mfma(2, 1, 6, FAKE, None) == -1      # changing operands: iters % 4 == 0
     assert L.moe_probe_mfma(0, 0, 1, FAKE, None) == -1
     assert L.moe_probe_mfma(0, 1, 1, None, None) == -1
     assert L.moe_probe_hbm_read(FAKE, 24, 1, 8, FAKE, None) == -1
