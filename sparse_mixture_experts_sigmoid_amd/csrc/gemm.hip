@@ -760,45 +760,24 @@ __device__ __forceinline__ void store_tile(const Acc<C>& acc, bf16_t* Cm, int64_
 }
 
 // out_row(tile_row) -> output row index, or < 0 to skip
-// The output rows of one accumulator fragment (i, j): 16 values per lane.
-template <class C, int I, int J, typename RowMap>
-__device__ __forceinline__ void store_glu_frag(const Acc<C>& acc, bf16_t* H, int64_t ldh, int f, float c,
-                                               float inv_c, RowMap out_row) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t orow = out_row(acc_row<C>(I, r));
-    if (orow < 0) continue;
-    H[orow * ldh + f] = f32_to_bf16(situ_glu(acc.c[I][J][r], acc.c[I][J + C::WN / 2][r], c, inv_c));
-  }
-}
-
-// Fragments (I .. WM-1, J) by recursion, so that every accumulator index is a
-// constant however long the unrolled epilogue grows (a rolled loop would put
-// the accumulators in scratch memory).
-template <class C, int I, int J, typename RowMap>
-__device__ __forceinline__ void store_glu_rows(const Acc<C>& acc, bf16_t* H, int64_t ldh, int f, float c,
-                                               float inv_c, RowMap out_row) {
-  if constexpr (I < C::WM) {
-    store_glu_frag<C, I, J>(acc, H, ldh, f, c, inv_c, out_row);
-    store_glu_rows<C, I + 1, J>(acc, H, ldh, f, c, inv_c, out_row);
-  }
-}
-
-template <class C, int J, typename RowMap>
-__device__ __forceinline__ void store_glu_cols(const Acc<C>& acc, bf16_t* H, int64_t ldh, int f0, int F,
-                                               float c, float inv_c, RowMap out_row) {
-  if constexpr (J < C::WN / 2) {
-    const int lane = threadIdx.x & 63;
-    const int f = f0 + wave_n<C>() * glu_half_rows<C>() + J * 32 + (lane & 31);
-    if (f < F) store_glu_rows<C, 0, J>(acc, H, ldh, f, c, inv_c, out_row);
-    store_glu_cols<C, J + 1>(acc, H, ldh, f0, F, c, inv_c, out_row);
-  }
-}
-
 template <class C, typename RowMap>
 __device__ __forceinline__ void store_glu(const Acc<C>& acc, bf16_t* H, int64_t ldh, int f0, int F,
                                           float c, RowMap out_row) {
-  store_glu_cols<C, 0>(acc, H, ldh, f0, F, c, 1.0f / c, out_row);
+  const int lane = threadIdx.x & 63, wn = wave_n<C>();
+  const float inv_c = 1.0f / c;
+#pragma unroll
+  for (int j = 0; j < C::WN / 2; ++j) {
+    const int f = f0 + wn * glu_half_rows<C>() + j * 32 + (lane & 31);
+    if (f >= F) continue;
+#pragma unroll
+    for (int i = 0; i < C::WM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t orow = out_row(acc_row<C>(i, r));
+        if (orow < 0) continue;
+        H[orow * ldh + f] = f32_to_bf16(situ_glu(acc.c[i][j][r], acc.c[i][j + C::WN / 2][r], c, inv_c));
+      }
+  }
 }
 
 // XCD-aware block order. Workgroups are handed to the 8 XCDs round-robin
@@ -1231,8 +1210,13 @@ int reduce_blocks(int64_t n4) { return (int)(ceil_div(n4, 256) < 2048 ? ceil_div
 // Approximate router logits (the exact routing is decided in router.hip):
 // 128 x 128 tiles of x W_r^T, K split over `splits` blocks whose fp32 partial
 // sums are added atomically (their order does not matter: the logits only
-// bound the fixed-order ones).
-using LogitCfg = Cfg<2, 2, 2, 2, 64, 3>;
+// bound the fixed-order ones). Two 32 KB stages, so that two blocks share a CU:
+// at the K3 prefill batch (896 tiles of 112 K-tiles) that halves the kernel's
+// time against three stages and one block per CU (0.50 against 0.93 ms).
+#ifndef MOE_LOGIT_CFG
+#define MOE_LOGIT_CFG Cfg<2, 2, 2, 2, 64, 2>
+#endif
+using LogitCfg = MOE_LOGIT_CFG;
 
 __global__ __launch_bounds__(LogitCfg::NT) void logits_kernel(LogitsArgs a) {
   using C = LogitCfg;
