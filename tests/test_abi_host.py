@@ -73,6 +73,14 @@ def test_configs_are_valid(cfg):
     assert moe.moe_check_desc(moe.make_desc(cfg)) == moe.MOE_OK
 
 
+def test_largest_k3_batch_is_accepted():
+    """T = 299593 is the largest batch at the K3 shape (z under 2 GiB); the GPU
+    runs it in tests/test_gpu_maxsize.py."""
+    d = moe.make_desc(synth.config("k3_prefill"))
+    d.T = 299_593
+    assert moe.moe_check_desc(d) == moe.MOE_OK
+
+
 def _desc(**kw):
     d = moe.make_desc(synth.config("k3_decode"))
     for k, v in kw.items():
@@ -100,6 +108,7 @@ def _desc(**kw):
     (dict(n_experts=5000, top_k=16), moe.MOE_ERR_UNSUPPORTED),
     (dict(n_shared=8), moe.MOE_ERR_UNSUPPORTED),
     (dict(T=300_000), moe.MOE_ERR_UNSUPPORTED),                # z over 2 GiB (32-bit gather offsets)
+    (dict(T=299_594), moe.MOE_ERR_UNSUPPORTED),                # the first T whose z reaches 2 GiB
     (dict(expert_w_tiled=2), moe.MOE_ERR_INVALID_ARG),
     (dict(expert_w_tiled=1, act_dtype=moe.MOE_F32, expert_w_dtype=moe.MOE_F32,
           latent_w_dtype=moe.MOE_F32, dense_w_dtype=moe.MOE_F32),
