@@ -1687,6 +1687,9 @@ struct Shape {
   }
 };
 using Wide = Shape<4, 4, 7>;
+// 32 x 512 (one row fragment per wave) for the MXFP4 kernels at batches of few
+// rows per expert
+using Thin = Shape<1, 4, 7>;
 constexpr int BM = Wide::BM, BN = Wide::BN, AR = Wide::AR;
 using L = Wide::L;
 
@@ -1897,23 +1900,19 @@ __device__ __forceinline__ void decode_kstep(const MxRing& r, bf16x8 (&fb)[4]) {
 // the packed codes of tile kt + LEADT (and, at even tiles, the scales of the
 // pair after the current one) loaded at each tile's first k-step, and the
 // next k-step's B fragments decoded while this one's MFMAs run.
-template <int NV, int Q>
-__device__ __forceinline__ void btmx_kstep(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const MxSrc& ms,
-                                           int q0, int K, MxRing& mr, bf16x8 (&fa0)[4], bf16x8 (&fa1)[4],
-                                           bf16x8 (&fb0)[4], bf16x8 (&fb1)[4], Acc<L>& acc) {
+template <class S, int NV, int Q>
+__device__ __forceinline__ void btmx_kstep(bf16_t* const (&st)[NSA], const Rows<S::AR>& ar, const MxSrc& ms,
+                                           int q0, int K, MxRing& mr, bf16x8 (&fa0)[S::WM],
+                                           bf16x8 (&fa1)[S::WM], bf16x8 (&fb0)[4], bf16x8 (&fb1)[4],
+                                           Acc<typename S::L>& acc) {
+  static_assert(S::WN == 4, "four B fragments per wave");
   constexpr int T = Q / KS, ks = Q % KS;
   const int t0 = q0 / KS;                              // first tile of the round (a multiple of 4)
   constexpr int QN = Q + 1, TN = (QN / KS) % NSA, KN = QN % KS;   // the next k-step
-  int nvmem = 0;
   if constexpr (ks == 0) {
     load_mx_tile(ms, t0 + T + LEADT, mr.p[(T + LEADT) % TSLOTS]);
-    nvmem += 4;
-    if constexpr (T % 2 == 0) {
-      load_mx_scales(ms, (t0 + T) / 2 + 1, mr.sc[(T / 2 + 1) % 2]);
-      nvmem += 4;
-    }
+    if constexpr (T % 2 == 0) load_mx_scales(ms, (t0 + T) / 2 + 1, mr.sc[(T / 2 + 1) % 2]);
   }
-  (void)nvmem;
   // next k-step's B fragments (the next tile's first when ks == 3)
   if constexpr (ks & 1) decode_kstep<TN % TSLOTS, (TN / 2) % 2, TN % 2, KN>(mr, fb0);
   else decode_kstep<TN % TSLOTS, (TN / 2) % 2, TN % 2, KN>(mr, fb1);
@@ -1921,12 +1920,13 @@ __device__ __forceinline__ void btmx_kstep(bf16_t* const (&st)[NSA], const Rows<
     if constexpr (ks & 1) read_a<NV>(st[T], ks + 1, fa0);
     else read_a<NV>(st[T], ks + 1, fa1);
   } else {
-    // as in bt_kstep; 16 = the vector-memory ops issued after the next tile's
-    // DMA in the first round (A of tiles 2, 3, then tile 3's codes and the
-    // second pair's scales)
-    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0_vm(16));
+    // as in bt_kstep; the count is that of the first tile of the first round
+    // (the A DMAs of tiles 2 and 3, then tile 0's codes and the second pair's
+    // scales), which later tiles exceed, so they wait a little longer than
+    // needed
+    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0_vm((NSA - 2) * S::AR + 8));
     wg_barrier();
-    dma_a<Wide>(ar, st[T], t0 + T + NSA, K);
+    dma_a<S>(ar, st[T], t0 + T + NSA, K);
     read_a<NV>(st[(T + 1) % NSA], 0, fa0);
   }
   if constexpr (ks & 1) mma_q<NV>(fa1, fb1, acc);
@@ -1942,19 +1942,20 @@ __device__ __forceinline__ void btmx_kstep(bf16_t* const (&st)[NSA], const Rows<
   }
 }
 
-template <int NV, int Q>
-__device__ __forceinline__ void btmx_round(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const MxSrc& ms,
-                                           int q0, int K, MxRing& mr, bf16x8 (&fa0)[4], bf16x8 (&fa1)[4],
-                                           bf16x8 (&fb0)[4], bf16x8 (&fb1)[4], Acc<L>& acc) {
+template <class S, int NV, int Q>
+__device__ __forceinline__ void btmx_round(bf16_t* const (&st)[NSA], const Rows<S::AR>& ar, const MxSrc& ms,
+                                           int q0, int K, MxRing& mr, bf16x8 (&fa0)[S::WM],
+                                           bf16x8 (&fa1)[S::WM], bf16x8 (&fb0)[4], bf16x8 (&fb1)[4],
+                                           Acc<typename S::L>& acc) {
   if constexpr (Q < NSA * KS) {
-    btmx_kstep<NV, Q>(st, ar, ms, q0, K, mr, fa0, fa1, fb0, fb1, acc);
-    btmx_round<NV, Q + 1>(st, ar, ms, q0, K, mr, fa0, fa1, fb0, fb1, acc);
+    btmx_kstep<S, NV, Q>(st, ar, ms, q0, K, mr, fa0, fa1, fb0, fb1, acc);
+    btmx_round<S, NV, Q + 1>(st, ar, ms, q0, K, mr, fa0, fa1, fb0, fb1, acc);
   }
 }
 
-template <int NV>
-__device__ __forceinline__ void btmx_mainloop(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const MxSrc& ms,
-                                              int K, Acc<L>& acc) {
+template <class S, int NV>
+__device__ __forceinline__ void btmx_mainloop(bf16_t* const (&st)[NSA], const Rows<S::AR>& ar, const MxSrc& ms,
+                                              int K, Acc<typename S::L>& acc) {
   static_assert(NSA % TSLOTS == 0 && LEADT < TSLOTS && NSA % 2 == 0, "slot rings");
   const int nq = (int)ceil_div(K, BK) * KS;
   MxRing mr;
@@ -1964,26 +1965,31 @@ __device__ __forceinline__ void btmx_mainloop(bf16_t* const (&st)[NSA], const Ro
   static_assert(LEADT == 3, "prologue");
   load_mx_scales(ms, 0, mr.sc[0]);
 #pragma unroll
-  for (int t = 0; t < NSA; ++t) dma_a<Wide>(ar, st[t], t, K);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(AR * (NSA - 1)));
+  for (int t = 0; t < NSA; ++t) dma_a<S>(ar, st[t], t, K);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(S::AR * (NSA - 1)));
   wg_barrier();
-  bf16x8 fa0[4], fa1[4], fb0[4], fb1[4];
+  bf16x8 fa0[S::WM], fa1[S::WM], fb0[4], fb1[4];
   read_a<NV>(st[0], 0, fa0);
   decode_kstep<0, 0, 0, 0>(mr, fb0);
-  for (int q0 = 0; q0 < nq; q0 += NSA * KS) btmx_round<NV, 0>(st, ar, ms, q0, K, mr, fa0, fa1, fb0, fb1, acc);
+  for (int q0 = 0; q0 < nq; q0 += NSA * KS)
+    btmx_round<S, NV, 0>(st, ar, ms, q0, K, mr, fa0, fa1, fb0, fb1, acc);
   __builtin_amdgcn_s_waitcnt(0);
   wg_barrier();
 }
 
-template <int UNUSED = 0>
-__device__ __forceinline__ void btmx_mainloop_rows(bf16_t* const (&st)[NSA], const Rows<AR>& ar, const MxSrc& ms,
-                                                   int K, int valid_rows, Acc<L>& acc) {
-  const int nv = __builtin_amdgcn_readfirstlane(max(0, min(4, (valid_rows + 31) / 32)));
-  if (nv >= 4) btmx_mainloop<4>(st, ar, ms, K, acc);
-  else if (nv == 3) btmx_mainloop<3>(st, ar, ms, K, acc);
-  else if (nv == 2) btmx_mainloop<2>(st, ar, ms, K, acc);
-  else if (nv == 1) btmx_mainloop<1>(st, ar, ms, K, acc);
-  else btmx_mainloop<0>(st, ar, ms, K, acc);
+// btmx_mainloop with NV = the number of this block's 32-row fragments that
+// hold valid rows (one instantiation per count).
+template <class S, int NV = S::WM>
+__device__ __forceinline__ void btmx_mainloop_rows(bf16_t* const (&st)[NSA], const Rows<S::AR>& ar,
+                                                   const MxSrc& ms, int K, int valid_rows,
+                                                   Acc<typename S::L>& acc) {
+  if constexpr (NV == 0) {
+    btmx_mainloop<S, 0>(st, ar, ms, K, acc);
+  } else {
+    const int nv = __builtin_amdgcn_readfirstlane(max(0, min(S::WM, (valid_rows + 31) / 32)));
+    if (nv >= NV) btmx_mainloop<S, NV>(st, ar, ms, K, acc);
+    else btmx_mainloop_rows<S, NV - 1>(st, ar, ms, K, valid_rows, acc);
+  }
 }
 
 // Byte offsets, in the fragment-tiled MXFP4 layout of a weight with K padded
@@ -2084,23 +2090,25 @@ __global__ __launch_bounds__(bt::NW * 64) void grouped_down_bt_kernel(GroupedDow
   store_tile(acc, (bf16_t*)a.O, a.N, row_lo, n0, row_hi, a.N);
 }
 
-// grouped_glu_bt on fragment-tiled MXFP4 weights (decoded in registers).
+// grouped_glu_bt on fragment-tiled MXFP4 weights (decoded in registers), on
+// block shape S (Wide: 128 rows; Thin: 32 rows, for few rows per expert).
+template <class S>
 __global__ __launch_bounds__(bt::NW * 64) void grouped_glu_btmx_kernel(GroupedGluArgs a) {
   using namespace bt;
-  using C = L;
-  MOE_BT_RING(BM);
-  const int ntn = (int)ceil_div(a.F, BN / 2);
+  using C = typename S::L;
+  MOE_BT_RING(S::BM);
+  const int ntn = (int)ceil_div(a.F, S::BN / 2);
   int64_t Li;
   if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, Li)) return;
   int e, nt, row_lo, row_hi;
-  grouped_item<BM>(a.tile_info, ntn, a.rows_cap, Li, e, nt, row_lo, row_hi);
-  const int f0 = nt * (BN / 2);
-  Rows<AR> ar;
+  grouped_item<S::BM>(a.tile_info, ntn, a.rows_cap, Li, e, nt, row_lo, row_hi);
+  const int f0 = nt * (S::BN / 2);
+  Rows<S::AR> ar;
   ar.r[0] = ar.r[1] = make_rsrc(a.Z, (int64_t)a.T * a.ldz * 2);
 #pragma unroll
-  for (int q = 0; q < AR; ++q) {
+  for (int q = 0; q < S::AR; ++q) {
     ar.sel[q] = 0;
-    const int row = row_lo + dma_row<C, AR>(q);
+    const int row = row_lo + dma_row<C, S::AR>(q);
     uint32_t off = kOOB;
     if (row >= 0 && row < row_hi) {
       const int src = a.perm_src[row];
@@ -2120,29 +2128,30 @@ __global__ __launch_bounds__(bt::NW * 64) void grouped_glu_btmx_kernel(GroupedGl
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int f = f0 + 64 * w + 32 * (j & 1);
-    ms.poff[j] = f < a.F ? bt::mx_tiled_poff(f, Kp) : kOOB;
-    ms.soff[j] = f < a.F ? bt::mx_tiled_soff(f, Kp) : kOOB;
+    ms.poff[j] = f < a.F ? mx_tiled_poff(f, Kp) : kOOB;
+    ms.soff[j] = f < a.F ? mx_tiled_soff(f, Kp) : kOOB;
   }
   Acc<C> acc;
   acc_zero(acc);
-  btmx_mainloop_rows(st, ar, ms, a.K, row_hi - row_lo, acc);
+  btmx_mainloop_rows<S>(st, ar, ms, a.K, row_hi - row_lo, acc);
   store_glu(acc, (bf16_t*)a.H, a.F, f0, a.F, a.c, [=](int tr) -> int64_t {
     const int r = row_lo + tr;
     return (r >= 0 && r < row_hi) ? (int64_t)r : -1;
   });
 }
 
+template <class S>
 __global__ __launch_bounds__(bt::NW * 64) void grouped_down_btmx_kernel(GroupedDownArgs a) {
   using namespace bt;
-  using C = L;
-  MOE_BT_RING(BM);
-  const int ntn = (int)ceil_div(a.N, BN);
+  using C = typename S::L;
+  MOE_BT_RING(S::BM);
+  const int ntn = (int)ceil_div(a.N, S::BN);
   int64_t Li;
   if (!xcd_item((int64_t)__builtin_amdgcn_readfirstlane(a.tile_off[a.E]) * ntn, Li)) return;
   int e, nt, row_lo, row_hi;
-  grouped_item<BM>(a.tile_info, ntn, a.rows_cap, Li, e, nt, row_lo, row_hi);
-  const int n0 = nt * BN;
-  const Rows<AR> ar = a_rows_dense<C, AR>(a.H, a.ldh, max(row_lo, 0), max(row_hi, 0));
+  grouped_item<S::BM>(a.tile_info, ntn, a.rows_cap, Li, e, nt, row_lo, row_hi);
+  const int n0 = nt * S::BN;
+  const Rows<S::AR> ar = a_rows_dense<C, S::AR>(a.H, a.ldh, max(row_lo, 0), max(row_hi, 0));
   const int Kp = (int)ceil_div(a.K, 128) * 128;
   const int64_t pbytes = (int64_t)a.N * Kp / 2, sbytes = (int64_t)a.N * Kp / 32;
   MxSrc ms;
@@ -2152,12 +2161,12 @@ __global__ __launch_bounds__(bt::NW * 64) void grouped_down_btmx_kernel(GroupedD
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int n = n0 + 128 * w + 32 * j;
-    ms.poff[j] = n < a.N ? bt::mx_tiled_poff(n, Kp) : kOOB;
-    ms.soff[j] = n < a.N ? bt::mx_tiled_soff(n, Kp) : kOOB;
+    ms.poff[j] = n < a.N ? mx_tiled_poff(n, Kp) : kOOB;
+    ms.soff[j] = n < a.N ? mx_tiled_soff(n, Kp) : kOOB;
   }
   Acc<C> acc;
   acc_zero(acc);
-  btmx_mainloop_rows(st, ar, ms, a.K, row_hi - row_lo, acc);
+  btmx_mainloop_rows<S>(st, ar, ms, a.K, row_hi - row_lo, acc);
   store_tile(acc, (bf16_t*)a.O, a.N, row_lo, n0, row_hi, a.N);
 }
 
@@ -2279,15 +2288,21 @@ int multiseg_slices(int act_dtype, int M, int N, int nseg) {
 // scaled-MFMA path and with MXFP4 weights; with bf16 weights, 320 (the
 // pipelined big tiles) once the experts average at least kBigRows rows, else
 // 128 (at decode sizes the weight stream sets the pace and the smaller tiles
-// waste no DMA on padding rows).
+// waste no DMA on padding rows). Fragment-tiled MXFP4 weights: 32-row tiles
+// while the experts average fewer than kThinRows rows, else 128.
 #ifndef MOE_BIG_ROWS
 #define MOE_BIG_ROWS 64
 #endif
-constexpr int kBigRows = MOE_BIG_ROWS;
+#ifndef MOE_THIN_ROWS
+#define MOE_THIN_ROWS 16
+#endif
+constexpr int kBigRows = MOE_BIG_ROWS, kThinRows = MOE_THIN_ROWS;
 int grouped_bm(int act_dtype, int expert_w_dtype, int act_mx8, int w_tiled, int64_t rows, int E) {
   if (act_dtype == DT_F32) return 1;
   if (act_mx8) return mx8::L::BM;
-  if (w_tiled) return bt::BM;         // fragment-tiled bf16 or MXFP4 weights
+  if (w_tiled && expert_w_dtype == DT_MXFP4)
+    return rows < (int64_t)kThinRows * E ? bt::Thin::BM : bt::Wide::BM;
+  if (w_tiled) return bt::BM;         // fragment-tiled bf16 weights
   if (expert_w_dtype == DT_BF16 && rows >= (int64_t)kBigRows * E) return GroupBigCfg::BM;
   return GroupCfg::BM;
 }
@@ -2346,10 +2361,16 @@ int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream) {
   }
   if (a.H == nullptr) return -1;
   if (a.w_tiled) {
-    if (a.bm != bt::BM) return -1;
-    dim3 grid((unsigned)xcd_grid(ceil_div(a.F, bt::BN / 2) * a.max_tiles));
-    if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(grouped_glu_btmx_kernel, grid, dim3(bt::NW * 64), 0, stream, a);
-    else hipLaunchKernelGGL(grouped_glu_bt_kernel, grid, dim3(bt::NW * 64), 0, stream, a);
+    dim3 grid((unsigned)xcd_grid(ceil_div(a.F, bt::BN / 2) * a.max_tiles));   // BN: every shape's
+    static_assert(bt::Thin::BN == bt::BN && bt::Wide::BN == bt::BN, "one n-tile width");
+    if (a.Wg.dtype == DT_MXFP4 && a.bm == bt::Thin::BM)
+      hipLaunchKernelGGL(grouped_glu_btmx_kernel<bt::Thin>, grid, dim3(bt::NW * 64), 0, stream, a);
+    else if (a.Wg.dtype == DT_MXFP4 && a.bm == bt::Wide::BM)
+      hipLaunchKernelGGL(grouped_glu_btmx_kernel<bt::Wide>, grid, dim3(bt::NW * 64), 0, stream, a);
+    else if (a.Wg.dtype == DT_BF16 && a.bm == bt::BM)
+      hipLaunchKernelGGL(grouped_glu_bt_kernel, grid, dim3(bt::NW * 64), 0, stream, a);
+    else
+      return -1;
     return (int)hipGetLastError();
   }
   if (a.bm == GroupBigCfg::BM && a.bm != GroupCfg::BM) {
@@ -2377,10 +2398,15 @@ int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream) {
     return (int)hipGetLastError();
   }
   if (a.w_tiled) {
-    if (a.bm != bt::BM) return -1;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.N, bt::BN) * a.max_tiles));
-    if (a.Wo.dtype == DT_MXFP4) hipLaunchKernelGGL(grouped_down_btmx_kernel, grid, dim3(bt::NW * 64), 0, stream, a);
-    else hipLaunchKernelGGL(grouped_down_bt_kernel, grid, dim3(bt::NW * 64), 0, stream, a);
+    if (a.Wo.dtype == DT_MXFP4 && a.bm == bt::Thin::BM)
+      hipLaunchKernelGGL(grouped_down_btmx_kernel<bt::Thin>, grid, dim3(bt::NW * 64), 0, stream, a);
+    else if (a.Wo.dtype == DT_MXFP4 && a.bm == bt::Wide::BM)
+      hipLaunchKernelGGL(grouped_down_btmx_kernel<bt::Wide>, grid, dim3(bt::NW * 64), 0, stream, a);
+    else if (a.Wo.dtype == DT_BF16 && a.bm == bt::BM)
+      hipLaunchKernelGGL(grouped_down_bt_kernel, grid, dim3(bt::NW * 64), 0, stream, a);
+    else
+      return -1;
     return (int)hipGetLastError();
   }
   if (a.bm == GroupBigCfg::BM && a.bm != GroupCfg::BM) {
