@@ -44,9 +44,18 @@ namespace {
 // WGM x WGN waves (NT = 64 WGM WGN threads); a wave owns WM x WN tiles of
 // 32x32 MFMA, so the block tile is (32 WM WGM) x (32 WN WGN). K is staged BK
 // (32 or 64) at a time through an NS-stage LDS ring (NS - 1 K-tiles in flight).
-template <int WGM_, int WGN_, int WM_, int WN_, int BK_, int NS_>
+// CP: cache policy of the B (weight) loads, the buffer instructions' aux field
+// (0, or kStream where each weight slice is read by one block only).
+// Streaming loads: aux bit 1 of gfx950's buffer instructions sets `nt`, so the
+// lines are not kept for reuse. Weights read once (one row tile per expert, at
+// decode batch sizes) then stream at 6.7 TB/s instead of 6.3 (the K3 decode
+// gate/up: 5.29 against 5.66-5.88 ms); where row tiles share a weight slice
+// through L2 (prefill) it costs 3-5%.
+constexpr int kStream = 2;
+
+template <int WGM_, int WGN_, int WM_, int WN_, int BK_, int NS_, int CP_ = 0>
 struct Cfg {
-  static constexpr int WGM = WGM_, WGN = WGN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+  static constexpr int WGM = WGM_, WGN = WGN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_, CP = CP_;
   static constexpr int NW = WGM * WGN, NT = 64 * NW;
   static constexpr int BM = 32 * WM * WGM, BN = 32 * WN * WGN;
   static constexpr int CH = BK / 8;            // 16-byte chunks per LDS row
@@ -64,7 +73,7 @@ struct Cfg {
   static constexpr bool MX_OK = MXU >= 1 && MXU * NT == BN * UR;
 };
 using DenseCfg = Cfg<2, 2, 4, 2, 64, 3>;   // 256 x 128, 4 waves, 3 stages of 48 KB
-using GroupCfg = Cfg<2, 4, 2, 2, 64, 3>;   // 128 x 256, 8 waves, 3 stages of 48 KB
+using GroupCfg = Cfg<2, 4, 2, 2, 64, 3, kStream>;   // 128 x 256, 8 waves, 3 stages of 48 KB
 // Grouped expert GEMMs on bf16 weights with many rows per expert: 320 x 256,
 // 8 waves of 160 x 64, the pipelined main loop (2 stages of 72 KB; 253 VGPRs).
 #ifndef MOE_BIG_CFG
@@ -115,7 +124,7 @@ __device__ __forceinline__ int wave_m() { return (threadIdx.x >> 6) / C::WGN; }
 template <class C>
 __device__ __forceinline__ int wave_n() { return (threadIdx.x >> 6) % C::WGN; }
 
-template <class C, int N>
+template <class C, int N, int CP = 0>
 __device__ __forceinline__ void dma_rows(const Rows<N>& rs, bf16_t* tile, int k0, int K) {
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: LDS base in M0
@@ -128,7 +137,7 @@ __device__ __forceinline__ void dma_rows(const Rows<N>& rs, bf16_t* tile, int k0
     const uint32_t o = rs.off[q];
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(tile + row0 * C::BK), 16,
                                              (k < K && o != kOOB) ? o + 2u * (uint32_t)k : kOOB,
-                                             0, 0, 0);
+                                             0, 0, CP);
   }
 }
 
@@ -161,8 +170,9 @@ __device__ __forceinline__ void load_mx(const MxRows<C::MXU>& m, int k0, int K,
     const bool ok = kin && m.poff[j] != kOOB;
     const rsrc_t rp = m.sel[j] ? m.rp[1] : m.rp[0];
     const rsrc_t rsc = m.sel[j] ? m.rs[1] : m.rs[0];
-    st[j].q = bload16(rp, ok ? m.poff[j] + (uint32_t)(k / 2) : kOOB);
-    st[j].s = __builtin_amdgcn_raw_buffer_load_b8(rsc, ok ? m.soff[j] + (uint32_t)(k / 32) : kOOB, 0, 0);
+    st[j].q = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            rp, ok ? m.poff[j] + (uint32_t)(k / 2) : kOOB, 0, C::CP));
+    st[j].s = __builtin_amdgcn_raw_buffer_load_b8(rsc, ok ? m.soff[j] + (uint32_t)(k / 32) : kOOB, 0, C::CP);
   }
 }
 
@@ -249,7 +259,7 @@ __device__ __forceinline__ void stage_issue(bf16_t* buf, const Rows<C::AR>& ar, 
     store_mx<C>(buf + C::BM * C::BK, mx);
   } else {
     dma_rows<C>(ar, buf, kt * C::BK, K);
-    dma_rows<C>(br, buf + C::BM * C::BK, kt * C::BK, K);
+    dma_rows<C, C::BR, C::CP>(br, buf + C::BM * C::BK, kt * C::BK, K);
   }
 }
 
@@ -544,7 +554,7 @@ __device__ __forceinline__ void pipe_step(bf16_t* R, const bf16_t* Nx, const Row
   __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0_vm(kLoads * (C::NS - 2)));
   wg_barrier();
   dma_rows<C>(ar, R, (kt + C::NS) * C::BK, K);
-  dma_rows<C>(br, R + C::BM * C::BK, (kt + C::NS) * C::BK, K);
+  dma_rows<C, C::BR, C::CP>(br, R + C::BM * C::BK, (kt + C::NS) * C::BK, K);
   read_kstep<C, NV>(Nx, 0, f0);
   mma_kstep<C, NV>(f1, acc);
   if constexpr (kMfma > 0) {
@@ -563,7 +573,7 @@ template <class C>
 __device__ __forceinline__ void stage_dma(bf16_t* S, const Rows<C::AR>& ar, const Rows<C::BR>& br, int kt,
                                           int K) {
   dma_rows<C>(ar, S, kt * C::BK, K);
-  dma_rows<C>(br, S + C::BM * C::BK, kt * C::BK, K);
+  dma_rows<C, C::BR, C::CP>(br, S + C::BM * C::BK, kt * C::BK, K);
 }
 
 // acc += A_tile B_tile^T over k in [0, K), bf16 A and B by DMA through the
@@ -1312,6 +1322,7 @@ struct Src {
 // Stage kt into buf (LDS byte buffer). A chunk c (16 bytes) of tile row r sits
 // in slot c ^ swz_a(r); B chunk c in slot c ^ swz_b(r). B chunk c of a row's
 // stage kt is at its offset boff + bdstep kt + 16 c in either layout.
+template <int CP>
 __device__ __forceinline__ void stage_issue(uint8_t* buf, const Src& s, int kt, int K) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1333,7 +1344,7 @@ __device__ __forceinline__ void stage_issue(uint8_t* buf, const Src& s, int kt, 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rb, (lds_ptr_t)(buf + kA + row0 * kBrow), 16,
                                              (k < K && o != kOOB) ? o + s.bdstep * (uint32_t)kt + 16u * (uint32_t)c
                                                                   : kOOB,
-                                             0, 0, 0);
+                                             0, 0, CP);
   }
   // four scale bytes (k-blocks 4kt .. 4kt+3) per row; K % 128 == 0
   const bool kin = kt * kBK < K;
@@ -1342,7 +1353,7 @@ __device__ __forceinline__ void stage_issue(uint8_t* buf, const Src& s, int kt, 
                                            0, 0, 0);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(s.rsb, (lds_ptr_t)(buf + kA + kB + kS + 256 * w), 4,
                                            (kin && s.bsoff != kOOB) ? s.bsoff + s.bsstep * (uint32_t)kt : kOOB,
-                                           0, 0, 0);
+                                           0, 0, CP);
 }
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -1399,39 +1410,41 @@ __device__ __forceinline__ void mma(const Frags& f, Acc<L>& acc) {
             (int)(f.sb[j] >> (8 * (2 * s + h))));
 }
 
-template <int NV>
+template <int NV, int CP>
 __device__ __forceinline__ void ring_step(const uint8_t* R, uint8_t* W, const Src& s, int kt, int K,
                                           Acc<L>& acc) {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoads * (kNS - 2)));
   wg_barrier();
   Frags f;
   read_frags<NV>(R, f);
-  stage_issue(W, s, kt + kNS - 1, K);
+  stage_issue<CP>(W, s, kt + kNS - 1, K);
   mma<NV>(f, acc);
 }
 
-template <int NV>
+template <int NV, int CP>
 __device__ __forceinline__ void mainloop(uint8_t* s0, uint8_t* s1, uint8_t* s2, const Src& s, int K,
                                          Acc<L>& acc) {
   const int nk = (int)ceil_div(K, kBK);
-  stage_issue(s0, s, 0, K);
-  stage_issue(s1, s, 1, K);
+  stage_issue<CP>(s0, s, 0, K);
+  stage_issue<CP>(s1, s, 1, K);
   for (int kt = 0; kt < nk; kt += 3) {
-    ring_step<NV>(s0, s2, s, kt, K, acc);
-    ring_step<NV>(s1, s0, s, kt + 1, K, acc);
-    ring_step<NV>(s2, s1, s, kt + 2, K, acc);
+    ring_step<NV, CP>(s0, s2, s, kt, K, acc);
+    ring_step<NV, CP>(s1, s0, s, kt + 1, K, acc);
+    ring_step<NV, CP>(s2, s1, s, kt + 2, K, acc);
   }
   __builtin_amdgcn_s_waitcnt(0);
   wg_barrier();
 }
 
+// CP: cache policy of the weight loads (kStream at decode batch sizes)
+template <int CP>
 __device__ __forceinline__ void mainloop_rows(uint8_t* s0, uint8_t* s1, uint8_t* s2, const Src& s, int K,
                                               int valid_rows, Acc<L>& acc) {
   const int first = wave_m<L>() * 64;
   const int nv = __builtin_amdgcn_readfirstlane(max(0, min(2, (valid_rows - first + 31) / 32)));
-  if (nv >= 2) mainloop<2>(s0, s1, s2, s, K, acc);
-  else if (nv == 1) mainloop<1>(s0, s1, s2, s, K, acc);
-  else mainloop<0>(s0, s1, s2, s, K, acc);
+  if (nv >= 2) mainloop<2, CP>(s0, s1, s2, s, K, acc);
+  else if (nv == 1) mainloop<1, CP>(s0, s1, s2, s, K, acc);
+  else mainloop<0, CP>(s0, s1, s2, s, K, acc);
 }
 
 #define MOE_MX8_RING                                          \
@@ -1571,6 +1584,7 @@ __device__ __forceinline__ void store_glu_q8(const Acc<L>& acc, uint8_t* lo, uin
 // H[r] = act(zq[perm_src[r] / k] W_g[e]^T, ... W_v[e]^T) for the rows of expert e,
 // zq in MXFP8 (codes Z, scales z_scale), W_g / W_v in MXFP4. With a.hq set the
 // rows go out in MXFP8 (hq, hqs) instead of bf16 H.
+template <int CP>
 __global__ __launch_bounds__(512) void grouped_glu_mx8_kernel(GroupedGluArgs a) {
   using C = mx8::L;
   MOE_MX8_RING;
@@ -1606,7 +1620,7 @@ __global__ __launch_bounds__(512) void grouped_glu_mx8_kernel(GroupedGluArgs a) 
   mx8::b_src_glu(s, a.Wg, a.Wv, (int64_t)e * a.F, a.K, f0, a.F, a.w_tiled != 0);
   Acc<C> acc;
   acc_zero(acc);
-  mx8::mainloop_rows(mx0, mx1, mx2, s, a.K, row_hi - row_lo, acc);
+  mx8::mainloop_rows<CP>(mx0, mx1, mx2, s, a.K, row_hi - row_lo, acc);
   const auto rowmap = [=](int tr) -> int64_t {
     const int r = row_lo + tr;
     return (r >= 0 && r < row_hi) ? (int64_t)r : -1;
@@ -1617,6 +1631,7 @@ __global__ __launch_bounds__(512) void grouped_glu_mx8_kernel(GroupedGluArgs a) 
 
 // O[r] = hq[r] W_o[e]^T for the rows of expert e, hq in MXFP8 (codes H, scales
 // h_scale), W_o in MXFP4.
+template <int CP>
 __global__ __launch_bounds__(512) void grouped_down_mx8_kernel(GroupedDownArgs a) {
   using C = mx8::L;
   MOE_MX8_RING;
@@ -1641,7 +1656,7 @@ __global__ __launch_bounds__(512) void grouped_down_mx8_kernel(GroupedDownArgs a
   mx8::b_src_plain(s, a.Wo, (int64_t)e * a.N, a.K, n0, a.N, a.w_tiled != 0);
   Acc<C> acc;
   acc_zero(acc);
-  mx8::mainloop_rows(mx0, mx1, mx2, s, a.K, row_hi - row_lo, acc);
+  mx8::mainloop_rows<CP>(mx0, mx1, mx2, s, a.K, row_hi - row_lo, acc);
   store_tile(acc, (bf16_t*)a.O, a.N, row_lo, n0, row_hi, a.N);
 }
 
@@ -1670,9 +1685,9 @@ namespace bt {
 constexpr int NW = 4, BK = 64, KS = BK / 16;
 constexpr int NSA = 4;                     // A stages
 
-template <int WM_, int WN_, int LEAD_>
+template <int WM_, int WN_, int LEAD_, int CP_ = 0>
 struct Shape {
-  static constexpr int WM = WM_, WN = WN_, LEAD = LEAD_, SLOTS = LEAD_ + 1;
+  static constexpr int WM = WM_, WN = WN_, LEAD = LEAD_, SLOTS = LEAD_ + 1, CP = CP_;   // CP: weight loads
   static constexpr int BM = 32 * WM, BN = 32 * WN * NW;
   static constexpr int AR = BM / (NW * 8);          // A DMA per wave per stage (8 rows of 128 B)
   using L = Cfg<1, NW, WM, WN, BK, 2>;              // accumulator / epilogue layout
@@ -1689,7 +1704,7 @@ struct Shape {
 using Wide = Shape<4, 4, 7>;
 // 32 x 512 (one row fragment per wave) for the MXFP4 kernels at batches of few
 // rows per expert
-using Thin = Shape<1, 4, 7>;
+using Thin = Shape<1, 4, 7, kStream>;
 constexpr int BM = Wide::BM, BN = Wide::BN, AR = Wide::AR;
 using L = Wide::L;
 
@@ -1701,13 +1716,13 @@ struct BSrc {
 
 // WN B fragments (one k-step) into slot registers: fragment j of k-step q is
 // the 1 KB at off[j] + 1024 q (the second half of the fragments through r[1]).
-template <int WN>
+template <int WN, int CP>
 __device__ __forceinline__ void load_b(const BSrc<WN>& b, int q, bf16x8 (&dst)[WN]) {
 #pragma unroll
   for (int j = 0; j < WN; ++j) {
     const uint32_t o = b.off[j];
     dst[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                            b.r[j >= WN / 2 ? 1 : 0], o + 1024u * (uint32_t)q, 0, 0));
+                                            b.r[j >= WN / 2 ? 1 : 0], o + 1024u * (uint32_t)q, 0, CP));
   }
 }
 
@@ -1756,7 +1771,7 @@ __device__ __forceinline__ void bt_kstep(bf16_t* const (&st)[NSA], const Rows<S:
                                          Acc<typename S::L>& acc) {
   constexpr int T = Q / KS, ks = Q % KS;
   constexpr int slot = Q % S::SLOTS, lslot = (Q + S::LEAD) % S::SLOTS;
-  load_b<S::WN>(bs, q0 + Q + S::LEAD, br.b[lslot]);
+  load_b<S::WN, S::CP>(bs, q0 + Q + S::LEAD, br.b[lslot]);
   if constexpr (ks + 1 < KS) {
     if constexpr (ks & 1) read_a<NV>(st[T], ks + 1, fa0);
     else read_a<NV>(st[T], ks + 1, fa1);
@@ -1808,7 +1823,7 @@ __device__ __forceinline__ void bt_mainloop(bf16_t* const (&st)[NSA], const Rows
   BRing<S> br;
   // B of k-steps 0 .. LEAD-1, then A of tiles 0 .. NSA-1
 #pragma unroll
-  for (int q = 0; q < S::LEAD; ++q) load_b<S::WN>(bs, q, br.b[q]);
+  for (int q = 0; q < S::LEAD; ++q) load_b<S::WN, S::CP>(bs, q, br.b[q]);
 #pragma unroll
   for (int t = 0; t < NSA; ++t) dma_a<S>(ar, st[t], t, K);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(S::AR * (NSA - 1)));
@@ -1863,14 +1878,18 @@ struct MxRing {
   uint32_t sc[2][4];             // scale dwords of a tile pair, per fragment
 };
 
+template <int CP>
 __device__ __forceinline__ void load_mx_tile(const MxSrc& m, int t, uint4 (&dst)[4]) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dst[j] = bload16(m.rp[j >= 2 ? 1 : 0], m.poff[j] + 1024u * (uint32_t)t);
+  for (int j = 0; j < 4; ++j)
+    dst[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           m.rp[j >= 2 ? 1 : 0], m.poff[j] + 1024u * (uint32_t)t, 0, CP));
 }
+template <int CP>
 __device__ __forceinline__ void load_mx_scales(const MxSrc& m, int pr, uint32_t (&dst)[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    dst[j] = __builtin_amdgcn_raw_buffer_load_b32(m.rs[j >= 2 ? 1 : 0], m.soff[j] + 128u * (uint32_t)pr, 0, 0);
+    dst[j] = __builtin_amdgcn_raw_buffer_load_b32(m.rs[j >= 2 ? 1 : 0], m.soff[j] + 128u * (uint32_t)pr, 0, CP);
 }
 
 // bf16 B fragments of one k-step from 8 e2m1 codes (a dword) and their e8m0 scale byte.
@@ -1910,8 +1929,8 @@ __device__ __forceinline__ void btmx_kstep(bf16_t* const (&st)[NSA], const Rows<
   const int t0 = q0 / KS;                              // first tile of the round (a multiple of 4)
   constexpr int QN = Q + 1, TN = (QN / KS) % NSA, KN = QN % KS;   // the next k-step
   if constexpr (ks == 0) {
-    load_mx_tile(ms, t0 + T + LEADT, mr.p[(T + LEADT) % TSLOTS]);
-    if constexpr (T % 2 == 0) load_mx_scales(ms, (t0 + T) / 2 + 1, mr.sc[(T / 2 + 1) % 2]);
+    load_mx_tile<S::CP>(ms, t0 + T + LEADT, mr.p[(T + LEADT) % TSLOTS]);
+    if constexpr (T % 2 == 0) load_mx_scales<S::CP>(ms, (t0 + T) / 2 + 1, mr.sc[(T / 2 + 1) % 2]);
   }
   // next k-step's B fragments (the next tile's first when ks == 3)
   if constexpr (ks & 1) decode_kstep<TN % TSLOTS, (TN / 2) % 2, TN % 2, KN>(mr, fb0);
@@ -1959,11 +1978,11 @@ __device__ __forceinline__ void btmx_mainloop(bf16_t* const (&st)[NSA], const Ro
   static_assert(NSA % TSLOTS == 0 && LEADT < TSLOTS && NSA % 2 == 0, "slot rings");
   const int nq = (int)ceil_div(K, BK) * KS;
   MxRing mr;
-  load_mx_tile(ms, 0, mr.p[0]);
-  load_mx_tile(ms, 1, mr.p[1]);
-  load_mx_tile(ms, 2, mr.p[2]);
+  load_mx_tile<S::CP>(ms, 0, mr.p[0]);
+  load_mx_tile<S::CP>(ms, 1, mr.p[1]);
+  load_mx_tile<S::CP>(ms, 2, mr.p[2]);
   static_assert(LEADT == 3, "prologue");
-  load_mx_scales(ms, 0, mr.sc[0]);
+  load_mx_scales<S::CP>(ms, 0, mr.sc[0]);
 #pragma unroll
   for (int t = 0; t < NSA; ++t) dma_a<S>(ar, st[t], t, K);
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(S::AR * (NSA - 1)));
@@ -2356,7 +2375,10 @@ int launch_grouped_glu(const GroupedGluArgs& a, hipStream_t stream) {
     // h goes either to bf16 H or, as MXFP8, to hq and hqs: never to neither
     if (a.hq != nullptr ? a.hqs == nullptr : a.H == nullptr) return -1;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.F, mx8::L::BN / 2) * a.max_tiles));
-    hipLaunchKernelGGL(grouped_glu_mx8_kernel, grid, dim3(mx8::L::NT), 0, stream, a);
+    if (a.rows_cap < (int64_t)kThinRows * a.E)   // weight slices read once: stream them
+      hipLaunchKernelGGL(grouped_glu_mx8_kernel<kStream>, grid, dim3(mx8::L::NT), 0, stream, a);
+    else
+      hipLaunchKernelGGL(grouped_glu_mx8_kernel<0>, grid, dim3(mx8::L::NT), 0, stream, a);
     return (int)hipGetLastError();
   }
   if (a.H == nullptr) return -1;
@@ -2394,7 +2416,10 @@ int launch_grouped_down(const GroupedDownArgs& a, hipStream_t stream) {
     if (a.bm != mx8::L::BM || a.Wo.dtype != DT_MXFP4 || a.K % mx8::kBK) return -1;
     if (a.w_tiled && (a.N % 64 || mx8::kBRW != 64)) return -1;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.N, mx8::L::BN) * a.max_tiles));
-    hipLaunchKernelGGL(grouped_down_mx8_kernel, grid, dim3(mx8::L::NT), 0, stream, a);
+    if (a.rows_cap < (int64_t)kThinRows * a.E)
+      hipLaunchKernelGGL(grouped_down_mx8_kernel<kStream>, grid, dim3(mx8::L::NT), 0, stream, a);
+    else
+      hipLaunchKernelGGL(grouped_down_mx8_kernel<0>, grid, dim3(mx8::L::NT), 0, stream, a);
     return (int)hipGetLastError();
   }
   if (a.w_tiled) {

@@ -96,17 +96,21 @@ __global__ __launch_bounds__(256) void mfma_f8f4_kernel(int iters, float* out) {
 // Each block reads contiguous spans of U x 256 16-byte chunks (all U loads of
 // a thread issued before any is used), spans handed out grid-stride; each
 // thread folds what it read into one word that it writes, so every load is live.
-template <int U>
-__global__ __launch_bounds__(256) void hbm_read_kernel(const uint4* __restrict__ p, int64_t n16,
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// NT: nontemporal loads (streamed past the caches' normal retention)
+template <int U, bool NT>
+__global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4* __restrict__ p, int64_t n16,
                                                        uint32_t* __restrict__ out) {
   uint32_t acc = 0;
   const int64_t span = (int64_t)U * 256;
   for (int64_t b = (int64_t)blockIdx.x * span; b < n16; b += (int64_t)gridDim.x * span) {
-    uint4 v[U];
+    u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = b + u * 256 + threadIdx.x;
-      v[u] = i < n16 ? p[i] : make_uint4(0, 0, 0, 0);
+      if (i < n16) v[u] = NT ? __builtin_nontemporal_load(p + i) : p[i];
+      else v[u] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
@@ -170,14 +174,20 @@ double moe_probe_mfma_flops(int kind, int blocks, int iters) {
 }
 
 int moe_probe_hbm_read(const void* buf, int64_t bytes, int blocks, int unroll, uint32_t* out, void* stream) {
+  const int u = unroll & 0xFF;
+  const bool nt = (unroll & 0x100) != 0;
   if (buf == nullptr || out == nullptr || bytes <= 0 || bytes % 16 || blocks <= 0 ||
-      ((uintptr_t)buf & 15u) || (unroll != 4 && unroll != 8 && unroll != 16))
+      ((uintptr_t)buf & 15u) || (u != 4 && u != 8 && u != 16) || (unroll & ~0x1FF))
     return -1;
-  const uint4* p = (const uint4*)buf;
+  const u32x4* p = (const u32x4*)buf;
   hipStream_t s = (hipStream_t)stream;
-  if (unroll == 4) hipLaunchKernelGGL(hbm_read_kernel<4>, dim3(blocks), dim3(256), 0, s, p, bytes / 16, out);
-  else if (unroll == 8) hipLaunchKernelGGL(hbm_read_kernel<8>, dim3(blocks), dim3(256), 0, s, p, bytes / 16, out);
-  else hipLaunchKernelGGL(hbm_read_kernel<16>, dim3(blocks), dim3(256), 0, s, p, bytes / 16, out);
+  const int64_t n = bytes / 16;
+  if (u == 4 && !nt) hipLaunchKernelGGL((hbm_read_kernel<4, false>), dim3(blocks), dim3(256), 0, s, p, n, out);
+  else if (u == 8 && !nt) hipLaunchKernelGGL((hbm_read_kernel<8, false>), dim3(blocks), dim3(256), 0, s, p, n, out);
+  else if (!nt) hipLaunchKernelGGL((hbm_read_kernel<16, false>), dim3(blocks), dim3(256), 0, s, p, n, out);
+  else if (u == 4) hipLaunchKernelGGL((hbm_read_kernel<4, true>), dim3(blocks), dim3(256), 0, s, p, n, out);
+  else if (u == 8) hipLaunchKernelGGL((hbm_read_kernel<8, true>), dim3(blocks), dim3(256), 0, s, p, n, out);
+  else hipLaunchKernelGGL((hbm_read_kernel<16, true>), dim3(blocks), dim3(256), 0, s, p, n, out);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
