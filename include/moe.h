@@ -267,8 +267,11 @@ int moe_output(const moe_desc_t* desc, const void* x, const void* n, const moe_w
    moe_trace_enable): per device, one non-blocking stream of default priority
    and two events, created by the first call on that device and kept until
    the process ends; a per-device mutex serialises the fork / join of
-   concurrent callers. Capture of this call into a HIP graph is not tested
-   and not promised. */
+   concurrent callers. HIP graph capture: after one eager call on the device
+   (which creates that stream and its events), the call can be captured on
+   `stream` (the fork and the join become graph dependencies); replays give
+   the eager result bit for bit (checked on the K3 decode layers, bf16 and
+   MXFP8 experts, with eager calls between the replays). */
 int moe_layer_forward(const moe_desc_t* desc, const moe_weights_t* w, const void* x, void* y,
                       int32_t* topk_idx_opt, float* topk_gate_opt, int32_t* counts_opt,
                       void* ws, size_t ws_bytes, void* stream);
@@ -285,7 +288,10 @@ int moe_layer_forward(const moe_desc_t* desc, const moe_weights_t* w, const void
    that is above about 360 tokens). All calls on one GPU share its array:
    calls that overlap on one GPU (different streams, or host threads) race and
    must be serialised by the caller. Nothing in the array needs clearing
-   between calls (every kernel writes what the same call later reads). */
+   between calls (every kernel writes what the same call later reads). The
+   first call on a device resolves the array's address (hipGetSymbolAddress);
+   after it the call can be captured into a HIP graph and replayed, bit for
+   bit like the eager call (same check as moe_layer_forward). */
 int moe_layer_forward_noalloc(const moe_desc_t* desc, const moe_weights_t* w, const void* x,
                               void* y, int32_t* topk_idx_opt, float* topk_gate_opt,
                               int32_t* counts_opt, void* stream);
