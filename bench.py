@@ -242,7 +242,9 @@ def run_workload(name, args, ceilings, cpu_seconds):
         step()
     torch.cuda.synchronize()
 
-    moe.moe_trace_enable(args.steps)
+    # timed region: only the dominant stage carries HIP events (each event
+    # costs the call a few microseconds)
+    moe.moe_trace_enable(args.steps, stages=["expert_gate_up"])
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
@@ -251,8 +253,16 @@ def run_workload(name, args, ceilings, cpu_seconds):
     end.record(stream)
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
-    stages, ncalls = moe.moe_trace_read()
+    timed_stages, ncalls = moe.moe_trace_read()
+    # stage breakdown: a few more calls with every stage traced, after the timed region
+    nbreak = min(args.steps, 5)
+    moe.moe_trace_enable(nbreak)
+    for _ in range(nbreak):
+        step()
+    torch.cuda.synchronize()
+    stages, _ = moe.moe_trace_read()
     moe.moe_trace_enable(0)
+    stages["expert_gate_up"] = timed_stages["expert_gate_up"]
     log(args, f"[bench] {cfg.name}: {ms:.3f} ms/step; stages " +
         ", ".join(f"{k} {v:.3f}" for k, v in stages.items()))
 
@@ -306,6 +316,8 @@ def run_workload(name, args, ceilings, cpu_seconds):
         "touched_experts": touched,
         "stage_ms": {k: round(v, 4) for k, v in stages.items()},
         "traced_calls": ncalls,
+        "stage_ms_source": (f"expert_gate_up: HIP events of the {ncalls} timed calls (their only events); "
+                            f"other stages: {nbreak} calls traced stage by stage after the timed region"),
     }
     base = None
     if cpu_seconds > 0:

@@ -378,9 +378,15 @@ int moe_qb_bias(const moe_desc_t* desc, const float* scores, float* bias_out, fl
    is named by moe_trace_stage_name(i). Stages on the second stream (latent
    down, shared gate/up) overlap the routing stages, so the stage times can add
    up to more than the call. The events are created by the library on the
-   device current at moe_trace_enable and live until the next enable. */
+   device current at moe_trace_enable and live until the next enable.
+   moe_trace_enable_stages(max_calls, stage_mask) records only the stages whose
+   bit (1 << i) is set in stage_mask (each recorded event can cost a few
+   microseconds of the call); moe_trace_read then reports -1 for the others.
+   moe_trace_enable(n) is moe_trace_enable_stages(n, all stages). A mask with
+   bits past the last stage is MOE_ERR_INVALID_ARG. */
 #define MOE_TRACE_STAGES 10
 int moe_trace_enable(int max_calls);
+int moe_trace_enable_stages(int max_calls, unsigned stage_mask);
 int moe_trace_read(float* ms, int max_stages, int* ncalls);
 const char* moe_trace_stage_name(int stage);
 

@@ -30,7 +30,8 @@ DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "mxfp4": MOE_MXFP4}
 EXPORTS = ["moe_workspace_bytes", "moe_check_desc", "moe_route", "moe_permute", "moe_latent_down",
            "moe_expert_ffn", "moe_expert_gate_up", "moe_combine", "moe_output", "moe_layer_forward",
            "moe_layer_forward_noalloc", "moe_noalloc_scratch_bytes",
-           "moe_status_string", "moe_last_error", "moe_trace_enable", "moe_trace_read",
+           "moe_status_string", "moe_last_error", "moe_trace_enable", "moe_trace_enable_stages",
+           "moe_trace_read",
            "moe_trace_stage_name", "moe_qb_bias", "moe_quantize_mxfp8", "moe_mxfp4_tile", "moe_bf16_tile",
            "moe_bf16_tiled_bytes", "moe_mxfp4_frag_tile", "moe_mxfp4_frag_tiled_bytes"]
 MOE_TRACE_STAGES = 10
@@ -87,6 +88,7 @@ def lib():
         "moe_status_string": ([i32], ctypes.c_char_p),
         "moe_last_error": ([], ctypes.c_char_p),
         "moe_trace_enable": ([i32], i32),
+        "moe_trace_enable_stages": ([i32, ctypes.c_uint], i32),
         "moe_trace_read": ([ctypes.POINTER(ctypes.c_float), i32, ctypes.POINTER(ctypes.c_int)], i32),
         "moe_trace_stage_name": ([i32], ctypes.c_char_p),
         "moe_qb_bias": ([D, vp, vp, vp, vp], i32),
@@ -334,8 +336,16 @@ def prepare_weights(cfg, weights: dict, stream=None) -> dict:
     return out
 
 
-def moe_trace_enable(max_calls: int):
-    _check(lib().moe_trace_enable(max_calls))
+def moe_trace_enable(max_calls: int, stages=None):
+    """Trace the next max_calls layer calls: every stage, or only the named ones."""
+    if stages is None:
+        _check(lib().moe_trace_enable(max_calls))
+        return
+    names = [lib().moe_trace_stage_name(i).decode() for i in range(MOE_TRACE_STAGES)]
+    mask = 0
+    for st in stages:
+        mask |= 1 << names.index(st)
+    _check(lib().moe_trace_enable_stages(max_calls, mask))
 
 
 def moe_trace_read() -> tuple[dict, int]:

@@ -269,20 +269,20 @@ const char* const kStageNames[MOE_TRACE_STAGES] = {
     "router", "topk", "permute", "latent_down", "tile_table",
     "expert_gate_up", "expert_down", "combine", "shared_gate_up", "output"};
 
+constexpr uint32_t kAllStages = (1u << MOE_TRACE_STAGES) - 1;
+
 struct Trace {
   std::mutex mu;
   int max_calls = 0;
   int used = 0;
+  uint32_t mask = kAllStages;  // stages whose events are recorded
   std::vector<hipEvent_t> ev;  // max_calls * 2 * MOE_TRACE_STAGES
 };
 Trace g_trace;
 
-// A slot for one traced call, or -1.
-int trace_begin() {
-  std::lock_guard<std::mutex> lk(g_trace.mu);
-  if (g_trace.used >= g_trace.max_calls) return -1;
-  return g_trace.used++;
-}
+struct Marker;
+// A slot for one traced call (slot -1: not traced) and the stages it records.
+Marker trace_begin();
 
 constexpr size_t kTraceEvents = 2 * MOE_TRACE_STAGES;   // per traced call
 
@@ -291,13 +291,21 @@ constexpr size_t kTraceEvents = 2 * MOE_TRACE_STAGES;   // per traced call
 // then returns the HIP error).
 struct Marker {
   int slot;
+  uint32_t mask = 0;
+  bool on(int stage) const { return slot >= 0 && ((mask >> stage) & 1u); }
   void beg(int stage, hipStream_t s) const {
-    if (slot >= 0) (void)hipEventRecord(g_trace.ev[(size_t)slot * kTraceEvents + 2 * stage], s);
+    if (on(stage)) (void)hipEventRecord(g_trace.ev[(size_t)slot * kTraceEvents + 2 * stage], s);
   }
   void end(int stage, hipStream_t s) const {
-    if (slot >= 0) (void)hipEventRecord(g_trace.ev[(size_t)slot * kTraceEvents + 2 * stage + 1], s);
+    if (on(stage)) (void)hipEventRecord(g_trace.ev[(size_t)slot * kTraceEvents + 2 * stage + 1], s);
   }
 };
+
+Marker trace_begin() {
+  std::lock_guard<std::mutex> lk(g_trace.mu);
+  if (g_trace.used >= g_trace.max_calls) return Marker{-1, 0};
+  return Marker{g_trace.used++, g_trace.mask};
+}
 
 // ------------------------------------------------------------------------------------------
 // stages (arguments already validated)
@@ -660,10 +668,14 @@ const char* moe_trace_stage_name(int stage) {
   return (stage >= 0 && stage < MOE_TRACE_STAGES) ? kStageNames[stage] : "";
 }
 
-int moe_trace_enable(int max_calls) {
+int moe_trace_enable(int max_calls) { return moe_trace_enable_stages(max_calls, kAllStages); }
+
+int moe_trace_enable_stages(int max_calls, unsigned stage_mask) {
   g_last_error.clear();
   if (max_calls < 0 || max_calls > 100000) return fail(MOE_ERR_INVALID_ARG, "max_calls out of range");
+  if (stage_mask & ~kAllStages) return fail(MOE_ERR_INVALID_ARG, "stage_mask has bits past stage %d", MOE_TRACE_STAGES - 1);
   std::lock_guard<std::mutex> lk(g_trace.mu);
+  g_trace.mask = stage_mask;
   for (hipEvent_t e : g_trace.ev) hipEventDestroy(e);
   g_trace.ev.clear();
   g_trace.max_calls = 0;
@@ -687,10 +699,11 @@ int moe_trace_read(float* ms, int max_stages, int* ncalls) {
   std::lock_guard<std::mutex> lk(g_trace.mu);
   const int used = g_trace.used;
   const int ns = max_stages < MOE_TRACE_STAGES ? max_stages : MOE_TRACE_STAGES;
-  for (int i = 0; i < ns; ++i) ms[i] = 0.0f;
+  for (int i = 0; i < ns; ++i) ms[i] = ((g_trace.mask >> i) & 1u) ? 0.0f : -1.0f;
   for (int c = 0; c < used; ++c) {
     hipEvent_t* ev = &g_trace.ev[(size_t)c * kTraceEvents];
     for (int i = 0; i < ns; ++i) {
+      if (!((g_trace.mask >> i) & 1u)) continue;
       hipError_t e = hipEventSynchronize(ev[2 * i + 1]);
       if (e != hipSuccess) return hip_fail((int)e, "trace_read");
       float t = 0.0f;
@@ -965,7 +978,7 @@ int moe_layer_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x
   MOE_CHECK(side_stream(&sd));
   std::lock_guard<std::mutex> lk(sd->mu);
   return run_layer(d, w, x, y, topk_idx_opt, topk_gate_opt, counts_opt, ws, (hipStream_t)stream, sd,
-                   Marker{trace_begin()});
+                   trace_begin());
 }
 
 size_t moe_noalloc_scratch_bytes(void) { return kScratchBytes; }

@@ -283,6 +283,9 @@ def test_trace_read_argument_checks():
     L = moe.lib()
     assert L.moe_trace_read(None, 3, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_trace_enable(-1) == moe.MOE_ERR_INVALID_ARG
+    L.moe_trace_enable_stages.argtypes = [ctypes.c_int, ctypes.c_uint]
+    assert L.moe_trace_enable_stages(-1, 1) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_trace_enable_stages(1, 1 << moe.MOE_TRACE_STAGES) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_qb_bias_validates_before_any_launch():
