@@ -18,7 +18,7 @@
  *
  * Library state: in device memory only the fixed scratch array of
  * moe_layer_forward_noalloc (one copy per GPU the library runs on). On the
- * host: the per-device side stream of moe_layer_forward (two events with it),
+ * host: the per-device side stream of moe_layer_forward (three events with it),
  * the device address of that scratch per GPU, the trace events of
  * moe_trace_enable, and the thread-local error text of moe_last_error.
  *
@@ -260,12 +260,14 @@ int moe_output(const moe_desc_t* desc, const void* x, const void* n, const moe_w
    topk_gate [T, k], counts [E]. The latent down-projection and the shared
    experts' gate/up do not depend on the routing: they run on a second stream
    that the library keeps per device, forked from `stream` with an event at
-   the start of the call and joined back into it before the routed experts,
+   the start of the call and joined back into it before the routed experts
+   (and, at batches of at most 1024 tokens, where the shared experts' share of
+   the output GEMM is also made there, again before the output's final sum),
    so the call remains ordered on `stream` like any other work there.
    Library state behind this call (host side, the only state the library
    keeps besides the thread-local error text and the trace events of
    moe_trace_enable): per device, one non-blocking stream of default priority
-   and two events, created by the first call on that device and kept until
+   and three events, created by the first call on that device and kept until
    the process ends; a per-device mutex serialises the fork / join of
    concurrent callers. HIP graph capture: after one eager call on the device
    (which creates that stream and its events), the call can be captured on

@@ -462,9 +462,10 @@ int do_shared_glu(const moe_desc_t* d, const void* x, const moe_weights_t* w, vo
 
 // y = sum_s Hs_s W_o^s^T + n W_up^T: one GEMM whose K runs over the shared
 // experts' down projections and then W_up.
-int do_output_gemm(const moe_desc_t* d, const void* n, const moe_weights_t* w, void* y,
-                   const void* Hs, float* P, hipStream_t st, Marker mk = {-1}) {
-  mk.beg(9, st);
+// The output GEMM: y = sum_s Hs_s W_os_s^T + n W_lu^T as one GEMM over the
+// concatenated K segments (shared experts first, W_up last).
+moe::MultiSegArgs output_args(const moe_desc_t* d, const void* n, const moe_weights_t* w, void* y,
+                              const void* Hs, float* P) {
   const int S = d->n_shared, Fs = d->d_ff_shared, D = d->d_model;
   const size_t eb = elem_bytes(d->act_dtype);
   moe::MultiSegArgs m{};
@@ -481,9 +482,23 @@ int do_output_gemm(const moe_desc_t* d, const void* n, const moe_weights_t* w, v
   m.seg[S].K = d->d_latent;
   m.nseg = S + 1;
   m.M = d->T; m.N = D; m.C = y; m.ldc = D; m.act_dtype = d->act_dtype; m.P = P;
-  MOE_LAUNCH(moe::launch_multiseg(m, st), "output");
+  return m;
+}
+
+int do_output_gemm(const moe_desc_t* d, const void* n, const moe_weights_t* w, void* y,
+                   const void* Hs, float* P, hipStream_t st, Marker mk = {-1}) {
+  mk.beg(9, st);
+  MOE_LAUNCH(moe::launch_multiseg(output_args(d, n, w, y, Hs, P), st), "output");
   mk.end(9, st);
   return MOE_OK;
+}
+
+// Whether the output GEMM takes its split form (per-segment fp32 partials and
+// an ordered sum): then the shared experts' partials need only Hs and can be
+// made early, off the critical path.
+bool output_split(const moe_desc_t* d) {
+  return d->n_shared > 0 &&
+         moe::multiseg_slices(d->act_dtype, d->T, d->d_model, d->n_shared + 1) > 0;
 }
 
 int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weights_t* w, void* y,
@@ -500,7 +515,7 @@ int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weigh
 struct SideStream {
   std::mutex mu;
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr, join_out = nullptr;
 };
 constexpr int kMaxDevices = 64;
 SideStream g_side[kMaxDevices];
@@ -515,18 +530,21 @@ int side_stream(SideStream** out) {
   SideStream& sd = g_side[dev];
   if (sd.s == nullptr) {
     hipStream_t s = nullptr;
-    hipEvent_t f = nullptr, j = nullptr;
+    hipEvent_t f = nullptr, j = nullptr, jo = nullptr;
     e = hipStreamCreateWithFlags(&s, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&f, hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&j, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&jo, hipEventDisableTiming);
     if (e != hipSuccess) {
-      if (j) hipEventDestroy(j);
-      if (f) hipEventDestroy(f);
-      if (s) hipStreamDestroy(s);
+      if (jo) (void)hipEventDestroy(jo);
+      if (j) (void)hipEventDestroy(j);
+      if (f) (void)hipEventDestroy(f);
+      if (s) (void)hipStreamDestroy(s);
       return hip_fail((int)e, "side stream");
     }
     sd.fork = f;
     sd.join = j;
+    sd.join_out = jo;
     sd.s = s;
   }
   *out = &sd;
@@ -585,6 +603,15 @@ int run_layer(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* 
   mk.end(3, side);
   MOE_CHECK(do_shared_glu(d, x, w, at(ws, lw.Hs), (float*)at(ws, lw.P), side, mk));
   if (sd != nullptr) MOE_LAUNCH((int)hipEventRecord(sd->join, sd->s), "join");
+  // split output GEMM: the shared experts' partials right after their H, on
+  // the side stream, while the routed experts run (same slices, same ordered
+  // sum at the end: the same bits as making them after the combine)
+  const moe::MultiSegArgs out = output_args(d, at(ws, lw.n), w, y, at(ws, lw.Hs), (float*)at(ws, lw.P));
+  const bool early = sd != nullptr && output_split(d);
+  if (early) {
+    MOE_LAUNCH(moe::launch_multiseg_partials(out, 0, d->n_shared, sd->s), "output (shared partials)");
+    MOE_LAUNCH((int)hipEventRecord(sd->join_out, sd->s), "join");
+  }
   // routing and permutation, then (after the join) the experts
   MOE_CHECK(do_route(d, x, w->router, w->router_bias, idx, gate, (float*)at(ws, lw.s),
                      (float*)at(ws, lw.key), (float*)at(ws, lw.norms), false, st, mk));
@@ -597,6 +624,14 @@ int run_layer(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* 
   mk.beg(7, st);
   MOE_CHECK(do_combine(d, at(ws, lw.O), inv, gate, w->rms_gain, at(ws, lw.n), nullptr, st));
   mk.end(7, st);
+  if (early) {
+    mk.beg(9, st);
+    MOE_LAUNCH(moe::launch_multiseg_partials(out, d->n_shared, 1, st), "output");
+    MOE_LAUNCH((int)hipStreamWaitEvent(st, sd->join_out, 0), "join");
+    MOE_LAUNCH(moe::launch_multiseg_reduce(out, st), "output");
+    mk.end(9, st);
+    return MOE_OK;
+  }
   MOE_CHECK(do_output_gemm(d, at(ws, lw.n), w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), st, mk));
   return MOE_OK;
 }

@@ -1149,15 +1149,16 @@ __global__ __launch_bounds__(SplitCfg::NT) void glu_split_kernel(GluArgs a) {
 
 // One work item per (segment, tile); segment s writes partial slice s.
 template <bool LAST_MX>
-__global__ __launch_bounds__(SplitCfg::NT) void multiseg_split_kernel(MultiSegArgs a) {
+__global__ __launch_bounds__(SplitCfg::NT) void multiseg_split_kernel(MultiSegArgs a, int s0, int ns) {
   using C = SplitCfg;
   MOE_LDS_RING(C);
   const int ntn = (int)ceil_div(a.N, C::BN);
   const int64_t tiles = ceil_div(a.M, C::BM) * ntn;
   int64_t L;
-  if (!xcd_item(tiles * a.nseg, L)) return;
+  if (!xcd_item(tiles * ns, L)) return;
   int s, m0, n0;
   split_item(L, tiles, ntn, s, m0, n0, C::BM, C::BN);
+  s += s0;
   const Segment& sg = a.seg[s];
   const Rows<C::AR> ar = a_rows_dense<C, C::AR>(sg.A, sg.lda, m0, a.M);
   Acc<C> acc;
@@ -2458,19 +2459,35 @@ int launch_multiseg(const MultiSegArgs& a, hipStream_t stream) {
     if (a.seg[i].B.dtype == DT_MXFP4) return -1;
   const bool last_mx = a.nseg > 0 && a.seg[a.nseg - 1].B.dtype == DT_MXFP4;
   if (multiseg_slices(a.act_dtype, a.M, a.N, a.nseg) > 0) {
-    using CS = SplitCfg;
-    dim3 g2((unsigned)xcd_grid(ceil_div(a.N, CS::BN) * ceil_div(a.M, CS::BM) * a.nseg));
-    if (last_mx) hipLaunchKernelGGL(multiseg_split_kernel<true>, g2, dim3(SplitCfg::NT), 0, stream, a);
-    else hipLaunchKernelGGL(multiseg_split_kernel<false>, g2, dim3(SplitCfg::NT), 0, stream, a);
-    const int64_t n4 = (int64_t)a.M * a.N / 4;
-    hipLaunchKernelGGL(reduce_store_kernel, dim3(reduce_blocks(n4)), dim3(256), 0, stream, a.P,
-                       a.nseg, a.M, a.N, (bf16_t*)a.C, a.ldc);
-    return (int)hipGetLastError();
+    const int e = launch_multiseg_partials(a, 0, a.nseg, stream);
+    return e != 0 ? e : launch_multiseg_reduce(a, stream);
   }
   if (last_mx)
     hipLaunchKernelGGL(multiseg_kernel<true>, grid, dim3(DenseCfg::NT), 0, stream, a);
   else
     hipLaunchKernelGGL(multiseg_kernel<false>, grid, dim3(DenseCfg::NT), 0, stream, a);
+  return (int)hipGetLastError();
+}
+
+int launch_multiseg_partials(const MultiSegArgs& a, int s0, int ns, hipStream_t stream) {
+  if (a.M == 0 || ns == 0) return 0;
+  if (multiseg_slices(a.act_dtype, a.M, a.N, a.nseg) == 0 || s0 < 0 || s0 + ns > a.nseg) return -1;
+  for (int i = 0; i + 1 < a.nseg; ++i)
+    if (a.seg[i].B.dtype == DT_MXFP4) return -1;   // only the last segment may be MXFP4
+  const bool last_mx = a.seg[a.nseg - 1].B.dtype == DT_MXFP4;
+  using CS = SplitCfg;
+  dim3 g2((unsigned)xcd_grid(ceil_div(a.N, CS::BN) * ceil_div(a.M, CS::BM) * ns));
+  if (last_mx) hipLaunchKernelGGL(multiseg_split_kernel<true>, g2, dim3(CS::NT), 0, stream, a, s0, ns);
+  else hipLaunchKernelGGL(multiseg_split_kernel<false>, g2, dim3(CS::NT), 0, stream, a, s0, ns);
+  return (int)hipGetLastError();
+}
+
+int launch_multiseg_reduce(const MultiSegArgs& a, hipStream_t stream) {
+  if (a.M == 0) return 0;
+  if (multiseg_slices(a.act_dtype, a.M, a.N, a.nseg) == 0) return -1;
+  const int64_t n4 = (int64_t)a.M * a.N / 4;
+  hipLaunchKernelGGL(reduce_store_kernel, dim3(reduce_blocks(n4)), dim3(256), 0, stream, a.P,
+                     a.nseg, a.M, a.N, (bf16_t*)a.C, a.ldc);
   return (int)hipGetLastError();
 }
 

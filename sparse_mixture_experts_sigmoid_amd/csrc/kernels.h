@@ -212,6 +212,13 @@ struct MultiSegArgs {
   float* P;                    // multiseg_slices(...) * M * N fp32 when that is > 0
 };
 int launch_multiseg(const MultiSegArgs& a, hipStream_t stream);
+// The split form in two parts (only when multiseg_slices(...) > 0): the fp32
+// partial products of segments s0 .. s0 + ns - 1 into P[s] (each segment's
+// own slice), then the ordered sum of all slices into C. launch_multiseg is
+// partials(0, nseg) followed by reduce; the parts may run on different
+// streams (the caller orders them).
+int launch_multiseg_partials(const MultiSegArgs& a, int s0, int ns, hipStream_t stream);
+int launch_multiseg_reduce(const MultiSegArgs& a, hipStream_t stream);
 
 // fp32-activation variants of the GEMM launchers (gemm_f32.hip).
 int launch_dense_f32(const DenseArgs& a, hipStream_t stream);
