@@ -120,15 +120,72 @@ __device__ __forceinline__ uint32_t key_code(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// One DPP step of a 64-bit value: lane i gets the value of the lane that
+// dpp control CTRL names within its row of 16 (every lane active).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Maximum over the wave (all 64 lanes active), the same value on every lane:
+// within each row of 16 lanes by DPP (swap neighbours, swap pairs, mirror
+// each half row, mirror the row: every lane then holds its row's maximum),
+// then across the four rows from one lane of each.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<0xB1>(v));    // quad_perm [1, 0, 3, 2]
+  v = max_u64(v, dpp_u64<0x4E>(v));    // quad_perm [2, 3, 0, 1]
+  v = max_u64(v, dpp_u64<0x141>(v));   // row_half_mirror
+  v = max_u64(v, dpp_u64<0x140>(v));   // row_mirror
+  return max_u64(max_u64(readlane_u64(v, 0), readlane_u64(v, 16)),
+                 max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
+}
+
+// A lane's two largest packed keys below `below` among its N slots (0: none;
+// keys are unique), with the values that ride along.
+template <int N, bool S>
+__device__ __forceinline__ void top2_below(const uint64_t (&v)[N], const float (&sv)[N], uint64_t below,
+                                           uint64_t& b1, float& s1, uint64_t& b2, float& s2) {
+  b1 = 0ull; b2 = 0ull; s1 = 0.0f; s2 = 0.0f;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
+  for (int i = 0; i < N; ++i) {
+    const uint64_t c = v[i] < below ? v[i] : 0ull;
+    const bool gt1 = c > b1, gt2 = c > b2;   // selects, not branches (keeps b1, b2 in registers)
+    b2 = gt1 ? b1 : gt2 ? c : b2;
+    b1 = gt1 ? c : b1;
+    if constexpr (S) {
+      s2 = gt1 ? s1 : gt2 ? sv[i] : s2;
+      s1 = gt1 ? sv[i] : s1;
+    }
   }
-  return v;
+}
+
+// k rounds of "take the wave's largest key" over per-lane slots, without
+// rescanning every slot each round: each lane keeps its two largest
+// remaining keys (b1 > b2). The lane whose b1 is taken moves b2 up while b2
+// is known to be its next key, and otherwise rescans its slots below the key
+// just taken (every slot above it is gone: a lane gives up its keys in
+// descending order). S: the value sv[i] rides along with key v[i]. Returns
+// true on the lane that held m.
+template <int N, bool S>
+__device__ __forceinline__ bool walk_take(const uint64_t (&v)[N], const float (&sv)[N], uint64_t m,
+                                          uint64_t& b1, float& s1, uint64_t& b2, float& s2,
+                                          bool& next_known) {
+  if (b1 != m) return false;   // m is held by exactly one lane's b1
+  if (next_known) {
+    b1 = b2; s1 = s2; b2 = 0ull; next_known = false;
+  } else {
+    top2_below<N, S>(v, sv, m, b1, s1, b2, s2);
+    next_known = true;
+  }
+  return true;
 }
 
 // One wave64 per token. Each lane holds NPER packed keys
@@ -292,17 +349,15 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coe
     }
   }
   uint64_t kth = 0;
-  for (int j = 0; j < a.k; ++j) {
-    uint64_t m = 0;
-#pragma unroll
-    for (int i = 0; i < NPER; ++i) m = lo_code[i] > m ? lo_code[i] : m;
-    m = wave_max_u64(m);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)m);
-#pragma unroll
-    for (int i = 0; i < NPER; ++i)
-      if (lo_code[i] == m) lo_code[i] = 0ull;   // codes are unique: one owner
-    kth = m;
-    (void)e;
+  {
+    uint64_t b1, b2;
+    float s1, s2;
+    bool next_known = true;
+    top2_below<NPER, false>(lo_code, key_hi, ~0ull, b1, s1, b2, s2);   // no values ride along
+    for (int j = 0; j < a.k; ++j) {
+      kth = wave_max_u64(b1);
+      walk_take<NPER, false>(lo_code, key_hi, kth, b1, s1, b2, s2, next_known);
+    }
   }
   const uint32_t kc = (uint32_t)(kth >> 32);  // invert the order-preserving code of L_k
   const float Lk = __uint_as_float((kc & 0x80000000u) ? (kc & 0x7FFFFFFFu) : ~kc);
@@ -321,7 +376,6 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coe
 
   // 2b. fixed-order logits of the candidates; candidate p = 64 r + lane ends
   //     in code[r], sc[r] of this lane
-  const rsrc_t wres = make_rsrc(a.W, (int64_t)a.E * a.d * 2);
   const rsrc_t xres = make_rsrc((const bf16_t*)a.x + (int64_t)t * a.d, (int64_t)a.d * 2);
   const int nchunks = a.d / kChunk;         // d % kChunk == 0 (checked by the launcher)
   uint64_t code[NPER];
@@ -331,13 +385,27 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coe
   const int npass = (int)ceil_div(ncand, 64);
   if constexpr (DIRECT) {
     extern __shared__ __align__(16) float xs_dyn[];
-    for (int i = lane; i < a.d / 8; i += 64) {
-      const uint4 v = bload16(xres, (uint32_t)i * 16u);
-      const uint32_t xv[4] = {v.x, v.y, v.z, v.w};
+    // x to LDS: a lane's 16-byte pieces (d / 512 of them) loaded 16 at a
+    // time, all in flight before the first is widened
+    constexpr int kXU = 16;
+    for (int i0 = lane; i0 < a.d / 8; i0 += 64 * kXU) {
+      uint4 xq[kXU];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        xs_dyn[8 * i + 2 * m] = __uint_as_float(xv[m] << 16);
-        xs_dyn[8 * i + 2 * m + 1] = __uint_as_float(xv[m] & 0xFFFF0000u);
+      for (int u = 0; u < kXU; ++u) {
+        const int i = i0 + 64 * u;
+        xq[u] = bload16(xres, i < a.d / 8 ? (uint32_t)i * 16u : kOOB);
+      }
+#pragma unroll
+      for (int u = 0; u < kXU; ++u) {
+        const int i = i0 + 64 * u;
+        if (i < a.d / 8) {
+          const uint32_t xv[4] = {xq[u].x, xq[u].y, xq[u].z, xq[u].w};
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            xs_dyn[8 * i + 2 * m] = __uint_as_float(xv[m] << 16);
+            xs_dyn[8 * i + 2 * m + 1] = __uint_as_float(xv[m] & 0xFFFF0000u);
+          }
+        }
       }
     }
     wave_sync();
@@ -347,13 +415,25 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coe
       const int ce = cand_e[p];              // in range: p < 64 NPER
       const uint32_t base = p < ncand ? (uint32_t)ce * (uint32_t)a.d * 2u : kOOB;
       uint4 q0[8], q1[8], q2[8], q3[8];
+      // chunk c through a resource that starts c 64-k chunks into W (scalar
+      // work only; a lane's offset is its row, or kOOB): past the row's end
+      // (the prefetch beyond the last chunk) a lane reads the next row, or
+      // zeros past W's end, and never uses what it read
+      const int64_t wbytes = (int64_t)a.E * a.d * 2;
       auto load = [&](uint4 (&q)[8], int c) {
+        const int64_t skip = 128 * (int64_t)c;
+        const rsrc_t rc = make_rsrc((const uint8_t*)a.W + skip, wbytes > skip ? wbytes - skip : 0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          q[j] = bload16(wres, (base != kOOB && c < nch) ? base + 128u * (uint32_t)c + 16u * (uint32_t)j : kOOB);
+        for (int j = 0; j < 8; ++j) q[j] = bload16(rc, base + 16u * (uint32_t)j);
       };
       float acc = 0.0f;
+      // scheduling barriers at each chunk (and between the first loads) keep
+      // the widening of a chunk's W after the chunk before it and the loads in
+      // chunk order, so that each chunk waits for its own loads only (left
+      // free, the scheduler hoists all four chunks' widening to the loop top
+      // and every round waits for every load in flight)
       auto chain = [&](uint4 (&q)[8], int c) {
+        __builtin_amdgcn_sched_barrier(0);
         float4 xv[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) xv[j] = *(const float4*)(xs_dyn + 64 * c + 4 * j);
@@ -373,8 +453,11 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coe
         load(q, c + 4);
       };
       load(q0, 0);
+      __builtin_amdgcn_sched_barrier(0);
       load(q1, 1);
+      __builtin_amdgcn_sched_barrier(0);
       load(q2, 2);
+      __builtin_amdgcn_sched_barrier(0);
       load(q3, 3);
       for (int c = 0; c < nch; c += 4) {
         chain(q0, c);
@@ -405,11 +488,15 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coe
     }
     const uint32_t xoff = lane < kPPR ? (uint32_t)lane * 16u : kOOB;
     uint4 pw[kNJ], px;
+    // chunk c (< nchunks) through resources that start at its first k (scalar
+    // work only; the lanes' offsets stay as they are)
     auto load_chunk = [&](int c) {
-      const uint32_t k0b = 2u * (uint32_t)(c * kChunk);
+      const int64_t k0b = 2 * (int64_t)c * kChunk;
+      const rsrc_t wc = make_rsrc((const uint8_t*)a.W + k0b, (int64_t)a.E * a.d * 2 - k0b);
+      const rsrc_t xc = make_rsrc((const uint8_t*)a.x + (int64_t)t * a.d * 2 + k0b, (int64_t)a.d * 2 - k0b);
 #pragma unroll
-      for (int j = 0; j < kNJ; ++j) pw[j] = bload16(wres, roff[j] != kOOB ? roff[j] + k0b : kOOB);
-      px = bload16(xres, xoff != kOOB ? xoff + k0b : kOOB);
+      for (int j = 0; j < kNJ; ++j) pw[j] = bload16(wc, roff[j]);
+      px = bload16(xc, xoff);
     };
     load_chunk(0);
     float acc = 0.0f;
@@ -462,32 +549,35 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coe
   int32_t* ir = a.idx + (int64_t)t * a.k;
   float* gr = a.gate + (int64_t)t * a.k;
   float total = 0.0f;
+  uint64_t b1, b2;
+  float s1, s2;
+  bool next_known = true;
+  top2_below<NPER, true>(code, sc, ~0ull, b1, s1, b2, s2);
+  float my_s = 0.0f;
   for (int j0 = 0; j0 < a.k; j0 += 64) {
     const int jn = min(64, a.k - j0);
     int my_e = 0;
     for (int j = 0; j < jn; ++j) {
-      uint64_t m = 0;
-#pragma unroll
-      for (int i = 0; i < NPER; ++i) m = code[i] > m ? code[i] : m;
-      const uint64_t wmax = wave_max_u64(m);
-      if (wmax != 0ull) {
-#pragma unroll
-        for (int i = 0; i < NPER; ++i)
-          if (code[i] == wmax) { sel_s[j] = sc[i]; code[i] = 0ull; }
-      }
+      const uint64_t wmax = wave_max_u64(b1);
+      const float s_taken = s1;
+      if (wmax != 0ull && walk_take<NPER, true>(code, sc, wmax, b1, s1, b2, s2, next_known)) sel_s[j] = s_taken;
       if (lane == j) my_e = (int)(0xFFFFFFFFu - (uint32_t)wmax);
     }
     wave_sync();
-    const float my_s = lane < jn ? sel_s[lane] : 0.0f;
+    my_s = lane < jn ? sel_s[lane] : 0.0f;
     if (lane < jn) {
       ir[j0 + lane] = my_e;
-      gr[j0 + lane] = my_s;  // the score for now; divided by the sum below
+      if (a.k > 64) gr[j0 + lane] = my_s;  // the score for now; divided by the sum below
     }
-    for (int j = 0; j < jn; ++j) total = __fadd_rn(total, __shfl(my_s, j, 64));
+    for (int j = 0; j < jn; ++j) total = __fadd_rn(total, sel_s[j]);   // slot order
     wave_sync();
   }
-  // slot j was written by lane j % 64 above (the same thread reads it back)
-  for (int j = lane; j < a.k; j += 64) gr[j] = __fdiv_rn(gr[j], total);
+  if (a.k <= 64) {
+    if (lane < a.k) gr[lane] = __fdiv_rn(my_s, total);
+  } else {
+    // slot j was written by lane j % 64 above (the same thread reads it back)
+    for (int j = lane; j < a.k; j += 64) gr[j] = __fdiv_rn(gr[j], total);
+  }
 }
 
 }  // namespace
