@@ -75,12 +75,21 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ block_co
   __shared__ int32_t sh[4096];
   __shared__ int32_t part[1024];
   __shared__ int32_t total;
+  // a thread per expert walks the token blocks in order, kScanU blocks' counts
+  // loaded at a time
+  constexpr int kScanU = 16;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int32_t run = 0;
-    for (int b = 0; b < nblk; ++b) {
-      int32_t c = block_counts[(int64_t)b * E + e];
-      block_counts[(int64_t)b * E + e] = run;
-      run += c;
+    for (int b0 = 0; b0 < nblk; b0 += kScanU) {
+      int32_t c[kScanU];
+#pragma unroll
+      for (int u = 0; u < kScanU; ++u) c[u] = b0 + u < nblk ? block_counts[(int64_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanU; ++u)
+        if (b0 + u < nblk) {
+          block_counts[(int64_t)(b0 + u) * E + e] = run;
+          run += c[u];
+        }
     }
     sh[e] = run;
     counts[e] = run;
@@ -91,7 +100,14 @@ __global__ __launch_bounds__(1024) void perm_scan(int32_t* __restrict__ block_co
   if (threadIdx.x == 0) offsets[E] = total;
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     const int32_t base = sh[e];
-    for (int b = 0; b < nblk; ++b) block_counts[(int64_t)b * E + e] += base;
+    for (int b0 = 0; b0 < nblk; b0 += kScanU) {
+      int32_t c[kScanU];
+#pragma unroll
+      for (int u = 0; u < kScanU; ++u) c[u] = b0 + u < nblk ? block_counts[(int64_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanU; ++u)
+        if (b0 + u < nblk) block_counts[(int64_t)(b0 + u) * E + e] = c[u] + base;
+    }
   }
 }
 
@@ -107,18 +123,39 @@ __global__ __launch_bounds__(256) void perm_scatter(const int32_t* __restrict__ 
   const int lane = threadIdx.x;
   const int t0 = blockIdx.x * kPermTokens;
   const int t1 = min(T, t0 + kPermTokens);
-  for (int t = t0; t < t1; ++t) {
-    for (int j = lane; j < k; j += 64) {
-      const int64_t a = (int64_t)t * k + j;
-      const int e = idx[a];
-      if (e >= 0 && e < E) {
-        const int p = atomicAdd(&pos[e], 1);
-        perm_src[p] = (int32_t)a;
-        inv_pos[a] = p;
-      } else {
-        inv_pos[a] = -1;
-      }
+  const auto place = [&](int64_t a, int e) {
+    if (e >= 0 && e < E) {
+      const int p = atomicAdd(&pos[e], 1);
+      perm_src[p] = (int32_t)a;
+      inv_pos[a] = p;
+    } else {
+      inv_pos[a] = -1;
     }
+  };
+  if (k <= 64) {
+    // lane j < k takes slot j of every token. All of the block's expert ids
+    // are loaded before the walk and every store waits until after it, so
+    // the walk (in token order) waits on its LDS fetch-adds only.
+    int32_t ev[kPermTokens], pv[kPermTokens];
+#pragma unroll
+    for (int i = 0; i < kPermTokens; ++i)
+      ev[i] = (lane < k && t0 + i < t1) ? idx[(int64_t)(t0 + i) * k + lane] : -1;
+#pragma unroll
+    for (int i = 0; i < kPermTokens; ++i)
+      pv[i] = (ev[i] >= 0 && ev[i] < E) ? atomicAdd(&pos[ev[i]], 1) : -1;
+#pragma unroll
+    for (int i = 0; i < kPermTokens; ++i)
+      if (t0 + i < t1 && lane < k) {
+        const int64_t a = (int64_t)(t0 + i) * k + lane;
+        if (pv[i] >= 0) perm_src[pv[i]] = (int32_t)a;
+        inv_pos[a] = pv[i];
+      }
+  } else {
+    for (int t = t0; t < t1; ++t)
+      for (int j = lane; j < k; j += 64) {
+        const int64_t a = (int64_t)t * k + j;
+        place(a, idx[a]);
+      }
   }
 }
 
