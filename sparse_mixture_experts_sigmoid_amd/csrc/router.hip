@@ -148,15 +148,15 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
                  max_u64(readlane_u64(v, 32), readlane_u64(v, 48)));
 }
 
-// A lane's two largest packed keys below `below` among its N slots (0: none;
-// keys are unique), with the values that ride along.
-template <int N, bool S>
+// A lane's two largest packed keys among its N slots (0: none; keys are
+// unique), with the values that ride along; BELOW: only keys below `below`.
+template <int N, bool S, bool BELOW>
 __device__ __forceinline__ void top2_below(const uint64_t (&v)[N], const float (&sv)[N], uint64_t below,
                                            uint64_t& b1, float& s1, uint64_t& b2, float& s2) {
   b1 = 0ull; b2 = 0ull; s1 = 0.0f; s2 = 0.0f;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const uint64_t c = v[i] < below ? v[i] : 0ull;
+    const uint64_t c = (!BELOW || v[i] < below) ? v[i] : 0ull;
     const bool gt1 = c > b1, gt2 = c > b2;   // selects, not branches (keeps b1, b2 in registers)
     b2 = gt1 ? b1 : gt2 ? c : b2;
     b1 = gt1 ? c : b1;
@@ -182,7 +182,7 @@ __device__ __forceinline__ bool walk_take(const uint64_t (&v)[N], const float (&
   if (next_known) {
     b1 = b2; s1 = s2; b2 = 0ull; next_known = false;
   } else {
-    top2_below<N, S>(v, sv, m, b1, s1, b2, s2);
+    top2_below<N, S, true>(v, sv, m, b1, s1, b2, s2);
     next_known = true;
   }
   return true;
@@ -353,7 +353,7 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coe
     uint64_t b1, b2;
     float s1, s2;
     bool next_known = true;
-    top2_below<NPER, false>(lo_code, key_hi, ~0ull, b1, s1, b2, s2);   // no values ride along
+    top2_below<NPER, false, false>(lo_code, key_hi, 0ull, b1, s1, b2, s2);   // no values ride along
     for (int j = 0; j < a.k; ++j) {
       kth = wave_max_u64(b1);
       walk_take<NPER, false>(lo_code, key_hi, kth, b1, s1, b2, s2, next_known);
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(64) void select_kernel(SelectArgs a, float beta_coe
   uint64_t b1, b2;
   float s1, s2;
   bool next_known = true;
-  top2_below<NPER, true>(code, sc, ~0ull, b1, s1, b2, s2);
+  top2_below<NPER, true, false>(code, sc, 0ull, b1, s1, b2, s2);
   float my_s = 0.0f;
   for (int j0 = 0; j0 < a.k; j0 += 64) {
     const int jn = min(64, a.k - j0);
