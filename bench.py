@@ -187,13 +187,14 @@ def measure_ceilings(stream):
         t = timed(launch)
         res[key] = round(L.moe_probe_mfma_flops(kind, blocks, iters) / t / 1e12, 1)
     # the best of a few launch shapes (blocks per CU x loads in flight per
-    # thread, plain or nontemporal loads)
+    # thread, plain or nontemporal loads, spans grid-stride or one contiguous
+    # part per block)
     nbytes = 4 << 30
     buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
     sink = torch.empty(256 * 16 * 256, dtype=torch.int32, device="cuda:0")
     best = 0.0
-    for per_cu in (4, 8, 16):
-        for unroll in (4, 8, 16, 0x100 | 8, 0x100 | 16):
+    for per_cu in (1, 2, 4, 8):
+        for unroll in (4, 8, 16, 0x100 | 8, 0x100 | 16, 0x200 | 8, 0x200 | 16, 0x300 | 8, 0x300 | 16):
             def read(per_cu=per_cu, unroll=unroll):
                 if L.moe_probe_hbm_read(ctypes.c_void_p(buf.data_ptr()), nbytes, 256 * per_cu, unroll,
                                         ctypes.c_void_p(sink.data_ptr()), sh) != 0:

@@ -32,7 +32,9 @@ double moe_probe_mfma_flops(int kind, int blocks, int iters);
 /* Streaming read of `bytes` (a multiple of 16; buf 16-byte aligned) by
    `blocks` workgroups of 256 threads, each thread with `unroll & 0xFF` (4, 8
    or 16) 16-byte loads in flight, nontemporal loads when unroll has bit
-   0x100; out: blocks * 256 words written. */
+   0x100. Spans of the buffer go to the blocks grid-stride, or, with bit
+   0x200, each block reads one contiguous part (1/blocks of the buffer) from
+   start to end. out: blocks * 256 words written. */
 int moe_probe_hbm_read(const void* buf, int64_t bytes, int blocks, int unroll, uint32_t* out, void* stream);
 
 #ifdef __cplusplus

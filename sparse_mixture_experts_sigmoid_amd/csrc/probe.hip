@@ -98,18 +98,25 @@ __global__ __launch_bounds__(256) void mfma_f8f4_kernel(int iters, float* out) {
 // thread folds what it read into one word that it writes, so every load is live.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// NT: nontemporal loads (streamed past the caches' normal retention)
-template <int U, bool NT>
+// NT: nontemporal loads (streamed past the caches' normal retention).
+// BLK: each block reads one contiguous part of the buffer (gridDim parts, in
+// spans of U x 256 chunks) from its start to its end, as a GEMM block streams
+// its own weight slice; otherwise the spans are handed out grid-stride.
+template <int U, bool NT, bool BLK>
 __global__ __launch_bounds__(256) void hbm_read_kernel(const u32x4* __restrict__ p, int64_t n16,
                                                        uint32_t* __restrict__ out) {
   uint32_t acc = 0;
   const int64_t span = (int64_t)U * 256;
-  for (int64_t b = (int64_t)blockIdx.x * span; b < n16; b += (int64_t)gridDim.x * span) {
+  const int64_t part = (n16 + (int64_t)gridDim.x * span - 1) / ((int64_t)gridDim.x * span) * span;
+  const int64_t b0 = BLK ? (int64_t)blockIdx.x * part : (int64_t)blockIdx.x * span;
+  const int64_t b1 = BLK ? (b0 + part < n16 ? b0 + part : n16) : n16;
+  const int64_t step = BLK ? span : (int64_t)gridDim.x * span;
+  for (int64_t b = b0; b < b1; b += step) {
     u32x4 v[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = b + u * 256 + threadIdx.x;
-      if (i < n16) v[u] = NT ? __builtin_nontemporal_load(p + i) : p[i];
+      if (i < b1) v[u] = NT ? __builtin_nontemporal_load(p + i) : p[i];
       else v[u] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
@@ -175,19 +182,27 @@ double moe_probe_mfma_flops(int kind, int blocks, int iters) {
 
 int moe_probe_hbm_read(const void* buf, int64_t bytes, int blocks, int unroll, uint32_t* out, void* stream) {
   const int u = unroll & 0xFF;
-  const bool nt = (unroll & 0x100) != 0;
+  const bool nt = (unroll & 0x100) != 0, blk = (unroll & 0x200) != 0;
   if (buf == nullptr || out == nullptr || bytes <= 0 || bytes % 16 || blocks <= 0 ||
-      ((uintptr_t)buf & 15u) || (u != 4 && u != 8 && u != 16) || (unroll & ~0x1FF))
+      ((uintptr_t)buf & 15u) || (u != 4 && u != 8 && u != 16) || (unroll & ~0x3FF))
     return -1;
   const u32x4* p = (const u32x4*)buf;
   hipStream_t s = (hipStream_t)stream;
   const int64_t n = bytes / 16;
-  if (u == 4 && !nt) hipLaunchKernelGGL((hbm_read_kernel<4, false>), dim3(blocks), dim3(256), 0, s, p, n, out);
-  else if (u == 8 && !nt) hipLaunchKernelGGL((hbm_read_kernel<8, false>), dim3(blocks), dim3(256), 0, s, p, n, out);
-  else if (!nt) hipLaunchKernelGGL((hbm_read_kernel<16, false>), dim3(blocks), dim3(256), 0, s, p, n, out);
-  else if (u == 4) hipLaunchKernelGGL((hbm_read_kernel<4, true>), dim3(blocks), dim3(256), 0, s, p, n, out);
-  else if (u == 8) hipLaunchKernelGGL((hbm_read_kernel<8, true>), dim3(blocks), dim3(256), 0, s, p, n, out);
-  else hipLaunchKernelGGL((hbm_read_kernel<16, true>), dim3(blocks), dim3(256), 0, s, p, n, out);
+#define MOE_HBM_READ(U, NT, BLK) \
+  hipLaunchKernelGGL((hbm_read_kernel<U, NT, BLK>), dim3(blocks), dim3(256), 0, s, p, n, out)
+#define MOE_HBM_READ_U(NT, BLK)         \
+  do {                                  \
+    if (u == 4) MOE_HBM_READ(4, NT, BLK);   \
+    else if (u == 8) MOE_HBM_READ(8, NT, BLK); \
+    else MOE_HBM_READ(16, NT, BLK);        \
+  } while (0)
+  if (!nt && !blk) MOE_HBM_READ_U(false, false);
+  else if (nt && !blk) MOE_HBM_READ_U(true, false);
+  else if (!nt) MOE_HBM_READ_U(false, true);
+  else MOE_HBM_READ_U(true, true);
+#undef MOE_HBM_READ_U
+#undef MOE_HBM_READ
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 

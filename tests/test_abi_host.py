@@ -55,7 +55,7 @@ def test_probe_library_exports_and_validates():
     assert L.moe_probe_hbm_read(FAKE, 24, 1, 8, FAKE, None) == -1
     assert L.moe_probe_hbm_read(MIS, 32, 1, 8, FAKE, None) == -1
     assert L.moe_probe_hbm_read(FAKE, 32, 1, 5, FAKE, None) == -1
-    assert L.moe_probe_hbm_read(FAKE, 32, 1, 0x208, FAKE, None) == -1
+    assert L.moe_probe_hbm_read(FAKE, 32, 1, 0x408, FAKE, None) == -1
     assert L.moe_probe_mfma_flops(0, 1, 1) == 4 * 4 * 2 * 32 * 32 * 16
     assert L.moe_probe_mfma_flops(1, 2, 3) == 2 * 3 * 4 * 4 * 2 * 32 * 32 * 64
 
