@@ -75,6 +75,13 @@ ROUTE_CASES = [
     LayerConfig("r3", T=130, d=160, d_lat=32, E=200, k=70, F=32, S=0, Fs=32, seed=23),    # k > 64
     LayerConfig("r4", T=33, d=64, d_lat=32, E=1, k=1, F=32, S=0, Fs=32, seed=24,
                 act="f32", expert_w="f32", latent_w="f32", dense_w="f32"),
+    # wide expert counts: 17-32 and 33-64 keys per lane in the recheck, with
+    # the register-streamed form (few tokens, d % 256 == 0), the LDS-staged
+    # form (d % 256 != 0, or 2048 tokens and more) and k > 64
+    LayerConfig("r5", T=70, d=256, d_lat=32, E=1500, k=24, F=32, S=0, Fs=32, seed=27),
+    LayerConfig("r6", T=40, d=192, d_lat=32, E=3000, k=100, F=32, S=0, Fs=32, seed=28),
+    LayerConfig("r7", T=50, d=512, d_lat=32, E=4000, k=32, F=32, S=0, Fs=32, seed=29),
+    LayerConfig("r8", T=2100, d=128, d_lat=32, E=2500, k=16, F=32, S=0, Fs=32, seed=30),
 ]
 
 
