@@ -119,6 +119,7 @@ struct Plan {
 struct LayerWs {
   size_t s, key, norms, idx, gate, counts, offsets, perm, inv, blk, z, tile_off, tile_info, H, O, n, Hs, P;
   size_t zq, zqs, hq, hqs;   // MXFP8 z and h (codes, scales) of the scaled-MFMA expert path
+  size_t wld, wlu;           // bf16 copies of MXFP4 W_ld / W_lu for the single-pass dense GEMMs
 };
 
 int max_tiles(const moe_desc_t* d) {
@@ -170,10 +171,27 @@ size_t output_partial_bytes(const moe_desc_t* d) {
                      d->T * d->d_model * 4;
   return glu > out ? glu : out;
 }
-void plan_latent(const moe_desc_t* d, Plan& p, LayerWs& w) { w.P = p.take(latent_partial_bytes(d)); }
+// MXFP4 latent maps at batch sizes where their dense GEMM runs in one pass:
+// the weight is decoded once per call (exactly) into a bf16 copy of d_lat x d
+// elements in the workspace, and the bf16 GEMM reads that copy. (The split
+// form at small batches reads the MXFP4 weight itself.)
+bool latent_down_decoded(const moe_desc_t* d) {
+  return d->latent_w_dtype == MOE_MXFP4 && d->T > 0 && latent_split(d).splits == 0;
+}
+bool output_decoded(const moe_desc_t* d) {
+  return d->latent_w_dtype == MOE_MXFP4 && d->T > 0 &&
+         moe::multiseg_slices(d->act_dtype, d->T, d->d_model, d->n_shared + 1) == 0;
+}
+size_t latent_copy_bytes(const moe_desc_t* d) { return (size_t)d->d_latent * d->d_model * 2; }
+
+void plan_latent(const moe_desc_t* d, Plan& p, LayerWs& w) {
+  w.P = p.take(latent_partial_bytes(d));
+  w.wld = p.take(latent_down_decoded(d) ? latent_copy_bytes(d) : 0);
+}
 void plan_output(const moe_desc_t* d, Plan& p, LayerWs& w) {
   w.Hs = p.take((size_t)d->T * d->n_shared * d->d_ff_shared * elem_bytes(d->act_dtype));
   w.P = p.take(output_partial_bytes(d));
+  w.wlu = p.take(output_decoded(d) ? latent_copy_bytes(d) : 0);
 }
 
 Plan plan_layer(const moe_desc_t* d, LayerWs& w) {
@@ -195,6 +213,8 @@ Plan plan_layer(const moe_desc_t* d, LayerWs& w) {
   // one partial buffer serves latent down, shared gate/up and the output GEMM (in turn)
   const size_t lp = latent_partial_bytes(d), op = output_partial_bytes(d);
   w.P = p.take(lp > op ? lp : op);
+  w.wld = p.take(latent_down_decoded(d) ? latent_copy_bytes(d) : 0);
+  w.wlu = p.take(output_decoded(d) ? latent_copy_bytes(d) : 0);
   return p;
 }
 
@@ -354,8 +374,16 @@ int do_permute(const moe_desc_t* d, const int32_t* idx, int32_t* counts, int32_t
   return MOE_OK;
 }
 
-int do_latent_down(const moe_desc_t* d, const void* x, moe_w_t w, void* z, float* P, hipStream_t st) {
-  moe::DenseArgs a{x, d->d_model, wop(w, d->latent_w_dtype), d->T, d->d_latent, d->d_model, z,
+// wcopy: workspace for the bf16 copy of an MXFP4 W_ld (used when
+// latent_down_decoded)
+int do_latent_down(const moe_desc_t* d, const void* x, moe_w_t w, void* z, float* P, void* wcopy,
+                   hipStream_t st) {
+  moe::WOperand W = wop(w, d->latent_w_dtype);
+  if (latent_down_decoded(d)) {
+    MOE_LAUNCH(moe::launch_decode_mxfp4(W, d->d_latent, d->d_model, wcopy, st), "latent_down (decode)");
+    W = moe::WOperand{wcopy, nullptr, MOE_BF16};
+  }
+  moe::DenseArgs a{x, d->d_model, W, d->T, d->d_latent, d->d_model, z,
                    d->d_latent, d->act_dtype, latent_split(d), P};
   MOE_LAUNCH(moe::launch_dense(a, st), "latent_down");
   return MOE_OK;
@@ -485,10 +513,17 @@ moe::MultiSegArgs output_args(const moe_desc_t* d, const void* n, const moe_weig
   return m;
 }
 
+// wcopy: workspace for the bf16 copy of an MXFP4 W_up (used when output_decoded)
 int do_output_gemm(const moe_desc_t* d, const void* n, const moe_weights_t* w, void* y,
-                   const void* Hs, float* P, hipStream_t st, Marker mk = {-1}) {
+                   const void* Hs, float* P, void* wcopy, hipStream_t st, Marker mk = {-1}) {
   mk.beg(9, st);
-  MOE_LAUNCH(moe::launch_multiseg(output_args(d, n, w, y, Hs, P), st), "output");
+  moe::MultiSegArgs m = output_args(d, n, w, y, Hs, P);
+  if (output_decoded(d)) {
+    moe::Segment& last = m.seg[m.nseg - 1];
+    MOE_LAUNCH(moe::launch_decode_mxfp4(last.B, d->d_model, d->d_latent, wcopy, st), "output (decode)");
+    last.B = moe::WOperand{wcopy, nullptr, MOE_BF16};
+  }
+  MOE_LAUNCH(moe::launch_multiseg(m, st), "output");
   mk.end(9, st);
   return MOE_OK;
 }
@@ -502,9 +537,9 @@ bool output_split(const moe_desc_t* d) {
 }
 
 int do_output(const moe_desc_t* d, const void* x, const void* n, const moe_weights_t* w, void* y,
-              void* Hs, float* P, hipStream_t st) {
+              void* Hs, float* P, void* wcopy, hipStream_t st) {
   MOE_CHECK(do_shared_glu(d, x, w, Hs, P, st));
-  return do_output_gemm(d, n, w, y, Hs, P, st);
+  return do_output_gemm(d, n, w, y, Hs, P, wcopy, st);
 }
 
 // A second stream per device for the work of moe_layer_forward that does not
@@ -599,7 +634,7 @@ int run_layer(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* 
   }
   // the routing-independent GEMMs (z and the shared experts' H)
   mk.beg(3, side);
-  MOE_CHECK(do_latent_down(d, x, w->lat_down, at(ws, lw.z), (float*)at(ws, lw.P), side));
+  MOE_CHECK(do_latent_down(d, x, w->lat_down, at(ws, lw.z), (float*)at(ws, lw.P), at(ws, lw.wld), side));
   mk.end(3, side);
   MOE_CHECK(do_shared_glu(d, x, w, at(ws, lw.Hs), (float*)at(ws, lw.P), side, mk));
   if (sd != nullptr) MOE_LAUNCH((int)hipEventRecord(sd->join, sd->s), "join");
@@ -632,7 +667,8 @@ int run_layer(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* 
     mk.end(9, st);
     return MOE_OK;
   }
-  MOE_CHECK(do_output_gemm(d, at(ws, lw.n), w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), st, mk));
+  MOE_CHECK(do_output_gemm(d, at(ws, lw.n), w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), at(ws, lw.wlu), st,
+                           mk));
   return MOE_OK;
 }
 
@@ -800,7 +836,7 @@ int moe_latent_down(const moe_desc_t* d, const void* x, moe_w_t lat_down, void* 
   Plan p;
   LayerWs lw{};
   plan_latent(d, p, lw);
-  return do_latent_down(d, x, lat_down, z, (float*)at(ws, lw.P), (hipStream_t)stream);
+  return do_latent_down(d, x, lat_down, z, (float*)at(ws, lw.P), at(ws, lw.wld), (hipStream_t)stream);
 }
 
 int moe_expert_ffn(const moe_desc_t* d, const void* z, const int32_t* perm_src,
@@ -894,7 +930,8 @@ int moe_output(const moe_desc_t* d, const void* x, const void* n, const moe_weig
   Plan p;
   LayerWs lw{};
   plan_output(d, p, lw);
-  return do_output(d, x, n, w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), (hipStream_t)stream);
+  return do_output(d, x, n, w, y, at(ws, lw.Hs), (float*)at(ws, lw.P), at(ws, lw.wlu),
+                   (hipStream_t)stream);
 }
 
 int moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, int64_t ld, uint8_t* codes,

@@ -99,7 +99,12 @@ struct DenseArgs {
   SplitK split;                // plan_split(act_dtype, M, N, K)
   float* P;                    // split.partial_bytes(M, N) bytes when split.splits > 0
 };
+// The split form reads bf16 or MXFP4 W; the single pass (split.splits == 0)
+// bf16 W only (an MXFP4 weight is decoded with launch_decode_mxfp4 first).
 int launch_dense(const DenseArgs& a, hipStream_t stream);
+// out[rows, K] bf16 = the exact values of the row-major MXFP4 weight w
+// (packed [rows, K/2], scales [rows, K/32]; K % 32 == 0).
+int launch_decode_mxfp4(const WOperand& w, int64_t rows, int K, void* out, hipStream_t stream);
 
 // H[M, F] = act(A Wg^T, A Wv^T), Wg/Wv [F, K]. (shared gate/up)
 struct GluArgs {
@@ -112,7 +117,7 @@ struct GluArgs {
   SplitK split;                // plan_split(act_dtype, M, 2 F, K)
   float* P;                    // split.partial_bytes(M, 2 F) bytes when split.splits > 0
 };
-int launch_glu(const GluArgs& a, hipStream_t stream);
+int launch_glu(const GluArgs& a, hipStream_t stream);   // single pass: bf16 Wg, Wv only
 
 // Grouped over experts: rows r in [offsets[e], offsets[e+1]) of expert e.
 // gate/up: A row = z[perm_src[r] / k]; H[r] = act(z Wg[e]^T, z Wv[e]^T).
@@ -211,6 +216,8 @@ struct MultiSegArgs {
   int act_dtype;
   float* P;                    // multiseg_slices(...) * M * N fp32 when that is > 0
 };
+// Only the last segment's B may be MXFP4, and then only in the split form
+// (multiseg_slices(...) > 0); the single pass takes bf16 B in every segment.
 int launch_multiseg(const MultiSegArgs& a, hipStream_t stream);
 // The split form in two parts (only when multiseg_slices(...) > 0): the fp32
 // partial products of segments s0 .. s0 + ns - 1 into P[s] (each segment's

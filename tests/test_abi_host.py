@@ -154,6 +154,22 @@ def test_mxfp8_workspace_holds_no_bf16_h():
     assert abs((w8 - wb) - (mx_copies - rows * F * 2)) <= 4 * 256   # 256-byte sub-buffer rounding
 
 
+def test_mxfp4_latent_maps_get_bf16_copies_where_their_gemms_run_in_one_pass():
+    """With MXFP4 latent maps, a batch whose latent-down and output GEMMs run in
+    one pass (K3 prefill) has room for a bf16 copy of W_ld and one of W_up
+    (d_lat x d bf16 each) beyond the bf16-latent workspace, in the layer and in
+    the two staged entry points; a batch that takes the split form (K3 decode)
+    reads the MXFP4 weights directly and needs no copy."""
+    for name, copies in (("k3_prefill_mxfp4", True), ("k3_decode_mxfp4", False)):
+        mx = synth.config(name)
+        bf = mx.replace(latent_w="bf16")
+        dm, db = moe.make_desc(mx), moe.make_desc(bf)
+        one = mx.d_lat * mx.d * 2 if copies else 0
+        for op, n in ((moe.MOE_OP_LATENT_DOWN, 1), (moe.MOE_OP_OUTPUT, 1), (moe.MOE_OP_LAYER, 2)):
+            extra = moe.moe_workspace_bytes(dm, op) - moe.moe_workspace_bytes(db, op)
+            assert extra == n * one, (name, op, extra)
+
+
 FAKE = 0x7f0000001000          # a 16-byte-aligned address that is never dereferenced
 MIS = FAKE + 4                 # misaligned
 

@@ -24,6 +24,11 @@ SMALL_MX = SMALL_BF16.replace(name="small_mxfp4", expert_w="mxfp4", latent_w="mx
 MID_BF16 = LayerConfig("mid_bf16", T=700, d=320, d_lat=192, E=6, k=2, F=224, S=1, Fs=160, seed=13,
                        bias=("uniform", 0.05))
 MID_MX = MID_BF16.replace(name="mid_mxfp4", expert_w="mxfp4", latent_w="mxfp4", seed=14)
+# a batch whose latent-down and output GEMMs run in one pass (at least 256
+# tiles of 256 x 256), so the MXFP4 latent maps go through their bf16 copies;
+# ragged in M, N and K
+WIDE_MX = LayerConfig("wide_mxfp4", T=16300, d=1056, d_lat=992, E=8, k=2, F=256, S=1, Fs=288, seed=15,
+                      bias=("uniform", 0.05), expert_w="mxfp4", latent_w="mxfp4")
 
 
 # ---------------------------------------------------------------------------
@@ -255,11 +260,12 @@ def test_staged_entry_points_equal_layer(device):
     assert np.abs(u.cpu().numpy() - u_ref).max() <= 2e-2 * np.sqrt((u_ref ** 2).mean())
 
 
-@pytest.mark.parametrize("cfg", [SMALL_MX, MID_MX], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [SMALL_MX, MID_MX, WIDE_MX], ids=lambda c: c.name)
 def test_mxfp4_path_equals_bf16_path_on_decoded_weights(cfg, device):
     """MXFP4 decoding is exact: the MXFP4 layer must equal, bit for bit, the bf16
-    layer run on the decoded weights (same kernels, same accumulation order).
-    The small layer has one row tile per expert, the mid one several, ragged."""
+    layer run on the decoded weights (same accumulation order). The small layer
+    has one row tile per expert, the mid one several, ragged; in the wide one
+    the latent maps are decoded to bf16 copies for single-pass dense GEMMs."""
     inp = synth.device_inputs(cfg, device)
     y_mx, _, _, _ = run_layer(cfg, inp, device)
     dec = dict(inp)
