@@ -171,7 +171,11 @@ typedef struct {
 } moe_weights_t;
 
 /* Bytes of workspace that entry point `op` needs for this descriptor
-   (0 for an invalid descriptor; check moe_check_desc first). */
+   (0 for an invalid descriptor; check moe_check_desc first). With MXFP4
+   latent maps and a batch whose latent-down / output GEMM runs in one pass
+   (at least 256 tiles of 256 x 256), the latent-down, output and layer
+   workspaces include a bf16 copy of W_ld / W_up (d_lat x d x 2 bytes each),
+   decoded exactly from the MXFP4 weight on every call. */
 size_t moe_workspace_bytes(const moe_desc_t* desc, int op);
 
 /* Host-only validation of a descriptor: MOE_OK, MOE_ERR_INVALID_ARG or

@@ -224,8 +224,12 @@ def test_layer_empty_batch(cfg, device):
     assert counts.cpu().numpy().tolist() == [0] * cfg.E
 
 
-def test_staged_entry_points_equal_layer(device):
-    cfg = MID_BF16
+@pytest.mark.parametrize("cfg", [MID_BF16, WIDE_MX], ids=lambda c: c.name)
+def test_staged_entry_points_equal_layer(cfg, device):
+    """The staged entry points, each on its own workspace, give the layer's
+    routing and output bit for bit (the wide MXFP4 layer: with the latent maps
+    decoded to bf16 copies in the latent-down and output workspaces); the mid
+    layer's z and u also against the oracle."""
     inp = synth.device_inputs(cfg, device)
     y_layer, idx_l, gate_l, _ = run_layer(cfg, inp, device)
     desc = moe.make_desc(cfg)
@@ -252,6 +256,8 @@ def test_staged_entry_points_equal_layer(device):
     torch.cuda.synchronize()
     assert torch.equal(idx, idx_l) and torch.equal(gate, gate_l)
     assert torch.equal(y, y_layer)
+    if cfg.T > 1000:
+        return
     # intermediates against the oracle
     y_ref, inter = oracle.forward(cfg, synth.HostWeights(cfg), keep=True)
     z_ref = inter["z"]
