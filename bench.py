@@ -150,9 +150,10 @@ PROBE_LIB = os.path.join(ROOT, "sparse_mixture_experts_sigmoid_amd", "libmoe_pro
 
 
 def measure_ceilings(stream):
-    """Measured ceilings of this GPU (libmoe_probe.so): back-to-back bf16 and
-    MXFP8 x MXFP4 matrix-core instructions with no memory traffic, and a plain
-    streaming read of a 4 GB buffer (16x the 256 MB last-level cache)."""
+    """Measured ceilings of this GPU (libmoe_probe.so): back-to-back bf16
+    (32x32x16 and 16x16x32) and MXFP8 x MXFP4 matrix-core instructions with no
+    memory traffic, on fixed and on changing operands, and a plain streaming
+    read of a 4 GB buffer (16x the 256 MB last-level cache)."""
     import ctypes
     import torch
     L = ctypes.CDLL(PROBE_LIB)
@@ -180,7 +181,8 @@ def measure_ceilings(stream):
     out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda:0")
     res = {}
     for kind, key in ((0, "mfma_bf16_tflops"), (1, "mfma_fp8xfp4_tflops"), (2, "mfma_bf16_changing_data_tflops"),
-                      (3, "mfma_fp8xfp4_changing_data_tflops")):
+                      (3, "mfma_fp8xfp4_changing_data_tflops"), (4, "mfma_bf16_16x16x32_tflops"),
+                      (5, "mfma_bf16_16x16x32_changing_data_tflops")):
         def launch(kind=kind):
             if L.moe_probe_mfma(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()), sh) != 0:
                 raise RuntimeError("moe_probe_mfma failed")
@@ -298,7 +300,10 @@ def run_workload(name, args, ceilings, cpu_seconds):
         achieved = algo / t_gu / 1e12
         f32 = cfg.act == "f32"
         peak = MFMA_FP8_PEAK_TFLOPS if mx8 else VALU_FP32_PEAK_TFLOPS if f32 else MFMA_BF16_PEAK_TFLOPS
-        meas = None if f32 else ceilings.get("mfma_fp8xfp4_tflops" if mx8 else "mfma_bf16_tflops")
+        # the best rate the matrix cores reach alone on this GPU (bf16: either instruction shape)
+        meas = (None if f32 else ceilings.get("mfma_fp8xfp4_tflops") if mx8 else
+                max((v for v in (ceilings.get("mfma_bf16_tflops"), ceilings.get("mfma_bf16_16x16x32_tflops"))
+                     if v), default=None))
         roof = {"bound": "alu" if f32 else "mfma",
                 "kernel": gu_name,
                 "achieved": round(achieved, 1), "peak": peak, "unit": "TFLOP/s",

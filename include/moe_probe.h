@@ -21,8 +21,9 @@ extern "C" {
    accumulators. kind 0: v_mfma_f32_32x32x16_bf16 on fixed operands; kind 1:
    v_mfma_scale_f32_32x32x64_f8f6f4 with E4M3 x E2M1 operands (the scaled-MFMA
    expert path); kinds 2 and 3: the same two instructions on pseudo-random
-   operands that change at every instruction, as in a real GEMM (iters a
-   multiple of 4). out: one float per wave (blocks * 4), written so the work is live; its
+   operands that change at every instruction, as in a real GEMM; kinds 4 and
+   5: v_mfma_f32_16x16x32_bf16 (8 independent accumulators) on fixed and on
+   changing operands (iters a multiple of 4 for kinds 2 to 5). out: one float per wave (blocks * 4), written so the work is live; its
    values mean nothing. */
 int moe_probe_mfma(int kind, int blocks, int iters, float* out, void* stream);
 

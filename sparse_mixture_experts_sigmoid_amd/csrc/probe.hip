@@ -11,6 +11,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kChains = 4;   // independent accumulators per wave (waves per SIMD give the rest)
@@ -158,24 +159,58 @@ __global__ __launch_bounds__(256) void mfma_f8f4_data_kernel(int iters, float* o
   if ((threadIdx.x & 63) == 0) out[blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64] = s;
 }
 
+// v_mfma_f32_16x16x32_bf16 (the same FLOP rate per clock as 32x32x16 on paper,
+// half the FLOP per instruction), 8 independent accumulators per wave: fixed
+// operands (DATA = false) or the changing ones of mfma_bf16_data_kernel.
+template <bool DATA>
+__global__ __launch_bounds__(256) void mfma_bf16_16_kernel(int iters, float* out) {
+  bf16x8 a[4], b[4];
+  for (int u = 0; u < 4; ++u)
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t ha = probe_hash(threadIdx.x * 64u + u * 8u + i + 1u);
+      const uint32_t hb = probe_hash(threadIdx.x * 64u + u * 8u + i + 0x9e3779b9u);
+      a[u][i] = DATA ? (__bf16)((float)(ha & 0xFFFFu) * (4.0f / 65536.0f) - 2.0f) : (__bf16)(float)((threadIdx.x + i) & 7);
+      b[u][i] = DATA ? (__bf16)((float)(hb & 0xFFFFu) * (4.0f / 65536.0f) - 2.0f) : (__bf16)(float)((threadIdx.x * 3 + i) & 7);
+    }
+  f32x4 acc[2 * kChains];
+  for (int c = 0; c < 2 * kChains; ++c)
+    for (int r = 0; r < 4; ++r) acc[c][r] = 0.0f;
+  for (int it = 0; it < iters; it += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int c = 0; c < 2 * kChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[(u + c) & 3], b[(u + 2 * c + (c >> 1)) & 3], acc[c], 0, 0, 0);
+  }
+  float s = 0.0f;
+  for (int c = 0; c < 2 * kChains; ++c)
+    for (int r = 0; r < 4; ++r) s += acc[c][r];
+  if ((threadIdx.x & 63) == 0) out[blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64] = s;
+}
+
 }  // namespace
 
 extern "C" {
 
 int moe_probe_mfma(int kind, int blocks, int iters, float* out, void* stream) {
-  if (blocks <= 0 || iters <= 0 || out == nullptr || kind < 0 || kind > 3 || (kind >= 2 && iters % 4)) return -1;
+  if (blocks <= 0 || iters <= 0 || out == nullptr || kind < 0 || kind > 5 || (kind >= 2 && iters % 4)) return -1;
   if (kind == 0)
     hipLaunchKernelGGL(mfma_bf16_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
   else if (kind == 1)
     hipLaunchKernelGGL(mfma_f8f4_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
   else if (kind == 2)
     hipLaunchKernelGGL(mfma_bf16_data_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
-  else
+  else if (kind == 3)
     hipLaunchKernelGGL(mfma_f8f4_data_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
+  else if (kind == 4)
+    hipLaunchKernelGGL(mfma_bf16_16_kernel<false>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
+  else
+    hipLaunchKernelGGL(mfma_bf16_16_kernel<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, iters, out);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
 double moe_probe_mfma_flops(int kind, int blocks, int iters) {
+  if (kind >= 4) return 2.0 * 16 * 16 * 32 * (2 * kChains) * 4.0 * blocks * (double)iters;
   const double per = (kind == 1 || kind == 3) ? 2.0 * 32 * 32 * 64 : 2.0 * 32 * 32 * 16;
   return per * kChains * 4.0 * blocks * (double)iters;   // 4 waves per block
 }

@@ -47,7 +47,10 @@ def test_probe_library_exports_and_validates():
     L.moe_probe_mfma_flops.restype = ctypes.c_double
     L.moe_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_void_p]
-    assert L.moe_probe_mfma(4, 1, 4, FAKE, None) == -1
+    assert L.moe_probe_mfma(6, 1, 4, FAKE, None) == -1
+    assert L.moe_probe_mfma(-1, 1, 4, FAKE, None) == -1
+    assert L.moe_probe_mfma(5, 1, 6, FAKE, None) == -1
+    assert L.moe_probe_mfma(4, 1, 6, FAKE, None) == -1
     assert L.moe_probe_mfma(3, 1, 6, FAKE, None) == -1
     assert L.moe_probe_mfma(2, 1, 6, FAKE, None) == -1      # changing operands: iters % 4 == 0
     assert L.moe_probe_mfma(0, 0, 1, FAKE, None) == -1
@@ -58,6 +61,7 @@ def test_probe_library_exports_and_validates():
     assert L.moe_probe_hbm_read(FAKE, 32, 1, 0x408, FAKE, None) == -1
     assert L.moe_probe_mfma_flops(0, 1, 1) == 4 * 4 * 2 * 32 * 32 * 16
     assert L.moe_probe_mfma_flops(1, 2, 3) == 2 * 3 * 4 * 4 * 2 * 32 * 32 * 64
+    assert L.moe_probe_mfma_flops(5, 1, 1) == 4 * 8 * 2 * 16 * 16 * 32   # 8 accumulators per wave
 
 
 def test_status_strings():
