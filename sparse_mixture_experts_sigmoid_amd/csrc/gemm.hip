@@ -1184,7 +1184,6 @@ __global__ __launch_bounds__(SplitCfg::NT) void dense_split_kernel(DenseArgs a) 
   store_partial(acc, a.P + (int64_t)sp * a.M * a.N, a.N, m0, n0, a.M, a.N);
 }
 
-template <bool B_MX>
 __global__ __launch_bounds__(SplitCfg::NT) void glu_split_kernel(GluArgs a) {
   using C = SplitCfg;
   MOE_LDS_RING(C);
@@ -1197,13 +1196,10 @@ __global__ __launch_bounds__(SplitCfg::NT) void glu_split_kernel(GluArgs a) {
   const int kb = sp * a.split.kchunk, klen = min(a.K - kb, a.split.kchunk);
   const WOperand Wg = shift_k(a.Wg, kb), Wv = shift_k(a.Wv, kb);
   const Rows<C::AR> ar = a_rows_dense<C, C::AR>((const bf16_t*)a.A + kb, a.lda, m0, a.M);
-  Rows<C::BR> br{};
-  MxRows<C::MXU> bm{};
-  if constexpr (B_MX) bm = b_mx_glu<C>(Wg, Wv, 0, a.K, f0, a.F);
-  else br = b_rows_glu<C>(Wg, Wv, 0, a.K, f0, a.F);
+  const Rows<C::BR> br = b_rows_glu<C>(Wg, Wv, 0, a.K, f0, a.F);
   Acc<C> acc;
   acc_zero(acc);
-  mainloop<C, B_MX>(MOE_RING, ar, br, bm, klen, acc);
+  mainloop<C, false>(MOE_RING, ar, br, MxRows<C::MXU>{}, klen, acc);
   store_partial_glu(acc, a.P + (int64_t)sp * a.M * 2 * a.F, a.F, f0, m0, a.M);
 }
 
@@ -2434,17 +2430,16 @@ int launch_dense(const DenseArgs& a, hipStream_t stream) {
 int launch_glu(const GluArgs& a, hipStream_t stream) {
   if (a.act_dtype == DT_F32) return launch_glu_f32(a, stream);
   if (a.M == 0) return 0;
+  if (a.Wg.dtype != DT_BF16 || a.Wv.dtype != DT_BF16) return -1;   // the shared experts are bf16
   if (a.split.splits > 0) {
     using C = SplitCfg;
     dim3 grid((unsigned)xcd_grid(ceil_div(a.F, C::BN / 2) * ceil_div(a.M, C::BM) * a.split.splits));
-    if (a.Wg.dtype == DT_MXFP4) hipLaunchKernelGGL(glu_split_kernel<true>, grid, dim3(SplitCfg::NT), 0, stream, a);
-    else hipLaunchKernelGGL(glu_split_kernel<false>, grid, dim3(SplitCfg::NT), 0, stream, a);
+    hipLaunchKernelGGL(glu_split_kernel, grid, dim3(SplitCfg::NT), 0, stream, a);
     const int64_t n4 = (int64_t)a.M * a.F / 4;
     hipLaunchKernelGGL(reduce_glu_kernel, dim3(reduce_blocks(n4)), dim3(256), 0, stream, a.P,
                        a.split.splits, a.M, a.F, a.c, (bf16_t*)a.H, a.ldh);
     return (int)hipGetLastError();
   }
-  if (a.Wg.dtype != DT_BF16 || a.Wv.dtype != DT_BF16) return -1;
   using C = DenseCfg;
   dim3 grid((unsigned)xcd_grid(ceil_div(a.F, C::BN / 2) * ceil_div(a.M, C::BM)));
   hipLaunchKernelGGL(glu_kernel, grid, dim3(DenseCfg::NT), 0, stream, a);

@@ -117,7 +117,7 @@ struct GluArgs {
   SplitK split;                // plan_split(act_dtype, M, 2 F, K)
   float* P;                    // split.partial_bytes(M, 2 F) bytes when split.splits > 0
 };
-int launch_glu(const GluArgs& a, hipStream_t stream);   // single pass: bf16 Wg, Wv only
+int launch_glu(const GluArgs& a, hipStream_t stream);   // bf16 Wg, Wv only
 
 // Grouped over experts: rows r in [offsets[e], offsets[e+1]) of expert e.
 // gate/up: A row = z[perm_src[r] / k]; H[r] = act(z Wg[e]^T, z Wv[e]^T).
