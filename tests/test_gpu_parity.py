@@ -284,6 +284,36 @@ def test_mxfp4_path_equals_bf16_path_on_decoded_weights(cfg, device):
     assert torch.equal(y_mx, y_b)
 
 
+def test_latent_down_mxfp4_copy_is_exact_for_every_code_and_scale(device):
+    """The single-pass latent down of a large batch reads an MXFP4 W_ld through
+    its bf16 copy, decoded in the call: for every E2M1 code and every scale byte
+    0..200 (scale 2^-127 .. 2^73) z equals, bit for bit, the same GEMM on the
+    oracle's decoding of the weight (an OCP E2M1 value times its e8m0 scale is
+    exact in bf16 down to 2^-128)."""
+    cfg = LayerConfig("latent_mx", T=16384, d=256, d_lat=1024, E=4, k=1, F=64, S=0, Fs=64, seed=21,
+                      bias=("uniform", 0.05), expert_w="mxfp4", latent_w="mxfp4")
+    cfg_b = cfg.replace(latent_w="bf16")
+    desc, desc_b = moe.make_desc(cfg), moe.make_desc(cfg_b)
+    # the copy is in use: its d_lat x d bf16 elements are in the workspace
+    ws_extra = (moe.moe_workspace_bytes(desc, moe.MOE_OP_LATENT_DOWN) -
+                moe.moe_workspace_bytes(desc_b, moe.MOE_OP_LATENT_DOWN))
+    assert ws_extra == cfg.d_lat * cfg.d * 2
+    g = torch.Generator().manual_seed(21)
+    x = torch.randn((cfg.T, cfg.d), generator=g).to(torch.bfloat16).to(device)
+    packed = torch.randint(0, 256, (cfg.d_lat, cfg.d // 2), generator=g, dtype=torch.int32).to(torch.uint8)
+    scales = (torch.arange(cfg.d_lat * (cfg.d // 32)) % 201).to(torch.uint8).reshape(cfg.d_lat, cfg.d // 32)
+    w_b = torch.from_numpy(oracle.widen(("mxfp4", (packed.numpy(), scales.numpy())))).to(torch.bfloat16)
+    assert torch.equal(w_b.float(), torch.from_numpy(oracle.widen(("mxfp4", (packed.numpy(), scales.numpy())))))
+    z_mx = torch.empty((cfg.T, cfg.d_lat), dtype=torch.bfloat16, device=device)
+    z_b = torch.empty_like(z_mx)
+    moe.moe_latent_down(desc, x, (packed.to(device), scales.to(device)), z_mx,
+                        moe.workspace(desc, moe.MOE_OP_LATENT_DOWN, device))
+    moe.moe_latent_down(desc_b, x, w_b.to(device), z_b, moe.workspace(desc_b, moe.MOE_OP_LATENT_DOWN, device))
+    torch.cuda.synchronize()
+    assert torch.isfinite(z_b.float()).all()
+    assert torch.equal(z_mx, z_b)
+
+
 def test_k3_decode_parity_and_determinism(device):
     cfg = synth.config("k3_decode")
     say("k3_decode: generating inputs on the GPU")
