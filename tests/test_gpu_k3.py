@@ -79,3 +79,26 @@ def test_k3_full_size(name, n_sample, device):
     y_st, idx_st = staged_on_z(cfg, inp, inp["x"][tk].contiguous(), z_ref, device)
     assert np.array_equal(idx_st.cpu().numpy(), ref["idx"][toks])
     check_y(cfg, to64(y_st), y_ref, " (sampled tokens, staged on the oracle's z)")
+
+
+@pytest.mark.parametrize("T,n_sample", [(1, 1), (5, 5), (3000, 256), (5000, 256)])
+def test_k3_batch_sizes_between_the_workloads(T, n_sample, device):
+    """The K3 bf16 layer at batch sizes between and below the benchmarked ones,
+    where the launch choices switch: one and five tokens (split-K dense GEMMs,
+    128-row expert tiles, the recheck with rows in registers), 3000 tokens
+    (split latent down, single-pass output GEMM: no early shared partials) and
+    5000 (every dense GEMM in one pass, 320-row expert tiles). Routing of every
+    token bit for bit; outputs on every token or a seeded sample incl. the
+    hottest and the coldest expert's."""
+    cfg = synth.config("k3_decode").replace(name=f"k3_T{T}", T=T, seed=40 + T % 7)
+    inp = synth.device_inputs(cfg, device)
+    y, idx, gate, counts = run_layer(cfg, inp, device)
+    w = synth.HostWeights(cfg)
+    ref = oracle.route_layer(cfg, w)
+    idx_np = idx.cpu().numpy()
+    assert np.array_equal(idx_np, ref["idx"]), "expert indices differ"
+    assert np.array_equal(gate.cpu().numpy(), ref["p"]), "gates differ"
+    assert np.array_equal(counts.cpu().numpy(), np.bincount(ref["idx"].ravel(), minlength=cfg.E))
+    toks = sample_tokens(cfg, idx_np, n_sample) if n_sample < T else np.arange(T)
+    y_ref = oracle.forward(cfg, w, tokens=toks, routing={"idx": ref["idx"][toks], "p": ref["p"][toks]})
+    check_y(cfg, to64(y)[toks], y_ref, f" (T = {T}, {len(toks)} tokens)")
