@@ -81,16 +81,19 @@ def test_k3_full_size(name, n_sample, device):
     check_y(cfg, to64(y_st), y_ref, " (sampled tokens, staged on the oracle's z)")
 
 
-@pytest.mark.parametrize("T,n_sample", [(1, 1), (5, 5), (3000, 256), (5000, 256)])
-def test_k3_batch_sizes_between_the_workloads(T, n_sample, device):
+@pytest.mark.parametrize("base,T,n_sample", [("k3_decode", 1, 1), ("k3_decode", 5, 5), ("k3_decode", 3000, 256),
+                                              ("k3_decode", 5000, 256), ("k3_prefill_mxfp4", 3000, 256)])
+def test_k3_batch_sizes_between_the_workloads(base, T, n_sample, device):
     """The K3 bf16 layer at batch sizes between and below the benchmarked ones,
     where the launch choices switch: one and five tokens (split-K dense GEMMs,
     128-row expert tiles, the recheck with rows in registers), 3000 tokens
     (split latent down, single-pass output GEMM: no early shared partials) and
-    5000 (every dense GEMM in one pass, 320-row expert tiles). Routing of every
-    token bit for bit; outputs on every token or a seeded sample incl. the
-    hottest and the coldest expert's."""
-    cfg = synth.config("k3_decode").replace(name=f"k3_T{T}", T=T, seed=40 + T % 7)
+    5000 (every dense GEMM in one pass, 320-row expert tiles); and the MXFP4
+    layer at 3000 tokens (latent down reading MXFP4 in split form, output GEMM
+    on the per-call bf16 copy of W_up). Routing of every token bit for bit;
+    outputs on every token or a seeded sample incl. the hottest and the
+    coldest expert's."""
+    cfg = synth.config(base).replace(name=f"{base}_T{T}", T=T, seed=40 + T % 7)
     inp = synth.device_inputs(cfg, device)
     y, idx, gate, counts = run_layer(cfg, inp, device)
     w = synth.HostWeights(cfg)
